@@ -1,0 +1,409 @@
+/*
+ * nvfp4_oracle.c -- plain, slow, scalar CPU oracle for the NVFP4 block-scaled
+ * quantize / dequantize / qmv / qqmm / gather_qmm path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file: only the tests, the package smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * generator with the HIP kernels.
+ *
+ * Pages cited (titles as published):
+ *   [DIFF-8]  "mlx 0.30.7.2 -> 0.30.7.6" source diff, page 8 (my.diffend.io):
+ *             ops.cpp hunks fp_quantize / fp_dequantize / validate_global_scale
+ *             / qqmm, primitives.cpp hunk QQMatmul::vjp.
+ *   [DIFF-7]  same diff, page 7: fp_quantize.cu hunks (fp_quantize_dequantize,
+ *             fp_quantize_rowwise, fp_dequantize), qqmm.cpp (QQMatmul::eval_gpu).
+ *   [PR4458]  "[Metal] global scale for qmm" (ml-explore/mlx pull request 4458):
+ *             statement and "Example" section.
+ *   [PR31]    osaurus-ai/mlx pull request 31 (CPU qqmm ignores nvfp4 global
+ *             scales): sections "What fails", "The test", "The fix",
+ *             "Verification".
+ *
+ * Arithmetic rules (each restated where it is used):
+ *   - every step the pages perform in float32 is done here in float32 with
+ *     IEEE round-to-nearest-even; the build uses -ffp-contract=off and no
+ *     fast-math, and x86-64 SSE evaluates float expressions in float;
+ *   - the e2m1 and e4m3 encoders are written as "nearest representable value,
+ *     ties to the even code, saturating", by exhaustive search over the code
+ *     set (no bit tricks), which is the format definition itself;
+ *   - rounding to bfloat16 / float16 is IEEE round-to-nearest-even with
+ *     overflow to infinity, written from the definition in double arithmetic;
+ *   - the matrix products accumulate in double, which is exact enough that
+ *     the only rounding that matters is the final one to the output type.
+ *
+ * Readings where the pages leave a step open (also listed in the design notes):
+ *   R1  nibble order: element 2j is the low nibble of byte j.
+ *   R2  a value that rounds to zero keeps its sign: -0 encodes to code 0x8.
+ *   R3  a block whose e4m3 scale is 0 gets encode factor 0, so its codes are
+ *       +-0 and it decodes to +-0 ([PR31] "The fix": "0 when s is 0").
+ *   R4  encode order of the CUDA rowwise kernel ([DIFF-7] fp_quantize_rowwise):
+ *       sd = (amax/6)*enc, enc_b = enc/sf, q = e2m1(x*enc_b), all in float32.
+ *   R5  e2m1 and e4m3 conversions round to nearest even and saturate.
+ *   R6  decode factor is g/2688 everywhere ([DIFF-8] fp_dequantize fallback).
+ *   R7  the global decode factor multiplies the block scale, not the sum
+ *       ([PR4458] statement; [PR31] "The fix").
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+
+/* Test-only switches that plant a known mistake (see orc_set_mutant). */
+#define MUT_NONE 0
+#define MUT_DROP_GW 1        /* (i)   decode of w ignores g_w                    */
+#define MUT_DROP_GX 2        /* (ii)  round trip of x ignores g_x                */
+#define MUT_GW_ON_SUM 3      /* (iii) g_w/2688 applied to a T-precision sum      */
+#define MUT_AMAX6_BF16 4     /* (iv)  amax/6 rounded to bfloat16 before * enc    */
+#define MUT_ENC_ORDER 5      /* (v)   q = e2m1((x*enc)/sf) instead of x*(enc/sf) */
+
+static int g_mutant = MUT_NONE;
+
+void orc_set_mutant(int m) { g_mutant = m; }
+int orc_get_mutant(void) { return g_mutant; }
+
+/* ------------------------------------------------------------------------ */
+/* Formats                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* e2m1 (OCP Microscaling v1.0 FP4): bit 3 sign, bits 2..1 exponent (bias 1),
+ * bit 0 mantissa; exponent 0 is subnormal with step 0.5.  No inf, no NaN. */
+double orc_e2m1_value(unsigned code) {
+  unsigned e = (code >> 1) & 3u, m = code & 1u;
+  double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+  return (code & 8u) ? -mag : mag;
+}
+
+/* Nearest e2m1 value to v, ties to the even code (mantissa bit 0), magnitudes
+ * above the largest finite value 6 saturate to 6.  The sign bit of v is kept,
+ * including for results of magnitude 0 (reading R2). */
+unsigned orc_e2m1_encode(float v) {
+  double a = fabs((double)v);
+  unsigned best = 7;
+  if (!(a > 6.0)) {
+    double bestd = INFINITY;
+    for (unsigned c = 0; c < 8; ++c) {
+      double d = fabs(a - orc_e2m1_value(c));
+      if (d < bestd || (d == bestd && (c & 1u) == 0)) {
+        best = c;
+        bestd = d;
+      }
+    }
+  }
+  return best | (signbit(v) ? 8u : 0u);
+}
+
+/* e4m3 (OCP 8-bit floating point, "E4M3FN"): bit 7 sign, bits 6..3 exponent
+ * (bias 7), bits 2..0 mantissa; exponent 0 is subnormal (m/8 * 2^-6);
+ * S.1111.111 is NaN; the largest finite value is 448 = 0x7E. */
+double orc_e4m3_value(unsigned b) {
+  unsigned e = (b >> 3) & 15u, m = b & 7u;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+  return (b & 0x80u) ? -mag : mag;
+}
+
+/* Nearest finite e4m3 value to v, ties to the even byte, saturating at 448
+ * ([DIFF-7] F8E4M3_MAX = 448; reading R5).  Exhaustive over the 127 finite
+ * non-negative bytes. */
+unsigned orc_e4m3_encode(float v) {
+  double a = fabs((double)v);
+  unsigned sign = signbit(v) ? 0x80u : 0u;
+  unsigned best = 0x7E;
+  if (!(a >= 448.0)) {
+    double bestd = INFINITY;
+    for (unsigned b = 0; b <= 0x7E; ++b) {
+      double d = fabs(a - orc_e4m3_value(b));
+      if (d < bestd || (d == bestd && (b & 1u) == 0)) {
+        best = b;
+        bestd = d;
+      }
+    }
+  }
+  return best | sign;
+}
+
+/* Round a double to an IEEE binary format with p fraction bits, minimum normal
+ * exponent emin and maximum exponent emax: round to nearest, ties to even,
+ * gradual underflow, overflow to infinity. */
+double orc_round_ieee(double v, int p, int emin, int emax) {
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  double a = fabs(v);
+  int e;
+  (void)frexp(a, &e); /* a = f * 2^e with f in [0.5, 1) */
+  e -= 1;             /* a = f' * 2^e with f' in [1, 2) */
+  if (e < emin) e = emin;
+  double ulp = ldexp(1.0, e - p);
+  double r = nearbyint(a / ulp) * ulp; /* a/ulp is exact; nearbyint is RNE */
+  double maxv = ldexp(2.0 - ldexp(1.0, -p), emax);
+  if (r > maxv) r = INFINITY;
+  return copysign(r, v);
+}
+
+/* Value of v after storing it in the element type T (float32, float16 or
+ * bfloat16); the result is exactly representable in float. */
+float orc_round_to(float v, int dtype) {
+  switch (dtype) {
+    case ORC_F16: return (float)orc_round_ieee((double)v, 10, -14, 15);
+    case ORC_BF16: return (float)orc_round_ieee((double)v, 7, -126, 127);
+    default: return v;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scalars                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Tensor amax as float32: max |x| over all elements ([DIFF-8] QQMatmul::vjp
+ * takes the cotangent's max(abs(.)) as float32).  Exact. */
+float orc_tensor_amax(const float* x, int64_t n) {
+  float m = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    if (a > m) m = a;
+  }
+  return m;
+}
+
+/* Global encode factor 2688/g and decode factor g/2688, each one float32
+ * division; both 1 without a global scale ([DIFF-7] fp_quantize_rowwise,
+ * fp_dequantize; [DIFF-8] fp_dequantize fallback; reading R6). */
+static float global_enc(int has_g, float g) {
+  volatile float c = 448.0f * 6.0f;
+  return has_g ? c / g : 1.0f;
+}
+static float global_dec(int has_g, float g) {
+  volatile float c = 448.0f * 6.0f;
+  return has_g ? g / c : 1.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block encode / decode                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Encode one group of 16 contiguous values ([DIFF-7] fp_quantize_rowwise:
+ * block amax, decode scale (amax/6)*enc stored as e4m3, encode factor
+ * enc/float(s), each element converted to e2m1 after multiplying by it;
+ * readings R2-R5).  Writes 16 codes and returns the scale byte. */
+static unsigned encode_group(const float* xb, float enc, unsigned char* q) {
+  float amax = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    float a = fabsf(xb[i]);
+    if (a > amax) amax = a;
+  }
+  float sd;
+  if (g_mutant == MUT_AMAX6_BF16) {
+    /* the op-level fallback divides in the input dtype (bfloat16 here) */
+    float t = orc_round_to(amax / 6.0f, ORC_BF16);
+    sd = t * enc;
+  } else {
+    volatile float t = amax / 6.0f;
+    sd = t * enc;
+  }
+  unsigned s = orc_e4m3_encode(sd);
+  float sf = (float)orc_e4m3_value(s);
+  float enc_b = (sf == 0.0f) ? 0.0f : enc / sf; /* reading R3 */
+  for (int i = 0; i < 16; ++i) {
+    float y;
+    if (g_mutant == MUT_ENC_ORDER) {
+      volatile float t = xb[i] * enc;
+      y = (sf == 0.0f) ? t * 0.0f : t / sf;
+    } else {
+      y = xb[i] * enc_b;
+    }
+    q[i] = (unsigned char)orc_e2m1_encode(y);
+  }
+  return s;
+}
+
+/* quantize: x [rows, k] (k % 16 == 0) -> codes [rows, k/2] (element 2j in the
+ * low nibble of byte j, reading R1) and e4m3 scales [rows, k/16]
+ * ([DIFF-8] fp_quantize; [DIFF-7] fp_quantize_rowwise). */
+void orc_quantize(const float* x, int64_t rows, int64_t k, int has_g, float g,
+                  uint8_t* codes, uint8_t* scales) {
+  float enc = global_enc(has_g, g);
+  unsigned char q[16];
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < k / 16; ++b) {
+      unsigned s = encode_group(x + r * k + b * 16, enc, q);
+      scales[r * (k / 16) + b] = (uint8_t)s;
+      for (int j = 0; j < 8; ++j)
+        codes[r * (k / 2) + b * 8 + j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+    }
+  }
+}
+
+static unsigned code_at(const uint8_t* codes_row, int64_t i) {
+  uint8_t byte = codes_row[i >> 1];
+  return (i & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+}
+
+/* Effective decode scale of one block: float(e4m3(s)) * (g/2688) in float32,
+ * the global factor on the block scale ([DIFF-7] fp_dequantize; [DIFF-8]
+ * fp_dequantize fallback; [PR31] "The fix"; reading R7). */
+static float block_scale(unsigned s, float dec) {
+  float sf = (float)orc_e4m3_value(s);
+  return sf * dec;
+}
+
+/* dequantize: codes/scales [rows, k] -> T values, x_hat = T(e2m1(q) * scale),
+ * where scale = float(e4m3(s)) * g/2688 ([DIFF-7] fp_dequantize). */
+void orc_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                    int has_g, float g, int out_dtype, float* out) {
+  float dec = global_dec(has_g, g);
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* cr = codes + r * (k / 2);
+    for (int64_t i = 0; i < k; ++i) {
+      float sc = block_scale(scales[r * (k / 16) + i / 16], dec);
+      float v = (float)orc_e2m1_value(code_at(cr, i)) * sc;
+      out[r * k + i] = orc_round_to(v, out_dtype);
+    }
+  }
+}
+
+/* quant_dequant: quantize then dequantize with the same g, result in x's type
+ * ([DIFF-7] fp_quantize_dequantize; [PR31] "The fix": x_hat = s*q/scale_enc,
+ * 0 when s is 0). */
+void orc_quant_dequant(const float* x, int64_t rows, int64_t k, int has_g, float g,
+                       int dtype, float* xhat) {
+  float dec = global_dec(has_g, g);
+  float enc = global_enc(has_g, g);
+  unsigned char q[16];
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < k / 16; ++b) {
+      unsigned s = encode_group(x + r * k + b * 16, enc, q);
+      float sc = block_scale(s, dec);
+      for (int i = 0; i < 16; ++i)
+        xhat[r * k + b * 16 + i] = orc_round_to((float)orc_e2m1_value(q[i]) * sc, dtype);
+    }
+  }
+}
+
+/* Dequantized weight row in float32, not rounded to any narrower type: the
+ * float32 contraction operand w = e2m1(q) * (float(e4m3(s)) * g/2688). */
+static void weight_row_f32(const uint8_t* codes_row, const uint8_t* scales_row, int64_t k,
+                           float dec, float* wrow) {
+  for (int64_t i = 0; i < k; ++i) {
+    float sc = block_scale(scales_row[i / 16], dec);
+    wrow[i] = (float)orc_e2m1_value(code_at(codes_row, i)) * sc;
+  }
+}
+
+/* Mutant (iii): block scale without g_w, product and running sum kept in T,
+ * g_w/2688 applied to the final sum ([PR31] "Verification", first mutation). */
+static float sum_in_t_then_scale(const float* xh, const uint8_t* codes_row,
+                                 const uint8_t* scales_row, int64_t k, float dec, int dtype) {
+  float acc = 0.0f;
+  for (int64_t i = 0; i < k; ++i) {
+    float sf = orc_round_to((float)orc_e4m3_value(scales_row[i / 16]), dtype);
+    float w = orc_round_to((float)orc_e2m1_value(code_at(codes_row, i)) * sf, dtype);
+    acc = orc_round_to(acc + orc_round_to(xh[i] * w, dtype), dtype);
+  }
+  return orc_round_to(acc * dec, dtype);
+}
+
+/* qqmm / qmv on a subset of the output: rows mi[0..nm) of x and columns
+ * ni[0..nn) of w.  x [m, k] holds values of type dtype; it goes through the
+ * nvfp4 round trip with g_x (reading: as [DIFF-7] QQMatmul::eval_gpu does for
+ * the activations), w is given quantized (codes [n, k/2], scales [n, k/16])
+ * and decoded with g_w on the block scale; the contraction sums
+ * x_hat * w in double; the result is rounded to dtype
+ * ([DIFF-8] qqmm; [PR31] "The fix"; [PR4458] statement).
+ * has_g: both global scales present (1) or neither (0) ([DIFF-8]
+ * validate_qqmm_inputs).  out is [nm, nn]. */
+void orc_qqmm_subset(const float* x, int dtype, int64_t m, int64_t k, int has_g, float gx,
+                     float gw, const uint8_t* wcodes, const uint8_t* wscales, int64_t n,
+                     const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn, float* out,
+                     int nthreads) {
+  (void)m;
+  (void)n;
+  int gx_on = has_g && g_mutant != MUT_DROP_GX;
+  float dec_w = (has_g && g_mutant != MUT_DROP_GW) ? global_dec(1, gw) : 1.0f;
+  float* xh = (float*)malloc(sizeof(float) * (size_t)(nm * k));
+  float* wr = (float*)malloc(sizeof(float) * (size_t)(nn * k));
+  for (int64_t a = 0; a < nm; ++a)
+    orc_quant_dequant(x + mi[a] * k, 1, k, gx_on, gx, dtype, xh + a * k);
+  for (int64_t b = 0; b < nn; ++b)
+    weight_row_f32(wcodes + ni[b] * (k / 2), wscales + ni[b] * (k / 16), k, dec_w,
+                   wr + b * k);
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+  for (int64_t a = 0; a < nm; ++a) {
+    for (int64_t b = 0; b < nn; ++b) {
+      float r;
+      if (g_mutant == MUT_GW_ON_SUM) {
+        r = sum_in_t_then_scale(xh + a * k, wcodes + ni[b] * (k / 2),
+                                wscales + ni[b] * (k / 16), k, global_dec(has_g, gw), dtype);
+      } else {
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; ++i) acc += (double)xh[a * k + i] * (double)wr[b * k + i];
+        r = orc_round_to((float)acc, dtype);
+      }
+      out[a * nn + b] = r;
+    }
+  }
+  free(xh);
+  free(wr);
+}
+
+/* gather_qmm on a subset of (token, slot) pairs and output columns:
+ * out[t, j, n] = T( sum_k x[t, k] * w_e[n, k] ), e = idx[t, j], with
+ * w_e decoded with that expert's global scale g[e]/2688 on the block scale
+ * ([PR4458] statement: x @ dequant(W) with the global scale inside the
+ * dequantization; per-expert scales of shape [E, 1, 1] in the test loops).
+ * x is used as given (reading: the pages quantize no activations here).
+ * g may be NULL (no global scale).  pairs holds np (t, j) pairs; out is
+ * [np, nn]. */
+void orc_gather_qmm_subset(const float* x, int dtype, int64_t t_count, int64_t k,
+                           const uint8_t* wcodes, const uint8_t* wscales, const float* g,
+                           int64_t e_count, int64_t n, const int32_t* idx, int64_t top_k,
+                           const int64_t* pairs_t, const int64_t* pairs_j, int64_t np,
+                           const int64_t* ni, int64_t nn, float* out, int nthreads) {
+  (void)t_count;
+  (void)e_count;
+#pragma omp parallel num_threads(nthreads)
+  {
+    float* wr = (float*)malloc(sizeof(float) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < np; ++a) {
+      int64_t t = pairs_t[a], j = pairs_j[a];
+      int64_t e = idx[t * top_k + j];
+      float dec = (g && g_mutant != MUT_DROP_GW) ? global_dec(1, g[e]) : 1.0f;
+      for (int64_t b = 0; b < nn; ++b) {
+        const uint8_t* cr = wcodes + (e * n + ni[b]) * (k / 2);
+        const uint8_t* sr = wscales + (e * n + ni[b]) * (k / 16);
+        weight_row_f32(cr, sr, k, dec, wr);
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; ++i) acc += (double)x[t * k + i] * (double)wr[i];
+        out[a * nn + b] = orc_round_to((float)acc, dtype);
+      }
+    }
+    free(wr);
+  }
+}
+
+/* Routing reference: tokens grouped by expert, stable (ascending t, then j).
+ * offsets [e_count + 1] is the exclusive prefix sum of the per-expert counts;
+ * perm [t_count * top_k] lists flat pair ids t*top_k + j in that order.
+ * Returns 0, or -1 if an index is out of range. */
+int orc_moe_route(const int32_t* idx, int64_t t_count, int64_t top_k, int64_t e_count,
+                  int32_t* offsets, int32_t* perm) {
+  int64_t total = t_count * top_k;
+  for (int64_t e = 0; e <= e_count; ++e) offsets[e] = 0;
+  for (int64_t p = 0; p < total; ++p) {
+    if (idx[p] < 0 || idx[p] >= e_count) return -1;
+    offsets[idx[p] + 1] += 1;
+  }
+  for (int64_t e = 0; e < e_count; ++e) offsets[e + 1] += offsets[e];
+  int64_t pos = 0;
+  for (int64_t e = 0; e < e_count; ++e)
+    for (int64_t p = 0; p < total; ++p)
+      if (idx[p] == e) perm[pos++] = (int32_t)p;
+  return 0;
+}
