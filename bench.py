@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 hot path on one MI355X (gfx950).
+
+Headline workload (one "step"): qqmm prefill, x bf16 [2048, 4096] Normal(0, 1)
+against w NVFP4 [14336, 4096] (quantized once, untimed, from bf16 Normal(0,
+0.02) with g_w = amax(w)).  A step is the whole path for one batch: the
+activation amax g_x (tensor_amax), then nvfp4_qqmm (the x round trip into
+bf16 x_hat, then the MFMA contraction with w decoded in the kernel).
+`value` is the step's algorithmic TFLOP/s, 2*M*N*K / step time.
+
+Beside it, on the same run:
+  roofline    the contraction kernel alone (nvfp4_qmm on x_hat), per-launch
+              time from HIP events on the launch stream, vs 2.5 PFLOP/s bf16;
+  qmv         decode x bf16 [1, 4096] @ the same w: algorithmic bytes per
+              launch / kernel time, vs 8 TB/s, with the weight rotated over
+              copies totalling > 512 MB so the Infinity Cache cannot serve it;
+  quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
+              outliers (also rotated), GB/s each;
+  gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
+  cpu_baseline  the oracle (plain C, double accumulation) on a bounded row
+              sample of the headline workload, on this host's cores.
+Inputs are synthetic and already resident in device memory when timing starts.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "nvfp4 qmv HBM GB/s + qqmm TFLOP/s on 1 MI355X; % of HBM/MFMA roofline"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+M, N, K = 2048, 14336, 4096
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def timed(fn, iters, warmup, graph=False):
+    """Average milliseconds per call of fn() over `iters` calls, from HIP events
+    recorded on the current stream (the stream the library launches on).  With
+    graph=True the calls are captured once into a HIP graph and replayed."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(iters):
+                    fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        g.replay()
+        end.record()
+        end.synchronize()
+        return start.elapsed_time(end) / iters
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(iters):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def bench_qqmm(args, nv, torch, W):
+    x, w = W.qqmm_inputs(device="cuda")
+    gw = nv.nvfp4_tensor_amax(w)
+    wc, ws = nv.nvfp4_quantize(w, gw)
+    w_host = w.cpu()  # for the oracle's own quantization in the CPU baseline
+    del w
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    gx = torch.empty(1, dtype=torch.float32, device="cuda")
+    wsp, nbytes = nv.qqmm_workspace(M, N, K, torch.bfloat16, "cuda")
+
+    def step():
+        nv.nvfp4_tensor_amax(x, out=gx)
+        nv.nvfp4_qqmm(x, wc, ws, gx, gw, out=out, workspace=wsp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = timed(step, args.steps, 0)
+    wall = time.perf_counter() - t0
+    flop = 2.0 * M * N * K
+    # the contraction kernel alone, on x_hat
+    xhat = nv.nvfp4_quant_dequant(x, gx)
+    ms_gemm = timed(lambda: nv.nvfp4_qmm(xhat, wc, ws, gw, out=out), args.steps, 2)
+    ms_prepass = timed(lambda: nv.nvfp4_quant_dequant(x, gx, out=xhat), args.steps, 2, graph=True)
+    torch.cuda.synchronize()
+    return dict(ms_step=ms_step, wall=wall, tflops=flop / ms_step / 1e9, ms_gemm=ms_gemm,
+                gemm_tflops=flop / ms_gemm / 1e9, ms_prepass=ms_prepass, flop=flop,
+                data=(x, w_host))
+
+
+def bench_qmv(args, nv, torch, W):
+    x, w = W.qmv_inputs(device="cuda")
+    gx, gw = nv.nvfp4_tensor_amax(x), nv.nvfp4_tensor_amax(w)
+    wc, ws = nv.nvfp4_quantize(w, gw)
+    del w
+    per = wc.numel() + ws.numel()
+    copies = max(2, -(-600_000_000 // per))  # > 512 MB of weights in rotation
+    wcs = [wc.clone() for _ in range(copies)]
+    wss = [ws.clone() for _ in range(copies)]
+    out = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
+    state = {"i": 0}
+
+    def call():
+        i = state["i"] % copies
+        state["i"] += 1
+        nv.nvfp4_qmv(x, wcs[i], wss[i], gx, gw, out=out)
+
+    iters = copies * 4
+    ms = timed(call, iters, copies, graph=True)
+    nbytes = per + x.numel() * 2 + N * 2
+    # warm (cache-resident) number for context: always the same copy
+    ms_warm = timed(lambda: nv.nvfp4_qmv(x, wc, ws, gx, gw, out=out), 64, 8, graph=True)
+    return dict(ms=ms, gbs=nbytes / ms / 1e6, bytes=nbytes, copies=copies, ms_warm=ms_warm,
+                gbs_warm=nbytes / ms_warm / 1e6)
+
+
+def bench_quantize(args, nv, torch, W):
+    w = W.quantize_weight(device="cuda")
+    rows, k = w.shape
+    copies = 16
+    ws_ = [w.clone() for _ in range(copies)]
+    g = nv.nvfp4_tensor_amax(w)
+    codes = [torch.empty(rows, k // 2, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    scales = [torch.empty(rows, k // 16, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    deq = [torch.empty(rows, k, dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    for i in range(copies):
+        nv.nvfp4_quantize(ws_[i], g, codes=codes[i], scales=scales[i])
+    st = {"a": 0, "q": 0, "d": 0}
+
+    def amax():
+        i = st["a"] % copies
+        st["a"] += 1
+        nv.nvfp4_tensor_amax(ws_[i], out=g)
+
+    def quant():
+        i = st["q"] % copies
+        st["q"] += 1
+        nv.nvfp4_quantize(ws_[i], g, codes=codes[i], scales=scales[i])
+
+    def dequant():
+        i = st["d"] % copies
+        st["d"] += 1
+        nv.nvfp4_dequantize(codes[i], scales[i], g, out=deq[i])
+
+    n = rows * k
+    b_amax = n * 2
+    b_q = n * 2 + n // 2 + n // 16
+    b_d = n // 2 + n // 16 + n * 2
+    r = {}
+    for name, fn, b in (("amax", amax, b_amax), ("quantize", quant, b_q), ("dequantize", dequant, b_d)):
+        ms = timed(fn, copies * 2, copies, graph=True)
+        r[name] = dict(ms=ms, gbs=b / ms / 1e6, bytes=b, frac=b / ms / 1e6 / PEAK_HBM_GBS)
+    return r
+
+
+def bench_gather(args, nv, torch, W):
+    T, E, Nn, Kk, top_k = 4096, 8, N, K, 2
+    x, w, idx = W.gather_inputs(device="cuda")
+    g = torch.empty(E, dtype=torch.float32, device="cuda")
+    wc = torch.empty(E, Nn, Kk // 2, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, Nn, Kk // 16, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        nv.nvfp4_tensor_amax(w[e], out=g[e:e + 1])
+        nv.nvfp4_quantize(w[e], g[e:e + 1], codes=wc[e], scales=wsc[e])
+    del w
+    torch.cuda.synchronize()
+    out = torch.empty(T, top_k, Nn, dtype=torch.bfloat16, device="cuda")
+    wsp, _ = nv.gather_workspace(T, top_k, E, Nn, Kk, "cuda")
+    ms = timed(lambda: nv.nvfp4_gather_qmm(x, wc, wsc, idx, g, out=out, workspace=wsp),
+               max(3, args.steps // 4), 2)
+    flop = 2.0 * T * top_k * Nn * Kk
+    return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS)
+
+
+def cpu_baseline(data, seconds_target=15.0, cols=2048):
+    """The oracle on a sample of the headline workload, on this host's cores:
+    the first `rows` rows of x against the first `cols` weight rows (the
+    oracle quantizes those itself, untimed), x round trip + float32 weight
+    decode + double sums.  Rows double until one run takes a quarter of
+    seconds_target."""
+    import numpy as np
+    import oracle as O
+    x, w_host = data
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    xh = x.float().cpu().numpy()
+    wh = w_host.float().numpy()
+    gxh, gwh = O.tensor_amax(xh), O.tensor_amax(wh)
+    oc, os_ = O.quantize(wh[:cols], gwh)
+    rows = 4
+    while True:
+        t0 = time.perf_counter()
+        O.qqmm(xh, oc, os_, gxh, gwh, dtype="bf16", rows=np.arange(rows), nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        if dt >= seconds_target / 4 or rows >= M:
+            break
+        rows *= 2
+    flop = 2.0 * rows * cols * K
+    return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nthreads, kind="oracle",
+                sample=f"oracle qqmm on {rows} of {M} rows x {cols} of {N} weight rows, K={K} "
+                       f"(x round trip, float32 weight decode, double sums): {dt:.2f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "quantize", "gather"])
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "the kernels run on one MI355X and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_block_scaled_amd as nv
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nv.load_library()
+    torch.cuda.set_device(0)
+
+    res = {}
+    if args.only in ("all", "qqmm"):
+        log("qqmm prefill ...")
+        res["qqmm"] = bench_qqmm(args, nv, torch, W)
+        log(f"  step {res['qqmm']['ms_step']:.3f} ms ({res['qqmm']['tflops']:.1f} TFLOP/s); "
+            f"gemm {res['qqmm']['ms_gemm']:.3f} ms ({res['qqmm']['gemm_tflops']:.1f} TFLOP/s); "
+            f"x pre-pass {res['qqmm']['ms_prepass'] * 1e3:.1f} us")
+    if args.only in ("all", "qmv"):
+        log("qmv decode ...")
+        res["qmv"] = bench_qmv(args, nv, torch, W)
+        log(f"  {res['qmv']['ms'] * 1e3:.2f} us/launch, {res['qmv']['gbs']:.0f} GB/s "
+            f"(warm {res['qmv']['gbs_warm']:.0f} GB/s)")
+    if args.only in ("all", "quantize"):
+        log("quantize / dequantize ...")
+        res["quantize"] = bench_quantize(args, nv, torch, W)
+        for k_, v in res["quantize"].items():
+            log(f"  {k_}: {v['ms'] * 1e3:.2f} us, {v['gbs']:.0f} GB/s")
+    if args.only in ("all", "gather"):
+        log("gather_qmm MoE ...")
+        res["gather"] = bench_gather(args, nv, torch, W)
+        log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s")
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded Normal activations/weights of the pages' shapes)"}
+    if "qqmm" in res:
+        q = res["qqmm"]
+        line.update(value=round(q["tflops"], 2), unit="TFLOP/s", ms_per_step=round(q["ms_step"], 4))
+        line["config"] = {"workload": "qqmm prefill: x bf16 [2048,4096] (amax + NVFP4 round trip) "
+                                      "@ NVFP4 w [14336,4096]^T, bf16 out",
+                          "m": M, "n": N, "k": K, "group_size": 16}
+        line["roofline"] = {"bound": "mfma", "kernel": "mfma_gemm_kernel (nvfp4_qmm on x_hat)",
+                            "achieved": round(q["gemm_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(q["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
+                            "traffic": None, "ms_per_launch": round(q["ms_gemm"], 4),
+                            "algorithmic_flop_per_launch": q["flop"]}
+        line["x_prepass_us"] = round(q["ms_prepass"] * 1e3, 2)
+    if "qmv" in res:
+        v = res["qmv"]
+        line["qmv"] = {"value": round(v["gbs"], 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                       "frac": round(v["gbs"] / PEAK_HBM_GBS, 4), "us_per_launch": round(v["ms"] * 1e3, 3),
+                       "algorithmic_bytes_per_launch": v["bytes"], "weight_copies_rotated": v["copies"],
+                       "warm_cache_GBps": round(v["gbs_warm"], 1),
+                       "workload": "qmv decode: x bf16 [1,4096] @ NVFP4 w [14336,4096]^T"}
+    if "quantize" in res:
+        line["quantize"] = {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["frac"], 4),
+                                 "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}
+                            for k_, v in res["quantize"].items()}
+    if "gather" in res:
+        gq = res["gather"]
+        line["gather_qmm"] = {"value": round(gq["tflops"], 2), "unit": "TFLOP/s",
+                              "frac": round(gq["frac"], 4), "ms": round(gq["ms"], 4),
+                              "workload": "4096 tokens x top-2 of 8 experts, NVFP4 w [8,14336,4096]"}
+    if "qqmm" in res and not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(res["qqmm"]["data"])
+    if "value" not in line:
+        line.update(value=None, unit=None, ms_per_step=None, config={"workload": args.only})
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

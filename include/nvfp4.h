@@ -1,0 +1,235 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 block-scaled quantize / dequantize /
+ * quantize-dequantize and the qmv, qqmm and gather_qmm contractions on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited:
+ *   "mlx 0.30.7.2 -> 0.30.7.6" source diff, page 8 (my.diffend.io): ops.cpp
+ *       hunks validate_global_scale, validate_qqmm_inputs, qqmm, fp_quantize,
+ *       quantize, fp_dequantize, dequantize; ops.h declarations.
+ *   same diff, page 7: fp_quantize.cu (fp_quantize_dequantize,
+ *       fp_quantize_rowwise, fp_dequantize and their host wrappers), qqmm.cpp
+ *       (QQMatmul::eval_gpu).
+ *   "[Metal] global scale for qmm", ml-explore/mlx pull request 4458:
+ *       statement and "Example"; gather_qmm test loops in the review.
+ *   osaurus-ai/mlx pull request 31: "What fails", "The test", "The fix".
+ *
+ * Number format (NVFP4): every 16 consecutive elements of a row share one
+ * e4m3 block scale; each element is a 4-bit e2m1 code.  An optional float32
+ * per-tensor global scale g (the tensor's absolute maximum) sets the encode
+ * factor 2688/g and the decode factor g/2688, 2688 = 448 * 6.  Decoding is
+ *     w = e2m1(q) * (e4m3(s) * g/2688)
+ * with the global factor on the block scale, never on the output.
+ *
+ * Layout of a quantized [rows, k] tensor (k a multiple of 16), all row-major,
+ * contiguous, no padding:
+ *   codes   uint8 [rows, k/2]   element 2j in the low nibble of byte j
+ *   scales  uint8 [rows, k/16]  e4m3 bytes
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers to caller-owned memory.  The
+ *     library never allocates, frees or keeps them, and keeps no state
+ *     between calls except a per-thread error message and a per-device
+ *     "architecture checked" flag.
+ *   - Every call enqueues work on `stream` and returns without waiting.
+ *   - A global scale is a device pointer to one float32 (per expert: e
+ *     floats), or NULL for "no global scale" (factors 1).  Its value must be
+ *     finite and > 0 (not checked: it lives on the device).
+ *   - Returns NVFP4_OK, or an error code with nothing enqueued; the message
+ *     is then available from nvfp4_last_error() on the same thread.  Argument
+ *     errors are detected on the host before any HIP call.
+ *   - Element types: NVFP4_F32, NVFP4_F16, NVFP4_BF16 (float64 is rejected
+ *     as in the pages' dispatch).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARGUMENT = 1, /* bad shape, pointer, dtype or combination     */
+  NVFP4_ERR_UNSUPPORTED = 2,      /* device is not gfx950, or size above a limit  */
+  NVFP4_ERR_DEVICE = 3            /* a HIP call failed (message has HIP's text)   */
+} nvfp4_status;
+
+typedef enum { NVFP4_F32 = 0, NVFP4_F16 = 1, NVFP4_BF16 = 2 } nvfp4_dtype;
+
+/* Message of the last failed call on this thread ("[op] ..."), or "". */
+const char* nvfp4_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+/*
+ * nvfp4_tensor_amax -- amax_out[0] = max |x[i]| over i < n, as float32.
+ * This is the per-tensor global scale g the configurations use (the
+ * cotangent amax of QQMatmul::vjp, diff page 8, is the same reduction).
+ *   x         device, n elements of type dt
+ *   amax_out  device, 1 float; written (n == 0 gives 0)
+ * Errors: NULL pointer, n < 0, bad dtype.
+ */
+nvfp4_status nvfp4_tensor_amax(const void* x, nvfp4_dtype dt, int64_t n, float* amax_out,
+                               hipStream_t stream);
+
+/*
+ * nvfp4_quantize -- NVFP4 encode of x [rows, k] (diff page 7,
+ * fp_quantize_rowwise; diff page 8, fp_quantize and quantize).  Per group of
+ * 16: sd = (amax/6) * (2688/g) in float32, s = e4m3(sd) (nearest-even,
+ * saturating), q_i = e2m1(x_i * ((2688/g) / e4m3value(s))); a block whose
+ * scale is 0 gets all-zero codes (sign kept).
+ *   x             device [rows, k] of type dt, row-major
+ *   global_scale  device float or NULL
+ *   codes         device uint8 [rows, k/2], written
+ *   scales        device uint8 [rows, k/16], written
+ * Errors: NULL pointer, rows < 0, k <= 0 or k % 16 != 0, bad dtype.
+ */
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t k,
+                            const float* global_scale, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream);
+
+/*
+ * nvfp4_dequantize -- out = T(e2m1(q) * (e4m3(s) * g/2688)) (diff page 7,
+ * fp_dequantize; diff page 8, fp_dequantize and dequantize).
+ *   codes, scales  device, layout above, [rows, k]
+ *   global_scale   device float or NULL
+ *   out            device [rows, k] of type out_dt, written
+ * Errors: NULL pointer, rows < 0, k <= 0 or k % 16 != 0, bad dtype.
+ */
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t k, const float* global_scale, void* out,
+                              nvfp4_dtype out_dt, hipStream_t stream);
+
+/*
+ * nvfp4_quant_dequant -- x_hat = dequantize(quantize(x, g), g) in x's type
+ * (diff page 7, fp_quantize_dequantize; osaurus-ai/mlx PR 31, "The fix").
+ *   x      device [rows, k] of type dt
+ *   x_hat  device [rows, k] of type dt, written (may equal x)
+ * Errors: as nvfp4_quantize.
+ */
+nvfp4_status nvfp4_quant_dequant(const void* x, nvfp4_dtype dt, int64_t rows, int64_t k,
+                                 const float* global_scale, void* x_hat, hipStream_t stream);
+
+/*
+ * nvfp4_qmv -- out[n] = T( sum_k x_hat[k] * w[n, k] ), M = 1 (diff page 7,
+ * QQMatmul::eval_gpu, M == 1 branch): x goes through the NVFP4 round trip with
+ * global_scale_x inside the kernel, w is decoded with global_scale_w on each
+ * block scale ("[Metal] global scale for qmm" PR 4458, statement), float32
+ * accumulation.
+ *   x               device [k] of type dt
+ *   global_scale_x  device float or NULL
+ *   w_codes         device uint8 [n, k/2];  w_scales device uint8 [n, k/16]
+ *   global_scale_w  device float or NULL; both or neither of the two global
+ *                   scales (diff page 8, validate_qqmm_inputs)
+ *   out             device [n] of type dt, written
+ * Errors: NULL pointer, n <= 0, k <= 0 or k % 16 != 0, exactly one global
+ * scale, bad dtype, k above 32768 (UNSUPPORTED).
+ */
+nvfp4_status nvfp4_qmv(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                       const uint8_t* w_codes, const uint8_t* w_scales,
+                       const float* global_scale_w, int64_t n, int64_t k, void* out,
+                       hipStream_t stream);
+
+/*
+ * nvfp4_qqmm_workspace_size -- bytes of device workspace nvfp4_qqmm needs for
+ * these sizes (0 when m == 1).  The workspace holds x_hat [m, k] of type dt.
+ */
+size_t nvfp4_qqmm_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt);
+
+/*
+ * nvfp4_qqmm -- out = T( x_hat @ w^T ), x [m, k] and w NVFP4 [n, k] (diff
+ * page 8, qqmm; diff page 7, QQMatmul::eval_gpu): x_hat is x after the NVFP4
+ * round trip with global_scale_x, w is decoded with global_scale_w on the
+ * block scale; float32 accumulation.  m == 1 runs the qmv kernel.
+ *   x               device [m, k] of type dt
+ *   w_codes/scales  device [n, k/2] / [n, k/16]
+ *   out             device [m, n] of type dt, written
+ *   workspace       device, at least nvfp4_qqmm_workspace_size() bytes,
+ *                   256-byte aligned; may be NULL when that size is 0
+ * Errors: NULL pointer, m, n <= 0, k <= 0 or k % 16 != 0, exactly one global
+ * scale, workspace too small or misaligned, bad dtype.
+ */
+nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                        const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* global_scale_w, int64_t m, int64_t n, int64_t k, void* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_qmm -- out = T( x @ w^T ) with x used as given (not quantized) and w
+ * NVFP4 decoded with global_scale_w on the block scale: the pages'
+ * quantized_matmul (diff page 8, ops.cpp quantized_matmul; "mlx 0.30.7" diff
+ * page 71, QuantizedMatmul::eval_gpu), i.e. the contraction of nvfp4_qqmm
+ * without the activation round trip.  No workspace.
+ *   x               device [m, k] of type dt, 16-byte aligned
+ *   w_codes/scales  device [n, k/2] / [n, k/16]
+ *   global_scale_w  device float or NULL
+ *   out             device [m, n] of type dt, written
+ * Errors: NULL pointer, m, n <= 0, k <= 0 or k % 16 != 0, bad dtype.
+ */
+nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                       const uint8_t* w_scales, const float* global_scale_w, int64_t m, int64_t n,
+                       int64_t k, void* out, hipStream_t stream);
+
+/*
+ * nvfp4_gather_qmm_workspace_size -- bytes of device workspace
+ * nvfp4_gather_qmm needs (routing tables: expert offsets and the token order).
+ */
+size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
+                                       int64_t k);
+
+/*
+ * nvfp4_gather_qmm -- mixture-of-experts product with per-expert NVFP4
+ * weights ("[Metal] global scale for qmm" PR 4458: x @ dequant(W) with the
+ * per-expert global scale, shape [E, 1, 1], inside the dequantization):
+ *     out[t, j, :] = T( x[t, :] @ w[idx[t, j]]^T )
+ * x is used as given (not quantized).  The pairs (t, j) are first grouped by
+ * expert in a stable order (ascending t, then j), then each expert's rows
+ * are multiplied by its decoded weights.
+ *   x               device [t, k] of type dt
+ *   w_codes         device uint8 [e, n, k/2];  w_scales uint8 [e, n, k/16]
+ *   global_scale_w  device float [e] or NULL
+ *   expert_idx      device int32 [t, top_k], each in [0, e) (not checked:
+ *                   it lives on the device; out-of-range pairs are skipped
+ *                   and their output rows left unwritten)
+ *   out             device [t, top_k, n] of type dt, written
+ *   workspace       device, at least nvfp4_gather_qmm_workspace_size() bytes
+ * Errors: NULL pointer, t, top_k, e, n <= 0, k <= 0 or k % 16 != 0, workspace
+ * too small, bad dtype.
+ */
+nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* global_scale_w,
+                              const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                              int64_t n, int64_t k, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_moe_route -- the routing step of nvfp4_gather_qmm on its own:
+ * offsets[0..e] = exclusive prefix sum of the per-expert pair counts,
+ * perm[offsets[x] .. offsets[x+1]) = the flat pair ids t*top_k + j routed to
+ * expert x, ascending.
+ *   expert_idx  device int32 [t, top_k]
+ *   offsets     device int32 [e + 1], written
+ *   perm        device int32 [t * top_k], written
+ * Errors: NULL pointer, t, top_k, e <= 0, t * top_k >= 2^31.
+ */
+nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                             int32_t* offsets, int32_t* perm, hipStream_t stream);
+
+/*
+ * Test hook: treat every device as having this gcnArchName (NULL restores the
+ * real query).  Lets host-only tests reach the unsupported-device error.
+ */
+void nvfp4_debug_set_arch_override(const char* arch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

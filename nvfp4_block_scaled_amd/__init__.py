@@ -1,0 +1,328 @@
+"""Python binding of libnvfp4.so: NVFP4 block-scaled quantize / dequantize /
+qmv / qqmm / gather_qmm on AMD Instinct MI355X (gfx950).
+
+This module only marshals arguments: torch supplies device memory and the
+current stream, every computation runs in the HIP kernels of libnvfp4.so.
+There is no CPU fallback: without the built library (or without a GPU) the
+calls raise.
+
+The functions carry the C entry points' names (see include/nvfp4.h):
+    nvfp4_tensor_amax(x)                              -> float32 [1]
+    nvfp4_quantize(x, global_scale=None)              -> (codes, scales)
+    nvfp4_dequantize(codes, scales, global_scale=None, dtype=torch.bfloat16)
+    nvfp4_quant_dequant(x, global_scale=None)         -> x_hat
+    nvfp4_qmv(x, w_codes, w_scales, global_scale_x=None, global_scale_w=None)
+    nvfp4_qqmm(x, w_codes, w_scales, global_scale_x=None, global_scale_w=None)
+    nvfp4_qmm(x, w_codes, w_scales, global_scale_w=None)   (x not quantized)
+    nvfp4_gather_qmm(x, w_codes, w_scales, expert_idx, global_scale_w=None)
+    nvfp4_moe_route(expert_idx, num_experts)          -> (offsets, perm)
+Global scales are float32 device tensors with one element (per expert: e
+elements, any shape such as [e, 1, 1]), as the pages' validate_global_scale
+requires ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_ERR_INVALID_ARGUMENT, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_DEVICE = 0, 1, 2, 3
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library():
+    """Load libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libnvfp4.so not built at {LIB_PATH}; run nvfp4_block_scaled_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "nvfp4_last_error": (ctypes.c_char_p, []),
+        "nvfp4_version": (I, []),
+        "nvfp4_debug_set_arch_override": (None, [ctypes.c_char_p]),
+        "nvfp4_tensor_amax": (I, [P, I, I64, P, P]),
+        "nvfp4_quantize": (I, [P, I, I64, I64, P, P, P, P]),
+        "nvfp4_dequantize": (I, [P, P, I64, I64, P, P, I, P]),
+        "nvfp4_quant_dequant": (I, [P, I, I64, I64, P, P, P]),
+        "nvfp4_qmv": (I, [P, I, P, P, P, P, I64, I64, P, P]),
+        "nvfp4_qqmm_workspace_size": (SZ, [I64, I64, I64, I]),
+        "nvfp4_qqmm": (I, [P, I, P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_qmm": (I, [P, I, P, P, P, I64, I64, I64, P, P]),
+        "nvfp4_gather_qmm_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
+        "nvfp4_gather_qmm": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_moe_route": (I, [P, I64, I64, I64, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != NVFP4_OK:
+        msg = load_library().nvfp4_last_error().decode()
+        if status == NVFP4_ERR_INVALID_ARGUMENT:
+            raise ValueError(msg)
+        raise NVFP4Error(status, msg)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype_code(t, name):
+    if t.dtype not in _DT:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype} (float32, float16, bfloat16 only)")
+    return _DT[t.dtype]
+
+
+def _gscale(g, name, numel=1):
+    """Device float32 global scale with `numel` elements, or None."""
+    if g is None:
+        return None
+    if not isinstance(g, torch.Tensor):
+        raise ValueError(f"{name} must be a float32 device tensor")
+    if g.numel() != numel:
+        raise ValueError(f"{name} must have {numel} element(s) but got shape {tuple(g.shape)}.")
+    if g.dtype != torch.float32:
+        raise ValueError(f"{name} must have dtype float32 but got {g.dtype}.")
+    return _dev(g, name)
+
+
+def _rows_k(x):
+    if x.dim() == 0:
+        raise ValueError("input must have at least one dimension")
+    k = x.shape[-1]
+    return x.numel() // k if k else 0, k
+
+
+# ------------------------------------------------------------------ codec
+
+def nvfp4_tensor_amax(x, out=None):
+    L = load_library()
+    _dev(x, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(L.nvfp4_tensor_amax(_ptr(x), _dtype_code(x, "x"), x.numel(), _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_quantize(x, global_scale=None, codes=None, scales=None):
+    L = load_library()
+    _dev(x, "x")
+    rows, k = _rows_k(x)
+    g = _gscale(global_scale, "global_scale")
+    shape = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(shape + (k // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(shape + (k // 16,), dtype=torch.uint8, device=x.device)
+    _check(L.nvfp4_quantize(_ptr(x), _dtype_code(x, "x"), rows, k, _ptr(g), _ptr(codes),
+                            _ptr(scales), _stream()))
+    return codes, scales
+
+
+def nvfp4_dequantize(codes, scales, global_scale=None, dtype=torch.bfloat16, out=None):
+    L = load_library()
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8")
+    k = codes.shape[-1] * 2
+    rows = codes.numel() // codes.shape[-1] if codes.shape[-1] else 0
+    if scales.numel() * 16 != rows * k:
+        raise ValueError("scales do not match codes")
+    g = _gscale(global_scale, "global_scale")
+    if out is None:
+        out = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    _check(L.nvfp4_dequantize(_ptr(codes), _ptr(scales), rows, k, _ptr(g), _ptr(out),
+                              _dtype_code(out, "out"), _stream()))
+    return out
+
+
+def nvfp4_quant_dequant(x, global_scale=None, out=None):
+    L = load_library()
+    _dev(x, "x")
+    rows, k = _rows_k(x)
+    g = _gscale(global_scale, "global_scale")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(L.nvfp4_quant_dequant(_ptr(x), _dtype_code(x, "x"), rows, k, _ptr(g), _ptr(out),
+                                 _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ contractions
+
+def _w_shapes(w_codes, w_scales, k):
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.uint8:
+        raise ValueError("w_codes and w_scales must be uint8")
+    if w_codes.shape[-1] * 2 != k or w_scales.shape[-1] * 16 != k:
+        raise ValueError(f"weights of inner size {w_codes.shape[-1] * 2} do not match x's {k}")
+
+
+def nvfp4_qmv(x, w_codes, w_scales, global_scale_x=None, global_scale_w=None, out=None):
+    L = load_library()
+    _dev(x, "x")
+    k = x.shape[-1]
+    if x.numel() != k:
+        raise ValueError("qmv takes a single row x")
+    _w_shapes(w_codes, w_scales, k)
+    n = w_codes.shape[0]
+    gx, gw = _gscale(global_scale_x, "global_scale_x"), _gscale(global_scale_w, "global_scale_w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    _check(L.nvfp4_qmv(_ptr(x), _dtype_code(x, "x"), _ptr(gx), _ptr(w_codes), _ptr(w_scales),
+                       _ptr(gw), n, k, _ptr(out), _stream()))
+    return out
+
+
+def qqmm_workspace(m, n, k, dtype, device):
+    nbytes = load_library().nvfp4_qqmm_workspace_size(m, n, k, _DT[dtype])
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def nvfp4_qqmm(x, w_codes, w_scales, global_scale_x=None, global_scale_w=None, out=None,
+               workspace=None):
+    """out = x_hat @ w^T with x [m, k] (at most 2-D, as the pages' qqmm)."""
+    L = load_library()
+    _dev(x, "x")
+    if x.dim() > 2 or w_codes.dim() > 2:
+        raise ValueError("[qqmm] Only 2D inputs are supported.")
+    x2 = x.reshape(-1, x.shape[-1])
+    m, k = x2.shape
+    _w_shapes(w_codes, w_scales, k)
+    n = w_codes.shape[0]
+    gx, gw = _gscale(global_scale_x, "global_scale_x"), _gscale(global_scale_w, "global_scale_w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = qqmm_workspace(m, n, k, x.dtype, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_qqmm(_ptr(x2), _dtype_code(x, "x"), _ptr(gx), _ptr(w_codes), _ptr(w_scales),
+                        _ptr(gw), m, n, k, _ptr(out), _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def nvfp4_qmm(x, w_codes, w_scales, global_scale_w=None, out=None):
+    """out = x @ dequant(w)^T with x used as given (the pages' quantized_matmul)."""
+    L = load_library()
+    _dev(x, "x")
+    x2 = x.reshape(-1, x.shape[-1])
+    m, k = x2.shape
+    _w_shapes(w_codes, w_scales, k)
+    n = w_codes.shape[0]
+    gw = _gscale(global_scale_w, "global_scale_w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    _check(L.nvfp4_qmm(_ptr(x2), _dtype_code(x, "x"), _ptr(w_codes), _ptr(w_scales), _ptr(gw),
+                       m, n, k, _ptr(out), _stream()))
+    return out
+
+
+def gather_workspace(t, top_k, e, n, k, device):
+    nbytes = load_library().nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def nvfp4_gather_qmm(x, w_codes, w_scales, expert_idx, global_scale_w=None, out=None,
+                     workspace=None):
+    """out[t, j, :] = x[t] @ dequant(w[expert_idx[t, j]])^T with per-expert g."""
+    L = load_library()
+    _dev(x, "x")
+    _dev(expert_idx, "expert_idx")
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2:
+        raise ValueError("expert_idx must be int32 [t, top_k]")
+    t, k = x.shape
+    top_k = expert_idx.shape[1]
+    if expert_idx.shape[0] != t:
+        raise ValueError("expert_idx rows must match x rows")
+    _w_shapes(w_codes, w_scales, k)
+    e, n = w_codes.shape[0], w_codes.shape[1]
+    g = _gscale(global_scale_w, "global_scale_w", numel=e)
+    if out is None:
+        out = torch.empty((t, top_k, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = gather_workspace(t, top_k, e, n, k, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_gather_qmm(_ptr(x), _dtype_code(x, "x"), _ptr(w_codes), _ptr(w_scales), _ptr(g),
+                              _ptr(expert_idx), t, top_k, e, n, k, _ptr(out), _ptr(workspace),
+                              nbytes, _stream()))
+    return out
+
+
+def nvfp4_moe_route(expert_idx, num_experts):
+    L = load_library()
+    _dev(expert_idx, "expert_idx")
+    t, top_k = expert_idx.shape
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=expert_idx.device)
+    perm = torch.empty(t * top_k, dtype=torch.int32, device=expert_idx.device)
+    _check(L.nvfp4_moe_route(_ptr(expert_idx), t, top_k, num_experts, _ptr(offsets), _ptr(perm),
+                             _stream()))
+    return offsets, perm
+
+
+# ------------------------------------------------------------------ MLX-style names
+
+def _mode_check(group_size, bits, mode):
+    if mode != "nvfp4" or group_size not in (None, 16) or bits not in (None, 4):
+        raise ValueError("[quantize] only mode='nvfp4' with group_size=16 and bits=4 is supported")
+
+
+def quantize(w, group_size=None, bits=None, mode="nvfp4", global_scale=None):
+    _mode_check(group_size, bits, mode)
+    return nvfp4_quantize(w, global_scale)
+
+
+def dequantize(w, scales, group_size=None, bits=None, mode="nvfp4", global_scale=None,
+               dtype=torch.bfloat16):
+    _mode_check(group_size, bits, mode)
+    return nvfp4_dequantize(w, scales, global_scale, dtype)
+
+
+def qqmm(x, w, scales, group_size=None, bits=None, mode="nvfp4", global_scale_x=None,
+         global_scale_w=None):
+    _mode_check(group_size, bits, mode)
+    return nvfp4_qqmm(x, w, scales, global_scale_x, global_scale_w)
+
+
+def gather_qmm(x, w, scales, rhs_indices, global_scale=None):
+    return nvfp4_gather_qmm(x, w, scales, rhs_indices, global_scale)
+
+
+__all__ = [
+    "load_library", "NVFP4Error", "nvfp4_tensor_amax", "nvfp4_quantize", "nvfp4_dequantize",
+    "nvfp4_quant_dequant", "nvfp4_qmv", "nvfp4_qqmm", "nvfp4_qmm", "nvfp4_gather_qmm", "nvfp4_moe_route",
+    "qqmm_workspace", "gather_workspace", "quantize", "dequantize", "qqmm", "gather_qmm",
+]

@@ -1,0 +1,349 @@
+// capi.hip -- the extern "C" entry points of libnvfp4.so (declared and
+// documented in include/nvfp4.h): host-side validation, the error
+// convention, the one-time architecture check, and dispatch to the kernels.
+//
+// Validation follows the pages' op layer ("mlx 0.30.7.2 -> 0.30.7.6" diff
+// page 8: validate_global_scale, validate_qqmm_inputs, fp_quantize's group
+// size / bits check, quantize / dequantize shape checks; page 7: float64
+// rejected in the dispatch).  Messages use the pages' "[op] message" form.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/nvfp4.h"
+#include "nvfp4_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::mutex g_arch_mu;
+std::string g_arch_override;
+bool g_has_override = false;
+int g_arch_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+nvfp4_status fail(nvfp4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+nvfp4_status ok() {
+  g_last_error.clear();
+  return NVFP4_OK;
+}
+
+bool dtype_ok(int dt) { return dt == NVFP4_F32 || dt == NVFP4_F16 || dt == NVFP4_BF16; }
+
+size_t dtype_size(int dt) { return dt == NVFP4_F32 ? 4 : 2; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define CHECK_PTR(op, p)                                                          \
+  do {                                                                            \
+    if ((p) == nullptr)                                                           \
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[" op "] " #p " must not be NULL."); \
+  } while (0)
+
+#define CHECK_DTYPE(op, dt)                                                               \
+  do {                                                                                    \
+    if (!dtype_ok(dt))                                                                    \
+      return fail(NVFP4_ERR_INVALID_ARGUMENT,                                             \
+                  "[" op "] Unsupported dtype code %d (float32, float16 and bfloat16 only).", \
+                  (int)(dt));                                                             \
+  } while (0)
+
+// Group size 16 along the last axis (the pages' nvfp4 mode: group 16, bits 4).
+nvfp4_status check_k(const char* op, int64_t k) {
+  if (k <= 0 || k % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] The last dimension (%lld) must be a positive multiple of the group size 16.",
+                op, (long long)k);
+  return NVFP4_OK;
+}
+
+// The device behind `stream` must be gfx950 (the analogue of the pages'
+// compute-capability gate in QQMatmul::eval_gpu).  Checked once per device.
+nvfp4_status check_device(const char* op) {
+  {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_has_override) {
+      if (g_arch_override.rfind("gfx950", 0) != 0)
+        return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Device architecture %s is not gfx950.", op,
+                    g_arch_override.c_str());
+      return NVFP4_OK;
+    }
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(NVFP4_ERR_DEVICE, "[%s] No HIP device: %s", op, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_DEVICE, "[%s] Device id %d out of range.", op, dev);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(NVFP4_ERR_DEVICE, "[%s] hipGetDeviceProperties: %s", op, hipGetErrorString(e));
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (g_arch_ok[dev] == 2) {
+      std::string name = prop.gcnArchName;
+      return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Device architecture %s is not gfx950.", op,
+                  name.c_str());
+    }
+  }
+  if (g_arch_ok[dev] == 2)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Device architecture is not gfx950.", op);
+  return NVFP4_OK;
+}
+
+nvfp4_status launched(const char* op, hipError_t e) {
+  if (e != hipSuccess) return fail(NVFP4_ERR_DEVICE, "[%s] Kernel launch failed: %s", op, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+int nvfp4_version(void) { return 100; }
+
+void nvfp4_debug_set_arch_override(const char* arch) {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (arch) {
+    g_arch_override = arch;
+    g_has_override = true;
+  } else {
+    g_arch_override.clear();
+    g_has_override = false;
+  }
+}
+
+nvfp4_status nvfp4_tensor_amax(const void* x, nvfp4_dtype dt, int64_t n, float* amax_out,
+                               hipStream_t stream) {
+  const char* op = "tensor_amax";
+  CHECK_DTYPE("tensor_amax", dt);
+  CHECK_PTR("tensor_amax", amax_out);
+  if (n < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[tensor_amax] n (%lld) must be >= 0.", (long long)n);
+  if (n > 0) CHECK_PTR("tensor_amax", x);
+  if (n > 0 && !aligned(x, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[tensor_amax] x must be 16-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_tensor_amax(x, dt, n, amax_out, stream));
+}
+
+static nvfp4_status check_codec(const char* op, const void* x, nvfp4_dtype dt, int64_t rows,
+                                int64_t k) {
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] Unsupported dtype code %d (float32, float16 and bfloat16 only).", op, (int)dt);
+  if (rows < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] rows (%lld) must be >= 0.", op, (long long)rows);
+  if (nvfp4_status st = check_k(op, k)) return st;
+  if (rows > 0 && x == nullptr) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] input must not be NULL.", op);
+  if (rows > 0 && !aligned(x, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] input must be 16-byte aligned.", op);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t k,
+                            const float* global_scale, uint8_t* codes, uint8_t* scales,
+                            hipStream_t stream) {
+  const char* op = "quantize";
+  if (nvfp4_status st = check_codec(op, x, dt, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("quantize", codes);
+    CHECK_PTR("quantize", scales);
+    if (!aligned(codes, 4))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quantize] codes must be 4-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_quantize(x, dt, rows, k, global_scale, codes, scales, stream));
+}
+
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t k, const float* global_scale, void* out,
+                              nvfp4_dtype out_dt, hipStream_t stream) {
+  const char* op = "dequantize";
+  if (nvfp4_status st = check_codec(op, out, out_dt, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("dequantize", codes);
+    CHECK_PTR("dequantize", scales);
+    if (!aligned(codes, 4))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[dequantize] codes must be 4-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_dequantize(codes, scales, rows, k, global_scale, out, out_dt, stream));
+}
+
+nvfp4_status nvfp4_quant_dequant(const void* x, nvfp4_dtype dt, int64_t rows, int64_t k,
+                                 const float* global_scale, void* x_hat, hipStream_t stream) {
+  const char* op = "quant_dequant";
+  if (nvfp4_status st = check_codec(op, x, dt, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("quant_dequant", x_hat);
+    if (!aligned(x_hat, 16))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quant_dequant] x_hat must be 16-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_quant_dequant(x, dt, rows, k, global_scale, x_hat, stream));
+}
+
+static nvfp4_status check_matmul(const char* op, const void* x, nvfp4_dtype dt, const float* gx,
+                                 const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t m,
+                                 int64_t n, int64_t k, const void* out) {
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] Unsupported dtype code %d (float32, float16 and bfloat16 only).", op, (int)dt);
+  if (m <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] m (%lld) and n (%lld) must be positive.", op,
+                (long long)m, (long long)n);
+  if (nvfp4_status st = check_k(op, k)) return st;
+  if (!x || !wc || !ws || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] x, w_codes, w_scales and out must not be NULL.", op);
+  if ((gx == nullptr) != (gw == nullptr))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] For nvfp4 mode, either both global_scale_x and global_scale_w must be "
+                "provided, or neither.", op);
+  if (!aligned(x, 16) || !aligned(wc, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] x and w_codes must be 16-byte aligned.", op);
+  if (m * n > (int64_t)1 << 46 || n > INT32_MAX || m > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Sizes too large.", op);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_qmv(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                       const uint8_t* w_codes, const uint8_t* w_scales,
+                       const float* global_scale_w, int64_t n, int64_t k, void* out,
+                       hipStream_t stream) {
+  const char* op = "qmv";
+  if (nvfp4_status st = check_matmul(op, x, dt, global_scale_x, w_codes, w_scales, global_scale_w,
+                                     1, n, k, out))
+    return st;
+  if (k > nvfp4::kQmvMaxK)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[qmv] k (%lld) above the supported maximum %lld.",
+                (long long)k, (long long)nvfp4::kQmvMaxK);
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_qmv(x, dt, global_scale_x, w_codes, w_scales, global_scale_w,
+                                        n, k, out, stream));
+}
+
+size_t nvfp4_qqmm_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt) {
+  (void)n;
+  if (m <= 1 || k <= 0 || !dtype_ok(dt)) return 0;
+  size_t bytes = (size_t)m * (size_t)k * dtype_size(dt);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                        const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* global_scale_w, int64_t m, int64_t n, int64_t k, void* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "qqmm";
+  if (nvfp4_status st = check_matmul(op, x, dt, global_scale_x, w_codes, w_scales, global_scale_w,
+                                     m, n, k, out))
+    return st;
+  if (m == 1 && k <= nvfp4::kQmvMaxK) {
+    if (nvfp4_status st = check_device(op)) return st;
+    return launched(op, nvfp4::launch_qmv(x, dt, global_scale_x, w_codes, w_scales,
+                                          global_scale_w, n, k, out, stream));
+  }
+  size_t need = (size_t)m * (size_t)k * dtype_size(dt);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm] workspace of %zu bytes is smaller than %zu.",
+                workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  hipError_t e = nvfp4::launch_quant_dequant(x, dt, m, k, global_scale_x, workspace, stream);
+  if (e != hipSuccess) return launched(op, e);
+  return launched(op, nvfp4::launch_qqmm_gemm(workspace, dt, w_codes, w_scales, global_scale_w, m,
+                                               n, k, out, stream));
+}
+
+nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                       const uint8_t* w_scales, const float* global_scale_w, int64_t m, int64_t n,
+                       int64_t k, void* out, hipStream_t stream) {
+  const char* op = "qmm";
+  if (nvfp4_status st = check_matmul(op, x, dt, global_scale_w, w_codes, w_scales, global_scale_w,
+                                     m, n, k, out))
+    return st;
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_qqmm_gemm(x, dt, w_codes, w_scales, global_scale_w, m, n, k,
+                                               out, stream));
+}
+
+size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
+                                       int64_t k) {
+  (void)n;
+  (void)k;
+  if (t <= 0 || top_k <= 0 || e <= 0) return 0;
+  size_t off = (size_t)(e + 1) * sizeof(int32_t);
+  off = (off + 255) & ~(size_t)255;
+  size_t perm = (size_t)t * (size_t)top_k * sizeof(int32_t);
+  return off + ((perm + 255) & ~(size_t)255);
+}
+
+nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                             int32_t* offsets, int32_t* perm, hipStream_t stream) {
+  const char* op = "moe_route";
+  if (t <= 0 || top_k <= 0 || e <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[moe_route] t, top_k and e must be positive.");
+  if (t * top_k >= ((int64_t)1 << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED, "[moe_route] t * top_k must be below 2^31.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[moe_route] at most 1024 experts are supported.");
+  CHECK_PTR("moe_route", expert_idx);
+  CHECK_PTR("moe_route", offsets);
+  CHECK_PTR("moe_route", perm);
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream));
+}
+
+nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* global_scale_w,
+                              const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                              int64_t n, int64_t k, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "gather_qmm";
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm] Unsupported dtype code %d (float32, float16 and bfloat16 only).", (int)dt);
+  if (t <= 0 || top_k <= 0 || e <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] t, top_k, e and n must be positive.");
+  if (nvfp4_status st = check_k(op, k)) return st;
+  if (!x || !w_codes || !w_scales || !expert_idx || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm] x, w_codes, w_scales, expert_idx and out must not be NULL.");
+  if (!aligned(x, 16) || !aligned(w_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] x and w_codes must be 16-byte aligned.");
+  if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm] Sizes too large.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm] at most 1024 experts are supported.");
+  size_t need = nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] workspace of %zu bytes is smaller than %zu.",
+                workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
+  size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream);
+  if (he != hipSuccess) return launched(op, he);
+  return launched(op, nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets,
+                                                perm, t, top_k, e, n, k, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,233 @@
+// codec.hip -- tensor amax, NVFP4 quantize, dequantize and quantize-dequantize
+// kernels for gfx950.
+//
+// All four are HBM-streaming kernels.  A quantized tensor [rows, k] with
+// k % 16 == 0 is a flat sequence of 16-element groups, so the kernels walk
+// groups, not rows: group G covers elements [16G, 16G + 16), codes bytes
+// [8G, 8G + 8) and scale byte G.  Two adjacent lanes share one group, each
+// loading 8 consecutive elements (16 B for 16-bit types), which keeps every
+// wave's loads and stores contiguous; the pair exchanges its half-block
+// amax with one lane swap.
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Loads 8 consecutive elements of type DT starting at element 8*h.
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t h, float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * h;
+    f32x4 a = __builtin_nontemporal_load(p);
+    f32x4 b = __builtin_nontemporal_load(p + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + h);
+    uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kBF16) {
+        v[2 * i] = __uint_as_float(q[i] << 16);
+        v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+      } else {
+        f16x2 hv = __builtin_bit_cast(f16x2, q[i]);
+        v[2 * i] = (float)hv.x;
+        v[2 * i + 1] = (float)hv.y;
+      }
+    }
+  }
+}
+
+// Stores 8 consecutive elements (already float) as type DT at element 8*h.
+template <int DT>
+__device__ __forceinline__ void store8(void* base, int64_t h, const float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * h;
+    p[0] = f32x4{v[0], v[1], v[2], v[3]};
+    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    using T = typename Elem<DT>::T;
+    typedef T T8 __attribute__((ext_vector_type(8)));
+    T8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = from_f32<DT>(v[i]);
+    reinterpret_cast<T8*>(base)[h] = o;
+  }
+}
+
+// ------------------------------------------------------------------ amax
+
+__global__ void amax_zero_kernel(float* out) { *out = 0.0f; }
+
+// max |x| over n elements: vectorised grid-stride loop over 8-element chunks,
+// a scalar tail, a wave max and one atomicMax per wave on the float's bit
+// pattern (non-negative floats order like their unsigned bits).
+template <int DT>
+__global__ void __launch_bounds__(kThreads) amax_kernel(const void* __restrict__ x, int64_t n,
+                                                        float* __restrict__ out) {
+  const int64_t chunks = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  float m = 0.0f;
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < chunks; h += stride) {
+    float v[8];
+    load8<DT>(x, h, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  for (int64_t i = chunks * 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += stride) {
+    using T = typename Elem<DT>::T;
+    m = fmaxf(m, __builtin_fabsf(to_f32<DT>(reinterpret_cast<const T*>(x)[i])));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+// ------------------------------------------------------------------ quantize
+
+// One lane per half group: h in [0, 2 * groups).  MODE 0 writes codes and
+// scales; MODE 1 writes the dequantized values x_hat in the input type.
+template <int DT, int MODE>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const void* __restrict__ x, int64_t halves, const float* __restrict__ gscale,
+                uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, void* __restrict__ xhat) {
+  const float enc = global_encode(gscale);
+  const float dec = global_decode(gscale);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < halves; h += stride) {
+    float v[8];
+    load8<DT>(x, h, v);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));  // the pair partner holds the other half
+    GroupScale gs = group_scale_from_amax(a, enc);
+    uint32_t word = 0;
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[i] = e2m1_encode_scaled(v[i], gs.enc_b);
+      word |= c[i] << (4 * i);
+    }
+    if constexpr (MODE == 0) {
+      codes[h] = word;
+      if ((h & 1) == 0) scales[h >> 1] = (uint8_t)gs.byte;
+    } else {
+      float sc;
+      {
+#pragma clang fp contract(off)
+        sc = e4m3_decode(gs.byte) * dec;
+      }
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+        o[i] = e2m1_decode(c[i]) * sc;
+      }
+      store8<DT>(xhat, h, o);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dequantize
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads)
+dequantize_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                  int64_t halves, const float* __restrict__ gscale, void* __restrict__ out) {
+  const float dec = global_decode(gscale);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < halves; h += stride) {
+    uint32_t word = __builtin_nontemporal_load(codes + h);
+    uint32_t s = scales[h >> 1];
+    float sc;
+    {
+#pragma clang fp contract(off)
+      sc = e4m3_decode(s) * dec;
+    }
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+      o[i] = e2m1_decode(word >> (4 * i)) * sc;
+    }
+    store8<DT>(out, h, o);
+  }
+}
+
+int grid_for(int64_t work, int per_block, int max_blocks) {
+  int64_t b = (work + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > max_blocks) b = max_blocks;
+  return (int)b;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipStream_t s) {
+  amax_zero_kernel<<<1, 1, 0, s>>>(out);
+  if (n > 0) {
+    int blocks = grid_for(n / 8 + 1, kThreads * 4, 2048);
+    switch (dt) {
+      case kF32: amax_kernel<kF32><<<blocks, kThreads, 0, s>>>(x, n, out); break;
+      case kF16: amax_kernel<kF16><<<blocks, kThreads, 0, s>>>(x, n, out); break;
+      default: amax_kernel<kBF16><<<blocks, kThreads, 0, s>>>(x, n, out); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_quantize_mode(const void* x, int dt, int64_t rows, int64_t k,
+                                       const float* g, uint8_t* codes, uint8_t* scales,
+                                       void* xhat, hipStream_t s) {
+  const int64_t halves = rows * k / 8;
+  if (halves == 0) return hipSuccess;
+  int blocks = grid_for(halves, kThreads, 1 << 20);
+  uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
+  switch (dt) {
+    case kF32:
+      quantize_kernel<kF32, MODE><<<blocks, kThreads, 0, s>>>(x, halves, g, c32, scales, xhat);
+      break;
+    case kF16:
+      quantize_kernel<kF16, MODE><<<blocks, kThreads, 0, s>>>(x, halves, g, c32, scales, xhat);
+      break;
+    default:
+      quantize_kernel<kBF16, MODE><<<blocks, kThreads, 0, s>>>(x, halves, g, c32, scales, xhat);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t k, const float* g,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  return launch_quantize_mode<0>(x, dt, rows, k, g, codes, scales, nullptr, s);
+}
+
+hipError_t launch_quant_dequant(const void* x, int dt, int64_t rows, int64_t k, const float* g,
+                                void* xhat, hipStream_t s) {
+  return launch_quantize_mode<1>(x, dt, rows, k, g, nullptr, nullptr, xhat, s);
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                             const float* g, void* out, int dt, hipStream_t s) {
+  const int64_t halves = rows * k / 8;
+  if (halves == 0) return hipSuccess;
+  int blocks = grid_for(halves, kThreads, 1 << 20);
+  const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
+  switch (dt) {
+    case kF32: dequantize_kernel<kF32><<<blocks, kThreads, 0, s>>>(c32, scales, halves, g, out); break;
+    case kF16: dequantize_kernel<kF16><<<blocks, kThreads, 0, s>>>(c32, scales, halves, g, out); break;
+    default: dequantize_kernel<kBF16><<<blocks, kThreads, 0, s>>>(c32, scales, halves, g, out); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,154 @@
+// nvfp4_device.h -- device-side building blocks of the NVFP4 kernels (gfx950).
+//
+// Formats (the pages fix them through their constants F4E2M1_MAX = 6 and
+// F8E4M3_MAX = 448, "mlx 0.30.7.2 -> 0.30.7.6" diff, page 7, fp_quantize.cu):
+//   e2m1  4-bit code s.ee.m, exponent bias 1, exponent 0 subnormal (step 0.5);
+//         magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+//   e4m3  8-bit s.eeee.mmm, bias 7, exponent 0 subnormal (m * 2^-9), largest
+//         finite 448 (0x7E), 0x7F / 0xFF NaN.
+// Both encoders round to nearest, ties to even, and saturate; a value that
+// rounds to zero keeps its sign (e2m1 code 0x8).
+//
+// Layout of a quantized tensor [rows, k] (k a multiple of 16): codes
+// [rows, k/2] bytes with element 2j in the low nibble of byte j, scales
+// [rows, k/16] e4m3 bytes, one per 16 consecutive elements of a row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+constexpr int kGroup = 16;
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// ----------------------------------------------------------------- element types
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { using T = float; };
+template <> struct Elem<kF16> { using T = _Float16; };
+template <> struct Elem<kBF16> { using T = __bf16; };
+
+// Round-to-nearest-even conversion of float to the element type (gfx950
+// v_cvt_pk_bf16_f32 / v_cvt_f16_f32 under the default round mode).
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::T from_f32(float v) {
+  return static_cast<typename Elem<DT>::T>(v);
+}
+template <int DT>
+__device__ __forceinline__ float to_f32(typename Elem<DT>::T v) {
+  return static_cast<float>(v);
+}
+
+// ----------------------------------------------------------------- global scale
+
+// Global encode factor 2688/g and decode factor g/2688, each one correctly
+// rounded float32 division; 1 without a global scale ("mlx 0.30.7.2 ->
+// 0.30.7.6" diff page 7, fp_quantize_rowwise and fp_dequantize; page 8,
+// fp_dequantize fallback).
+__device__ __forceinline__ float global_encode(const float* g) {
+#pragma clang fp contract(off)
+  return g ? (kE4M3Max * kE2M1Max) / *g : 1.0f;
+}
+__device__ __forceinline__ float global_decode(const float* g) {
+#pragma clang fp contract(off)
+  return g ? *g / (kE4M3Max * kE2M1Max) : 1.0f;
+}
+
+// ----------------------------------------------------------------- e4m3
+
+// Decode an e4m3 byte.  Exponent field 0 is subnormal: m * 2^-9.
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  uint32_t mag = b & 0x7Fu;
+  float normal = __uint_as_float((mag << 20) + (120u << 23));
+  float sub = (float)(mag & 7u) * 0.001953125f;
+  float v = (mag >> 3) ? normal : sub;
+  return (b & 0x80u) ? -v : v;
+}
+
+// Encode v >= 0 to e4m3: nearest, ties to even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
+  if (!(v < kE4M3Max)) return 0x7Eu;
+  if (v < 0.015625f) {  // below 2^-6: the subnormal grid has step 2^-9
+    return (uint32_t)__builtin_rintf(v * 512.0f);
+  }
+  uint32_t u = __float_as_uint(v);
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;  // keep 3 fraction bits
+  return r - (120u << 3);                                   // rebias 127 -> 7
+}
+
+// ----------------------------------------------------------------- e2m1
+
+// Encode y to an e2m1 code: nearest grid value, ties to the even code,
+// |y| > 6 saturates to 6, the sign bit of y is kept.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+  float a = __builtin_fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Value of an e2m1 code (low 4 bits of c) as float.
+__device__ __forceinline__ float e2m1_decode(uint32_t c) {
+  uint32_t m = c & 7u;
+  // m >= 2: exponent (m >> 1) - 1, fraction bit m & 1; m == 1: 0.5; m == 0: 0
+  uint32_t bits = (m >= 2u) ? ((m + 252u) << 22) : (m ? 0x3F000000u : 0u);
+  return __uint_as_float(bits | ((c & 8u) << 28));
+}
+
+// ----------------------------------------------------------------- group encode
+
+// Encode 16 values of one group ("mlx 0.30.7.2 -> 0.30.7.6" diff page 7,
+// fp_quantize_rowwise): amax of the block, decode scale (amax / 6) * enc
+// stored as e4m3, block encode factor enc / float(scale) (0 when the scale is
+// 0), each value multiplied by it and rounded to e2m1.  Float32 throughout,
+// no contraction.  Returns the scale byte; codes[i] receives code i.
+struct GroupScale {
+  uint32_t byte;
+  float enc_b;
+};
+
+__device__ __forceinline__ GroupScale group_scale_from_amax(float amax, float enc) {
+#pragma clang fp contract(off)
+  float sd = (amax / kE2M1Max) * enc;
+  uint32_t s = e4m3_encode_nonneg(sd);
+  float sf = e4m3_decode(s);
+  GroupScale gs;
+  gs.byte = s;
+  gs.enc_b = (sf == 0.0f) ? 0.0f : enc / sf;
+  return gs;
+}
+
+__device__ __forceinline__ uint32_t e2m1_encode_scaled(float x, float enc_b) {
+#pragma clang fp contract(off)
+  return e2m1_encode(x * enc_b);
+}
+
+// ----------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace nvfp4

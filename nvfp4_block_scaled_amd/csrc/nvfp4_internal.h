@@ -1,0 +1,38 @@
+// nvfp4_internal.h -- host-side launchers shared between the C ABI layer and
+// the kernel translation units.  Each launcher enqueues on `s` and returns the
+// HIP status of the launch; argument validation happens in capi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// codec.hip
+hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipStream_t s);
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t k, const float* g,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_dequant(const void* x, int dt, int64_t rows, int64_t k, const float* g,
+                                void* xhat, hipStream_t s);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                             const float* g, void* out, int dt, hipStream_t s);
+
+// qmv.hip
+constexpr int64_t kQmvMaxK = 32768;
+hipError_t launch_qmv(const void* x, int dt, const float* gx, const uint8_t* wc,
+                      const uint8_t* ws, const float* gw, int64_t n, int64_t k, void* out,
+                      hipStream_t s);
+
+// gemm.hip
+hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
+                            const float* gw, int64_t m, int64_t n, int64_t k, void* out,
+                            hipStream_t s);
+hipError_t launch_moe_route(const int32_t* idx, int64_t t, int64_t top_k, int64_t e,
+                            int32_t* offsets, int32_t* perm, hipStream_t s);
+hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
+                              const float* gw, const int32_t* offsets, const int32_t* perm,
+                              int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                              void* out, hipStream_t s);
+
+}  // namespace nvfp4

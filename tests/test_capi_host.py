@@ -1,0 +1,149 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load and export every entry point that include/nvfp4.h
+declares, and every argument error must be reported on the host, before any
+HIP call, with the pages' "[op] message" convention ("mlx 0.30.7.2 ->
+0.30.7.6" diff page 8: validate_global_scale, validate_qqmm_inputs).
+Addresses passed here are fake; validation rejects the call before anything
+dereferences them, and the architecture override stops every call that
+passes validation before it reaches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_block_scaled_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+INV, UNSUP = nv.NVFP4_ERR_INVALID_ARGUMENT, nv.NVFP4_ERR_UNSUPPORTED
+F32, F16, BF16 = 0, 1, 2
+A = 0x10000  # a fake, 256-byte aligned "device address"
+B = 0x20000
+C = 0x30000
+G = 0x40000
+W = 0x50000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        from nvfp4_block_scaled_amd import build
+        build.build()
+    lib = nv.load_library()
+    lib.nvfp4_debug_set_arch_override(b"gfx942")  # nothing reaches a device
+    yield lib
+    lib.nvfp4_debug_set_arch_override(None)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_version(L):
+    assert L.nvfp4_version() >= 100
+
+
+def err(L):
+    return L.nvfp4_last_error().decode()
+
+
+def test_quantize_argument_errors(L):
+    q = L.nvfp4_quantize
+    assert q(A, BF16, 4, 24, None, B, C, None) == INV and "group size 16" in err(L)
+    assert q(A, BF16, 4, 0, None, B, C, None) == INV
+    assert q(A, 7, 4, 32, None, B, C, None) == INV and "Unsupported dtype" in err(L)
+    assert q(A, BF16, -1, 32, None, B, C, None) == INV
+    assert q(None, BF16, 4, 32, None, B, C, None) == INV and "NULL" in err(L)
+    assert q(A, BF16, 4, 32, None, None, C, None) == INV
+    assert q(A + 2, BF16, 4, 32, None, B, C, None) == INV and "aligned" in err(L)
+    # valid arguments stop at the (overridden) architecture check
+    assert q(A, BF16, 4, 32, G, B, C, None) == UNSUP and "gfx950" in err(L)
+
+
+def test_dequantize_and_quant_dequant_errors(L):
+    assert L.nvfp4_dequantize(A, B, 4, 40, None, C, BF16, None) == INV
+    assert L.nvfp4_dequantize(None, B, 4, 32, None, C, BF16, None) == INV
+    assert L.nvfp4_dequantize(A, B, 4, 32, None, C, 3, None) == INV
+    assert L.nvfp4_quant_dequant(A, F16, 4, 32, None, None, None) == INV
+    assert L.nvfp4_quant_dequant(A, F16, 4, 32, None, C + 8, None) == INV
+    assert L.nvfp4_quant_dequant(A, F16, 4, 32, None, C, None) == UNSUP
+
+
+def test_qqmm_global_scales_both_or_neither(L):
+    ws = L.nvfp4_qqmm_workspace_size(8, 16, 32, BF16)
+    assert ws >= 8 * 32 * 2 and ws % 256 == 0
+    args = (A, BF16, G, W, B, None, 8, 16, 32, C, 0x60000, ws, None)
+    assert L.nvfp4_qqmm(*args) == INV
+    assert "both global_scale_x and global_scale_w" in err(L)
+    args = (A, BF16, None, W, B, G, 8, 16, 32, C, 0x60000, ws, None)
+    assert L.nvfp4_qqmm(*args) == INV
+    assert L.nvfp4_qmv(A, BF16, G, W, B, None, 16, 32, C, None) == INV
+    assert L.nvfp4_qmv(A, BF16, G, W, B, G, 16, 32, C, None) == UNSUP
+    assert L.nvfp4_qmv(A, BF16, None, W, B, None, 16, 32, C, None) == UNSUP
+
+
+def test_qqmm_shapes_and_workspace(L):
+    ws = L.nvfp4_qqmm_workspace_size(8, 16, 32, BF16)
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 8, 16, 20, C, 0x60000, ws, None) == INV
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 0, 16, 32, C, 0x60000, ws, None) == INV
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 8, 16, 32, C, 0x60000, ws - 1, None) == INV
+    assert "workspace" in err(L)
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 8, 16, 32, C, 0x60010, ws, None) == INV
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 8, 16, 32, C, 0x60000, ws, None) == UNSUP
+    # m == 1 needs no workspace
+    assert L.nvfp4_qqmm_workspace_size(1, 16, 32, BF16) == 0
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 1, 16, 32, C, None, 0, None) == UNSUP
+    assert L.nvfp4_qmv(A, BF16, None, W, B, None, 16, 65536, C, None) == UNSUP
+
+
+def test_gather_qmm_errors(L):
+    ws = L.nvfp4_gather_qmm_workspace_size(10, 2, 4, 16, 32)
+    assert ws >= (5 + 20) * 4
+    ok = (A, BF16, W, B, G, 0x70000, 10, 2, 4, 16, 32, C, 0x60000, ws, None)
+    assert L.nvfp4_gather_qmm(*ok) == UNSUP
+    bad = list(ok)
+    bad[10] = 24
+    assert L.nvfp4_gather_qmm(*bad) == INV
+    bad = list(ok)
+    bad[13] = ws - 4
+    assert L.nvfp4_gather_qmm(*bad) == INV
+    bad = list(ok)
+    bad[5] = None
+    assert L.nvfp4_gather_qmm(*bad) == INV
+    bad = list(ok)
+    bad[8] = 2000
+    assert L.nvfp4_gather_qmm(*bad) == UNSUP
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 0, A, B, None) == INV
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, None) == UNSUP
+
+
+def test_tensor_amax_errors(L):
+    assert L.nvfp4_tensor_amax(A, BF16, -1, B, None) == INV
+    assert L.nvfp4_tensor_amax(A, BF16, 10, None, None) == INV
+    assert L.nvfp4_tensor_amax(A, 9, 10, B, None) == INV
+    assert L.nvfp4_tensor_amax(A, BF16, 10, B, None) == UNSUP
+
+
+def test_python_binding_rejects_host_tensors_and_bad_modes():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize(x)
+    with pytest.raises(ValueError):
+        nv.quantize(x, group_size=32, mode="nvfp4")
+    with pytest.raises(ValueError):
+        nv.quantize(x, mode="mxfp4")

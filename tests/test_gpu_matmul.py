@@ -1,0 +1,287 @@
+"""GPU parity of the contractions (qmv, qqmm, gather_qmm, routing) against the
+oracle.  Exact-grid cases must match bit for bit; general data must meet the
+norm-wise 1e-2 bar (and, as a sharper regression guard, nearly every output
+must sit within one unit in the last place of the oracle's)."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_amd as nv
+import workloads as W
+from _parity import (O, assert_bytes_equal, assert_close, assert_values_equal, dev, host,
+                     oracle_dtype, say, scalar, ulp_fraction)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    nv.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _exact(x, w, dtype):
+    y = np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+    return np.array([[O.round_to(float(v), dtype) for v in row] for row in y], np.float32)
+
+
+# ------------------------------------------------------------------ exact grid cases
+
+@pytest.mark.parametrize("case", ["A", "B", "C", "D"])
+def test_grid_cases_qmv_bit_exact(case):
+    """x [1, 32], w [4, 32] on the e2m1 grid (osaurus-ai/mlx PR 31, "The test");
+    case A is the tiny exact configuration (float32, g_x = 2688, g_w = 336)."""
+    say(f"grid case {case} (qmv)")
+    c = W.grid_case(case)
+    tdt = {"f32": torch.float32, "f16": torch.float16}[c["dtype"]]
+    x, w = c["x"].to(tdt), c["w"].to(tdt)
+    gx, gw = scalar(c["g_x"]), scalar(c["g_w"])
+    wc, ws = nv.nvfp4_quantize(w.cuda(), gw)
+    y_qmv = nv.nvfp4_qmv(x.cuda(), wc, ws, gx, gw)
+    y_qqmm = nv.nvfp4_qqmm(x.cuda(), wc, ws, gx, gw)
+    torch.cuda.synchronize()
+    oc, os_ = O.quantize(host(w), c["g_w"])
+    assert_bytes_equal(wc.cpu().numpy(), oc, "w codes")
+    assert_bytes_equal(ws.cpu().numpy(), os_, "w scales")
+    ref = O.qqmm(host(x), oc, os_, c["g_x"], c["g_w"], dtype=c["dtype"])
+    assert np.array_equal(ref, _exact(host(x), host(w), c["dtype"]))
+    assert_values_equal(host(y_qmv), ref, "qmv")
+    assert_values_equal(host(y_qqmm), ref, "qqmm m=1")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("gx,gw", [(2688.0, 336.0), (None, None), (2688.0, 10.5), (1344.0, 2688.0)])
+def test_grid_qqmm_multi_row_bit_exact(dtype, gx, gw):
+    """Exact-grid operands at M > 1 (several tiles in N and a ragged tail)."""
+    say(f"grid qqmm {dtype} gx={gx} gw={gw}")
+    x = W.grid_tensor(37, 64, seed=5)
+    w = W.grid_tensor(300, 64, seed=6)
+    if gx == 1344.0:
+        x = x * 0.5  # enc = 2 puts x's block scales at 1 again
+    od = oracle_dtype(dtype)
+    wc, ws = nv.nvfp4_quantize(w.to(dtype).cuda(), scalar(gw))
+    y = nv.nvfp4_qqmm(x.to(dtype).cuda(), wc, ws, scalar(gx), scalar(gw))
+    torch.cuda.synchronize()
+    ref = _exact(host(x.to(dtype)), host(w.to(dtype)), od)
+    oc, os_ = O.quantize(host(w.to(dtype)), gw)
+    assert np.array_equal(O.qqmm(host(x.to(dtype)), oc, os_, gx, gw, dtype=od), ref)
+    assert_values_equal(host(y), ref, "grid qqmm")
+
+
+# ------------------------------------------------------------------ qmv
+
+def _quantized_weight(w, g_host):
+    """Oracle codes for w (the kernel under test gets the same bytes)."""
+    return O.quantize(host(w), g_host)
+
+
+def test_qmv_decode_14336x4096():
+    """x bf16 [1, 4096] Normal(0, 1), w [14336, 4096] from Normal(0, 0.02),
+    g_x = amax(x), g_w = amax(w)."""
+    say("qmv decode 1x4096 @ 14336x4096")
+    x, w = W.qmv_inputs()
+    xd, wd = x.cuda(), w.cuda()
+    gx, gw = nv.nvfp4_tensor_amax(xd), nv.nvfp4_tensor_amax(wd)
+    wc, ws = nv.nvfp4_quantize(wd, gw)
+    y = nv.nvfp4_qmv(xd, wc, ws, gx, gw)
+    torch.cuda.synchronize()
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    assert float(gx.item()) == gxh and float(gw.item()) == gwh
+    oc, os_ = _quantized_weight(w, gwh)
+    assert_bytes_equal(ws.cpu().numpy(), os_, "w scales")
+    assert_bytes_equal(wc.cpu().numpy(), oc, "w codes")
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16")
+    got = host(y)
+    assert_close(got, ref, what="qmv")
+    frac = ulp_fraction(got, ref, "bf16")
+    say(f"  within 1 bf16 ulp: {frac:.4f}")
+    assert frac >= 0.99
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("n,k", [(1, 16), (5, 32), (1000, 1040), (77, 4096), (33, 8192), (3, 32768)])
+def test_qmv_shapes(dtype, n, k):
+    say(f"qmv {dtype} n={n} k={k}")
+    x = W.normal((1, k), 1.0, 10 + k, oracle_dtype(dtype))
+    w = W.normal((n, k), 0.02, 20 + n, oracle_dtype(dtype))
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    y = nv.nvfp4_qmv(x.cuda(), dev(oc), dev(os_), scalar(gxh), scalar(gwh))
+    y0 = nv.nvfp4_qmv(x.cuda(), dev(oc), dev(os_), None, None)
+    torch.cuda.synchronize()
+    od = oracle_dtype(dtype)
+    assert_close(host(y), O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od), what="qmv g")
+    assert_close(host(y0), O.qqmm(host(x), oc, os_, None, None, dtype=od), what="qmv no g")
+
+
+# ------------------------------------------------------------------ qqmm
+
+@pytest.mark.parametrize("m", [256, 512, 67])
+@pytest.mark.parametrize("n", [64, 256, 512])
+@pytest.mark.parametrize("k", [256, 4096])
+def test_qqmm_sweep(m, n, k):
+    """The pages' qqmm test sweep M in {256, 512, 67} x N in {64, 256, 512}."""
+    say(f"qqmm sweep m={m} n={n} k={k}")
+    x, w = W.qqmm_inputs(seed=40 + m + n, m=m, n=n, k=k)
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    y = nv.nvfp4_qqmm(x.cuda(), dev(oc), dev(os_), scalar(gxh), scalar(gwh))
+    torch.cuda.synchronize()
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16")
+    got = host(y)
+    assert_close(got, ref, what="qqmm")
+    assert ulp_fraction(got, ref, "bf16") >= 0.99
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("m,n,k", [(2, 17, 16), (300, 300, 80), (257, 1, 1040), (64, 513, 128)])
+def test_qqmm_ragged(dtype, m, n, k):
+    say(f"qqmm ragged {dtype} {m}x{n}x{k}")
+    x, w = W.qqmm_inputs(seed=m + n + k, m=m, n=n, k=k, dtype=oracle_dtype(dtype))
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    y = nv.nvfp4_qqmm(x.cuda(), dev(oc), dev(os_), scalar(gxh), scalar(gwh))
+    torch.cuda.synchronize()
+    assert_close(host(y), O.qqmm(host(x), oc, os_, gxh, gwh, dtype=oracle_dtype(dtype)),
+                 what="qqmm ragged")
+
+
+def test_qqmm_prefill_2048x14336x4096_sampled():
+    """x bf16 [2048, 4096] Normal(0, 1), w [14336, 4096] from Normal(0, 0.02);
+    every output row/column band is sampled against the oracle."""
+    say("qqmm prefill 2048x4096 @ 14336x4096 (sampled)")
+    x, w = W.qqmm_inputs()
+    xd, wd = x.cuda(), w.cuda()
+    gx, gw = nv.nvfp4_tensor_amax(xd), nv.nvfp4_tensor_amax(wd)
+    wc, ws = nv.nvfp4_quantize(wd, gw)
+    y = nv.nvfp4_qqmm(xd, wc, ws, gx, gw)
+    torch.cuda.synchronize()
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    assert float(gx.item()) == gxh and float(gw.item()) == gwh
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 2047], rng.integers(0, 2048, 19)]))
+    cols = np.unique(np.concatenate([[0, 1, 255, 256, 14335], rng.integers(0, 14336, 251)]))
+    oc, os_ = O.quantize(host(w[torch.from_numpy(cols)]), gwh)
+    assert_bytes_equal(wc[torch.from_numpy(cols).cuda()].cpu().numpy(), oc, "sampled w codes")
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16", rows=rows)
+    got = host(y)[rows][:, cols]
+    assert_close(got, ref, what="qqmm prefill sample")
+    assert ulp_fraction(got, ref, "bf16") >= 0.99
+
+
+# ------------------------------------------------------------------ routing / gather
+
+@pytest.mark.parametrize("t,e,top_k", [(1, 1, 1), (257, 8, 2), (4096, 8, 2), (3000, 64, 4),
+                                        (100, 5, 3)])
+def test_moe_route_bit_exact(t, e, top_k):
+    say(f"moe_route t={t} e={e} top_k={top_k}")
+    idx = W.expert_indices(t, e, top_k, seed=t + e)
+    off, perm = nv.nvfp4_moe_route(idx.cuda(), e)
+    torch.cuda.synchronize()
+    ooff, operm = O.moe_route(idx.numpy(), e)
+    assert_bytes_equal(off.cpu().numpy(), ooff, "offsets")
+    assert_bytes_equal(perm.cpu().numpy(), operm, "perm")
+
+
+def test_gather_qmm_grid_bit_exact():
+    say("gather_qmm exact grid")
+    E, T, K, N, top_k = 3, 40, 64, 300, 2
+    gs = [336.0, 2688.0, 10.5]
+    ws_ = [W.grid_tensor(N, K, seed=300 + e) for e in range(E)]
+    codes = np.stack([O.quantize(ws_[e].numpy(), gs[e])[0] for e in range(E)])
+    scales = np.stack([O.quantize(ws_[e].numpy(), gs[e])[1] for e in range(E)])
+    x = W.grid_tensor(T, K, seed=310)
+    idx = W.expert_indices(T, E, top_k, seed=311)
+    for dtype in (torch.float32, torch.float16, torch.bfloat16):
+        g = torch.tensor(gs, dtype=torch.float32, device="cuda").reshape(E, 1, 1)
+        y = nv.nvfp4_gather_qmm(x.to(dtype).cuda(), dev(codes), dev(scales), idx.cuda(), g)
+        torch.cuda.synchronize()
+        od = oracle_dtype(dtype)
+        ref = O.gather_qmm(host(x.to(dtype)), codes, scales, idx.numpy(), np.array(gs), dtype=od)
+        for t in range(T):
+            for j in range(top_k):
+                ex = _exact(host(x.to(dtype))[t:t + 1], ws_[idx[t, j]].numpy(), od)[0]
+                assert np.array_equal(ref[t, j], ex)
+        assert_values_equal(host(y), ref, f"gather grid {dtype}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+def test_gather_qmm_ragged_experts(dtype):
+    """Uneven expert loads including an expert with no tokens, ragged N and K."""
+    say(f"gather_qmm ragged {dtype}")
+    E, T, K, N, top_k = 5, 300, 272, 300, 2
+    od = oracle_dtype(dtype)
+    x = W.normal((T, K), 1.0, 50, od)
+    w = W.normal((E, N, K), 0.02, 51, od)
+    idx = W.expert_indices(T, E - 1, top_k, seed=52)  # expert E-1 receives nothing
+    idx = torch.where(idx == 1, torch.full_like(idx, 2), idx)  # expert 1 empty too
+    idx[0, 0], idx[0, 1] = 3, 0
+    gs = np.array([O.tensor_amax(host(w[e])) for e in range(E)], np.float32)
+    codes = np.stack([O.quantize(host(w[e]), float(gs[e]))[0] for e in range(E)])
+    scales = np.stack([O.quantize(host(w[e]), float(gs[e]))[1] for e in range(E)])
+    y = nv.nvfp4_gather_qmm(x.cuda(), dev(codes), dev(scales), idx.cuda(), dev(gs))
+    y0 = nv.nvfp4_gather_qmm(x.cuda(), dev(codes), dev(scales), idx.cuda(), None)
+    torch.cuda.synchronize()
+    ref = O.gather_qmm(host(x), codes, scales, idx.numpy(), gs, dtype=od)
+    assert_close(host(y), ref, what="gather ragged")
+    ref0 = O.gather_qmm(host(x), codes, scales, idx.numpy(), None, dtype=od)
+    assert_close(host(y0), ref0, what="gather ragged no g")
+
+
+def test_gather_qmm_moe_8x14336x4096_sampled():
+    """8 experts [14336, 4096] from Normal(0, 0.02) with per-expert amax global
+    scales [8, 1, 1]; x bf16 [4096, 4096] Normal(0, 1); top-2 uniform."""
+    say("gather_qmm MoE 4096 tokens x 8 experts 14336x4096 (sampled)")
+    T, E, N, K, top_k = 4096, 8, 14336, 4096, 2
+    x, w, idx = W.gather_inputs(device="cuda")
+    g = torch.empty(E, dtype=torch.float32, device="cuda")
+    for e in range(E):
+        nv.nvfp4_tensor_amax(w[e], out=g[e:e + 1])
+    wc = torch.empty(E, N, K // 2, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(E, N, K // 16, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        nv.nvfp4_quantize(w[e], g[e:e + 1], codes=wc[e], scales=ws[e])
+    y = nv.nvfp4_gather_qmm(x, wc, ws, idx, g.reshape(E, 1, 1))
+    torch.cuda.synchronize()
+    g_dev = g.cpu().numpy()
+    gh = np.zeros(E, np.float32)
+    rng = np.random.default_rng(5)
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.integers(0, N, 124)]))
+    pairs = [(0, 0), (0, 1), (T - 1, 1)] + [(int(a), int(b)) for a, b in
+                                            zip(rng.integers(0, T, 29), rng.integers(0, 2, 29))]
+    idx_h = idx.cpu().numpy()
+    xh = host(x)
+    col_t = torch.from_numpy(cols).cuda()
+    codes_s = np.zeros((E, len(cols), K // 2), np.uint8)
+    scales_s = np.zeros((E, len(cols), K // 16), np.uint8)
+    for e in range(E):
+        we = host(w[e])
+        gh[e] = O.tensor_amax(we)
+        assert float(g_dev[e]) == float(gh[e])
+        oc, os_ = O.quantize(we[cols], float(gh[e]))
+        assert_bytes_equal(wc[e][col_t].cpu().numpy(), oc, f"expert {e} sampled codes")
+        codes_s[e], scales_s[e] = oc, os_
+    ref = O.gather_qmm(xh, codes_s, scales_s, idx_h, gh, dtype="bf16", pairs=pairs)
+    got = np.stack([host(y[t, j])[cols] for t, j in pairs])
+    assert_close(got, ref, what="gather MoE sample")
+    assert ulp_fraction(got, ref, "bf16") >= 0.99
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("m,n,k", [(1, 300, 256), (130, 260, 4096), (7, 33, 48)])
+def test_qmm_unquantized_activations(dtype, m, n, k):
+    """x @ dequant(w)^T with x as given (the pages' quantized_matmul)."""
+    say(f"qmm {dtype} {m}x{n}x{k}")
+    od = oracle_dtype(dtype)
+    x = W.normal((m, k), 1.0, 60 + m, od)
+    w = W.normal((1, n, k), 0.02, 61 + n, od)
+    gwh = O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w[0]), gwh)
+    y = nv.nvfp4_qmm(x.cuda(), dev(oc), dev(os_), scalar(gwh))
+    torch.cuda.synchronize()
+    # the same contraction as a one-expert gather with every token routed to it
+    ref = O.gather_qmm(host(x), oc[None], os_[None], np.zeros((m, 1), np.int32), np.array([gwh]),
+                       dtype=od)[:, 0]
+    assert_close(host(y), ref, what="qmm")
