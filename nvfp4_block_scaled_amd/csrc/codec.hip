@@ -62,18 +62,30 @@ __device__ __forceinline__ void store8(void* base, int64_t h, const float (&v)[8
 
 // ------------------------------------------------------------------ amax
 
+constexpr int kAmaxBlocks = 512;
+
 __global__ void amax_zero_kernel(float* out) { *out = 0.0f; }
 
-// max |x| over n elements: vectorised grid-stride loop over 8-element chunks,
-// a scalar tail, a wave max and one atomicMax per wave on the float's bit
-// pattern (non-negative floats order like their unsigned bits).
+// max |x| over n elements: grid-stride loop over 8-element chunks (two in
+// flight per lane), a scalar tail, a wave max, a workgroup max through LDS and
+// one atomicMax per workgroup on the float's bit pattern (non-negative floats
+// order like their unsigned bits).
 template <int DT>
 __global__ void __launch_bounds__(kThreads) amax_kernel(const void* __restrict__ x, int64_t n,
                                                         float* __restrict__ out) {
+  __shared__ float part[kThreads / 64];
   const int64_t chunks = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   float m = 0.0f;
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < chunks; h += stride) {
+  int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; h + stride < chunks; h += 2 * stride) {
+    float v[8], u[8];
+    load8<DT>(x, h, v);
+    load8<DT>(x, h + stride, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fmaxf(__builtin_fabsf(v[i]), __builtin_fabsf(u[i])));
+  }
+  if (h < chunks) {
     float v[8];
     load8<DT>(x, h, v);
 #pragma unroll
@@ -85,13 +97,53 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const void* __restrict__
     m = fmaxf(m, __builtin_fabsf(to_f32<DT>(reinterpret_cast<const T*>(x)[i])));
   }
   m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = part[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, part[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(b));
+  }
 }
 
 // ------------------------------------------------------------------ quantize
 
-// One lane per half group: h in [0, 2 * groups).  MODE 0 writes codes and
-// scales; MODE 1 writes the dequantized values x_hat in the input type.
+// One lane per half group: h in [0, 2 * groups), two half groups (h and
+// h + stride) in flight per iteration.  MODE 0 writes codes and scales;
+// MODE 1 writes the dequantized values x_hat in the input type.  Pair
+// partners (h, h ^ 1) always take the same branches: halves and the stride
+// are even.
+template <int DT, int MODE>
+__device__ __forceinline__ void quantize_one(const float (&v)[8], int64_t h, float enc, float dec,
+                                             uint32_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales, void* __restrict__ xhat) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));  // the pair partner holds the other half
+  uint32_t byte;
+  const uint32_t word = encode_half_group(v, a, enc, byte);
+  if constexpr (MODE == 0) {
+    codes[h] = word;
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)byte;
+  } else {
+    float sc;
+    {
+#pragma clang fp contract(off)
+      sc = e4m3_decode(byte) * dec;
+    }
+    float q[8], o[8];
+    e2m1_decode8_f32(word, q);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+      o[i] = q[i] * sc;
+    }
+    store8<DT>(xhat, h, o);
+  }
+}
+
 template <int DT, int MODE>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const void* __restrict__ x, int64_t halves, const float* __restrict__ gscale,
@@ -99,65 +151,58 @@ quantize_kernel(const void* __restrict__ x, int64_t halves, const float* __restr
   const float enc = global_encode(gscale);
   const float dec = global_decode(gscale);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;  // even
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < halves; h += stride) {
+  int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; h + stride < halves; h += 2 * stride) {
+    float v[8], u[8];
+    load8<DT>(x, h, v);
+    load8<DT>(x, h + stride, u);
+    quantize_one<DT, MODE>(v, h, enc, dec, codes, scales, xhat);
+    quantize_one<DT, MODE>(u, h + stride, enc, dec, codes, scales, xhat);
+  }
+  if (h < halves) {
     float v[8];
     load8<DT>(x, h, v);
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-    a = fmaxf(a, __shfl_xor(a, 1, 64));  // the pair partner holds the other half
-    GroupScale gs = group_scale_from_amax(a, enc);
-    uint32_t word = 0;
-    uint32_t c[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      c[i] = e2m1_encode_scaled(v[i], gs.enc_b);
-      word |= c[i] << (4 * i);
-    }
-    if constexpr (MODE == 0) {
-      codes[h] = word;
-      if ((h & 1) == 0) scales[h >> 1] = (uint8_t)gs.byte;
-    } else {
-      float sc;
-      {
-#pragma clang fp contract(off)
-        sc = e4m3_decode(gs.byte) * dec;
-      }
-      float o[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-        o[i] = e2m1_decode(c[i]) * sc;
-      }
-      store8<DT>(xhat, h, o);
-    }
+    quantize_one<DT, MODE>(v, h, enc, dec, codes, scales, xhat);
   }
 }
 
 // ------------------------------------------------------------------ dequantize
 
 template <int DT>
+__device__ __forceinline__ void dequantize_one(uint32_t word, uint32_t s, float dec, int64_t h,
+                                               void* __restrict__ out) {
+  float sc;
+  {
+#pragma clang fp contract(off)
+    sc = e4m3_decode(s) * dec;
+  }
+  float q[8], o[8];
+  e2m1_decode8_f32(word, q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    o[i] = q[i] * sc;
+  }
+  store8<DT>(out, h, o);
+}
+
+// One lane per half group (one code dword), two in flight per iteration.
+template <int DT>
 __global__ void __launch_bounds__(kThreads)
 dequantize_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                   int64_t halves, const float* __restrict__ gscale, void* __restrict__ out) {
   const float dec = global_decode(gscale);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h < halves; h += stride) {
-    uint32_t word = __builtin_nontemporal_load(codes + h);
-    uint32_t s = scales[h >> 1];
-    float sc;
-    {
-#pragma clang fp contract(off)
-      sc = e4m3_decode(s) * dec;
-    }
-    float o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-      o[i] = e2m1_decode(word >> (4 * i)) * sc;
-    }
-    store8<DT>(out, h, o);
+  int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; h + stride < halves; h += 2 * stride) {
+    uint32_t w0 = __builtin_nontemporal_load(codes + h);
+    uint32_t w1 = __builtin_nontemporal_load(codes + h + stride);
+    uint32_t s0 = scales[h >> 1];
+    uint32_t s1 = scales[(h + stride) >> 1];
+    dequantize_one<DT>(w0, s0, dec, h, out);
+    dequantize_one<DT>(w1, s1, dec, h + stride, out);
   }
+  if (h < halves) dequantize_one<DT>(__builtin_nontemporal_load(codes + h), scales[h >> 1], dec, h, out);
 }
 
 int grid_for(int64_t work, int per_block, int max_blocks) {
@@ -174,7 +219,7 @@ int grid_for(int64_t work, int per_block, int max_blocks) {
 hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipStream_t s) {
   amax_zero_kernel<<<1, 1, 0, s>>>(out);
   if (n > 0) {
-    int blocks = grid_for(n / 8 + 1, kThreads * 4, 2048);
+    int blocks = grid_for(n / 8 + 1, kThreads * 2, kAmaxBlocks);
     switch (dt) {
       case kF32: amax_kernel<kF32><<<blocks, kThreads, 0, s>>>(x, n, out); break;
       case kF16: amax_kernel<kF16><<<blocks, kThreads, 0, s>>>(x, n, out); break;
@@ -190,7 +235,7 @@ static hipError_t launch_quantize_mode(const void* x, int dt, int64_t rows, int6
                                        void* xhat, hipStream_t s) {
   const int64_t halves = rows * k / 8;
   if (halves == 0) return hipSuccess;
-  int blocks = grid_for(halves, kThreads, 1 << 20);
+  int blocks = grid_for(halves, kThreads * 2, 1 << 20);
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
   switch (dt) {
     case kF32:
@@ -220,7 +265,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
                              const float* g, void* out, int dt, hipStream_t s) {
   const int64_t halves = rows * k / 8;
   if (halves == 0) return hipSuccess;
-  int blocks = grid_for(halves, kThreads, 1 << 20);
+  int blocks = grid_for(halves, kThreads * 2, 1 << 20);
   const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
   switch (dt) {
     case kF32: dequantize_kernel<kF32><<<blocks, kThreads, 0, s>>>(c32, scales, halves, g, out); break;

@@ -109,13 +109,56 @@ __device__ __forceinline__ float e2m1_decode(uint32_t c) {
   return __uint_as_float(bits | ((c & 8u) << 28));
 }
 
+// ----------------------------------------------------------------- gfx950 conversions
+//
+// v_cvt_scalef32_pk_* convert two e2m1 values to or from a wider type.  Their
+// scale operand contributes only its exponent (a power of two, as for MX
+// block scales), so every call here passes 1.0 and the NVFP4 block scale is
+// applied with an ordinary float32 multiply.  With unit scale the encode is
+// round-to-nearest-even with saturation at 6 and keeps the sign of zero,
+// which equals e2m1_encode above for every float32 input; the decodes are
+// exact.  Element 2j of a byte is its low nibble.
+
+// Encode 8 values into the 8 nibbles of a dword (element i in bits 4i..4i+3).
+__device__ __forceinline__ uint32_t e2m1_encode8(const float (&y)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+
+// Decode the two nibbles of byte B of w.
+template <int B>
+__device__ __forceinline__ f32x2 e2m1_decode2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ bf16x2 e2m1_decode2_bf16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B);
+}
+template <int B>
+__device__ __forceinline__ f16x2 e2m1_decode2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B);
+}
+
+// Decode the 8 nibbles of a dword to float32.
+__device__ __forceinline__ void e2m1_decode8_f32(uint32_t w, float (&v)[8]) {
+  f32x2 a = e2m1_decode2_f32<0>(w), b = e2m1_decode2_f32<1>(w);
+  f32x2 c = e2m1_decode2_f32<2>(w), d = e2m1_decode2_f32<3>(w);
+  v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
+}
+
 // ----------------------------------------------------------------- group encode
 
-// Encode 16 values of one group ("mlx 0.30.7.2 -> 0.30.7.6" diff page 7,
-// fp_quantize_rowwise): amax of the block, decode scale (amax / 6) * enc
-// stored as e4m3, block encode factor enc / float(scale) (0 when the scale is
-// 0), each value multiplied by it and rounded to e2m1.  Float32 throughout,
-// no contraction.  Returns the scale byte; codes[i] receives code i.
+// Encode one group of 16 ("mlx 0.30.7.2 -> 0.30.7.6" diff page 7,
+// fp_quantize_rowwise): from the block amax, the decode scale (amax / 6) * enc
+// stored as e4m3, and the block encode factor enc / float(scale) (0 when the
+// scale is 0, so such a block encodes to signed zeros); each value is then
+// multiplied by that factor and rounded to e2m1.  Float32 throughout, no
+// contraction.
 struct GroupScale {
   uint32_t byte;
   float enc_b;
@@ -137,6 +180,21 @@ __device__ __forceinline__ uint32_t e2m1_encode_scaled(float x, float enc_b) {
   return e2m1_encode(x * enc_b);
 }
 
+// Encode 8 values of a half group whose group amax is `amax`: returns the 8
+// codes as one dword and sets `byte` to the group's scale byte.
+__device__ __forceinline__ uint32_t encode_half_group(const float (&v)[8], float amax, float enc,
+                                                      uint32_t& byte) {
+  GroupScale gs = group_scale_from_amax(amax, enc);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    y[i] = v[i] * gs.enc_b;
+  }
+  byte = gs.byte;
+  return e2m1_encode8(y);
+}
+
 // ----------------------------------------------------------------- wave reductions
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -149,6 +207,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Sum over the 64 lanes, returned as a wave-uniform value: four DPP steps
+// reduce each row of 16 lanes (xor 1, xor 2, half-row mirror, row mirror),
+// then the four row sums are read from lanes 0, 16, 32 and 48.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
 }
 
 }  // namespace nvfp4

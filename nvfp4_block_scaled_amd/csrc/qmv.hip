@@ -5,18 +5,25 @@
 // QQMatmul::eval_gpu, M == 1 branch; "[Metal] global scale for qmm" PR 4458,
 // statement: the global factor belongs inside the dequantization).
 //
-// Design (HBM-bound: the weight stream is 9/16 byte per element):
-//   * every workgroup first rebuilds x_hat from x (k/8 half groups spread over
-//     its 512 lanes) into LDS as float32; the first weight rows are already in
-//     flight while it does so;
-//   * each wave then owns a contiguous range of rows; for a row, lane l holds
-//     GPL consecutive groups of 16 (GPL = 4: 32 B of codes + 4 B of scales,
-//     two 16-byte loads and one dword), so one wave reads a 4096-wide row in
-//     one coalesced sweep;
-//   * the block partial sum_i x_hat_i * e2m1(q_i) is formed in float32 and
-//     multiplied by the block's effective scale e4m3(s) * g_w/2688, i.e. the
-//     global factor sits on the block scale as in the pages;
-//   * a wave-wide reduction and one store per row.
+// The kernel is HBM-bound: the weight stream is 9/16 byte per element and
+// nothing is reused, so the design is about keeping enough bytes in flight.
+//
+// Register path (k = 4096 * CH, CH = 1 or 2 for 16-bit x, 1 for float32):
+//   * every wave owns up to R consecutive rows and issues the loads of all of
+//     them (per row and lane: CH x 32 code bytes + CH x 4 scale bytes, the
+//     lanes of a wave covering each 2 KB chunk of a row contiguously) before
+//     doing anything else, so the whole matrix is requested at once;
+//   * meanwhile the workgroup rebuilds x_hat = T(dequant(quant(x, g_x))) in
+//     LDS (one half group of 8 per lane and chunk) and every lane then keeps
+//     the 64 * CH x_hat values of its k slice in registers;
+//   * per row, each group of 16 is decoded two codes per instruction
+//     (v_cvt_scalef32_pk_*_fp4, exact) and contracted with x_hat two at a time
+//     (v_dot2_f32_bf16 / _f16: exact products, float32 sums, or float32 FMAs),
+//     and the block's partial sum is multiplied by its effective scale
+//     e4m3(s) * g_w/2688 -- the global factor rides on the block scale;
+//   * a DPP row reduction plus four lane reads give the row sum.
+// Generic path (any k % 16 == 0 up to 32768): one group per lane per sweep,
+// x_hat in LDS as float32 padded to 17 words per group (conflict-free reads).
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -26,6 +33,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreadsQ = kWaves * 64;
+constexpr int kMaxRows = 8;  // rows per wave on the register path
 
 template <int DT>
 __device__ __forceinline__ void load8x(const void* base, int64_t h, float (&v)[8]) {
@@ -51,122 +59,271 @@ __device__ __forceinline__ void load8x(const void* base, int64_t h, float (&v)[8
   }
 }
 
-// Sum over one group of 16 of x_hat_i * e2m1(q_i); codes lo/hi hold the 16
-// nibbles (element 2j in the low nibble of byte j).
-__device__ __forceinline__ float group_dot(const float* xg, uint32_t lo, uint32_t hi) {
-  float p = 0.0f;
+// x_hat of one half group (8 values at element 8h), rounded to T, as floats.
+// The pair partner (lane ^ 1) holds the other half of the group.
+template <int DT>
+__device__ __forceinline__ void xhat_half_group(const float (&v)[8], float enc, float dec,
+                                                float (&o)[8]) {
+  float a = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p = __builtin_fmaf(xg[i], e2m1_decode(lo >> (4 * i)), p);
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  uint32_t byte;
+  uint32_t codes = encode_half_group(v, a, enc, byte);
+  float sc;
+  {
+#pragma clang fp contract(off)
+    sc = e4m3_decode(byte) * dec;
+  }
+  float q[8];
+  e2m1_decode8_f32(codes, q);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p = __builtin_fmaf(xg[8 + i], e2m1_decode(hi >> (4 * i)), p);
-  return p;
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    o[i] = to_f32<DT>(from_f32<DT>(q[i] * sc));
+  }
 }
 
-template <int DT, int GPL>
-__global__ void __launch_bounds__(kThreadsQ)
-qmv_kernel(const void* __restrict__ x, const float* __restrict__ gx,
-           const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-           const float* __restrict__ gw, int n, int k, void* __restrict__ out) {
-  extern __shared__ float xs[];  // x_hat, k floats
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int groups = k >> 4;
+// Partial dot product of one group of 16 (codes in dwords c0, c1) with
+// x_hat (16-bit pairs xp[0..7], or floats xf[0..15]).
+template <int DT>
+__device__ __forceinline__ float group_dot16(uint32_t c0, uint32_t c1, const uint32_t* xp,
+                                             const float* xf) {
+  if constexpr (DT == kBF16) {
+    float p = 0.0f;
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<0>(c0), __builtin_bit_cast(bf16x2, xp[0]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<1>(c0), __builtin_bit_cast(bf16x2, xp[1]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<2>(c0), __builtin_bit_cast(bf16x2, xp[2]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<3>(c0), __builtin_bit_cast(bf16x2, xp[3]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<0>(c1), __builtin_bit_cast(bf16x2, xp[4]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<1>(c1), __builtin_bit_cast(bf16x2, xp[5]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<2>(c1), __builtin_bit_cast(bf16x2, xp[6]), p, false);
+    p = __builtin_amdgcn_fdot2_f32_bf16(e2m1_decode2_bf16<3>(c1), __builtin_bit_cast(bf16x2, xp[7]), p, false);
+    return p;
+  } else if constexpr (DT == kF16) {
+    float p = 0.0f;
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<0>(c0), __builtin_bit_cast(f16x2, xp[0]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<1>(c0), __builtin_bit_cast(f16x2, xp[1]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<2>(c0), __builtin_bit_cast(f16x2, xp[2]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<3>(c0), __builtin_bit_cast(f16x2, xp[3]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<0>(c1), __builtin_bit_cast(f16x2, xp[4]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<1>(c1), __builtin_bit_cast(f16x2, xp[5]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<2>(c1), __builtin_bit_cast(f16x2, xp[6]), p, false);
+    p = __builtin_amdgcn_fdot2(e2m1_decode2_f16<3>(c1), __builtin_bit_cast(f16x2, xp[7]), p, false);
+    return p;
+  } else {
+    float q[16];
+    float(&lo)[8] = *reinterpret_cast<float(*)[8]>(q);
+    float(&hi)[8] = *reinterpret_cast<float(*)[8]>(q + 8);
+    e2m1_decode8_f32(c0, lo);
+    e2m1_decode8_f32(c1, hi);
+    float p = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(q[i], xf[i], p);
+    return p;
+  }
+}
 
-  // ---- x_hat = dequantize(quantize(x, g_x), g_x), rounded to T, into LDS
+// ------------------------------------------------------------------ register path
+
+template <int DT, int CH>
+__global__ void __launch_bounds__(kThreadsQ)
+qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+               const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+               const float* __restrict__ gw, int n, int rpw, void* __restrict__ out) {
+  constexpr int K = 4096 * CH;
+  constexpr bool kF = (DT == kF32);
+  // x_hat in LDS: 16-bit values for 16-bit T, float32 otherwise
+  __shared__ __attribute__((aligned(16))) uint32_t xs[kF ? K : K / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // 1. this thread's half groups of x (K / 8 = 512 * CH of them)
+  float xv[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) load8x<DT>(x, tid + kThreadsQ * c, xv[c]);
+
+  // 2. all weight loads of this wave's rows
+  const int r0 = (blockIdx.x * kWaves + wave) * rpw;
+  u32x4 ca[kMaxRows][CH], cb[kMaxRows][CH];
+  uint32_t sw[kMaxRows][CH];
+#pragma unroll
+  for (int i = 0; i < kMaxRows; ++i) {
+    const int r = min(r0 + i, n - 1);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = c * 64 + lane;  // chunk of 64 elements = 4 groups
+      const u32x4* cp = reinterpret_cast<const u32x4*>(wc + (int64_t)r * (K / 2) + ci * 32);
+      if (i < rpw) {
+        ca[i][c] = __builtin_nontemporal_load(cp);
+        cb[i][c] = __builtin_nontemporal_load(cp + 1);
+        sw[i][c] = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(ws + (int64_t)r * (K / 16) + ci * 4));
+      }
+    }
+  }
+
+  // 3. x_hat into LDS
   {
     const float enc = global_encode(gx);
     const float dec = global_decode(gx);
-    const int halves = k >> 3;  // even
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int h = tid + kThreadsQ * c;
+      float o[8];
+      xhat_half_group<DT>(xv[c], enc, dec, o);
+      if constexpr (kF) {
+        f32x4* p = reinterpret_cast<f32x4*>(xs) + 2 * h;
+        p[0] = f32x4{o[0], o[1], o[2], o[3]};
+        p[1] = f32x4{o[4], o[5], o[6], o[7]};
+      } else {
+        using T = typename Elem<DT>::T;
+        typedef T T8 __attribute__((ext_vector_type(8)));
+        T8 t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = from_f32<DT>(o[i]);
+        reinterpret_cast<T8*>(xs)[h] = t;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. this lane's k slices of x_hat into registers
+  uint32_t xp[CH][32];  // 16-bit pairs (16-bit T)
+  float xf[64];          // float32 values (T = float32, CH = 1)
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = c * 64 + lane;
+    if constexpr (kF) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        f32x4 t = reinterpret_cast<const f32x4*>(xs)[ci * 16 + q];
+        xf[4 * q] = t.x; xf[4 * q + 1] = t.y; xf[4 * q + 2] = t.z; xf[4 * q + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        u32x4 t = reinterpret_cast<const u32x4*>(xs)[ci * 8 + q];
+        xp[c][4 * q] = t.x; xp[c][4 * q + 1] = t.y; xp[c][4 * q + 2] = t.z; xp[c][4 * q + 3] = t.w;
+      }
+    }
+  }
+
+  // 5. rows
+  const float dec_w = global_decode(gw);
+  using T = typename Elem<DT>::T;
+#pragma unroll
+  for (int i = 0; i < kMaxRows; ++i) {
+    if (i < rpw && r0 + i < n) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const uint32_t cw[8] = {ca[i][c].x, ca[i][c].y, ca[i][c].z, ca[i][c].w,
+                                cb[i][c].x, cb[i][c].y, cb[i][c].z, cb[i][c].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float se;
+          {
+#pragma clang fp contract(off)
+            se = e4m3_decode((sw[i][c] >> (8 * j)) & 0xFFu) * dec_w;
+          }
+          float p = group_dot16<DT>(cw[2 * j], cw[2 * j + 1], &xp[c][8 * j], &xf[16 * j]);
+          acc = __builtin_fmaf(p, se, acc);
+        }
+      }
+      float s = wave_sum_uniform(acc);
+      if (lane == 0) reinterpret_cast<T*>(out)[r0 + i] = from_f32<DT>(s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ generic path
+
+template <int DT>
+__global__ void __launch_bounds__(kThreadsQ)
+qmv_generic_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+                   const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                   const float* __restrict__ gw, int n, int k, void* __restrict__ out) {
+  extern __shared__ float xs[];  // x_hat, group g at words [17 g, 17 g + 16)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int groups = k >> 4;
+  {
+    const float enc = global_encode(gx);
+    const float dec = global_decode(gx);
+    const int halves = k >> 3;  // even: pair partners are both in range
     for (int h = threadIdx.x; h < halves; h += kThreadsQ) {
-      float v[8];
+      float v[8], o[8];
       load8x<DT>(x, h, v);
-      float a = 0.0f;
+      xhat_half_group<DT>(v, enc, dec, o);
+      float* dst = xs + 17 * (h >> 1) + 8 * (h & 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-      a = fmaxf(a, __shfl_xor(a, 1, 64));
-      GroupScale gs = group_scale_from_amax(a, enc);
-      float sc;
-      {
-#pragma clang fp contract(off)
-        sc = e4m3_decode(gs.byte) * dec;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-        float o = e2m1_decode(e2m1_encode_scaled(v[i], gs.enc_b)) * sc;
-        xs[8 * h + i] = to_f32<DT>(from_f32<DT>(o));
-      }
+      for (int i = 0; i < 8; ++i) dst[i] = o[i];
     }
   }
   __syncthreads();
 
   const float dec_w = global_decode(gw);
   const int total_waves = gridDim.x * kWaves;
-  const int gwave = blockIdx.x * kWaves + wave;
-  const int rpw = (n + total_waves - 1) / total_waves;
-  const int r0 = gwave * rpw;
-  const int r1 = min(n, r0 + rpw);
-  const int per_step = 64 * GPL;  // groups covered by one wave sweep
-
-  for (int r = r0; r < r1; ++r) {
+  for (int r = blockIdx.x * kWaves + wave; r < n; r += total_waves) {
     const uint8_t* crow = wc + (int64_t)r * (k >> 1);
     const uint8_t* srow = ws + (int64_t)r * groups;
     float acc = 0.0f;
-    for (int g0 = 0; g0 < groups; g0 += per_step) {
-      const int gb = g0 + lane * GPL;
-      if constexpr (GPL == 4) {
-        // groups gb..gb+3: 32 code bytes, 4 scale bytes
-        const u32x4* cp = reinterpret_cast<const u32x4*>(crow + (int64_t)gb * 8);
-        u32x4 c0 = __builtin_nontemporal_load(cp);
-        u32x4 c1 = __builtin_nontemporal_load(cp + 1);
-        uint32_t sw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(srow + gb));
-        uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float se;
-          {
+    for (int g = lane; g < groups; g += 64) {
+      u32x2 c = *reinterpret_cast<const u32x2*>(crow + (int64_t)g * 8);
+      float se;
+      {
 #pragma clang fp contract(off)
-            se = e4m3_decode((sw >> (8 * j)) & 0xFFu) * dec_w;
-          }
-          float p = group_dot(xs + (gb + j) * 16, cw[2 * j], cw[2 * j + 1]);
-          acc = __builtin_fmaf(p, se, acc);
-        }
-      } else {
-        if (gb < groups) {
-          u32x2 c = *reinterpret_cast<const u32x2*>(crow + (int64_t)gb * 8);
-          float se;
-          {
-#pragma clang fp contract(off)
-            se = e4m3_decode(srow[gb]) * dec_w;
-          }
-          float p = group_dot(xs + gb * 16, c.x, c.y);
-          acc = __builtin_fmaf(p, se, acc);
-        }
+        se = e4m3_decode(srow[g]) * dec_w;
       }
+      float q[16];
+      float(&lo)[8] = *reinterpret_cast<float(*)[8]>(q);
+      float(&hi)[8] = *reinterpret_cast<float(*)[8]>(q + 8);
+      e2m1_decode8_f32(c.x, lo);
+      e2m1_decode8_f32(c.y, hi);
+      const float* xg = xs + 17 * g;
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p = __builtin_fmaf(q[i], xg[i], p);
+      acc = __builtin_fmaf(p, se, acc);
     }
-    acc = wave_sum(acc);
-    if (lane == 0) reinterpret_cast<typename Elem<DT>::T*>(out)[r] = from_f32<DT>(acc);
+    float s = wave_sum_uniform(acc);
+    if (lane == 0) reinterpret_cast<typename Elem<DT>::T*>(out)[r] = from_f32<DT>(s);
   }
 }
 
 template <int DT>
 hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                         const float* gw, int64_t n, int64_t k, void* out, hipStream_t s) {
-  // aim for ~7 rows per wave, at most one workgroup per row group
-  int64_t blocks = (n + kWaves * 7 - 1) / (kWaves * 7);
-  if (blocks < 1) blocks = 1;
-  if (blocks > 4096) blocks = 4096;
-  size_t lds = (size_t)k * sizeof(float);
+  const int chunks = (k % 4096 == 0) ? (int)(k / 4096) : 0;
+  const bool reg_path = chunks == 1 || (chunks == 2 && DT != kF32);
+  if (reg_path) {
+    // at least one workgroup per CU, at most kMaxRows rows per wave
+    int64_t blocks = (n + kWaves * kMaxRows - 1) / (kWaves * kMaxRows);
+    if (blocks < 256) blocks = 256;
+    int64_t waves = blocks * kWaves;
+    int rpw = (int)((n + waves - 1) / waves);
+    blocks = (n + (int64_t)kWaves * rpw - 1) / ((int64_t)kWaves * rpw);
+    if constexpr (DT == kF32) {
+      qmv_reg_kernel<DT, 1><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+    } else {
+      if (chunks == 1)
+        qmv_reg_kernel<DT, 1><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+      else
+        qmv_reg_kernel<DT, 2><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+    }
+    return hipGetLastError();
+  }
+  int64_t blocks = (n + kWaves - 1) / kWaves;
+  if (blocks > 1024) blocks = 1024;
+  size_t lds = (size_t)(k / 16) * 17 * sizeof(float);
   if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(k % 4096 == 0 ? qmv_kernel<DT, 4> : qmv_kernel<DT, 1>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(qmv_generic_kernel<DT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (k % 4096 == 0)
-    qmv_kernel<DT, 4><<<(int)blocks, kThreadsQ, lds, s>>>(x, gx, wc, ws, gw, (int)n, (int)k, out);
-  else
-    qmv_kernel<DT, 1><<<(int)blocks, kThreadsQ, lds, s>>>(x, gx, wc, ws, gw, (int)n, (int)k, out);
+  qmv_generic_kernel<DT><<<(int)blocks, kThreadsQ, lds, s>>>(x, gx, wc, ws, gw, (int)n, (int)k, out);
   return hipGetLastError();
 }
 

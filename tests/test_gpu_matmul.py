@@ -1,7 +1,8 @@
 """GPU parity of the contractions (qmv, qqmm, gather_qmm, routing) against the
 oracle.  Exact-grid cases must match bit for bit; general data must meet the
-norm-wise 1e-2 bar (and, as a sharper regression guard, nearly every output
-must sit within one unit in the last place of the oracle's)."""
+norm-wise 1e-2 bar.  Sharper regression guards: qmv (float32 products) must
+put nearly every output within one unit in the last place of the oracle's;
+the matrix-core paths must stay within MFMA_FRO_GUARD."""
 import numpy as np
 import pytest
 import torch
@@ -12,6 +13,12 @@ from _parity import (O, assert_bytes_equal, assert_close, assert_values_equal, d
                      oracle_dtype, say, scalar, ulp_fraction)
 
 pytestmark = pytest.mark.gpu
+
+# The matrix-core paths round each decoded weight e2m1(q) * e4m3(s) * g/2688 to
+# bfloat16 before the products (the oracle keeps it in float32); on Normal
+# data that rounding alone gives a norm-wise error near 2.5e-3.  Twice that is
+# the regression guard, well inside the 1e-2 bar.
+MFMA_FRO_GUARD = 5e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -108,12 +115,16 @@ def test_qmv_shapes(dtype, n, k):
     w = W.normal((n, k), 0.02, 20 + n, oracle_dtype(dtype))
     gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
     oc, os_ = O.quantize(host(w), gwh)
+    oc0, os0 = O.quantize(host(w), None)  # without global scales on either side
     y = nv.nvfp4_qmv(x.cuda(), dev(oc), dev(os_), scalar(gxh), scalar(gwh))
-    y0 = nv.nvfp4_qmv(x.cuda(), dev(oc), dev(os_), None, None)
+    y0 = nv.nvfp4_qmv(x.cuda(), dev(oc0), dev(os0), None, None)
     torch.cuda.synchronize()
     od = oracle_dtype(dtype)
-    assert_close(host(y), O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od), what="qmv g")
-    assert_close(host(y0), O.qqmm(host(x), oc, os_, None, None, dtype=od), what="qmv no g")
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od)
+    assert_close(host(y), ref, what="qmv g")
+    if od != "f32":  # float32 outputs carry the float32 summation order
+        assert ulp_fraction(host(y), ref, od) >= 0.99
+    assert_close(host(y0), O.qqmm(host(x), oc0, os0, None, None, dtype=od), what="qmv no g")
 
 
 # ------------------------------------------------------------------ qqmm
@@ -131,8 +142,8 @@ def test_qqmm_sweep(m, n, k):
     torch.cuda.synchronize()
     ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16")
     got = host(y)
-    assert_close(got, ref, what="qqmm")
-    assert ulp_fraction(got, ref, "bf16") >= 0.99
+    fro, _ = assert_close(got, ref, what="qqmm")
+    assert fro <= MFMA_FRO_GUARD
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32, torch.bfloat16])
@@ -167,8 +178,8 @@ def test_qqmm_prefill_2048x14336x4096_sampled():
     assert_bytes_equal(wc[torch.from_numpy(cols).cuda()].cpu().numpy(), oc, "sampled w codes")
     ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16", rows=rows)
     got = host(y)[rows][:, cols]
-    assert_close(got, ref, what="qqmm prefill sample")
-    assert ulp_fraction(got, ref, "bf16") >= 0.99
+    fro, _ = assert_close(got, ref, what="qqmm prefill sample")
+    assert fro <= MFMA_FRO_GUARD
 
 
 # ------------------------------------------------------------------ routing / gather
@@ -265,8 +276,8 @@ def test_gather_qmm_moe_8x14336x4096_sampled():
         codes_s[e], scales_s[e] = oc, os_
     ref = O.gather_qmm(xh, codes_s, scales_s, idx_h, gh, dtype="bf16", pairs=pairs)
     got = np.stack([host(y[t, j])[cols] for t, j in pairs])
-    assert_close(got, ref, what="gather MoE sample")
-    assert ulp_fraction(got, ref, "bf16") >= 0.99
+    fro, _ = assert_close(got, ref, what="gather MoE sample")
+    assert fro <= MFMA_FRO_GUARD
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
