@@ -279,6 +279,261 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
   }
 }
 
+// ------------------------------------------------------------------ fast path (k % 64 == 0)
+//
+// Same tile (256 x 256 x 64) with the work split for gfx950:
+//   * the four waves split the 256 output columns (64 each) and all share the
+//     256 rows of A, so every weight element is decoded exactly once per
+//     workgroup, by the wave that multiplies with it, straight into the MFMA
+//     operand registers -- the decoded weights never touch LDS;
+//   * A tiles and the raw NVFP4 weight tiles (codes + scales, 9/16 of a byte
+//     per element) go global -> LDS with global_load_lds_dwordx4, no VGPRs;
+//     A has 3 LDS stages, raw weights 4, so loads are issued two k-steps
+//     before their use and one barrier per k-step suffices;
+//   * in k-step i a wave runs its 128 MFMAs on stage i while it decodes the
+//     weights of step i + 1 (two codes per v_cvt_scalef32_pk_f32_fp4, one
+//     multiply by e4m3(s) * g/2688, two values per v_cvt_pk_bf16_f32);
+//   * inside a 64-wide k-step, MFMA lane group g (= lane / 16) takes the 16
+//     consecutive k of weight group g (8 per 16x16x32 step): one 8-byte code
+//     load and one scale byte per column; A is read with the same k order;
+//   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
+//     works on its own contiguous set of weight column panels.
+constexpr int kStagesA = 3, kStagesB = 4;
+constexpr int kAStageBytes = BM * BK * 2;                   // 32 KB of 16-bit A
+constexpr int kBCodeBytes = BN * BK / 2;                    // 8 KB of codes
+constexpr int kBStageBytes = kBCodeBytes + BN * BK / 16;    // + 1 KB of scales
+constexpr int kLoadsPerStage = 8 + 2 + 1;                   // per wave: A, codes, scales
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+template <int DT>
+__device__ __forceinline__ typename Mfma<DT>::V8 decode_frag(uint32_t codes, float se) {
+  float q[8];
+  e2m1_decode8_f32(codes, q);
+  typename Mfma<DT>::V8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    o[i] = from_f32<DT>(q[i] * se);
+  }
+  return o;
+}
+
+template <int DT, bool GATHER>
+__global__ void __launch_bounds__(kGemmThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_gemm_fast_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc,
+                      const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N,
+                      int K, void* __restrict__ out, const int32_t* __restrict__ offsets,
+                      const int32_t* __restrict__ perm, int top_k, int E, int tiles_m) {
+  using T = typename Elem<DT>::T;
+  using V8 = typename Mfma<DT>::V8;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStagesA * kAStageBytes + kStagesB * kBStageBytes];
+  __shared__ int64_t out_rows[BM];
+  uint8_t* const lds_a = smem;
+  uint8_t* const lds_b = smem + kStagesA * kAStageBytes;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // ---------------------------------------------------------------- tile of this workgroup
+  int L = blockIdx.x;
+  if ((gridDim.x & 7) == 0) L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int tile_n = L / tiles_m;
+  int tile_m = L % tiles_m;
+  int expert = 0, row_lo = 0, row_count = M;
+  if constexpr (GATHER) {
+    int acc_tiles = 0;
+    expert = -1;
+    for (int e = 0; e < E; ++e) {
+      const int cnt = offsets[e + 1] - offsets[e];
+      const int tiles = (cnt + BM - 1) / BM;
+      if (tile_m < acc_tiles + tiles) {
+        expert = e;
+        tile_m -= acc_tiles;
+        row_lo = offsets[e];
+        row_count = cnt;
+        break;
+      }
+      acc_tiles += tiles;
+    }
+    if (expert < 0) return;
+  }
+  const int bm = tile_m * BM;
+  const int bn = tile_n * BN;
+  const float dec_w = GATHER ? (gw ? gw[expert] / (kE4M3Max * kE2M1Max) : 1.0f) : global_decode(gw);
+  const int64_t w_row0 = (int64_t)expert * N;
+
+  // output row of each tile row (-1: outside the tile's row count)
+  for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
+    int64_t o = -1;
+    if (bm + r < row_count) {
+      if constexpr (GATHER)
+        o = perm[row_lo + bm + r];
+      else
+        o = bm + r;
+    }
+    out_rows[r] = o;
+  }
+
+  // ---------------------------------------------------------------- load addresses
+  // A: instruction j of wave w fills LDS 16-byte slots (w*8 + j)*64 + lane:
+  // tile row r = (w*8 + j)*8 + lane/8, slot p = lane % 8 holding k-chunk p ^ (r % 8).
+  const T* A = reinterpret_cast<const T*>(a_base);
+  const T* a_src[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wave * 8 + j) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    int64_t arow;
+    const int rr = (bm + r < row_count) ? r : 0;  // rows past the count re-read row 0
+    if constexpr (GATHER)
+      arow = perm[row_lo + bm + rr] / top_k;
+    else
+      arow = bm + rr;
+    a_src[j] = A + arow * K + chunk * 8;
+  }
+  // codes: instruction j of wave w fills bytes ((w*2 + j)*64 + lane)*16 of the code tile:
+  // tile column (w*2 + j)*32 + lane/2, half lane % 2 (16 of its 32 bytes per k-step)
+  const uint8_t* c_src[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = (wave * 2 + j) * 32 + (lane >> 1);
+    const int64_t wrow = w_row0 + min(bn + col, N - 1);
+    c_src[j] = wc + wrow * (K / 2) + (lane & 1) * 16;
+  }
+  // scales: wave w fills 4-byte slots w*64 + lane = tile column, 4 scale bytes per k-step
+  const uint8_t* s_src = ws + (w_row0 + min(bn + wave * 64 + lane, N - 1)) * (K / 16);
+
+  auto issue_a = [&](int kt) {
+    uint8_t* dst = lds_a + (kt % kStagesA) * kAStageBytes + wave * 8 * 1024;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) g2lds16(a_src[j] + kt * BK, dst + j * 1024);
+  };
+  auto issue_b = [&](int kt) {
+    uint8_t* dst = lds_b + (kt % kStagesB) * kBStageBytes;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) g2lds16(c_src[j] + kt * (BK / 2), dst + (wave * 2 + j) * 1024);
+    g2lds4(s_src + kt * (BK / 16), dst + kBCodeBytes + wave * 256);
+  };
+
+  // ---------------------------------------------------------------- operand fragments
+  const int fr = lane & 15;  // MFMA row / column inside a 16 x 16 tile
+  const int fg = lane >> 4;  // k group: elements 16 fg .. 16 fg + 15 of a k-step
+  V8 bcur[4][2], bnext[4][2];
+  auto decode_b = [&](int kt, V8 (&dst)[4][2]) {
+    const uint8_t* src = lds_b + (kt % kStagesB) * kBStageBytes;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int col = wave * 64 + t * 16 + fr;
+      const u32x2 code = *reinterpret_cast<const u32x2*>(src + col * 32 + fg * 8);
+      const uint32_t sbyte = src[kBCodeBytes + col * 4 + fg];
+      float se;
+      {
+#pragma clang fp contract(off)
+        se = e4m3_decode(sbyte) * dec_w;
+      }
+      dst[t][0] = decode_frag<DT>(code.x, se);
+      dst[t][1] = decode_frag<DT>(code.y, se);
+    }
+  };
+
+  f32x4 acc[4][16];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---------------------------------------------------------------- prologue
+  const int KT = K / BK;
+  issue_a(0);
+  issue_b(0);
+  if (KT > 1) { issue_a(1); issue_b(1); }
+  if (KT > 2) issue_b(2);
+  wait_vmcnt<0>();
+  __syncthreads();
+  decode_b(0, bcur);
+
+  // ---------------------------------------------------------------- main loop
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt > 0) {
+      // A(kt) and raw B(kt + 1) were issued two steps ago (or in the
+      // prologue); what the previous step issued may stay in flight: A(kt + 1)
+      // and B(kt + 2) while both exist, A(kt + 1) alone when B(kt + 2) is past
+      // the end, nothing at the last step
+      if (kt + 3 <= KT)
+        wait_vmcnt<kLoadsPerStage>();
+      else if (kt + 2 == KT)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (kt + 2 < KT) issue_a(kt + 2);
+    if (kt + 3 < KT) issue_b(kt + 3);
+    const uint8_t* la = lds_a + (kt % kStagesA) * kAStageBytes;
+    const bool more = (kt + 1 < KT);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = i * 16 + fr;
+        const V8 a = *reinterpret_cast<const V8*>(la + m * 128 + (((2 * fg + s) ^ (m & 7)) << 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][s], a, acc[t][i]);
+        if (s == 0 && i == 7 && more) decode_b(kt + 1, bnext);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bcur[t][0] = bnext[t][0];
+        bcur[t][1] = bnext[t][1];
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // acc[t][i][v]: tile row 16 i + fr, tile column 64 w + 16 t + 4 fg + v
+  T* O = reinterpret_cast<T*>(out);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t orow = out_rows[i * 16 + fr];
+    if (orow < 0) continue;
+    T* op = O + orow * N;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = bn + wave * 64 + t * 16 + 4 * fg;
+      if (c + 3 < N) {
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        T4 v;
+        v[0] = from_f32<DT>(acc[t][i][0]);
+        v[1] = from_f32<DT>(acc[t][i][1]);
+        v[2] = from_f32<DT>(acc[t][i][2]);
+        v[3] = from_f32<DT>(acc[t][i][3]);
+        *reinterpret_cast<T4*>(op + c) = v;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (c + v < N) op[c + v] = from_f32<DT>(acc[t][i][v]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ float32 path
 
 constexpr int FT = 64, FK = 16;
@@ -397,73 +652,86 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxE = 1024;
 
-// One workgroup: per-expert counts, exclusive scan, then a stable scatter of
-// the pair ids in chunks of 1024 (rank inside a wave from ballots of equal
-// experts, wave offsets from a per-chunk table).  Out-of-range experts are
-// skipped.
+// Groups of equal experts inside one wave: returns the lanes (bit mask) that
+// share this lane's expert; the lowest lane of each group also records the
+// group's expert and size through `on_group`.
+template <typename F>
+__device__ __forceinline__ uint64_t match_experts(int e, bool valid, F on_group) {
+  uint64_t remaining = __ballot(valid);
+  uint64_t same = 0;
+  while (remaining) {
+    const int leader = __builtin_ctzll(remaining);
+    const int le = __shfl(e, leader, 64);
+    const uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) same = m;
+    if ((int)(threadIdx.x & 63) == leader) on_group(le, __builtin_popcountll(m));
+    remaining &= ~m;
+  }
+  return same;
+}
+
+// One workgroup of 1024 lanes.  Pass 1 counts pairs per expert (one LDS
+// atomic per expert group of a wave), then an exclusive scan gives the
+// expert offsets.  Pass 2 walks the pairs again in chunks of 1024 in order:
+// a pair's slot is its expert's running base, plus the same-expert pairs of
+// earlier waves of the chunk (a per-wave count table), plus its rank among
+// the same-expert lanes of its wave -- i.e. ascending pair id within each
+// expert.  Out-of-range experts are skipped.
 __global__ void __launch_bounds__(kRouteThreads)
 moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __restrict__ offsets,
                  int32_t* __restrict__ perm) {
-  __shared__ int counts[kRouteMaxE];
   __shared__ int base[kRouteMaxE];
-  __shared__ int wcount[kRouteWaves][64];  // per wave: counts of the (up to 64) experts it saw
-  __shared__ int wexp[kRouteWaves][64];    // ... and which experts they are
-  __shared__ int wn[kRouteWaves];
+  __shared__ int scan[kRouteThreads];
+  __shared__ int wcnt[kRouteWaves * kRouteMaxE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) counts[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < total; p += kRouteThreads) {
-    int e = idx[p];
-    if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      base[e] = run;
-      run += counts[e];
-    }
-    offsets[E] = run;
-  }
+  for (int e = tid; e < E; e += kRouteThreads) base[e] = 0;
   __syncthreads();
   for (int c0 = 0; c0 < total; c0 += kRouteThreads) {
     const int p = c0 + tid;
     const int e = (p < total) ? idx[p] : -1;
     const bool valid = (e >= 0 && e < E);
-    // groups of equal experts inside this wave, in lane order
-    uint64_t remaining = __ballot(valid);
-    uint64_t same = 0;
-    int ngroups = 0;
-    while (remaining) {
-      int leader = __builtin_ctzll(remaining);
-      int le = __shfl(e, leader, 64);
-      uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) same = m;
-      if (lane == 0) {
-        wexp[wave][ngroups] = le;
-        wcount[wave][ngroups] = __builtin_popcountll(m);
-      }
-      ++ngroups;
-      remaining &= ~m;
-    }
-    if (lane == 0) wn[wave] = ngroups;
-    const int rank = __builtin_popcountll(same & ((1ull << lane) - 1ull));
+    match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
+  }
+  __syncthreads();
+  // exclusive scan of the counts (E <= 1024, one entry per lane)
+  const int mycount = (tid < E) ? base[tid] : 0;
+  scan[tid] = mycount;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int v = (tid >= off) ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = scan[tid] - mycount;
+    offsets[tid] = excl;
+    base[tid] = excl;
+  }
+  if (tid == kRouteThreads - 1) offsets[E] = scan[tid];
+  __syncthreads();
+
+  for (int c0 = 0; c0 < total; c0 += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int p = c0 + tid;
+    const int e = (p < total) ? idx[p] : -1;
+    const bool valid = (e >= 0 && e < E);
+    const uint64_t same =
+        match_experts(e, valid, [&](int le, int cnt) { wcnt[wave * E + le] = cnt; });
     __syncthreads();
     if (valid) {
-      int before = 0;  // same-expert pairs of earlier waves in this chunk
-      for (int w = 0; w < wave; ++w)
-        for (int g = 0; g < wn[w]; ++g)
-          if (wexp[w][g] == e) before += wcount[w][g];
-      perm[base[e] + before + rank] = p;
+      int pos = base[e] + __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+      perm[pos] = p;
     }
     __syncthreads();
-    // advance the per-expert bases by this chunk's counts
-    if (tid == 0) {
-      for (int w = 0; w < kRouteWaves; ++w)
-        for (int g = 0; g < wn[w]; ++g) base[wexp[w][g]] += wcount[w][g];
+    for (int x = tid; x < E; x += kRouteThreads) {
+      int add = 0;
+      for (int w = 0; w < kRouteWaves; ++w) add += wcnt[w * E + x];
+      base[x] += add;
     }
     __syncthreads();
   }
@@ -484,6 +752,16 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
     return hipGetLastError();
   }
   int64_t blocks = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if (k % BK == 0 && n % 4 == 0) {
+    const int tiles_m = (int)((m + BM - 1) / BM);
+    if (dt == kF16)
+      mfma_gemm_fast_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
+          xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+    else
+      mfma_gemm_fast_kernel<kBF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
+          xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+    return hipGetLastError();
+  }
   if (dt == kF16)
     mfma_gemm_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
         xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1);
@@ -514,6 +792,15 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
   }
   int64_t mt = (pairs + BM - 1) / BM + e;
   int64_t blocks = mt * ((n + BN - 1) / BN);
+  if (k % BK == 0 && n % 4 == 0) {
+    if (dt == kF16)
+      mfma_gemm_fast_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+          x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+    else
+      mfma_gemm_fast_kernel<kBF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+          x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+    return hipGetLastError();
+  }
   if (dt == kF16)
     mfma_gemm_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
         x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e);

@@ -69,13 +69,15 @@ __device__ __forceinline__ float global_decode(const float* g) {
 
 // ----------------------------------------------------------------- e4m3
 
-// Decode an e4m3 byte.  Exponent field 0 is subnormal: m * 2^-9.
+// Decode an e4m3 byte (the low byte of b; v_cvt_f32_fp8 decodes gfx950's
+// OCP E4M3 exactly, including the subnormals m * 2^-9 and NaN for 0x7F/0xFF).
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  uint32_t mag = b & 0x7Fu;
-  float normal = __uint_as_float((mag << 20) + (120u << 23));
-  float sub = (float)(mag & 7u) * 0.001953125f;
-  float v = (mag >> 3) ? normal : sub;
-  return (b & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+// Decode byte B of a dword of scales.
+template <int B>
+__device__ __forceinline__ float e4m3_decode_byte(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
 }
 
 // Encode v >= 0 to e4m3: nearest, ties to even, saturating at 448.

@@ -126,11 +126,20 @@ __device__ __forceinline__ float group_dot16(uint32_t c0, uint32_t c1, const uin
 
 // ------------------------------------------------------------------ register path
 
-template <int DT, int CH>
+// One 16-byte code load covers 32 elements = 2 groups; its two scale bytes
+// come from one 2-byte load.  For chunk c of a row (4096 elements), lane l
+// takes the 32 elements at 32 l and at 2048 + 32 l, so each of the two code
+// loads of a wave reads 1 KB of contiguous memory.
+struct RowPiece {
+  u32x4 code;
+  uint32_t scale;  // the aligned scale dword holding this piece's two bytes
+};
+
+template <int DT, int CH, int R>
 __global__ void __launch_bounds__(kThreadsQ)
 qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
                const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-               const float* __restrict__ gw, int n, int rpw, void* __restrict__ out) {
+               const float* __restrict__ gw, int n, void* __restrict__ out) {
   constexpr int K = 4096 * CH;
   constexpr bool kF = (DT == kF32);
   // x_hat in LDS: 16-bit values for 16-bit T, float32 otherwise
@@ -139,29 +148,33 @@ qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // 1. this thread's half groups of x (K / 8 = 512 * CH of them)
+  // 1. this thread's half groups of x (K / 8 = 512 * CH of them), first in the
+  //    load queue so that waiting for them leaves the weight loads in flight
   float xv[CH][8];
 #pragma unroll
   for (int c = 0; c < CH; ++c) load8x<DT>(x, tid + kThreadsQ * c, xv[c]);
+  __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weight loads
 
-  // 2. all weight loads of this wave's rows
-  const int r0 = (blockIdx.x * kWaves + wave) * rpw;
-  u32x4 ca[kMaxRows][CH], cb[kMaxRows][CH];
-  uint32_t sw[kMaxRows][CH];
+  // 2. every weight load of this wave's R rows (rows past n re-read row n - 1)
+  const int r0 = (blockIdx.x * kWaves + wave) * R;
+  RowPiece wp[R][CH][2];
 #pragma unroll
-  for (int i = 0; i < kMaxRows; ++i) {
+  for (int i = 0; i < R; ++i) {
     const int r = min(r0 + i, n - 1);
+    const uint8_t* crow = wc + (int64_t)r * (K / 2);
+    const uint8_t* srow = ws + (int64_t)r * (K / 16);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int ci = c * 64 + lane;  // chunk of 64 elements = 4 groups
-      const u32x4* cp = reinterpret_cast<const u32x4*>(wc + (int64_t)r * (K / 2) + ci * 32);
-      if (i < rpw) {
-        ca[i][c] = __builtin_nontemporal_load(cp);
-        cb[i][c] = __builtin_nontemporal_load(cp + 1);
-        sw[i][c] = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t*>(ws + (int64_t)r * (K / 16) + ci * 4));
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int e0 = c * 4096 + hh * 2048 + 32 * lane;  // first element
+        wp[i][c][hh].code =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + e0 / 2));
+        wp[i][c][hh].scale = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t*>(srow + ((e0 / 16) & ~3)));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // rows arrive in the order they are used
   }
 
   // 3. x_hat into LDS
@@ -189,53 +202,65 @@ qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
   __syncthreads();
 
-  // 4. this lane's k slices of x_hat into registers
-  uint32_t xp[CH][32];  // 16-bit pairs (16-bit T)
-  float xf[64];          // float32 values (T = float32, CH = 1)
+  // 4. this lane's x_hat pieces into registers: 32 elements per piece
+  uint32_t xp[CH][2][16];  // 16-bit pairs (16-bit T)
+  float xf[CH][2][32];     // float32 values (T = float32)
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int ci = c * 64 + lane;
-    if constexpr (kF) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        f32x4 t = reinterpret_cast<const f32x4*>(xs)[ci * 16 + q];
-        xf[4 * q] = t.x; xf[4 * q + 1] = t.y; xf[4 * q + 2] = t.z; xf[4 * q + 3] = t.w;
-      }
-    } else {
+    for (int hh = 0; hh < 2; ++hh) {
+      const int e0 = c * 4096 + hh * 2048 + 32 * lane;
+      if constexpr (kF) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        u32x4 t = reinterpret_cast<const u32x4*>(xs)[ci * 8 + q];
-        xp[c][4 * q] = t.x; xp[c][4 * q + 1] = t.y; xp[c][4 * q + 2] = t.z; xp[c][4 * q + 3] = t.w;
+        for (int q = 0; q < 8; ++q) {
+          f32x4 t = reinterpret_cast<const f32x4*>(xs)[e0 / 4 + q];
+          xf[c][hh][4 * q] = t.x; xf[c][hh][4 * q + 1] = t.y;
+          xf[c][hh][4 * q + 2] = t.z; xf[c][hh][4 * q + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x4 t = reinterpret_cast<const u32x4*>(xs)[e0 / 8 + q];
+          xp[c][hh][4 * q] = t.x; xp[c][hh][4 * q + 1] = t.y;
+          xp[c][hh][4 * q + 2] = t.z; xp[c][hh][4 * q + 3] = t.w;
+        }
       }
     }
   }
 
-  // 5. rows
+  // 5. rows: group partial sums times e4m3(s) * g_w/2688, then the row sum
   const float dec_w = global_decode(gw);
-  using T = typename Elem<DT>::T;
+  const int sshift = 8 * ((2 * lane) & 3);  // this lane's two bytes inside the scale dword
+  float rs[R];
 #pragma unroll
-  for (int i = 0; i < kMaxRows; ++i) {
-    if (i < rpw && r0 + i < n) {
-      float acc = 0.0f;
+  for (int i = 0; i < R; ++i) {
+    float acc = 0.0f;
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const uint32_t cw[8] = {ca[i][c].x, ca[i][c].y, ca[i][c].z, ca[i][c].w,
-                                cb[i][c].x, cb[i][c].y, cb[i][c].z, cb[i][c].w};
+    for (int c = 0; c < CH; ++c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float se;
-          {
+      for (int hh = 0; hh < 2; ++hh) {
+        const RowPiece& pc = wp[i][c][hh];
+        float se0, se1;
+        {
 #pragma clang fp contract(off)
-            se = e4m3_decode((sw[i][c] >> (8 * j)) & 0xFFu) * dec_w;
-          }
-          float p = group_dot16<DT>(cw[2 * j], cw[2 * j + 1], &xp[c][8 * j], &xf[16 * j]);
-          acc = __builtin_fmaf(p, se, acc);
+          const uint32_t sc = pc.scale >> sshift;
+          se0 = e4m3_decode_byte<0>(sc) * dec_w;
+          se1 = e4m3_decode_byte<1>(sc) * dec_w;
         }
+        float p0 = group_dot16<DT>(pc.code.x, pc.code.y, &xp[c][hh][0], &xf[c][hh][0]);
+        float p1 = group_dot16<DT>(pc.code.z, pc.code.w, &xp[c][hh][8], &xf[c][hh][16]);
+        acc = __builtin_fmaf(p0, se0, acc);
+        acc = __builtin_fmaf(p1, se1, acc);
       }
-      float s = wave_sum_uniform(acc);
-      if (lane == 0) reinterpret_cast<T*>(out)[r0 + i] = from_f32<DT>(s);
     }
+    rs[i] = wave_sum_uniform(acc);
+    __builtin_amdgcn_sched_barrier(0);  // consume rows in load order
   }
+  // 6. lane i stores row r0 + i
+  float mine = rs[0];
+#pragma unroll
+  for (int i = 1; i < R; ++i) mine = (lane == i) ? rs[i] : mine;
+  if (lane < R && r0 + lane < n) reinterpret_cast<typename Elem<DT>::T*>(out)[r0 + lane] = from_f32<DT>(mine);
 }
 
 // ------------------------------------------------------------------ generic path
@@ -293,6 +318,27 @@ qmv_generic_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
 }
 
+template <int DT, int CH, int R>
+void launch_reg(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
+                const float* gw, int64_t n, void* out, int64_t blocks, hipStream_t s) {
+  qmv_reg_kernel<DT, CH, R><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, out);
+}
+
+template <int DT, int CH>
+void launch_reg_r(int r, const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
+                  const float* gw, int64_t n, void* out, int64_t blocks, hipStream_t s) {
+  switch (r) {
+    case 1: launch_reg<DT, CH, 1>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 2: launch_reg<DT, CH, 2>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 3: launch_reg<DT, CH, 3>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 4: launch_reg<DT, CH, 4>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 5: launch_reg<DT, CH, 5>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 6: launch_reg<DT, CH, 6>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 7: launch_reg<DT, CH, 7>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+    default: launch_reg<DT, CH, 8>(x, gx, wc, ws, gw, n, out, blocks, s); break;
+  }
+}
+
 template <int DT>
 hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                         const float* gw, int64_t n, int64_t k, void* out, hipStream_t s) {
@@ -302,16 +348,16 @@ hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const
     // at least one workgroup per CU, at most kMaxRows rows per wave
     int64_t blocks = (n + kWaves * kMaxRows - 1) / (kWaves * kMaxRows);
     if (blocks < 256) blocks = 256;
-    int64_t waves = blocks * kWaves;
-    int rpw = (int)((n + waves - 1) / waves);
+    const int64_t waves = blocks * kWaves;
+    const int rpw = (int)((n + waves - 1) / waves);
     blocks = (n + (int64_t)kWaves * rpw - 1) / ((int64_t)kWaves * rpw);
     if constexpr (DT == kF32) {
-      qmv_reg_kernel<DT, 1><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+      launch_reg_r<DT, 1>(rpw, x, gx, wc, ws, gw, n, out, blocks, s);
     } else {
       if (chunks == 1)
-        qmv_reg_kernel<DT, 1><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+        launch_reg_r<DT, 1>(rpw, x, gx, wc, ws, gw, n, out, blocks, s);
       else
-        qmv_reg_kernel<DT, 2><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, rpw, out);
+        launch_reg_r<DT, 2>(rpw, x, gx, wc, ws, gw, n, out, blocks, s);
     }
     return hipGetLastError();
   }
