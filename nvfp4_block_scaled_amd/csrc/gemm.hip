@@ -285,38 +285,36 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //   * the four waves split the 256 output columns (64 each) and all share the
 //     256 rows of A, so every weight element is decoded exactly once per
 //     workgroup, by the wave that multiplies with it, straight into the MFMA
-//     operand registers -- the decoded weights never touch LDS;
-//   * A tiles and the raw NVFP4 weight tiles (codes + scales, 9/16 of a byte
-//     per element) go global -> LDS with global_load_lds_dwordx4, no VGPRs;
-//     A has 3 LDS stages, raw weights 4, so loads are issued two k-steps
-//     before their use and one barrier per k-step suffices;
-//   * in k-step i a wave runs its 128 MFMAs on stage i while it decodes the
-//     weights of step i + 1 (two codes per v_cvt_scalef32_pk_f32_fp4, one
-//     multiply by e4m3(s) * g/2688, two values per v_cvt_pk_bf16_f32);
+//     operand registers -- the weights never touch LDS: each wave loads its
+//     own packed codes (8 bytes per column and lane group) and scale dwords
+//     with buffer loads, about 1.5 k-steps ahead of their use;
+//   * A is double-buffered in LDS: the loads of A(i + 1) are issued at the top
+//     of step i and written to LDS (16-byte chunks XOR-swizzled by row) after
+//     the step's MFMAs have been issued; one barrier per k-step, without a
+//     memory fence, so the weight loads stay in flight across it;
+//   * a k-step is two halves of 64 MFMAs (16x16x32); each half uses one of
+//     two weight fragments per column tile and, in between its MFMAs, decodes
+//     the fragment the next half needs (two codes per
+//     v_cvt_scalef32_pk_f32_fp4, one multiply by e4m3(s) * g/2688, two values
+//     per v_cvt_pk_bf16_f32);
 //   * inside a 64-wide k-step, MFMA lane group g (= lane / 16) takes the 16
-//     consecutive k of weight group g (8 per 16x16x32 step): one 8-byte code
-//     load and one scale byte per column; A is read with the same k order;
+//     consecutive k of weight group g (8 per half); A is read with the same k
+//     order;
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
 //     works on its own contiguous set of weight column panels.
-constexpr int kStagesA = 3, kStagesB = 4;
-constexpr int kAStageBytes = BM * BK * 2;                   // 32 KB of 16-bit A
-constexpr int kBCodeBytes = BN * BK / 2;                    // 8 KB of codes
-constexpr int kBStageBytes = kBCodeBytes + BN * BK / 16;    // + 1 KB of scales
-constexpr int kLoadsPerStage = 8 + 2 + 1;                   // per wave: A, codes, scales
+constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void g2lds16(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+// LDS barrier without a memory fence: finish this wave's LDS operations, then
+// meet the other waves.  The "memory" clobber keeps the compiler from moving
+// memory accesses across it; outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0xFFFFFFFFull ? -1 : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
 }
 
 template <int DT>
@@ -332,22 +330,29 @@ __device__ __forceinline__ typename Mfma<DT>::V8 decode_frag(uint32_t codes, flo
   return o;
 }
 
+// Raw weights of one k-step for one lane: for each of its 4 column tiles,
+// the 8 code bytes of its group and the dword of the column's 4 scales.
+struct BRaw {
+  u32x2 code[4];
+  uint32_t scale[4];
+};
+
 template <int DT, bool GATHER>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-mfma_gemm_fast_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc,
-                      const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N,
-                      int K, void* __restrict__ out, const int32_t* __restrict__ offsets,
-                      const int32_t* __restrict__ perm, int top_k, int E, int tiles_m) {
+mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
+                      const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                      const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
+                      const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                      int top_k, int E, int tiles_m) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStagesA * kAStageBytes + kStagesB * kBStageBytes];
-  __shared__ int64_t out_rows[BM];
-  uint8_t* const lds_a = smem;
-  uint8_t* const lds_b = smem + kStagesA * kAStageBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2 * kAStageBytes];
+  __shared__ int out_rows[BM];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------------------------------------------------------- tile of this workgroup
   int L = blockIdx.x;
@@ -375,11 +380,10 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, const uint8_t* __restrict
   const int bm = tile_m * BM;
   const int bn = tile_n * BN;
   const float dec_w = GATHER ? (gw ? gw[expert] / (kE4M3Max * kE2M1Max) : 1.0f) : global_decode(gw);
-  const int64_t w_row0 = (int64_t)expert * N;
 
   // output row of each tile row (-1: outside the tile's row count)
-  for (int r = threadIdx.x; r < BM; r += kGemmThreads) {
-    int64_t o = -1;
+  for (int r = tid; r < BM; r += kGemmThreads) {
+    int o = -1;
     if (bm + r < row_count) {
       if constexpr (GATHER)
         o = perm[row_lo + bm + r];
@@ -389,66 +393,68 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, const uint8_t* __restrict
     out_rows[r] = o;
   }
 
-  // ---------------------------------------------------------------- load addresses
-  // A: instruction j of wave w fills LDS 16-byte slots (w*8 + j)*64 + lane:
-  // tile row r = (w*8 + j)*8 + lane/8, slot p = lane % 8 holding k-chunk p ^ (r % 8).
-  const T* A = reinterpret_cast<const T*>(a_base);
-  const T* a_src[8];
+  // ---------------------------------------------------------------- buffer resources / offsets
+  const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_base, (uint64_t)a_rows * K * sizeof(T));
+  const uint8_t* wc_e = wc + (int64_t)expert * N * (K / 2);
+  const uint8_t* ws_e = ws + (int64_t)expert * N * (K / 16);
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(wc_e, (uint64_t)N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws_e, (uint64_t)N * (K / 16));
+
+  // A: chunk j of this thread is tile row (tid >> 3) + 32 j, k-chunk tid & 7,
+  // stored at LDS slot (tid & 7) ^ (row & 7) of that row (row & 7 does not
+  // depend on j, so chunk j lands 32 rows = 4096 bytes after chunk 0).
+  uint32_t a_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = (wave * 8 + j) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (r & 7);
-    int64_t arow;
+    const int r = (tid >> 3) + 32 * j;
     const int rr = (bm + r < row_count) ? r : 0;  // rows past the count re-read row 0
+    int64_t arow;
     if constexpr (GATHER)
       arow = perm[row_lo + bm + rr] / top_k;
     else
       arow = bm + rr;
-    a_src[j] = A + arow * K + chunk * 8;
+    a_off[j] = (uint32_t)((arow * K + (tid & 7) * 8) * (int64_t)sizeof(T));
   }
-  // codes: instruction j of wave w fills bytes ((w*2 + j)*64 + lane)*16 of the code tile:
-  // tile column (w*2 + j)*32 + lane/2, half lane % 2 (16 of its 32 bytes per k-step)
-  const uint8_t* c_src[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = (wave * 2 + j) * 32 + (lane >> 1);
-    const int64_t wrow = w_row0 + min(bn + col, N - 1);
-    c_src[j] = wc + wrow * (K / 2) + (lane & 1) * 16;
-  }
-  // scales: wave w fills 4-byte slots w*64 + lane = tile column, 4 scale bytes per k-step
-  const uint8_t* s_src = ws + (w_row0 + min(bn + wave * 64 + lane, N - 1)) * (K / 16);
-
-  auto issue_a = [&](int kt) {
-    uint8_t* dst = lds_a + (kt % kStagesA) * kAStageBytes + wave * 8 * 1024;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) g2lds16(a_src[j] + kt * BK, dst + j * 1024);
-  };
-  auto issue_b = [&](int kt) {
-    uint8_t* dst = lds_b + (kt % kStagesB) * kBStageBytes;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) g2lds16(c_src[j] + kt * (BK / 2), dst + (wave * 2 + j) * 1024);
-    g2lds4(s_src + kt * (BK / 16), dst + kBCodeBytes + wave * 256);
-  };
-
-  // ---------------------------------------------------------------- operand fragments
+  const int a_dst = (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 3) & 7)) << 4);
   const int fr = lane & 15;  // MFMA row / column inside a 16 x 16 tile
   const int fg = lane >> 4;  // k group: elements 16 fg .. 16 fg + 15 of a k-step
-  V8 bcur[4][2], bnext[4][2];
-  auto decode_b = [&](int kt, V8 (&dst)[4][2]) {
-    const uint8_t* src = lds_b + (kt % kStagesB) * kBStageBytes;
+  const int a_rd0 = fr * 128 + (((2 * fg) ^ (fr & 7)) << 4);
+  const int a_rd1 = fr * 128 + (((2 * fg + 1) ^ (fr & 7)) << 4);
+  // weights: column tile t of this wave is column bn + 64 w + 16 t + fr
+  uint32_t c_off[4], s_off[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int col = min(bn + wave * 64 + t * 16 + fr, N - 1);
+    c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fg * 8;
+    s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
+  }
+
+  u32x4 astage[8];
+  auto load_a = [&](int kt) {
+    const int so = kt * BK * (int)sizeof(T);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      astage[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[j], so, 0));
+  };
+  auto store_a = [&](int kt) {
+    uint8_t* base = sa + (kt & 1) * kAStageBytes + a_dst;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(base + j * 4096) = astage[j];
+  };
+  auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int col = wave * 64 + t * 16 + fr;
-      const u32x2 code = *reinterpret_cast<const u32x2*>(src + col * 32 + fg * 8);
-      const uint32_t sbyte = src[kBCodeBytes + col * 4 + fg];
-      float se;
-      {
-#pragma clang fp contract(off)
-        se = e4m3_decode(sbyte) * dec_w;
-      }
-      dst[t][0] = decode_frag<DT>(code.x, se);
-      dst[t][1] = decode_frag<DT>(code.y, se);
+      b.code[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_c, c_off[t], kt * (BK / 2), 0));
+      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * (BK / 16), 0);
     }
+  };
+  auto decode = [&](const BRaw& b, int t, int s) -> V8 {
+    float se;
+    {
+#pragma clang fp contract(off)
+      se = e4m3_decode(b.scale[t] >> (8 * fg)) * dec_w;
+    }
+    return decode_frag<DT>(s ? b.code[t].y : b.code[t].x, se);
   };
 
   f32x4 acc[4][16];
@@ -457,63 +463,76 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, const uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---------------------------------------------------------------- prologue
   const int KT = K / BK;
-  issue_a(0);
-  issue_b(0);
-  if (KT > 1) { issue_a(1); issue_b(1); }
-  if (KT > 2) issue_b(2);
-  wait_vmcnt<0>();
-  __syncthreads();
-  decode_b(0, bcur);
+  V8 bcur[4][2], bnext[4][2];
+  BRaw raw;  // raw weights of the next k-step
+
+  // Step kt: MFMAs on A(kt) (LDS stage kt & 1) and bcur; the loads of A(kt + 1)
+  // are in flight meanwhile; the second half decodes the weights of kt + 1
+  // from `raw` into bnext, after which `raw` is reloaded with kt + 2.  The
+  // body is straight-line: past the end of k the loads re-read the last
+  // k-step and the extra decode is discarded, so every wait the compiler
+  // places counts exactly the loads that are in flight.
+  auto step = [&](int kt) {
+    load_a(min(kt + 1, KT - 1));
+    const uint8_t* la = sa + (kt & 1) * kAStageBytes;
+    // The A fragment of m-tile i + 1 is read while the MFMAs of i issue; the
+    // scheduling barriers keep that one-ahead structure (and the register
+    // footprint) as written.
+    V8 a_cur = *reinterpret_cast<const V8*>(la + a_rd0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      V8 a_nxt;
+      if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd0 + (i + 1) * 2048);
+      else a_nxt = *reinterpret_cast<const V8*>(la + a_rd1);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][0], a_cur, acc[t][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      a_cur = a_nxt;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      V8 a_nxt = a_cur;
+      if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd1 + (i + 1) * 2048);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][1], a_cur, acc[t][i]);
+      if (i & 1) bnext[i >> 2][(i >> 1) & 1] = decode(raw, i >> 2, (i >> 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      a_cur = a_nxt;
+    }
+    store_a(kt + 1);  // into the other stage; past the end nobody reads it
+    lds_barrier();
+    load_b(min(kt + 2, KT - 1), raw);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bcur[t][0] = bnext[t][0];
+      bcur[t][1] = bnext[t][1];
+    }
+  };
+
+  // ---------------------------------------------------------------- prologue
+  load_a(0);
+  load_b(0, raw);
+  store_a(0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bcur[t][0] = decode(raw, t, 0);
+    bcur[t][1] = decode(raw, t, 1);
+  }
+  load_b(min(1, KT - 1), raw);
+  lds_barrier();
 
   // ---------------------------------------------------------------- main loop
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt > 0) {
-      // A(kt) and raw B(kt + 1) were issued two steps ago (or in the
-      // prologue); what the previous step issued may stay in flight: A(kt + 1)
-      // and B(kt + 2) while both exist, A(kt + 1) alone when B(kt + 2) is past
-      // the end, nothing at the last step
-      if (kt + 3 <= KT)
-        wait_vmcnt<kLoadsPerStage>();
-      else if (kt + 2 == KT)
-        wait_vmcnt<8>();
-      else
-        wait_vmcnt<0>();
-      __syncthreads();
-    }
-    if (kt + 2 < KT) issue_a(kt + 2);
-    if (kt + 3 < KT) issue_b(kt + 3);
-    const uint8_t* la = lds_a + (kt % kStagesA) * kAStageBytes;
-    const bool more = (kt + 1 < KT);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = i * 16 + fr;
-        const V8 a = *reinterpret_cast<const V8*>(la + m * 128 + (((2 * fg + s) ^ (m & 7)) << 4));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][s], a, acc[t][i]);
-        if (s == 0 && i == 7 && more) decode_b(kt + 1, bnext);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bcur[t][0] = bnext[t][0];
-        bcur[t][1] = bnext[t][1];
-      }
-    }
-  }
+  for (int kt = 0; kt < KT; ++kt) step(kt);
 
   // ---------------------------------------------------------------- epilogue
   // acc[t][i][v]: tile row 16 i + fr, tile column 64 w + 16 t + 4 fg + v
   T* O = reinterpret_cast<T*>(out);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int64_t orow = out_rows[i * 16 + fr];
+    const int orow = out_rows[i * 16 + fr];
     if (orow < 0) continue;
-    T* op = O + orow * N;
+    T* op = O + (int64_t)orow * N;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int c = bn + wave * 64 + t * 16 + 4 * fg;
@@ -756,10 +775,10 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
     const int tiles_m = (int)((m + BM - 1) / BM);
     if (dt == kF16)
       mfma_gemm_fast_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+          xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
     else
       mfma_gemm_fast_kernel<kBF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+          xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
     return hipGetLastError();
   }
   if (dt == kF16)
@@ -795,10 +814,10 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
   if (k % BK == 0 && n % 4 == 0) {
     if (dt == kF16)
       mfma_gemm_fast_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-          x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+          x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
     else
       mfma_gemm_fast_kernel<kBF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-          x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+          x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
     return hipGetLastError();
   }
   if (dt == kF16)
