@@ -37,13 +37,32 @@ template <> struct Mfma<kBF16> {
   static __device__ __forceinline__ f32x4 run(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // Accumulator pinned to AGPRs (see mfma_gemm_fast_kernel).  The operands
+  // are VGPRs written by LDS loads (ordered by s_waitcnt) or by VALU code at
+  // least a k-step earlier.
+  static __device__ __forceinline__ void run_agpr(V8 a, V8 b, f32x4& c) {
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
 };
 template <> struct Mfma<kF16> {
   using V8 = f16x8;
   static __device__ __forceinline__ f32x4 run(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ void run_agpr(V8 a, V8 b, f32x4& c) {
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
 };
+
+// Wait states around the pinned-accumulator MFMAs, which the compiler cannot
+// see: before the first MFMA (the accumulators were just zeroed by VALU
+// writes) and before the accumulators are read back (an MFMA result needs
+// more than a dozen wait states before another instruction may read it).
+// The scheduling barrier keeps every instruction on its side.
+__device__ __forceinline__ void mfma_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // element offset of chunk c (8 elements) of row r inside a 64-wide LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
@@ -301,7 +320,11 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     consecutive k of weight group g (8 per half); A is read with the same k
 //     order;
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
-//     works on its own contiguous set of weight column panels.
+//     works on its own contiguous set of weight column panels;
+//   * the 256 accumulator registers of a wave fill the AGPR file exactly; the
+//     MFMAs are written with AGPR-constrained operands so the register
+//     allocator keeps every accumulator in place (left to itself it splits
+//     them between the two files and moves them around every k-step).
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
@@ -486,7 +509,7 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd0 + (i + 1) * 2048);
       else a_nxt = *reinterpret_cast<const V8*>(la + a_rd1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][0], a_cur, acc[t][i]);
+      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][0], a_cur, acc[t][i]);
       __builtin_amdgcn_sched_barrier(0);
       a_cur = a_nxt;
     }
@@ -495,7 +518,7 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       V8 a_nxt = a_cur;
       if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd1 + (i + 1) * 2048);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t][i] = Mfma<DT>::run(bcur[t][1], a_cur, acc[t][i]);
+      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][1], a_cur, acc[t][i]);
       if (i & 1) bnext[i >> 2][(i >> 1) & 1] = decode(raw, i >> 2, (i >> 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       a_cur = a_nxt;
@@ -523,7 +546,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   lds_barrier();
 
   // ---------------------------------------------------------------- main loop
+  // the zeroed accumulators are materialised in AGPRs before the fence
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[t][i]));
+  mfma_fence();
   for (int kt = 0; kt < KT; ++kt) step(kt);
+  mfma_fence();
 
   // ---------------------------------------------------------------- epilogue
   // acc[t][i][v]: tile row 16 i + fr, tile column 64 w + 16 t + 4 fg + v
