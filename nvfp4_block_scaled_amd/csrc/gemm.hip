@@ -424,8 +424,12 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws_e, (uint64_t)N * (K / 16));
 
   // A: chunk j of this thread is tile row (tid >> 3) + 32 j, k-chunk tid & 7,
-  // stored at LDS slot (tid & 7) ^ (row & 7) of that row (row & 7 does not
-  // depend on j, so chunk j lands 32 rows = 4096 bytes after chunk 0).
+  // stored at LDS slot (tid & 7) ^ swz(row) of that row, swz(r) = (r & 7) ^
+  // ((r >> 3) & 1): any 8 consecutive rows, and each parity class of any 16
+  // consecutive rows, put a given k-chunk in distinct 16-byte slots, so the
+  // fragment reads (16 rows, one chunk) and the stores (8 rows x 8 chunks)
+  // are free of bank conflicts whether a bank row spans one 128-byte tile row
+  // or two.  swz does not depend on j: chunk j lands 4096 bytes after chunk 0.
   uint32_t a_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -438,11 +442,12 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       arow = bm + rr;
     a_off[j] = (uint32_t)((arow * K + (tid & 7) * 8) * (int64_t)sizeof(T));
   }
-  const int a_dst = (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+  const int a_dst = (tid >> 3) * 128 + (((tid & 7) ^ swz(tid >> 3)) << 4);
   const int fr = lane & 15;  // MFMA row / column inside a 16 x 16 tile
   const int fg = lane >> 4;  // k group: elements 16 fg .. 16 fg + 15 of a k-step
-  const int a_rd0 = fr * 128 + (((2 * fg) ^ (fr & 7)) << 4);
-  const int a_rd1 = fr * 128 + (((2 * fg + 1) ^ (fr & 7)) << 4);
+  const int a_rd0 = fr * 128 + (((2 * fg) ^ swz(fr)) << 4);
+  const int a_rd1 = fr * 128 + (((2 * fg + 1) ^ swz(fr)) << 4);
   // weights: column tile t of this wave is column bn + 64 w + 16 t + fr
   uint32_t c_off[4], s_off[4];
 #pragma unroll
@@ -488,44 +493,40 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 
   const int KT = K / BK;
   V8 bcur[4][2], bnext[4][2];
-  BRaw raw;  // raw weights of the next k-step
+  BRaw raw0, raw1;  // raw weights of even / odd k-steps
 
-  // Step kt: MFMAs on A(kt) (LDS stage kt & 1) and bcur; the loads of A(kt + 1)
-  // are in flight meanwhile; the second half decodes the weights of kt + 1
-  // from `raw` into bnext, after which `raw` is reloaded with kt + 2.  The
-  // body is straight-line: past the end of k the loads re-read the last
-  // k-step and the extra decode is discarded, so every wait the compiler
-  // places counts exactly the loads that are in flight.
-  auto step = [&](int kt) {
+  // Step kt: MFMAs on A(kt) (LDS stage kt & 1) and bcur.  At its top it
+  // issues the loads of A(kt + 1) and of the raw weights of kt + 2 (into the
+  // set raw(kt) used to occupy); its second half decodes the weights of
+  // kt + 1 from the other set into bnext.  The body is straight-line: past
+  // the end of k the loads re-read the last k-step and the extra decode is
+  // discarded, so every wait the compiler places counts exactly the loads
+  // that are in flight.
+  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext) {
     load_a(min(kt + 1, KT - 1));
+    load_b(min(kt + 2, KT - 1), rfill);
     const uint8_t* la = sa + (kt & 1) * kAStageBytes;
-    // The A fragment of m-tile i + 1 is read while the MFMAs of i issue; the
-    // scheduling barriers keep that one-ahead structure (and the register
-    // footprint) as written.
-    V8 a_cur = *reinterpret_cast<const V8*>(la + a_rd0);
+    // A fragments are read three m-tiles ahead of their MFMAs; the scheduling
+    // barriers keep that structure (and the register footprint) as written.
+    V8 ar[3];
+    ar[0] = *reinterpret_cast<const V8*>(la + a_rd0);
+    ar[1] = *reinterpret_cast<const V8*>(la + a_rd0 + 2048);
+    ar[2] = *reinterpret_cast<const V8*>(la + a_rd0 + 4096);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      V8 a_nxt;
-      if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd0 + (i + 1) * 2048);
-      else a_nxt = *reinterpret_cast<const V8*>(la + a_rd1);
+    for (int q = 0; q < 32; ++q) {
+      const int s = q >> 4, i = q & 15;
+      const V8 a = ar[q % 3];
+      if (q + 3 < 32) {
+        const int q3 = q + 3;
+        ar[q % 3] = *reinterpret_cast<const V8*>(la + ((q3 >> 4) ? a_rd1 : a_rd0) + (q3 & 15) * 2048);
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][0], a_cur, acc[t][i]);
+      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][s], a, acc[t][i]);
+      if (s == 1 && (i & 1)) bnext[i >> 2][(i >> 1) & 1] = decode(rnext, i >> 2, (i >> 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      a_cur = a_nxt;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      V8 a_nxt = a_cur;
-      if (i < 15) a_nxt = *reinterpret_cast<const V8*>(la + a_rd1 + (i + 1) * 2048);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][1], a_cur, acc[t][i]);
-      if (i & 1) bnext[i >> 2][(i >> 1) & 1] = decode(raw, i >> 2, (i >> 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      a_cur = a_nxt;
     }
     store_a(kt + 1);  // into the other stage; past the end nobody reads it
     lds_barrier();
-    load_b(min(kt + 2, KT - 1), raw);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bcur[t][0] = bnext[t][0];
@@ -535,14 +536,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 
   // ---------------------------------------------------------------- prologue
   load_a(0);
-  load_b(0, raw);
+  load_b(0, raw0);
+  load_b(min(1, KT - 1), raw1);
   store_a(0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    bcur[t][0] = decode(raw, t, 0);
-    bcur[t][1] = decode(raw, t, 1);
+    bcur[t][0] = decode(raw0, t, 0);
+    bcur[t][1] = decode(raw0, t, 1);
   }
-  load_b(min(1, KT - 1), raw);
   lds_barrier();
 
   // ---------------------------------------------------------------- main loop
@@ -552,7 +553,13 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 #pragma unroll
     for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[t][i]));
   mfma_fence();
-  for (int kt = 0; kt < KT; ++kt) step(kt);
+  // two steps per trip so that the raw-weight sets swap roles statically
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(kt, raw0, raw1);
+    step(kt + 1, raw1, raw0);
+  }
+  if (kt < KT) step(kt, raw0, raw1);
   mfma_fence();
 
   // ---------------------------------------------------------------- epilogue
