@@ -192,6 +192,16 @@ def bench_gather(args, nv, torch, W):
     return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS)
 
 
+def bench_copy(args, torch):
+    """A plain device-to-device copy of 512 MiB: the calibration kernel for the
+    HBM byte counters (FETCH_SIZE / WRITE_SIZE read against known bytes)."""
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 256)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), args.steps, args.warmup)
+    return dict(ms=ms, bytes_read=n, bytes_written=n, gbs=2 * n / ms / 1e6)
+
+
 def cpu_baseline(data, seconds_target=15.0, cols=2048):
     """The oracle on a sample of the headline workload, on this host's cores:
     the first `rows` rows of x against the first `cols` weight rows (the
@@ -226,7 +236,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "quantize", "gather"])
+    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "quantize", "gather", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -262,6 +272,12 @@ def main():
         log("gather_qmm MoE ...")
         res["gather"] = bench_gather(args, nv, torch, W)
         log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s")
+
+    if args.only == "copy":
+        c = bench_copy(args, torch)
+        log(f"copy 512 MiB: {c['ms'] * 1e3:.1f} us, {c['gbs']:.0f} GB/s")
+        print(json.dumps({"workload": "device copy (counter calibration)", **c}), flush=True)
+        return
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

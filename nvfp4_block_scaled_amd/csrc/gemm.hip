@@ -306,16 +306,20 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     workgroup, by the wave that multiplies with it, straight into the MFMA
 //     operand registers -- the weights never touch LDS: each wave loads its
 //     own packed codes (8 bytes per column and lane group) and scale dwords
-//     with buffer loads, about 1.5 k-steps ahead of their use;
-//   * A is double-buffered in LDS: the loads of A(i + 1) are issued at the top
-//     of step i and written to LDS (16-byte chunks XOR-swizzled by row) after
-//     the step's MFMAs have been issued; one barrier per k-step, without a
-//     memory fence, so the weight loads stay in flight across it;
-//   * a k-step is two halves of 64 MFMAs (16x16x32); each half uses one of
-//     two weight fragments per column tile and, in between its MFMAs, decodes
-//     the fragment the next half needs (two codes per
-//     v_cvt_scalef32_pk_f32_fp4, one multiply by e4m3(s) * g/2688, two values
-//     per v_cvt_pk_bf16_f32);
+//     with buffer loads two k-steps ahead of their use;
+//   * A goes through three LDS stages: A(i + 2) is written in the middle of
+//     step i from registers loaded one step earlier, right after the one
+//     barrier of the step (no memory fence, so loads stay in flight across
+//     it); the last A fragments of step i are read three MFMA groups ahead,
+//     running into the first fragments of step i + 1, so a step starts
+//     without waiting for LDS;
+//   * a k-step is 32 groups of 4 MFMAs (16x16x32); group q uses the A
+//     fragment of m-tile q % 16 and k-half q / 16, and carries one quarter
+//     of the decode of one weight fragment of step i + 1 (e4m3 scale once per
+//     column tile; then per dword: two codes by v_cvt_scalef32_pk_f32_fp4,
+//     two multiplies by e4m3(s) * g/2688, one conversion to two 16-bit
+//     values), so the decode is spread evenly between the MFMAs of the wave
+//     (one wave per SIMD issues in order);
 //   * inside a 64-wide k-step, MFMA lane group g (= lane / 16) takes the 16
 //     consecutive k of weight group g (8 per half); A is read with the same k
 //     order;
@@ -326,6 +330,7 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     allocator keeps every accumulator in place (left to itself it splits
 //     them between the two files and moves them around every k-step).
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
+constexpr int kAStages = 3;
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 
 // LDS barrier without a memory fence: finish this wave's LDS operations, then
@@ -335,22 +340,42 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The same, but only this wave's LDS operations older than its 4 most recent
+// ones must have finished: the main loop's barrier, where the most recent LDS
+// operations are A-fragment reads (at most 4 in flight) and the stores that
+// must be visible were issued a whole k-step earlier.
+__device__ __forceinline__ void lds_barrier_lag4() {
+  asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const int n = bytes >= 0xFFFFFFFFull ? -1 : (int)(uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
 }
 
+// Two 16-bit values (element 2j low) from two floats.
 template <int DT>
-__device__ __forceinline__ typename Mfma<DT>::V8 decode_frag(uint32_t codes, float se) {
-  float q[8];
-  e2m1_decode8_f32(codes, q);
-  typename Mfma<DT>::V8 o;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  using T = typename Elem<DT>::T;
+  typedef T T2 __attribute__((ext_vector_type(2)));
+  T2 v;
+  v[0] = from_f32<DT>(a);
+  v[1] = from_f32<DT>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Dword P of a decoded weight fragment: the two codes of byte P of the code
+// word, times the effective block scale, as two 16-bit values.
+template <int DT, int P>
+__device__ __forceinline__ uint32_t decode_dword(uint32_t codes, float se) {
+  const f32x2 v = e2m1_decode2_f32<P>(codes);
+  float a, b;
+  {
 #pragma clang fp contract(off)
-    o[i] = from_f32<DT>(q[i] * se);
+    a = v.x * se;
+    b = v.y * se;
   }
-  return o;
+  return pack2<DT>(a, b);
 }
 
 // Raw weights of one k-step for one lane: for each of its 4 column tiles,
@@ -370,7 +395,7 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
                       int top_k, int E, int tiles_m) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
-  __shared__ __attribute__((aligned(16))) uint8_t sa[2 * kAStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sa[kAStages * kAStageBytes];
   __shared__ int out_rows[BM];
 
   const int tid = threadIdx.x;
@@ -464,8 +489,8 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     for (int j = 0; j < 8; ++j)
       astage[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[j], so, 0));
   };
-  auto store_a = [&](int kt) {
-    uint8_t* base = sa + (kt & 1) * kAStageBytes + a_dst;
+  auto store_a = [&](int stage_off) {
+    uint8_t* base = sa + stage_off + a_dst;
 #pragma unroll
     for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(base + j * 4096) = astage[j];
   };
@@ -476,13 +501,23 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * (BK / 16), 0);
     }
   };
-  auto decode = [&](const BRaw& b, int t, int s) -> V8 {
+  auto scale_of = [&](const BRaw& b, int t) -> float {
     float se;
     {
 #pragma clang fp contract(off)
       se = e4m3_decode(b.scale[t] >> (8 * fg)) * dec_w;
     }
-    return decode_frag<DT>(s ? b.code[t].y : b.code[t].x, se);
+    return se;
+  };
+  // one quarter (dword p) of weight fragment (t, s)
+  auto decode_part = [&](const BRaw& b, int t, int s, int p, float se) -> uint32_t {
+    const uint32_t w = s ? b.code[t].y : b.code[t].x;
+    switch (p) {
+      case 0: return decode_dword<DT, 0>(w, se);
+      case 1: return decode_dword<DT, 1>(w, se);
+      case 2: return decode_dword<DT, 2>(w, se);
+      default: return decode_dword<DT, 3>(w, se);
+    }
   };
 
   f32x4 acc[4][16];
@@ -492,59 +527,75 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     for (int i = 0; i < 16; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = K / BK;
-  V8 bcur[4][2], bnext[4][2];
-  BRaw raw0, raw1;  // raw weights of even / odd k-steps
+  u32x4 b0[4][2], b1[4][2];  // decoded weight fragments of even / odd k-steps
+  BRaw raw0, raw1;           // raw weights of even / odd k-steps
+  V8 ar[4];                  // A fragment ring: fragment q of a step in ar[q % 4]
+  int st_cur = 0, st_nxt = kAStageBytes, st_new = 2 * kAStageBytes;  // stages of A(i), A(i+1), A(i+2)
 
-  // Step kt: MFMAs on A(kt) (LDS stage kt & 1) and bcur.  At its top it
-  // issues the loads of A(kt + 1) and of the raw weights of kt + 2 (into the
-  // set raw(kt) used to occupy); its second half decodes the weights of
-  // kt + 1 from the other set into bnext.  The body is straight-line: past
-  // the end of k the loads re-read the last k-step and the extra decode is
-  // discarded, so every wait the compiler places counts exactly the loads
-  // that are in flight.
-  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext) {
-    load_a(min(kt + 1, KT - 1));
+  // Step kt: MFMAs on A(kt) and the fragments bc; loads the raw weights of
+  // kt + 2 into rfill (which held those of kt) and decodes rnext (kt + 1)
+  // into bn_; in its middle, after the barrier, writes A(kt + 2) to LDS and
+  // loads A(kt + 3).  The body is straight-line: past the end of k the loads
+  // re-read the last k-step and the extra work is discarded, so every wait
+  // the compiler places counts exactly the loads that are in flight.
+  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext, const u32x4 (&bc)[4][2], u32x4 (&bn_)[4][2]) {
     load_b(min(kt + 2, KT - 1), rfill);
-    const uint8_t* la = sa + (kt & 1) * kAStageBytes;
-    // A fragments are read three m-tiles ahead of their MFMAs; the scheduling
-    // barriers keep that structure (and the register footprint) as written.
-    V8 ar[3];
-    ar[0] = *reinterpret_cast<const V8*>(la + a_rd0);
-    ar[1] = *reinterpret_cast<const V8*>(la + a_rd0 + 2048);
-    ar[2] = *reinterpret_cast<const V8*>(la + a_rd0 + 4096);
+    const uint8_t* la = sa + st_cur;
+    const uint8_t* ln = sa + st_nxt;
+    float se = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
       const int s = q >> 4, i = q & 15;
-      const V8 a = ar[q % 3];
-      if (q + 3 < 32) {
+      const V8 a = ar[q & 3];
+      {
         const int q3 = q + 3;
-        ar[q % 3] = *reinterpret_cast<const V8*>(la + ((q3 >> 4) ? a_rd1 : a_rd0) + (q3 & 15) * 2048);
+        if (q3 < 32)
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(la + ((q3 >> 4) ? a_rd1 : a_rd0) + (q3 & 15) * 2048);
+        else
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd0 + (q3 - 32) * 2048);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(bcur[t][s], a, acc[t][i]);
-      if (s == 1 && (i & 1)) bnext[i >> 2][(i >> 1) & 1] = decode(rnext, i >> 2, (i >> 1) & 1);
+      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(__builtin_bit_cast(V8, bc[t][s]), a, acc[t][i]);
+      // decode: column tile dt = q / 8, half ds = (q / 4) & 1, dword q % 4
+      {
+        const int dt = q >> 3, ds = (q >> 2) & 1, dp = q & 3;
+        if ((q & 7) == 0) se = scale_of(rnext, dt);
+        bn_[dt][ds][dp] = decode_part(rnext, dt, ds, dp, se);
+      }
+      if (q == 15) {
+        lds_barrier_lag4();
+        store_a(st_new);
+        load_a(min(kt + 3, KT - 1));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    store_a(kt + 1);  // into the other stage; past the end nobody reads it
-    lds_barrier();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bcur[t][0] = bnext[t][0];
-      bcur[t][1] = bnext[t][1];
-    }
+    const int t0 = st_cur;
+    st_cur = st_nxt;
+    st_nxt = st_new;
+    st_new = t0;
   };
 
   // ---------------------------------------------------------------- prologue
+  // A(0), A(1) into stages 0 and 1, A(2) in registers, raw weights of steps
+  // 0 and 1, step 0's fragments decoded, the first three A fragments read.
   load_a(0);
+  store_a(0);
+  load_a(min(1, KT - 1));
+  store_a(kAStageBytes);
+  load_a(min(2, KT - 1));
   load_b(0, raw0);
   load_b(min(1, KT - 1), raw1);
-  store_a(0);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    bcur[t][0] = decode(raw0, t, 0);
-    bcur[t][1] = decode(raw0, t, 1);
+    const float se = scale_of(raw0, t);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b0[t][s][p] = decode_part(raw0, t, s, p, se);
   }
   lds_barrier();
+#pragma unroll
+  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa + a_rd0 + q * 2048);
 
   // ---------------------------------------------------------------- main loop
   // the zeroed accumulators are materialised in AGPRs before the fence
@@ -553,13 +604,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 #pragma unroll
     for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[t][i]));
   mfma_fence();
-  // two steps per trip so that the raw-weight sets swap roles statically
+  // two steps per trip so that the raw and decoded weight sets swap roles
+  // statically
   int kt = 0;
   for (; kt + 2 <= KT; kt += 2) {
-    step(kt, raw0, raw1);
-    step(kt + 1, raw1, raw0);
+    step(kt, raw0, raw1, b0, b1);
+    step(kt + 1, raw1, raw0, b1, b0);
   }
-  if (kt < KT) step(kt, raw0, raw1);
+  if (kt < KT) step(kt, raw0, raw1, b0, b1);
   mfma_fence();
 
   // ---------------------------------------------------------------- epilogue
