@@ -202,12 +202,12 @@ def bench_copy(args, torch):
     return dict(ms=ms, bytes_read=n, bytes_written=n, gbs=2 * n / ms / 1e6)
 
 
-def cpu_baseline(data, seconds_target=15.0, cols=2048):
+def cpu_baseline(data, seconds_target=12.0):
     """The oracle on a sample of the headline workload, on this host's cores:
     the first `rows` rows of x against the first `cols` weight rows (the
-    oracle quantizes those itself, untimed), x round trip + float32 weight
-    decode + double sums.  Rows double until one run takes a quarter of
-    seconds_target."""
+    oracle quantizes w itself, untimed), x round trip + float32 weight decode
+    + double sums.  The sample grows (rows first, then weight rows) until one
+    run takes a second, then is scaled to about seconds_target."""
     import numpy as np
     import oracle as O
     x, w_host = data
@@ -215,15 +215,29 @@ def cpu_baseline(data, seconds_target=15.0, cols=2048):
     xh = x.float().cpu().numpy()
     wh = w_host.float().numpy()
     gxh, gwh = O.tensor_amax(xh), O.tensor_amax(wh)
-    oc, os_ = O.quantize(wh[:cols], gwh)
-    rows = 4
-    while True:
+    oc, os_ = O.quantize(wh, gwh)
+
+    def run(rows, cols):
         t0 = time.perf_counter()
-        O.qqmm(xh, oc, os_, gxh, gwh, dtype="bf16", rows=np.arange(rows), nthreads=nthreads)
-        dt = time.perf_counter() - t0
-        if dt >= seconds_target / 4 or rows >= M:
+        O.qqmm(xh, oc[:cols], os_[:cols], gxh, gwh, dtype="bf16", rows=np.arange(rows),
+               nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    rows, cols = 4, 256
+    while True:
+        dt = run(rows, cols)
+        if dt >= 1.0 or (rows >= M and cols >= N):
             break
-        rows *= 2
+        if rows < M:
+            rows = min(M, rows * 2)
+        else:
+            cols = min(N, cols * 2)
+    if dt < seconds_target / 2:
+        if rows < M:
+            rows = min(M, max(rows, int(rows * seconds_target / dt)))
+        else:
+            cols = min(N, max(cols, int(cols * seconds_target / dt)))
+        dt = run(rows, cols)
     flop = 2.0 * rows * cols * K
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nthreads, kind="oracle",
                 sample=f"oracle qqmm on {rows} of {M} rows x {cols} of {N} weight rows, K={K} "

@@ -304,25 +304,28 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //   * the four waves split the 256 output columns (64 each) and all share the
 //     256 rows of A, so every weight element is decoded exactly once per
 //     workgroup, by the wave that multiplies with it, straight into the MFMA
-//     operand registers -- the weights never touch LDS: each wave loads its
-//     own packed codes (8 bytes per column and lane group) and scale dwords
-//     with buffer loads two k-steps ahead of their use;
+//     operand registers -- the weights never touch LDS: per k-step each lane
+//     loads 16 code bytes and one scale dword for each of its two columns,
+//     two k-steps ahead of their use;
+//   * the products are v_mfma_f32_32x32x16 (32 columns x 32 rows x 16 k): a
+//     wave's 64 x 256 block is 2 x 8 of them per 16-k sub-step, 64 per k-step.
+//     Per flop this issues half the MFMA instructions of the 16x16x32 form and
+//     leaves twice the room between them for the decode, which the single
+//     wave per SIMD issues in order with its MFMAs;
+//   * k order inside a 64-wide k-step: MFMA lane half h (= lane / 32) at
+//     sub-step u takes the 8 k from 32 h + 8 u, i.e. half u & 1 of weight
+//     group 2 h + u / 2 -- so a lane's codes for the whole k-step are 16
+//     consecutive bytes (groups 2h and 2h + 1), dword u feeding sub-step u; A
+//     is read from LDS in the same k order;
 //   * A goes through three LDS stages: A(i + 2) is written in the middle of
 //     step i from registers loaded one step earlier, right after the one
 //     barrier of the step (no memory fence, so loads stay in flight across
-//     it); the last A fragments of step i are read three MFMA groups ahead,
-//     running into the first fragments of step i + 1, so a step starts
-//     without waiting for LDS;
-//   * a k-step is 32 groups of 4 MFMAs (16x16x32); group q uses the A
-//     fragment of m-tile q % 16 and k-half q / 16, and carries one quarter
-//     of the decode of one weight fragment of step i + 1 (e4m3 scale once per
-//     column tile; then per dword: two codes by v_cvt_scalef32_pk_f32_fp4,
-//     two multiplies by e4m3(s) * g/2688, one conversion to two 16-bit
-//     values), so the decode is spread evenly between the MFMAs of the wave
-//     (one wave per SIMD issues in order);
-//   * inside a 64-wide k-step, MFMA lane group g (= lane / 16) takes the 16
-//     consecutive k of weight group g (8 per half); A is read with the same k
-//     order;
+//     it); A fragments are read three MFMA pairs ahead, running into the first
+//     fragments of step i + 1, so a step starts without waiting for LDS;
+//   * fragment pair q of a step (sub-step q / 8, row tile q % 8) carries one
+//     dword of the decode of step i + 1's weights (two codes by
+//     v_cvt_scalef32_pk_f32_fp4, two multiplies by e4m3(s) * g/2688, one
+//     conversion to two 16-bit values; every eighth pair also decodes a scale);
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
 //     works on its own contiguous set of weight column panels;
 //   * the 256 accumulator registers of a wave fill the AGPR file exactly; the
@@ -332,6 +335,24 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
 constexpr int kAStages = 3;
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
+
+template <int DT> struct Mfma32;
+template <> struct Mfma32<kBF16> {
+  static __device__ __forceinline__ void run_agpr(bf16x8 a, bf16x8 b, f32x16& c) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct Mfma32<kF16> {
+  static __device__ __forceinline__ void run_agpr(f16x8 a, f16x8 b, f32x16& c) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+
+// Wait states before the accumulators of the 32x32 MFMAs are read back.
+__device__ __forceinline__ void mfma32_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // LDS barrier without a memory fence: finish this wave's LDS operations, then
 // meet the other waves.  The "memory" clobber keeps the compiler from moving
@@ -378,11 +399,12 @@ __device__ __forceinline__ uint32_t decode_dword(uint32_t codes, float se) {
   return pack2<DT>(a, b);
 }
 
-// Raw weights of one k-step for one lane: for each of its 4 column tiles,
-// the 8 code bytes of its group and the dword of the column's 4 scales.
+// Raw weights of one k-step for one lane: for each of its 2 column tiles, the
+// 16 code bytes of its lane half (groups 2h, 2h + 1) and the dword of the
+// column's 4 scales.
 struct BRaw {
-  u32x2 code[4];
-  uint32_t scale[4];
+  u32x4 code[2];
+  uint32_t scale[2];
 };
 
 template <int DT, bool GATHER>
@@ -452,9 +474,10 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   // stored at LDS slot (tid & 7) ^ swz(row) of that row, swz(r) = (r & 7) ^
   // ((r >> 3) & 1): any 8 consecutive rows, and each parity class of any 16
   // consecutive rows, put a given k-chunk in distinct 16-byte slots, so the
-  // fragment reads (16 rows, one chunk) and the stores (8 rows x 8 chunks)
-  // are free of bank conflicts whether a bank row spans one 128-byte tile row
-  // or two.  swz does not depend on j: chunk j lands 4096 bytes after chunk 0.
+  // fragment reads (16 rows, one chunk per lane half) and the stores (8 rows
+  // x 8 chunks) are free of bank conflicts whether a bank row spans one
+  // 128-byte tile row or two.  swz does not depend on j: chunk j lands 4096
+  // bytes after chunk 0.
   uint32_t a_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -469,16 +492,18 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   }
   auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
   const int a_dst = (tid >> 3) * 128 + (((tid & 7) ^ swz(tid >> 3)) << 4);
-  const int fr = lane & 15;  // MFMA row / column inside a 16 x 16 tile
-  const int fg = lane >> 4;  // k group: elements 16 fg .. 16 fg + 15 of a k-step
-  const int a_rd0 = fr * 128 + (((2 * fg) ^ swz(fr)) << 4);
-  const int a_rd1 = fr * 128 + (((2 * fg + 1) ^ swz(fr)) << 4);
-  // weights: column tile t of this wave is column bn + 64 w + 16 t + fr
-  uint32_t c_off[4], s_off[4];
+  const int fr = lane & 31;  // MFMA row of A / column of B inside a 32-wide tile
+  const int fh = lane >> 5;  // lane half: k 8 fh .. 8 fh + 7 of each 16-k sub-step
+  // fragment of row tile mt, sub-step u: tile row 32 mt + fr, k-chunk 4 fh + u
+  int a_rd[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int col = min(bn + wave * 64 + t * 16 + fr, N - 1);
-    c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fg * 8;
+  for (int u = 0; u < 4; ++u) a_rd[u] = fr * 128 + (((4 * fh + u) ^ swz(fr)) << 4);
+  // weights: column tile t of this wave is column bn + 64 w + 32 t + fr
+  uint32_t c_off[2], s_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int col = min(bn + wave * 64 + t * 32 + fr, N - 1);
+    c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fh * 16;
     s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
   }
 
@@ -496,22 +521,23 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   };
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      b.code[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_c, c_off[t], kt * (BK / 2), 0));
+    for (int t = 0; t < 2; ++t) {
+      b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * (BK / 2), 0));
       b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * (BK / 16), 0);
     }
   };
-  auto scale_of = [&](const BRaw& b, int t) -> float {
+  // effective scale of group 2 fh + gi (gi = 0, 1) of column tile t
+  auto scale_of = [&](const BRaw& b, int t, int gi) -> float {
     float se;
     {
 #pragma clang fp contract(off)
-      se = e4m3_decode(b.scale[t] >> (8 * fg)) * dec_w;
+      se = e4m3_decode(b.scale[t] >> (16 * fh + 8 * gi)) * dec_w;
     }
     return se;
   };
-  // one quarter (dword p) of weight fragment (t, s)
-  auto decode_part = [&](const BRaw& b, int t, int s, int p, float se) -> uint32_t {
-    const uint32_t w = s ? b.code[t].y : b.code[t].x;
+  // dword p of the fragment of column tile t, sub-step u
+  auto decode_part = [&](const BRaw& b, int t, int u, int p, float se) -> uint32_t {
+    const uint32_t w = b.code[t][u];
     switch (p) {
       case 0: return decode_dword<DT, 0>(w, se);
       case 1: return decode_dword<DT, 1>(w, se);
@@ -520,14 +546,16 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     }
   };
 
-  f32x4 acc[4][16];
+  f32x16 acc[2][8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][i][v] = 0.f;
 
   const int KT = K / BK;
-  u32x4 b0[4][2], b1[4][2];  // decoded weight fragments of even / odd k-steps
+  u32x4 b0[2][4], b1[2][4];  // decoded weight fragments [column tile][sub-step] of even / odd k-steps
   BRaw raw0, raw1;           // raw weights of even / odd k-steps
   V8 ar[4];                  // A fragment ring: fragment q of a step in ar[q % 4]
   int st_cur = 0, st_nxt = kAStageBytes, st_new = 2 * kAStageBytes;  // stages of A(i), A(i+1), A(i+2)
@@ -538,30 +566,32 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   // loads A(kt + 3).  The body is straight-line: past the end of k the loads
   // re-read the last k-step and the extra work is discarded, so every wait
   // the compiler places counts exactly the loads that are in flight.
-  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext, const u32x4 (&bc)[4][2], u32x4 (&bn_)[4][2]) {
+  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext, const u32x4 (&bc)[2][4], u32x4 (&bn_)[2][4]) {
     load_b(min(kt + 2, KT - 1), rfill);
     const uint8_t* la = sa + st_cur;
     const uint8_t* ln = sa + st_nxt;
     float se = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-      const int s = q >> 4, i = q & 15;
+      const int u = q >> 3, i = q & 7;
       const V8 a = ar[q & 3];
       {
         const int q3 = q + 3;
         if (q3 < 32)
-          ar[q3 & 3] = *reinterpret_cast<const V8*>(la + ((q3 >> 4) ? a_rd1 : a_rd0) + (q3 & 15) * 2048);
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(la + a_rd[q3 >> 3] + (q3 & 7) * 4096);
         else
-          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd0 + (q3 - 32) * 2048);
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd[0] + (q3 - 32) * 4096);
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) Mfma<DT>::run_agpr(__builtin_bit_cast(V8, bc[t][s]), a, acc[t][i]);
-      // decode: column tile dt = q / 8, half ds = (q / 4) & 1, dword q % 4
-      {
-        const int dt = q >> 3, ds = (q >> 2) & 1, dp = q & 3;
-        if ((q & 7) == 0) se = scale_of(rnext, dt);
-        bn_[dt][ds][dp] = decode_part(rnext, dt, ds, dp, se);
-      }
+      // decode: column tile dt = q / 16, sub-step du = (q / 4) % 4, dword q % 4
+      const int dt = q >> 4, du = (q >> 2) & 3, dp = q & 3;
+      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bc[0][u]), a, acc[0][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((q & 7) == 0) se = scale_of(rnext, dt, du >> 1);
+      const uint32_t part = decode_part(rnext, dt, du, dp, se);
+      __builtin_amdgcn_sched_barrier(0);
+      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bc[1][u]), a, acc[1][i]);
+      __builtin_amdgcn_sched_barrier(0);
+      bn_[dt][du][dp] = part;
       if (q == 15) {
         lds_barrier_lag4();
         store_a(st_new);
@@ -586,24 +616,28 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   load_b(0, raw0);
   load_b(min(1, KT - 1), raw1);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const float se = scale_of(raw0, t);
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int u = 0; u < 4; ++u) {
+      const float se = scale_of(raw0, t, u >> 1);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) b0[t][s][p] = decode_part(raw0, t, s, p, se);
-  }
+      for (int p = 0; p < 4; ++p) b0[t][u][p] = decode_part(raw0, t, u, p, se);
+    }
   lds_barrier();
+  // no scalar (kernel argument) load may still be outstanding when the loop
+  // starts, or the first fragment wait of every trip becomes a full drain
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa + a_rd0 + q * 2048);
+  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa + a_rd[0] + q * 4096);
 
   // ---------------------------------------------------------------- main loop
   // the zeroed accumulators are materialised in AGPRs before the fence
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("" : "+a"(acc[t][i]));
-  mfma_fence();
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(acc[t][i]));
+  mfma32_fence();
   // two steps per trip so that the raw and decoded weight sets swap roles
   // statically
   int kt = 0;
@@ -612,33 +646,36 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     step(kt + 1, raw1, raw0, b1, b0);
   }
   if (kt < KT) step(kt, raw0, raw1, b0, b1);
-  mfma_fence();
+  mfma32_fence();
 
   // ---------------------------------------------------------------- epilogue
-  // acc[t][i][v]: tile row 16 i + fr, tile column 64 w + 16 t + 4 fg + v
+  // acc[t][i][v]: tile row 32 i + fr, tile column 64 w + 32 t + 8 (v / 4) +
+  // 4 fh + v % 4
   T* O = reinterpret_cast<T*>(out);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int orow = out_rows[i * 16 + fr];
+  for (int i = 0; i < 8; ++i) {
+    const int orow = out_rows[i * 32 + fr];
     if (orow < 0) continue;
     T* op = O + (int64_t)orow * N;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = bn + wave * 64 + t * 16 + 4 * fg;
-      if (c + 3 < N) {
-        typedef T T4 __attribute__((ext_vector_type(4)));
-        T4 v;
-        v[0] = from_f32<DT>(acc[t][i][0]);
-        v[1] = from_f32<DT>(acc[t][i][1]);
-        v[2] = from_f32<DT>(acc[t][i][2]);
-        v[3] = from_f32<DT>(acc[t][i][3]);
-        *reinterpret_cast<T4*>(op + c) = v;
-      } else {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (c + v < N) op[c + v] = from_f32<DT>(acc[t][i][v]);
+      for (int g = 0; g < 4; ++g) {
+        const int c = bn + wave * 64 + t * 32 + 8 * g + 4 * fh;
+        if (c + 3 < N) {
+          typedef T T4 __attribute__((ext_vector_type(4)));
+          T4 v;
+          v[0] = from_f32<DT>(acc[t][i][4 * g + 0]);
+          v[1] = from_f32<DT>(acc[t][i][4 * g + 1]);
+          v[2] = from_f32<DT>(acc[t][i][4 * g + 2]);
+          v[3] = from_f32<DT>(acc[t][i][4 * g + 3]);
+          *reinterpret_cast<T4*>(op + c) = v;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (c + v < N) op[c + v] = from_f32<DT>(acc[t][i][4 * g + v]);
+        }
       }
-    }
   }
 }
 
