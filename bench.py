@@ -37,6 +37,27 @@ PEAK_BF16_TFLOPS = 2500.0
 
 M, N, K = 2048, 14336, 4096
 
+# HBM bytes per launch from two rocprofv3 counter runs (FETCH_SIZE, then
+# WRITE_SIZE), each scaled by what the same counter reads for a 512 MiB device
+# copy (fetch x 1.9999, write x 1.0000).  A figure holds only for the kernel
+# source it was measured on (sha256 prefix of the file), else it is reported
+# as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
+MEASURED_TRAFFIC = {
+    "gemm": ("gemm.hip", "6454c3ec9bf973f8", 360599224),
+    "qmv": ("qmv.hip", "09301831f4c6ad9f", 33246960),
+}
+
+
+def measured_traffic(kernel):
+    import hashlib
+    src, sha, nbytes = MEASURED_TRAFFIC[kernel]
+    path = os.path.join(ROOT, "nvfp4_block_scaled_amd", "csrc", src)
+    try:
+        cur = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    return nbytes if cur == sha else None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -302,17 +323,19 @@ def main():
         line["config"] = {"workload": "qqmm prefill: x bf16 [2048,4096] (amax + NVFP4 round trip) "
                                       "@ NVFP4 w [14336,4096]^T, bf16 out",
                           "m": M, "n": N, "k": K, "group_size": 16}
-        line["roofline"] = {"bound": "mfma", "kernel": "mfma_gemm_kernel (nvfp4_qmm on x_hat)",
+        line["roofline"] = {"bound": "mfma", "kernel": "mfma_gemm_fast_kernel<bf16> (nvfp4_qmm on x_hat)",
                             "achieved": round(q["gemm_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(q["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
-                            "traffic": None, "ms_per_launch": round(q["ms_gemm"], 4),
-                            "algorithmic_flop_per_launch": q["flop"]}
+                            "traffic": measured_traffic("gemm"), "ms_per_launch": round(q["ms_gemm"], 4),
+                            "algorithmic_flop_per_launch": q["flop"],
+                            "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2}
         line["x_prepass_us"] = round(q["ms_prepass"] * 1e3, 2)
     if "qmv" in res:
         v = res["qmv"]
         line["qmv"] = {"value": round(v["gbs"], 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,
                        "frac": round(v["gbs"] / PEAK_HBM_GBS, 4), "us_per_launch": round(v["ms"] * 1e3, 3),
-                       "algorithmic_bytes_per_launch": v["bytes"], "weight_copies_rotated": v["copies"],
+                       "algorithmic_bytes_per_launch": v["bytes"], "traffic": measured_traffic("qmv"),
+                       "weight_copies_rotated": v["copies"],
                        "warm_cache_GBps": round(v["gbs_warm"], 1),
                        "workload": "qmv decode: x bf16 [1,4096] @ NVFP4 w [14336,4096]^T"}
     if "quantize" in res:
