@@ -20,6 +20,9 @@ Beside it, on the same run:
   cpu_baseline  the oracle (plain C, double accumulation) on a bounded row
               sample of the headline workload, on this host's cores.
 Inputs are synthetic and already resident in device memory when timing starts.
+Each timed section first runs its own work untimed for 50-150 ms (the clocks
+ramp for about 40 ms once sustained load starts), then the warm-up calls, then
+the timed calls.
 """
 import argparse
 import json
@@ -61,6 +64,19 @@ def measured_traffic(kernel):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def settle(fn, seconds=0.15):
+    """Run fn untimed for `seconds` of continuous GPU work.  The MI355X's clocks
+    ramp for about 40 ms after sustained matrix-core load starts (the qqmm
+    contraction runs ~20 % slower in its first milliseconds); the steady state
+    is what a serving loop sees, so every timed section starts after this."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def timed(fn, iters, warmup, graph=False):
@@ -112,6 +128,7 @@ def bench_qqmm(args, nv, torch, W):
         nv.nvfp4_tensor_amax(x, out=gx)
         nv.nvfp4_qqmm(x, wc, ws, gx, gw, out=out, workspace=wsp)
 
+    settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -121,6 +138,7 @@ def bench_qqmm(args, nv, torch, W):
     flop = 2.0 * M * N * K
     # the contraction kernel alone, on x_hat
     xhat = nv.nvfp4_quant_dequant(x, gx)
+    settle(lambda: nv.nvfp4_qmm(xhat, wc, ws, gw, out=out), 0.05)
     ms_gemm = timed(lambda: nv.nvfp4_qmm(xhat, wc, ws, gw, out=out), args.steps, 2)
     ms_prepass = timed(lambda: nv.nvfp4_quant_dequant(x, gx, out=xhat), args.steps, 2, graph=True)
     torch.cuda.synchronize()
@@ -147,6 +165,7 @@ def bench_qmv(args, nv, torch, W):
         nv.nvfp4_qmv(x, wcs[i], wss[i], gx, gw, out=out)
 
     iters = copies * 4
+    settle(call, 0.05)
     ms = timed(call, iters, copies, graph=True)
     nbytes = per + x.numel() * 2 + N * 2
     # warm (cache-resident) number for context: always the same copy
@@ -207,8 +226,9 @@ def bench_gather(args, nv, torch, W):
     torch.cuda.synchronize()
     out = torch.empty(T, top_k, Nn, dtype=torch.bfloat16, device="cuda")
     wsp, _ = nv.gather_workspace(T, top_k, E, Nn, Kk, "cuda")
-    ms = timed(lambda: nv.nvfp4_gather_qmm(x, wc, wsc, idx, g, out=out, workspace=wsp),
-               max(3, args.steps // 4), 2)
+    gq = lambda: nv.nvfp4_gather_qmm(x, wc, wsc, idx, g, out=out, workspace=wsp)
+    settle(gq)
+    ms = timed(gq, max(3, args.steps // 4), 2)
     flop = 2.0 * T * top_k * Nn * Kk
     return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS)
 
@@ -223,7 +243,7 @@ def bench_copy(args, torch):
     return dict(ms=ms, bytes_read=n, bytes_written=n, gbs=2 * n / ms / 1e6)
 
 
-def cpu_baseline(data, seconds_target=12.0):
+def cpu_baseline(data, seconds_target=20.0):
     """The oracle on a sample of the headline workload, on this host's cores:
     the first `rows` rows of x against the first `cols` weight rows (the
     oracle quantizes w itself, untimed), x round trip + float32 weight decode
