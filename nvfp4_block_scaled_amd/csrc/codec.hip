@@ -62,30 +62,34 @@ __device__ __forceinline__ void store8(void* base, int64_t h, const float (&v)[8
 
 // ------------------------------------------------------------------ amax
 
-constexpr int kAmaxBlocks = 512;
+constexpr int kAmaxBlocks = 256;    // one workgroup per CU
+constexpr int kAmaxThreads = 1024;
 
 __global__ void amax_zero_kernel(float* out) { *out = 0.0f; }
 
-// max |x| over n elements: grid-stride loop over 8-element chunks (two in
-// flight per lane), a scalar tail, a wave max, a workgroup max through LDS and
-// one atomicMax per workgroup on the float's bit pattern (non-negative floats
-// order like their unsigned bits).
+// max |x| over n elements: one 1024-thread workgroup per CU, a grid-stride
+// loop over 8-element chunks with four chunks in flight per lane (a whole
+// 16.8 MB activation is one round of loads), a scalar tail, a wave max, a
+// workgroup max through LDS and one atomicMax per workgroup on the float's
+// bit pattern (non-negative floats order like their unsigned bits).
 template <int DT>
-__global__ void __launch_bounds__(kThreads) amax_kernel(const void* __restrict__ x, int64_t n,
-                                                        float* __restrict__ out) {
-  __shared__ float part[kThreads / 64];
+__global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restrict__ x, int64_t n,
+                                                            float* __restrict__ out) {
+  __shared__ float part[kAmaxThreads / 64];
   const int64_t chunks = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   float m = 0.0f;
   int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; h + stride < chunks; h += 2 * stride) {
-    float v[8], u[8];
-    load8<DT>(x, h, v);
-    load8<DT>(x, h + stride, u);
+  for (; h + 3 * stride < chunks; h += 4 * stride) {
+    float v[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fmaxf(__builtin_fabsf(v[i]), __builtin_fabsf(u[i])));
+    for (int u = 0; u < 4; ++u) load8<DT>(x, h + u * stride, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[u][i]));
   }
-  if (h < chunks) {
+  for (; h < chunks; h += stride) {
     float v[8];
     load8<DT>(x, h, v);
 #pragma unroll
@@ -102,7 +106,7 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const void* __restrict__
   if (threadIdx.x == 0) {
     float b = part[0];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) b = fmaxf(b, part[w]);
+    for (int w = 1; w < kAmaxThreads / 64; ++w) b = fmaxf(b, part[w]);
     atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(b));
   }
 }
@@ -219,11 +223,11 @@ int grid_for(int64_t work, int per_block, int max_blocks) {
 hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipStream_t s) {
   amax_zero_kernel<<<1, 1, 0, s>>>(out);
   if (n > 0) {
-    int blocks = grid_for(n / 8 + 1, kThreads * 2, kAmaxBlocks);
+    int blocks = grid_for(n / 8 + 1, kAmaxThreads * 4, kAmaxBlocks);
     switch (dt) {
-      case kF32: amax_kernel<kF32><<<blocks, kThreads, 0, s>>>(x, n, out); break;
-      case kF16: amax_kernel<kF16><<<blocks, kThreads, 0, s>>>(x, n, out); break;
-      default: amax_kernel<kBF16><<<blocks, kThreads, 0, s>>>(x, n, out); break;
+      case kF32: amax_kernel<kF32><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
+      case kF16: amax_kernel<kF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
+      default: amax_kernel<kBF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
     }
   }
   return hipGetLastError();
