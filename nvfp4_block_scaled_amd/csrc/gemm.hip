@@ -20,6 +20,8 @@
 //   * the MFMA takes the weight fragment as its first operand, so each lane
 //     ends with 4 consecutive output columns of one row (one 8-byte store).
 // float32 inputs use a plain LDS-tiled FMA kernel with float32 weights.
+#include <type_traits>
+
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -317,15 +319,21 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     group 2 h + u / 2 -- so a lane's codes for the whole k-step are 16
 //     consecutive bytes (groups 2h and 2h + 1), dword u feeding sub-step u; A
 //     is read from LDS in the same k order;
-//   * A goes through three LDS stages: A(i + 2) is written in the middle of
-//     step i from registers loaded one step earlier, right after the one
-//     barrier of the step (no memory fence, so loads stay in flight across
-//     it); A fragments are read three MFMA pairs ahead, running into the first
+//   * A goes through three LDS stages (three separate LDS arrays, so that the
+//     compiler can tell a stage being filled from the ones being read): in the
+//     middle of step i, right after the step's one barrier, every wave loads
+//     its quarter of A(i + 2) from global memory straight into LDS
+//     (buffer_load ... lds: no registers, no LDS store instructions); the
+//     barrier of step i + 1 first waits for that load.  The barrier carries no
+//     memory fence, so the weight loads stay in flight across it.  A
+//     fragments are read three MFMA pairs ahead, running into the first
 //     fragments of step i + 1, so a step starts without waiting for LDS;
 //   * fragment pair q of a step (sub-step q / 8, row tile q % 8) carries one
 //     dword of the decode of step i + 1's weights (two codes by
 //     v_cvt_scalef32_pk_f32_fp4, two multiplies by e4m3(s) * g/2688, one
 //     conversion to two 16-bit values; every eighth pair also decodes a scale);
+//   * the k loop is unrolled by six steps (three A stages x two weight register
+//     sets), so every stage and register set is fixed in the code;
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
 //     works on its own contiguous set of weight column panels;
 //   * the 256 accumulator registers of a wave fill the AGPR file exactly; the
@@ -333,8 +341,8 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     allocator keeps every accumulator in place (left to itself it splits
 //     them between the two files and moves them around every k-step).
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
-constexpr int kAStages = 3;
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
+constexpr int kBLoadsPerStep = 4;          // weight loads issued per k-step and wave
 
 template <int DT> struct Mfma32;
 template <> struct Mfma32<kBF16> {
@@ -361,12 +369,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The same, but only this wave's LDS operations older than its 4 most recent
-// ones must have finished: the main loop's barrier, where the most recent LDS
-// operations are A-fragment reads (at most 4 in flight) and the stores that
-// must be visible were issued a whole k-step earlier.
-__device__ __forceinline__ void lds_barrier_lag4() {
-  asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
+// The main loop's barrier: this wave's global-to-LDS load of the A stage
+// needed next has landed -- it was issued a step ago and only the
+// kBLoadsPerStep weight loads of this step are younger -- then meet the other
+// waves.
+__device__ __forceinline__ void a_stage_barrier() {
+  static_assert(kBLoadsPerStep == 4, "the wait count below is the number of weight loads per step");
+  asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
@@ -407,6 +416,8 @@ struct BRaw {
   uint32_t scale[2];
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 template <int DT, bool GATHER>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -417,8 +428,11 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
                       int top_k, int E, int tiles_m) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
-  __shared__ __attribute__((aligned(16))) uint8_t sa[kAStages * kAStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kAStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[kAStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa2[kAStageBytes];
   __shared__ int out_rows[BM];
+  uint8_t* const stage[3] = {sa0, sa1, sa2};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -470,28 +484,28 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(wc_e, (uint64_t)N * (K / 2));
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws_e, (uint64_t)N * (K / 16));
 
-  // A: chunk j of this thread is tile row (tid >> 3) + 32 j, k-chunk tid & 7,
-  // stored at LDS slot (tid & 7) ^ swz(row) of that row, swz(r) = (r & 7) ^
-  // ((r >> 3) & 1): any 8 consecutive rows, and each parity class of any 16
-  // consecutive rows, put a given k-chunk in distinct 16-byte slots, so the
-  // fragment reads (16 rows, one chunk per lane half) and the stores (8 rows
-  // x 8 chunks) are free of bank conflicts whether a bank row spans one
-  // 128-byte tile row or two.  swz does not depend on j: chunk j lands 4096
-  // bytes after chunk 0.
+  // A stage layout: tile row r at byte 128 r, its 16-byte k-chunk c in slot
+  // c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows,
+  // and each parity class of any 16 consecutive rows, put a given k-chunk in
+  // distinct slots, so the fragment reads (16 rows, one chunk per lane half)
+  // are free of bank conflicts whether a bank row spans one 128-byte tile row
+  // or two.  Wave w fills rows 64 w .. 64 w + 63 with 8 loads of 1 KB: load j,
+  // lane l writes slot l % 8 of row 64 w + 8 j + l / 8, i.e. fetches k-chunk
+  // (l % 8) ^ swz(row) of that row.
+  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
   uint32_t a_off[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int r = (tid >> 3) + 32 * j;
+    const int r = 64 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
     const int rr = (bm + r < row_count) ? r : 0;  // rows past the count re-read row 0
     int64_t arow;
     if constexpr (GATHER)
       arow = perm[row_lo + bm + rr] / top_k;
     else
       arow = bm + rr;
-    a_off[j] = (uint32_t)((arow * K + (tid & 7) * 8) * (int64_t)sizeof(T));
+    a_off[j] = (uint32_t)((arow * K + c * 8) * (int64_t)sizeof(T));
   }
-  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
-  const int a_dst = (tid >> 3) * 128 + (((tid & 7) ^ swz(tid >> 3)) << 4);
   const int fr = lane & 31;  // MFMA row of A / column of B inside a 32-wide tile
   const int fh = lane >> 5;  // lane half: k 8 fh .. 8 fh + 7 of each 16-k sub-step
   // fragment of row tile mt, sub-step u: tile row 32 mt + fr, k-chunk 4 fh + u
@@ -507,17 +521,13 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
   }
 
-  u32x4 astage[8];
-  auto load_a = [&](int kt) {
+  // this wave's quarter of A(kt) into stage si, straight from global memory
+  auto load_a = [&](int kt, int si) {
     const int so = kt * BK * (int)sizeof(T);
+    uint8_t* dst = stage[si] + wave * 8192;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      astage[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_a, a_off[j], so, 0));
-  };
-  auto store_a = [&](int stage_off) {
-    uint8_t* base = sa + stage_off + a_dst;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(base + j * 4096) = astage[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(dst + j * 1024), 16, a_off[j], so, 0, 0);
   };
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
@@ -555,21 +565,24 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       for (int v = 0; v < 16; ++v) acc[t][i][v] = 0.f;
 
   const int KT = K / BK;
-  u32x4 b0[2][4], b1[2][4];  // decoded weight fragments [column tile][sub-step] of even / odd k-steps
-  BRaw raw0, raw1;           // raw weights of even / odd k-steps
-  V8 ar[4];                  // A fragment ring: fragment q of a step in ar[q % 4]
-  int st_cur = 0, st_nxt = kAStageBytes, st_new = 2 * kAStageBytes;  // stages of A(i), A(i+1), A(i+2)
+  u32x4 bf[2][2][4];  // decoded weight fragments [k-step parity][column tile][sub-step]
+  BRaw raw[2];        // raw weights of even / odd k-steps
+  V8 ar[4];           // A fragment ring: fragment q of a step in ar[q % 4]
 
-  // Step kt: MFMAs on A(kt) and the fragments bc; loads the raw weights of
-  // kt + 2 into rfill (which held those of kt) and decodes rnext (kt + 1)
-  // into bn_; in its middle, after the barrier, writes A(kt + 2) to LDS and
-  // loads A(kt + 3).  The body is straight-line: past the end of k the loads
-  // re-read the last k-step and the extra work is discarded, so every wait
-  // the compiler places counts exactly the loads that are in flight.
-  auto step = [&](int kt, BRaw& rfill, const BRaw& rnext, const u32x4 (&bc)[2][4], u32x4 (&bn_)[2][4]) {
-    load_b(min(kt + 2, KT - 1), rfill);
-    const uint8_t* la = sa + st_cur;
-    const uint8_t* ln = sa + st_nxt;
+  // Step kt, at position P of the six-step cycle (kt = P mod 6): MFMAs on
+  // A(kt) (stage P % 3) and the fragments bf[P % 2]; loads the raw weights of
+  // kt + 2 into raw[P % 2] (which held those of kt) and decodes raw[1 - P % 2]
+  // (kt + 1) into bf[1 - P % 2]; in its middle, after the barrier, loads
+  // A(kt + 2) into stage (P + 2) % 3.  The body is straight-line: past the end
+  // of k the loads re-read the last k-step and the extra work is discarded, so
+  // every wait the compiler places counts exactly the loads that are in flight.
+  auto step = [&](auto pos, int kt) {
+    constexpr int P = decltype(pos)::value;
+    constexpr int cur = P % 3, nxt = (P + 1) % 3, nw = (P + 2) % 3, rs = P % 2;
+    load_b(min(kt + 2, KT - 1), raw[rs]);
+    const uint8_t* la = stage[cur];
+    const uint8_t* ln = stage[nxt];
+    const BRaw& rnext = raw[1 - rs];
     float se = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
@@ -584,52 +597,43 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       }
       // decode: column tile dt = q / 16, sub-step du = (q / 4) % 4, dword q % 4
       const int dt = q >> 4, du = (q >> 2) & 3, dp = q & 3;
-      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bc[0][u]), a, acc[0][i]);
+      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][0][u]), a, acc[0][i]);
       __builtin_amdgcn_sched_barrier(0);
       if ((q & 7) == 0) se = scale_of(rnext, dt, du >> 1);
       const uint32_t part = decode_part(rnext, dt, du, dp, se);
       __builtin_amdgcn_sched_barrier(0);
-      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bc[1][u]), a, acc[1][i]);
+      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][1][u]), a, acc[1][i]);
       __builtin_amdgcn_sched_barrier(0);
-      bn_[dt][du][dp] = part;
+      bf[1 - rs][dt][du][dp] = part;
       if (q == 15) {
-        lds_barrier_lag4();
-        store_a(st_new);
-        load_a(min(kt + 3, KT - 1));
+        a_stage_barrier();
+        load_a(min(kt + 2, KT - 1), nw);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    const int t0 = st_cur;
-    st_cur = st_nxt;
-    st_nxt = st_new;
-    st_new = t0;
   };
 
   // ---------------------------------------------------------------- prologue
-  // A(0), A(1) into stages 0 and 1, A(2) in registers, raw weights of steps
-  // 0 and 1, step 0's fragments decoded, the first three A fragments read.
-  load_a(0);
-  store_a(0);
-  load_a(min(1, KT - 1));
-  store_a(kAStageBytes);
-  load_a(min(2, KT - 1));
-  load_b(0, raw0);
-  load_b(min(1, KT - 1), raw1);
+  // A(0), A(1) into stages 0 and 1, raw weights of steps 0 and 1, step 0's
+  // fragments decoded, the first three A fragments read.
+  load_a(0, 0);
+  load_a(min(1, KT - 1), 1);
+  load_b(0, raw[0]);
+  load_b(min(1, KT - 1), raw[1]);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float se = scale_of(raw0, t, u >> 1);
+      const float se = scale_of(raw[0], t, u >> 1);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) b0[t][u][p] = decode_part(raw0, t, u, p, se);
+      for (int p = 0; p < 4; ++p) bf[0][t][u][p] = decode_part(raw[0], t, u, p, se);
     }
+  // every load of the prologue (and every scalar load) has landed, then meet
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   lds_barrier();
-  // no scalar (kernel argument) load may still be outstanding when the loop
-  // starts, or the first fragment wait of every trip becomes a full drain
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa + a_rd[0] + q * 4096);
+  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa0 + a_rd[0] + q * 4096);
 
   // ---------------------------------------------------------------- main loop
   // the zeroed accumulators are materialised in AGPRs before the fence
@@ -638,14 +642,26 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(acc[t][i]));
   mfma32_fence();
-  // two steps per trip so that the raw and decoded weight sets swap roles
-  // statically
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using P4 = std::integral_constant<int, 4>;
+  using P5 = std::integral_constant<int, 5>;
   int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(kt, raw0, raw1, b0, b1);
-    step(kt + 1, raw1, raw0, b1, b0);
+  for (; kt + 6 <= KT; kt += 6) {
+    step(P0{}, kt);
+    step(P1{}, kt + 1);
+    step(P2{}, kt + 2);
+    step(P3{}, kt + 3);
+    step(P4{}, kt + 4);
+    step(P5{}, kt + 5);
   }
-  if (kt < KT) step(kt, raw0, raw1, b0, b1);
+  if (kt < KT) step(P0{}, kt);
+  if (kt + 1 < KT) step(P1{}, kt + 1);
+  if (kt + 2 < KT) step(P2{}, kt + 2);
+  if (kt + 3 < KT) step(P3{}, kt + 3);
+  if (kt + 4 < KT) step(P4{}, kt + 4);
   mfma32_fence();
 
   // ---------------------------------------------------------------- epilogue

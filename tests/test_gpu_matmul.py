@@ -146,6 +146,41 @@ def test_qqmm_sweep(m, n, k):
     assert fro <= MFMA_FRO_GUARD
 
 
+# The matrix-core path walks k in 64-wide steps, six per trip of its main loop,
+# with every trip position unrolled: these k cover a lone remainder step, each
+# remainder length, whole trips, and trips followed by a remainder.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("ksteps", [1, 2, 3, 5, 6, 7, 11, 12, 13])
+def test_qqmm_every_k_step_count(dtype, ksteps):
+    m, n, k = 130, 260, 64 * ksteps
+    say(f"qqmm k-steps {dtype} {m}x{n}x{k}")
+    od = oracle_dtype(dtype)
+    x, w = W.qqmm_inputs(seed=70 + ksteps, m=m, n=n, k=k, dtype=od)
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    y = nv.nvfp4_qqmm(x.cuda(), dev(oc), dev(os_), scalar(gxh), scalar(gwh))
+    torch.cuda.synchronize()
+    fro, _ = assert_close(host(y), O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od), what="qqmm k-steps")
+    assert fro <= MFMA_FRO_GUARD
+
+
+@pytest.mark.parametrize("ksteps", [3, 5, 7])
+def test_gather_qmm_k_step_counts(ksteps):
+    E, T, N, K, top_k = 3, 200, 260, 64 * ksteps, 2
+    say(f"gather_qmm k-steps {T}x{top_k} E={E} N={N} K={K}")
+    x = W.normal((T, K), 1.0, 80 + ksteps, "bf16")
+    w = W.normal((E, N, K), 0.02, 90 + ksteps, "bf16")
+    idx = W.expert_indices(T, E, top_k, seed=100 + ksteps)
+    gs = np.array([O.tensor_amax(host(w[e])) for e in range(E)], np.float32)
+    codes = np.stack([O.quantize(host(w[e]), float(gs[e]))[0] for e in range(E)])
+    scales = np.stack([O.quantize(host(w[e]), float(gs[e]))[1] for e in range(E)])
+    y = nv.nvfp4_gather_qmm(x.cuda(), dev(codes), dev(scales), idx.cuda(), dev(gs))
+    torch.cuda.synchronize()
+    ref = O.gather_qmm(host(x), codes, scales, idx.numpy(), gs, dtype="bf16")
+    fro, _ = assert_close(host(y), ref, what="gather k-steps")
+    assert fro <= MFMA_FRO_GUARD
+
+
 @pytest.mark.parametrize("dtype", [torch.float16, torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("m,n,k", [(2, 17, 16), (300, 300, 80), (257, 1, 1040), (64, 513, 128)])
 def test_qqmm_ragged(dtype, m, n, k):
