@@ -666,32 +666,53 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 
   // ---------------------------------------------------------------- epilogue
   // acc[t][i][v]: tile row 32 i + fr, tile column 64 w + 32 t + 8 (v / 4) +
-  // 4 fh + v % 4
+  // 4 fh + v % 4.  Each lane holds 4 consecutive columns of 16 rows, so the
+  // block goes through LDS (the A stages are free now) to leave as whole
+  // rows: per half of the tile's rows, wave w writes its 128 x 64 block
+  // (16 KB, 16-byte chunk c of row r in slot c ^ (r & 7)) and reads it back
+  // with lane l on row 8 j + l / 8, chunk l % 8, so that one store
+  // instruction writes 8 full 128-byte row segments.
+  // this wave's discarded last stage load has landed and every wave is done
+  // with the stages
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  lds_barrier();
   T* O = reinterpret_cast<T*>(out);
+  uint8_t* const eb = ((wave >> 1) ? sa1 : sa0) + (wave & 1) * 16384;
+  const int col0 = bn + wave * 64;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int orow = out_rows[i * 32 + fr];
-    if (orow < 0) continue;
-    T* op = O + (int64_t)orow * N;
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = bn + wave * 64 + t * 32 + 8 * g + 4 * fh;
-        if (c + 3 < N) {
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r = 32 * i + fr, c = 4 * t + g;
           typedef T T4 __attribute__((ext_vector_type(4)));
           T4 v;
-          v[0] = from_f32<DT>(acc[t][i][4 * g + 0]);
-          v[1] = from_f32<DT>(acc[t][i][4 * g + 1]);
-          v[2] = from_f32<DT>(acc[t][i][4 * g + 2]);
-          v[3] = from_f32<DT>(acc[t][i][4 * g + 3]);
-          *reinterpret_cast<T4*>(op + c) = v;
-        } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (c + v < N) op[c + v] = from_f32<DT>(acc[t][i][4 * g + v]);
+          for (int e = 0; e < 4; ++e) v[e] = from_f32<DT>(acc[t][4 * h + i][4 * g + e]);
+          *reinterpret_cast<T4*>(eb + r * 128 + ((c ^ (r & 7)) << 4) + 8 * fh) = v;
+        }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * j + (lane >> 3), c = lane & 7;
+      const u32x4 d = *reinterpret_cast<const u32x4*>(eb + r * 128 + ((c ^ (r & 7)) << 4));
+      const int orow = out_rows[128 * h + r];
+      const int col = col0 + 8 * c;
+      if (orow >= 0) {
+        T* op = O + (int64_t)orow * N + col;
+        if (col + 8 <= N) {
+          *reinterpret_cast<u32x4*>(op) = d;
+        } else {
+          typedef T T8 __attribute__((ext_vector_type(8)));
+          const T8 e8 = __builtin_bit_cast(T8, d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < N) op[e] = e8[e];
         }
       }
+    }
   }
 }
 
