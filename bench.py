@@ -3,13 +3,15 @@
 
 Headline workload (one "step"): qqmm prefill, x bf16 [2048, 4096] Normal(0, 1)
 against w NVFP4 [14336, 4096] (quantized once, untimed, from bf16 Normal(0,
-0.02) with g_w = amax(w)).  A step is the whole path for one batch: the
-activation amax g_x (tensor_amax), then nvfp4_qqmm (the x round trip into
-bf16 x_hat, then the MFMA contraction with w decoded in the kernel).
+0.02) with g_w = amax(w), then packed once into the matrix-core order,
+untimed, nvfp4_mfma_pack).  A step is the whole path for one batch: the
+activation amax g_x (tensor_amax), then nvfp4_qqmm_packed (the x round trip
+into bf16 x_hat, then the MFMA contraction with w decoded in the kernel).
 `value` is the step's algorithmic TFLOP/s, 2*M*N*K / step time.
 
 Beside it, on the same run:
-  roofline    the contraction kernel alone (nvfp4_qmm on x_hat), per-launch
+  row_major_weight_step  the same step on the row-major weight (nvfp4_qqmm);
+  roofline    the contraction kernel alone (nvfp4_qmm_packed on x_hat), per-launch
               time from HIP events on the launch stream, vs 2.5 PFLOP/s bf16;
   qmv         decode x bf16 [1, 4096] @ the same w: algorithmic bytes per
               launch / kernel time, vs 8 TB/s, with the weight rotated over
@@ -123,8 +125,15 @@ def bench_qqmm(args, nv, torch, W):
     out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
     gx = torch.empty(1, dtype=torch.float32, device="cuda")
     wsp, nbytes = nv.qqmm_workspace(M, N, K, torch.bfloat16, "cuda")
+    # the weight's packed copy for the matrix-core kernel, made once (untimed,
+    # like the quantization itself)
+    wp = nv.nvfp4_mfma_pack(wc, ws)
 
     def step():
+        nv.nvfp4_tensor_amax(x, out=gx)
+        nv.nvfp4_qqmm_packed(x, wp, gx, gw, out=out, workspace=wsp)
+
+    def step_row_major():
         nv.nvfp4_tensor_amax(x, out=gx)
         nv.nvfp4_qqmm(x, wc, ws, gx, gw, out=out, workspace=wsp)
 
@@ -136,15 +145,18 @@ def bench_qqmm(args, nv, torch, W):
     ms_step = timed(step, args.steps, 0)
     wall = time.perf_counter() - t0
     flop = 2.0 * M * N * K
+    # the same step on the row-major weight
+    ms_step_rm = timed(step_row_major, args.steps, 2)
     # the contraction kernel alone, on x_hat
     xhat = nv.nvfp4_quant_dequant(x, gx)
-    settle(lambda: nv.nvfp4_qmm(xhat, wc, ws, gw, out=out), 0.05)
-    ms_gemm = timed(lambda: nv.nvfp4_qmm(xhat, wc, ws, gw, out=out), args.steps, 2)
+    gemm = lambda: nv.nvfp4_qmm_packed(xhat, wp, gw, out=out)
+    settle(gemm, 0.05)
+    ms_gemm = timed(gemm, args.steps, 2)
     ms_prepass = timed(lambda: nv.nvfp4_quant_dequant(x, gx, out=xhat), args.steps, 2, graph=True)
     torch.cuda.synchronize()
     return dict(ms_step=ms_step, wall=wall, tflops=flop / ms_step / 1e9, ms_gemm=ms_gemm,
                 gemm_tflops=flop / ms_gemm / 1e9, ms_prepass=ms_prepass, flop=flop,
-                data=(x, w_host))
+                ms_step_rm=ms_step_rm, data=(x, w_host))
 
 
 def bench_qmv(args, nv, torch, W):
@@ -310,7 +322,8 @@ def main():
     if args.only in ("all", "qqmm"):
         log("qqmm prefill ...")
         res["qqmm"] = bench_qqmm(args, nv, torch, W)
-        log(f"  step {res['qqmm']['ms_step']:.3f} ms ({res['qqmm']['tflops']:.1f} TFLOP/s); "
+        log(f"  step {res['qqmm']['ms_step']:.3f} ms ({res['qqmm']['tflops']:.1f} TFLOP/s; row-major weight "
+            f"{res['qqmm']['flop'] / res['qqmm']['ms_step_rm'] / 1e9:.1f}); "
             f"gemm {res['qqmm']['ms_gemm']:.3f} ms ({res['qqmm']['gemm_tflops']:.1f} TFLOP/s); "
             f"x pre-pass {res['qqmm']['ms_prepass'] * 1e3:.1f} us")
     if args.only in ("all", "qmv"):
@@ -341,15 +354,18 @@ def main():
         q = res["qqmm"]
         line.update(value=round(q["tflops"], 2), unit="TFLOP/s", ms_per_step=round(q["ms_step"], 4))
         line["config"] = {"workload": "qqmm prefill: x bf16 [2048,4096] (amax + NVFP4 round trip) "
-                                      "@ NVFP4 w [14336,4096]^T, bf16 out",
+                                      "@ NVFP4 w [14336,4096]^T (packed once for the matrix cores), bf16 out",
                           "m": M, "n": N, "k": K, "group_size": 16}
-        line["roofline"] = {"bound": "mfma", "kernel": "mfma_gemm_fast_kernel<bf16> (nvfp4_qmm on x_hat)",
+        line["roofline"] = {"bound": "mfma",
+                            "kernel": "mfma_gemm_fast_kernel<bf16, packed> (nvfp4_qmm_packed on x_hat)",
                             "achieved": round(q["gemm_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(q["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
                             "traffic": measured_traffic("gemm"), "ms_per_launch": round(q["ms_gemm"], 4),
                             "algorithmic_flop_per_launch": q["flop"],
                             "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2}
         line["x_prepass_us"] = round(q["ms_prepass"] * 1e3, 2)
+        line["row_major_weight_step"] = {"value": round(q["flop"] / q["ms_step_rm"] / 1e9, 2),
+                                         "unit": "TFLOP/s", "ms_per_step": round(q["ms_step_rm"], 4)}
     if "qmv" in res:
         v = res["qmv"]
         line["qmv"] = {"value": round(v["gbs"], 1), "unit": "GB/s", "peak": PEAK_HBM_GBS,

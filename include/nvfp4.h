@@ -223,6 +223,67 @@ nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k
                              int32_t* offsets, int32_t* perm, hipStream_t stream);
 
 /*
+ * Packed weights for the matrix-core contractions.
+ *
+ * The row-major layout above is the exchange format (quantize, dequantize,
+ * qmv and the contractions all accept it).  A weight that will be multiplied
+ * many times can also be repacked once into the order the gfx950 matrix-core
+ * kernel reads it in, the analogue of the pages' one-time scale swizzle into
+ * the block-scaled GEMM's tile layout ("mlx 0.30.7.2 -> 0.30.7.6" diff page
+ * 7, qqmm_utils / QQMatmul::eval_gpu).  The values are the same bytes; only
+ * their order changes.  For 32-row tile T and 64-wide k-step s:
+ *   packed codes   1 KB block (T, s); bytes 16 l .. 16 l + 15 are row-major
+ *                  code bytes 32 s + 16 (l / 32) .. + 15 of row 32 T + l % 32
+ *   packed scales  128-byte block (T, s); bytes 4 c .. 4 c + 3 are row-major
+ *                  scale bytes 4 s .. 4 s + 3 of row 32 T + c
+ * blocks in (T, s) order, rows past `rows` zero.  k must be a multiple of 64.
+ * Experts stack as consecutive row ranges, so a stacked [e, n, k] weight is
+ * packed as rows = e * n (n a multiple of 32 for gather_qmm_packed).
+ */
+
+/*
+ * nvfp4_mfma_pack_size -- bytes of the packed codes and scales of a
+ * [rows, k] NVFP4 weight.
+ * Errors: NULL pointer, rows <= 0, k not a positive multiple of 64 (the
+ * outputs are then 0).
+ */
+nvfp4_status nvfp4_mfma_pack_size(int64_t rows, int64_t k, size_t* codes_bytes,
+                                  size_t* scales_bytes);
+
+/*
+ * nvfp4_mfma_pack -- write the packed copy of a row-major NVFP4 weight.
+ *   codes, scales                device [rows, k/2] / [rows, k/16], row-major
+ *   packed_codes, packed_scales  device, sizes from nvfp4_mfma_pack_size,
+ *                                written
+ * Errors: as nvfp4_mfma_pack_size; NULL pointer; codes / packed_codes not
+ * 16-byte or scales / packed_scales not 4-byte aligned.
+ */
+nvfp4_status nvfp4_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                             uint8_t* packed_codes, uint8_t* packed_scales, hipStream_t stream);
+
+/*
+ * nvfp4_qqmm_packed, nvfp4_qmm_packed, nvfp4_gather_qmm_packed -- nvfp4_qqmm,
+ * nvfp4_qmm and nvfp4_gather_qmm with the weight given as its packed copy
+ * (same results).  They run the matrix-core path only: x float16 or
+ * bfloat16, k a multiple of 64, n a multiple of 4 (gather: of 32).  The
+ * remaining arguments, workspaces and errors are those of the row-major
+ * calls; any m >= 1 runs the matrix-core kernel.
+ */
+nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                               const uint8_t* packed_codes, const uint8_t* packed_scales,
+                               const float* global_scale_w, int64_t m, int64_t n, int64_t k,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+nvfp4_status nvfp4_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* packed_codes,
+                              const uint8_t* packed_scales, const float* global_scale_w, int64_t m,
+                              int64_t n, int64_t k, void* out, hipStream_t stream);
+nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* packed_codes,
+                                     const uint8_t* packed_scales, const float* global_scale_w,
+                                     const int32_t* expert_idx, int64_t t, int64_t top_k,
+                                     int64_t e, int64_t n, int64_t k, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Test hook: treat every device as having this gcnArchName (NULL restores the
  * real query).  Lets host-only tests reach the unsupported-device error.
  */

@@ -16,6 +16,9 @@ The functions carry the C entry points' names (see include/nvfp4.h):
     nvfp4_qmm(x, w_codes, w_scales, global_scale_w=None)   (x not quantized)
     nvfp4_gather_qmm(x, w_codes, w_scales, expert_idx, global_scale_w=None)
     nvfp4_moe_route(expert_idx, num_experts)          -> (offsets, perm)
+    nvfp4_mfma_pack(w_codes, w_scales)                -> MfmaPacked (packed copy)
+    nvfp4_qqmm_packed / nvfp4_qmm_packed / nvfp4_gather_qmm_packed
+                                                      (same, on the packed copy)
 Global scales are float32 device tensors with one element (per expert: e
 elements, any shape such as [e, 1, 1]), as the pages' validate_global_scale
 requires ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8).
@@ -64,6 +67,11 @@ def load_library():
         "nvfp4_gather_qmm_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "nvfp4_gather_qmm": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_moe_route": (I, [P, I64, I64, I64, P, P, P]),
+        "nvfp4_mfma_pack_size": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "nvfp4_mfma_pack": (I, [P, P, I64, I64, P, P, P]),
+        "nvfp4_qqmm_packed": (I, [P, I, P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_qmm_packed": (I, [P, I, P, P, P, I64, I64, I64, P, P]),
+        "nvfp4_gather_qmm_packed": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -291,6 +299,102 @@ def nvfp4_moe_route(expert_idx, num_experts):
     _check(L.nvfp4_moe_route(_ptr(expert_idx), t, top_k, num_experts, _ptr(offsets), _ptr(perm),
                              _stream()))
     return offsets, perm
+
+
+# ------------------------------------------------------------------ packed weights
+
+class MfmaPacked:
+    """The packed copy of an NVFP4 weight ([rows, k] or stacked experts
+    [e, n, k]) for the matrix-core contractions: codes and scales as flat uint8
+    device tensors in the order include/nvfp4.h describes."""
+
+    def __init__(self, codes, scales, shape):
+        self.codes, self.scales, self.shape = codes, scales, tuple(shape)
+
+    @property
+    def k(self):
+        return self.shape[-1]
+
+
+def nvfp4_mfma_pack(w_codes, w_scales):
+    L = load_library()
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    k = w_codes.shape[-1] * 2
+    if w_scales.shape[-1] * 16 != k or w_codes.shape[:-1] != w_scales.shape[:-1]:
+        raise ValueError("w_codes and w_scales describe different shapes")
+    rows = w_codes.numel() // w_codes.shape[-1]
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(L.nvfp4_mfma_pack_size(rows, k, ctypes.byref(cb), ctypes.byref(sb)))
+    pc = torch.empty(cb.value, dtype=torch.uint8, device=w_codes.device)
+    ps = torch.empty(sb.value, dtype=torch.uint8, device=w_codes.device)
+    _check(L.nvfp4_mfma_pack(_ptr(w_codes), _ptr(w_scales), rows, k, _ptr(pc), _ptr(ps), _stream()))
+    return MfmaPacked(pc, ps, tuple(w_codes.shape[:-1]) + (k,))
+
+
+def nvfp4_qqmm_packed(x, w, global_scale_x=None, global_scale_w=None, out=None, workspace=None):
+    """nvfp4_qqmm with w an MfmaPacked [n, k]."""
+    L = load_library()
+    _dev(x, "x")
+    if x.dim() > 2 or len(w.shape) != 2:
+        raise ValueError("[qqmm] Only 2D inputs are supported.")
+    x2 = x.reshape(-1, x.shape[-1])
+    m, k = x2.shape
+    n = w.shape[0]
+    if w.k != k:
+        raise ValueError(f"weights of inner size {w.k} do not match x's {k}")
+    gx, gw = _gscale(global_scale_x, "global_scale_x"), _gscale(global_scale_w, "global_scale_w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = qqmm_workspace(max(m, 2), n, k, x.dtype, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_qqmm_packed(_ptr(x2), _dtype_code(x, "x"), _ptr(gx), _ptr(w.codes), _ptr(w.scales),
+                               _ptr(gw), m, n, k, _ptr(out), _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def nvfp4_qmm_packed(x, w, global_scale_w=None, out=None):
+    """nvfp4_qmm with w an MfmaPacked [n, k]."""
+    L = load_library()
+    _dev(x, "x")
+    x2 = x.reshape(-1, x.shape[-1])
+    m, k = x2.shape
+    n = w.shape[0]
+    if len(w.shape) != 2 or w.k != k:
+        raise ValueError("weights must be a packed [n, k] with x's k")
+    gw = _gscale(global_scale_w, "global_scale_w")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    _check(L.nvfp4_qmm_packed(_ptr(x2), _dtype_code(x, "x"), _ptr(w.codes), _ptr(w.scales), _ptr(gw),
+                              m, n, k, _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_gather_qmm_packed(x, w, expert_idx, global_scale_w=None, out=None, workspace=None):
+    """nvfp4_gather_qmm with w an MfmaPacked of stacked experts [e, n, k]."""
+    L = load_library()
+    _dev(x, "x")
+    _dev(expert_idx, "expert_idx")
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2:
+        raise ValueError("expert_idx must be int32 [t, top_k]")
+    t, k = x.shape
+    top_k = expert_idx.shape[1]
+    if len(w.shape) != 3 or w.k != k:
+        raise ValueError("weights must be a packed [e, n, k] with x's k")
+    e, n = w.shape[0], w.shape[1]
+    g = _gscale(global_scale_w, "global_scale_w", numel=e)
+    if out is None:
+        out = torch.empty((t, top_k, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = gather_workspace(t, top_k, e, n, k, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_gather_qmm_packed(_ptr(x), _dtype_code(x, "x"), _ptr(w.codes), _ptr(w.scales), _ptr(g),
+                                     _ptr(expert_idx), t, top_k, e, n, k, _ptr(out), _ptr(workspace),
+                                     nbytes, _stream()))
+    return out
 
 
 # ------------------------------------------------------------------ MLX-style names

@@ -346,4 +346,138 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
                                                 perm, t, top_k, e, n, k, out, stream));
 }
 
+// ------------------------------------------------------------------ packed weights
+
+nvfp4_status nvfp4_mfma_pack_size(int64_t rows, int64_t k, size_t* codes_bytes,
+                                  size_t* scales_bytes) {
+  CHECK_PTR("mfma_pack_size", codes_bytes);
+  CHECK_PTR("mfma_pack_size", scales_bytes);
+  *codes_bytes = 0;
+  *scales_bytes = 0;
+  if (rows <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mfma_pack_size] rows (%lld) must be positive.",
+                (long long)rows);
+  if (k <= 0 || k % nvfp4::kPackK != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mfma_pack_size] k (%lld) must be a positive multiple of 64.", (long long)k);
+  const size_t blocks = (size_t)((rows + 31) / 32) * (size_t)(k / nvfp4::kPackK);
+  *codes_bytes = blocks * (size_t)nvfp4::kPackCodeBytes;
+  *scales_bytes = blocks * (size_t)nvfp4::kPackScaleBytes;
+  return ok();
+}
+
+nvfp4_status nvfp4_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                             uint8_t* packed_codes, uint8_t* packed_scales, hipStream_t stream) {
+  const char* op = "mfma_pack";
+  size_t cb = 0, sb = 0;
+  if (nvfp4_status st = nvfp4_mfma_pack_size(rows, k, &cb, &sb)) {
+    g_last_error.replace(0, std::strlen("[mfma_pack_size]"), "[mfma_pack]");
+    return st;
+  }
+  CHECK_PTR("mfma_pack", codes);
+  CHECK_PTR("mfma_pack", scales);
+  CHECK_PTR("mfma_pack", packed_codes);
+  CHECK_PTR("mfma_pack", packed_scales);
+  if (!aligned(codes, 16) || !aligned(packed_codes, 16) || !aligned(scales, 4) ||
+      !aligned(packed_scales, 4))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mfma_pack] codes must be 16-byte and scales 4-byte aligned.");
+  if (rows > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mfma_pack] Sizes too large.");
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_mfma_pack(codes, scales, rows, k, packed_codes, packed_scales,
+                                              stream));
+}
+
+// the packed contractions run only the matrix-core path
+static nvfp4_status check_packed(const char* op, nvfp4_dtype dt, int64_t n, int64_t k) {
+  if (dt != NVFP4_F16 && dt != NVFP4_BF16)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] packed weights need float16 or bfloat16 activations (dtype code %d).", op,
+                (int)dt);
+  if (k % nvfp4::kPackK != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] packed weights need k (%lld) a multiple of 64.",
+                op, (long long)k);
+  if (n % 4 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] packed weights need n (%lld) a multiple of 4.",
+                op, (long long)n);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* global_scale_x,
+                               const uint8_t* packed_codes, const uint8_t* packed_scales,
+                               const float* global_scale_w, int64_t m, int64_t n, int64_t k,
+                               void* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const char* op = "qqmm_packed";
+  if (nvfp4_status st = check_matmul(op, x, dt, global_scale_x, packed_codes, packed_scales,
+                                     global_scale_w, m, n, k, out))
+    return st;
+  if (nvfp4_status st = check_packed(op, dt, n, k)) return st;
+  size_t need = (size_t)m * (size_t)k * dtype_size(dt);
+  if (workspace_bytes < need || workspace == nullptr)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_packed] workspace of %zu bytes is smaller than %zu.",
+                workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_packed] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  hipError_t e = nvfp4::launch_quant_dequant(x, dt, m, k, global_scale_x, workspace, stream);
+  if (e != hipSuccess) return launched(op, e);
+  return launched(op, nvfp4::launch_qqmm_gemm_packed(workspace, dt, packed_codes, packed_scales,
+                                                      global_scale_w, m, n, k, out, stream));
+}
+
+nvfp4_status nvfp4_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* packed_codes,
+                              const uint8_t* packed_scales, const float* global_scale_w, int64_t m,
+                              int64_t n, int64_t k, void* out, hipStream_t stream) {
+  const char* op = "qmm_packed";
+  if (nvfp4_status st = check_matmul(op, x, dt, global_scale_w, packed_codes, packed_scales,
+                                     global_scale_w, m, n, k, out))
+    return st;
+  if (nvfp4_status st = check_packed(op, dt, n, k)) return st;
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_qqmm_gemm_packed(x, dt, packed_codes, packed_scales,
+                                                      global_scale_w, m, n, k, out, stream));
+}
+
+nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* packed_codes,
+                                     const uint8_t* packed_scales, const float* global_scale_w,
+                                     const int32_t* expert_idx, int64_t t, int64_t top_k,
+                                     int64_t e, int64_t n, int64_t k, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "gather_qmm_packed";
+  if (t <= 0 || top_k <= 0 || e <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_packed] t, top_k, e and n must be positive.");
+  if (nvfp4_status st = check_k(op, k)) return st;
+  if (nvfp4_status st = check_packed(op, dt, n, k)) return st;
+  if (n % 32 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_packed] packed experts need n (%lld) a multiple of 32.", (long long)n);
+  if (!x || !packed_codes || !packed_scales || !expert_idx || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_packed] x, packed_codes, packed_scales, expert_idx and out must not be NULL.");
+  if (!aligned(x, 16) || !aligned(packed_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_packed] x and packed_codes must be 16-byte aligned.");
+  if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_packed] Sizes too large.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_packed] at most 1024 experts are supported.");
+  size_t need = nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_packed] workspace of %zu bytes is smaller than %zu.", workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_packed] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
+  size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream);
+  if (he != hipSuccess) return launched(op, he);
+  return launched(op, nvfp4::launch_gather_gemm_packed(x, dt, packed_codes, packed_scales,
+                                                       global_scale_w, offsets, perm, t, top_k, e,
+                                                       n, k, out, stream));
+}
+
 }  // extern "C"

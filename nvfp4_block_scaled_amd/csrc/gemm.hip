@@ -343,6 +343,8 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 constexpr int kBLoadsPerStep = 4;          // weight loads issued per k-step and wave
+constexpr int kPackCodeBlock = 1024;       // packed codes per 32-column tile and k-step
+constexpr int kPackScaleBlock = 128;       // packed scales per 32-column tile and k-step
 
 template <int DT> struct Mfma32;
 template <> struct Mfma32<kBF16> {
@@ -418,7 +420,7 @@ struct BRaw {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int DT, bool GATHER>
+template <int DT, bool GATHER, bool PACKED>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
@@ -479,10 +481,15 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 
   // ---------------------------------------------------------------- buffer resources / offsets
   const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a_base, (uint64_t)a_rows * K * sizeof(T));
-  const uint8_t* wc_e = wc + (int64_t)expert * N * (K / 2);
-  const uint8_t* ws_e = ws + (int64_t)expert * N * (K / 16);
-  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(wc_e, (uint64_t)N * (K / 2));
-  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws_e, (uint64_t)N * (K / 16));
+  // weights of this expert: row-major codes / scales, or the packed layout
+  // (blocks of 1 KB of codes and 128 bytes of scales per 32-column tile and
+  // k-step, see mfma_pack_kernel)
+  const int KT = K / BK;
+  const int64_t col_tiles = (N + 31) / 32;
+  const uint64_t wc_bytes = PACKED ? (uint64_t)col_tiles * KT * kPackCodeBlock : (uint64_t)N * (K / 2);
+  const uint64_t ws_bytes = PACKED ? (uint64_t)col_tiles * KT * kPackScaleBlock : (uint64_t)N * (K / 16);
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(wc + (int64_t)expert * wc_bytes, wc_bytes);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws + (int64_t)expert * ws_bytes, ws_bytes);
 
   // A stage layout: tile row r at byte 128 r, its 16-byte k-chunk c in slot
   // c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1): any 8 consecutive rows,
@@ -512,14 +519,27 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   int a_rd[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) a_rd[u] = fr * 128 + (((4 * fh + u) ^ swz(fr)) << 4);
-  // weights: column tile t of this wave is column bn + 64 w + 32 t + fr
+  // weights: column tile t of this wave is column bn + 64 w + 32 t + fr.
+  // Row-major: the lane's 16 code bytes of step kt start at col * K/2 +
+  // 32 kt + 16 fh, its scale dword at col * K/16 + 4 kt (32 rows per load).
+  // Packed: the 1 KB code block of (tile, kt) holds lane l's 16 bytes at
+  // 16 l, the 128-byte scale block column c's dword at 4 c (one contiguous
+  // run per load).  Tiles past n read as zeros (buffer range checks).
   uint32_t c_off[2], s_off[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int col = min(bn + wave * 64 + t * 32 + fr, N - 1);
-    c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fh * 16;
-    s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
+    if constexpr (PACKED) {
+      const uint32_t tile = (uint32_t)((bn + wave * 64 + t * 32) / 32);
+      c_off[t] = tile * (uint32_t)KT * kPackCodeBlock + lane * 16;
+      s_off[t] = tile * (uint32_t)KT * kPackScaleBlock + fr * 4;
+    } else {
+      const int col = min(bn + wave * 64 + t * 32 + fr, N - 1);
+      c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fh * 16;
+      s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
+    }
   }
+  const int c_step = PACKED ? kPackCodeBlock : BK / 2;    // code bytes per k-step
+  const int s_step = PACKED ? kPackScaleBlock : BK / 16;  // scale bytes per k-step
 
   // this wave's quarter of A(kt) into stage si, straight from global memory
   auto load_a = [&](int kt, int si) {
@@ -532,8 +552,8 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * (BK / 2), 0));
-      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * (BK / 16), 0);
+      b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * c_step, 0));
+      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * s_step, 0);
     }
   };
   // effective scale of group 2 fh + gi (gi = 0, 1) of column tile t
@@ -564,7 +584,6 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][i][v] = 0.f;
 
-  const int KT = K / BK;
   u32x4 bf[2][2][4];  // decoded weight fragments [k-step parity][column tile][sub-step]
   BRaw raw[2];        // raw weights of even / odd k-steps
   V8 ar[4];           // A fragment ring: fragment q of a step in ar[q % 4]
@@ -714,6 +733,42 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ packed weight layout
+//
+// The fast path reads, per k-step, 16 code bytes and one scale dword for each
+// of its columns; in the row-major layout those lie in 32 different rows per
+// load instruction.  The packed layout puts them in MFMA lane order, once per
+// weight: for column tile T (columns 32 T .. 32 T + 31) and k-step s (64 k),
+//   codes  block (T, s) of 1 KB: bytes 16 l .. 16 l + 15 = the codes of
+//          column 32 T + l % 32, groups 4 s + 2 h and 4 s + 2 h + 1
+//          (h = l / 32) -- i.e. row-major bytes 32 s + 16 h .. + 15 of that row;
+//   scales block (T, s) of 128 bytes: dword c = the 4 scales of column 32 T + c
+//          for step s -- row-major bytes 4 s .. 4 s + 3 of that row;
+// blocks ordered by T, then s; columns past the row count are zero.  Several
+// experts stack as consecutive row ranges (their row count a multiple of 32).
+// One thread per 16-byte code piece; threads of lanes 0..31 also move the
+// scale dword of their column.
+__global__ void __launch_bounds__(256)
+mfma_pack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+                 int K, uint8_t* __restrict__ pc, uint8_t* __restrict__ ps, int64_t pieces) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= pieces) return;
+  const int KT = K / BK;
+  const int l = (int)(i & 63);
+  const int64_t blk = i >> 6;  // T * KT + s
+  const int64_t T = blk / KT;
+  const int st = (int)(blk - T * KT);
+  const int64_t col = 32 * T + (l & 31);
+  u32x4 c = {0u, 0u, 0u, 0u};
+  uint32_t sc = 0u;
+  if (col < rows) {
+    c = *reinterpret_cast<const u32x4*>(codes + col * (K / 2) + 32 * st + 16 * (l >> 5));
+    sc = *reinterpret_cast<const uint32_t*>(scales + col * (K / 16) + 4 * st);
+  }
+  *reinterpret_cast<u32x4*>(pc + blk * kPackCodeBlock + 16 * l) = c;
+  if (l < 32) *reinterpret_cast<uint32_t*>(ps + blk * kPackScaleBlock + 4 * l) = sc;
 }
 
 // ------------------------------------------------------------------ float32 path
@@ -923,6 +978,44 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
 
 // ------------------------------------------------------------------ launchers
 
+hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                            uint8_t* pc, uint8_t* ps, hipStream_t s) {
+  const int64_t pieces = ((rows + 31) / 32) * (k / BK) * 64;
+  if (pieces == 0) return hipSuccess;
+  mfma_pack_kernel<<<(int)((pieces + 255) / 256), 256, 0, s>>>(codes, scales, rows, (int)k, pc, ps, pieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_qqmm_gemm_packed(const void* xhat, int dt, const uint8_t* pc, const uint8_t* ps,
+                                   const float* gw, int64_t m, int64_t n, int64_t k, void* out,
+                                   hipStream_t s) {
+  const int64_t blocks = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int tiles_m = (int)((m + BM - 1) / BM);
+  if (dt == kF16)
+    mfma_gemm_fast_kernel<kF16, false, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+        xhat, m, pc, ps, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+  else
+    mfma_gemm_fast_kernel<kBF16, false, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+        xhat, m, pc, ps, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, const uint8_t* ps,
+                                     const float* gw, const int32_t* offsets, const int32_t* perm,
+                                     int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                                     void* out, hipStream_t s) {
+  const int64_t pairs = t * top_k;
+  const int64_t mt = (pairs + BM - 1) / BM + e;
+  const int64_t blocks = mt * ((n + BN - 1) / BN);
+  if (dt == kF16)
+    mfma_gemm_fast_kernel<kF16, true, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+        x, t, pc, ps, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+  else
+    mfma_gemm_fast_kernel<kBF16, true, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+        x, t, pc, ps, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
+  return hipGetLastError();
+}
+
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
                             const float* gw, int64_t m, int64_t n, int64_t k, void* out,
                             hipStream_t s) {
@@ -937,10 +1030,10 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
   if (k % BK == 0 && n % 4 == 0) {
     const int tiles_m = (int)((m + BM - 1) / BM);
     if (dt == kF16)
-      mfma_gemm_fast_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
+      mfma_gemm_fast_kernel<kF16, false, false><<<(int)blocks, kGemmThreads, 0, s>>>(
           xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
     else
-      mfma_gemm_fast_kernel<kBF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
+      mfma_gemm_fast_kernel<kBF16, false, false><<<(int)blocks, kGemmThreads, 0, s>>>(
           xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
     return hipGetLastError();
   }
@@ -976,10 +1069,10 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
   int64_t blocks = mt * ((n + BN - 1) / BN);
   if (k % BK == 0 && n % 4 == 0) {
     if (dt == kF16)
-      mfma_gemm_fast_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+      mfma_gemm_fast_kernel<kF16, true, false><<<(int)blocks, kGemmThreads, 0, s>>>(
           x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
     else
-      mfma_gemm_fast_kernel<kBF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
+      mfma_gemm_fast_kernel<kBF16, true, false><<<(int)blocks, kGemmThreads, 0, s>>>(
           x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
     return hipGetLastError();
   }

@@ -34,5 +34,18 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
                               const float* gw, const int32_t* offsets, const int32_t* perm,
                               int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
                               void* out, hipStream_t s);
+// the packed weight layout of the matrix-core path (gemm.hip, mfma_pack_kernel)
+constexpr int64_t kPackK = 64;             // k must be a multiple of this
+constexpr int64_t kPackCodeBytes = 1024;   // per 32-row tile and 64-wide k-step
+constexpr int64_t kPackScaleBytes = 128;
+hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                            uint8_t* pc, uint8_t* ps, hipStream_t s);
+hipError_t launch_qqmm_gemm_packed(const void* xhat, int dt, const uint8_t* pc, const uint8_t* ps,
+                                   const float* gw, int64_t m, int64_t n, int64_t k, void* out,
+                                   hipStream_t s);
+hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, const uint8_t* ps,
+                                     const float* gw, const int32_t* offsets, const int32_t* perm,
+                                     int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                                     void* out, hipStream_t s);
 
 }  // namespace nvfp4

@@ -147,3 +147,48 @@ def test_python_binding_rejects_host_tensors_and_bad_modes():
         nv.quantize(x, group_size=32, mode="nvfp4")
     with pytest.raises(ValueError):
         nv.quantize(x, mode="mxfp4")
+
+
+def test_mfma_pack_sizes_and_errors(L):
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    # 100 rows -> 4 tiles of 32 rows; k = 256 -> 4 k-steps of 64
+    assert L.nvfp4_mfma_pack_size(100, 256, ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 4 * 4 * 1024 and sb.value == 4 * 4 * 128
+    assert L.nvfp4_mfma_pack_size(100, 96, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert "multiple of 64" in err(L) and cb.value == 0 and sb.value == 0
+    assert L.nvfp4_mfma_pack_size(0, 64, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert L.nvfp4_mfma_pack(A, B, 100, 96, C, G, None) == INV and "[mfma_pack]" in err(L)
+    assert L.nvfp4_mfma_pack(A + 4, B, 100, 64, C, G, None) == INV and "aligned" in err(L)
+    assert L.nvfp4_mfma_pack(A, B, 100, 64, None, G, None) == INV
+    assert L.nvfp4_mfma_pack(A, B, 100, 64, C, G, None) == UNSUP
+
+
+def test_packed_matmul_errors(L):
+    ws = L.nvfp4_qqmm_workspace_size(8, 16, 64, BF16)
+    ok = (A, BF16, G, W, B, G, 8, 16, 64, C, 0x60000, ws, None)
+    assert L.nvfp4_qqmm_packed(*ok) == UNSUP
+    bad = list(ok)
+    bad[1] = F32
+    assert L.nvfp4_qqmm_packed(*bad) == INV and "float16 or bfloat16" in err(L)
+    bad = list(ok)
+    bad[8] = 32
+    assert L.nvfp4_qqmm_packed(*bad) == INV and "multiple of 64" in err(L)
+    bad = list(ok)
+    bad[7] = 18
+    assert L.nvfp4_qqmm_packed(*bad) == INV and "multiple of 4" in err(L)
+    bad = list(ok)
+    bad[5] = None
+    assert L.nvfp4_qqmm_packed(*bad) == INV and "both global_scale_x" in err(L)
+    # m == 1 still runs the matrix-core path, so it needs the workspace
+    assert L.nvfp4_qqmm_packed(A, BF16, G, W, B, G, 1, 16, 64, C, None, 0, None) == INV
+    assert L.nvfp4_qmm_packed(A, F16, W, B, G, 8, 16, 64, C, None) == UNSUP
+    assert L.nvfp4_qmm_packed(A, F16, W, B, G, 8, 16, 80, C, None) == INV
+    gws = L.nvfp4_gather_qmm_workspace_size(10, 2, 4, 64, 64)
+    gok = (A, BF16, W, B, G, 0x70000, 10, 2, 4, 64, 64, C, 0x60000, gws, None)
+    assert L.nvfp4_gather_qmm_packed(*gok) == UNSUP
+    bad = list(gok)
+    bad[9] = 48
+    assert L.nvfp4_gather_qmm_packed(*bad) == INV and "multiple of 32" in err(L)
+    bad = list(gok)
+    bad[13] = gws - 4
+    assert L.nvfp4_gather_qmm_packed(*bad) == INV and "workspace" in err(L)
