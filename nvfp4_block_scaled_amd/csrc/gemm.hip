@@ -6,20 +6,18 @@
 // global scale for qmm" PR 4458, statement: the global factor sits inside
 // the dequantization, per expert for gather_qmm).
 //
-// 16-bit inputs run on the matrix cores (v_mfma_f32_16x16x32_bf16 / _f16):
-//   * workgroup tile 256 x 256 x 64, four waves in a 2 x 2 grid, each wave a
-//     128 x 128 block of 8 x 8 MFMA tiles with float32 accumulators;
-//   * A (x_hat or the gathered x rows) is copied to LDS as is; B is read as
-//     packed e2m1 codes + e4m3 scales, decoded by the VALU to T with the
-//     effective scale e4m3(s) * g/2688 and written to LDS, so every weight
-//     element is decoded once per workgroup;
-//   * both LDS tiles are double-buffered: the global loads for k-step i + 1
-//     are in flight while the MFMAs of step i run;
-//   * LDS rows are 64 elements (128 B) with the 16-byte chunks XOR-swizzled by
-//     row, so fragment reads of 16 consecutive rows hit distinct banks;
-//   * the MFMA takes the weight fragment as its first operand, so each lane
-//     ends with 4 consecutive output columns of one row (one 8-byte store).
-// float32 inputs use a plain LDS-tiled FMA kernel with float32 weights.
+// Three kernels, by operand type and shape:
+//   * mfma_gemm_fast_kernel / mfma_gemm_fast2_kernel (16-bit x, k % 64 == 0,
+//     n % 4 == 0): the matrix-core path on v_mfma_f32_32x32x16 with the
+//     weights decoded in registers, A staged through LDS; it reads the weight
+//     either row-major or in the packed layout of mfma_pack_kernel (details
+//     at the kernel body);
+//   * mfma_gemm_kernel (16-bit x, any k % 16 == 0): the general matrix-core
+//     path on v_mfma_f32_16x16x32, 256 x 256 x 64 tiles with both A and the
+//     decoded weight tile (written by the VALU) in double-buffered LDS;
+//   * f32_gemm_kernel (float32 x): an LDS-tiled FMA kernel over float32
+//     decoded weights.
+// The routing of gather_qmm (moe_route_kernel) is at the end of the file.
 #include <type_traits>
 
 #include "nvfp4_device.h"
@@ -81,6 +79,16 @@ __device__ __forceinline__ typename Mfma<DT>::V8 decode8(uint32_t word, float se
   return o;
 }
 
+// ------------------------------------------------------------------ general path (k % 16 == 0)
+//
+// Workgroup tile 256 x 256 x 64, four waves in a 2 x 2 grid, each a 128 x 128
+// block of 8 x 8 v_mfma_f32_16x16x32 tiles with float32 accumulators.  A is
+// copied to LDS as is; the weight tile is read as codes + scales, decoded by
+// the VALU to T with e4m3(s) * g/2688 and written to LDS, so every weight
+// element is decoded once per workgroup.  Both LDS tiles are double-buffered;
+// LDS rows of 64 elements have their 16-byte chunks XOR-swizzled by row; the
+// MFMA takes the weight fragment first, so each lane ends with 4 consecutive
+// output columns of one row.  Partial k-steps load group by group.
 template <int DT, bool GATHER>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -302,7 +310,7 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 
 // ------------------------------------------------------------------ fast path (k % 64 == 0)
 //
-// Same tile (256 x 256 x 64) with the work split for gfx950:
+// Workgroup tile 256 (or 128) rows x 256 columns x 64 k, four waves:
 //   * the four waves split the 256 output columns (64 each) and all share the
 //     256 rows of A, so every weight element is decoded exactly once per
 //     workgroup, by the wave that multiplies with it, straight into the MFMA
@@ -336,6 +344,8 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     sets), so every stage and register set is fixed in the code;
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
 //     works on its own contiguous set of weight column panels;
+//   * with 128-row tiles (used up to 128 rows) every number above halves
+//     except the weight work per wave, and two workgroups share a CU;
 //   * the 256 accumulator registers of a wave fill the AGPR file exactly; the
 //     MFMAs are written with AGPR-constrained operands so the register
 //     allocator keeps every accumulator in place (left to itself it splits
@@ -420,20 +430,26 @@ struct BRaw {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int DT, bool GATHER, bool PACKED>
-__global__ void __launch_bounds__(kGemmThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
-                      const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                      const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
-                      const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                      int top_k, int E, int tiles_m) {
+// RT = 32-row tiles per workgroup: 8 (256 rows, 256 accumulators per wave, one
+// workgroup per CU) or 4 (128 rows, 128 accumulators per wave, two workgroups
+// per CU, so that each SIMD interleaves two waves' instruction streams).
+template <int DT, bool GATHER, bool PACKED, int RT>
+__device__ __forceinline__ void
+mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
+                    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                    const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
+                    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+                    int top_k, int E, int tiles_m) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
-  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kAStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa1[kAStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa2[kAStageBytes];
-  __shared__ int out_rows[BM];
+  constexpr int TM = 32 * RT;              // tile rows
+  constexpr int kStage = TM * BK * 2;      // bytes of one A stage
+  constexpr int NQ = 4 * RT;               // fragment pairs per k-step
+  constexpr int DPQ = 32 / NQ;             // decoded dwords per fragment pair
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa2[kStage];
+  __shared__ int out_rows[TM];
   uint8_t* const stage[3] = {sa0, sa1, sa2};
 
   const int tid = threadIdx.x;
@@ -451,7 +467,7 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     expert = -1;
     for (int e = 0; e < E; ++e) {
       const int cnt = offsets[e + 1] - offsets[e];
-      const int tiles = (cnt + BM - 1) / BM;
+      const int tiles = (cnt + TM - 1) / TM;
       if (tile_m < acc_tiles + tiles) {
         expert = e;
         tile_m -= acc_tiles;
@@ -463,12 +479,12 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     }
     if (expert < 0) return;
   }
-  const int bm = tile_m * BM;
+  const int bm = tile_m * TM;
   const int bn = tile_n * BN;
   const float dec_w = GATHER ? (gw ? gw[expert] / (kE4M3Max * kE2M1Max) : 1.0f) : global_decode(gw);
 
   // output row of each tile row (-1: outside the tile's row count)
-  for (int r = tid; r < BM; r += kGemmThreads) {
+  for (int r = tid; r < TM; r += kGemmThreads) {
     int o = -1;
     if (bm + r < row_count) {
       if constexpr (GATHER)
@@ -496,14 +512,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   // and each parity class of any 16 consecutive rows, put a given k-chunk in
   // distinct slots, so the fragment reads (16 rows, one chunk per lane half)
   // are free of bank conflicts whether a bank row spans one 128-byte tile row
-  // or two.  Wave w fills rows 64 w .. 64 w + 63 with 8 loads of 1 KB: load j,
-  // lane l writes slot l % 8 of row 64 w + 8 j + l / 8, i.e. fetches k-chunk
-  // (l % 8) ^ swz(row) of that row.
+  // or two.  Wave w fills rows 8 RT w .. 8 RT w + 8 RT - 1 with RT loads of
+  // 1 KB: load j, lane l writes slot l % 8 of row 8 RT w + 8 j + l / 8, i.e.
+  // fetches k-chunk (l % 8) ^ swz(row) of that row.
   auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
-  uint32_t a_off[8];
+  uint32_t a_off[RT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 64 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < RT; ++j) {
+    const int r = 8 * RT * wave + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     const int rr = (bm + r < row_count) ? r : 0;  // rows past the count re-read row 0
     int64_t arow;
@@ -544,9 +560,9 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   // this wave's quarter of A(kt) into stage si, straight from global memory
   auto load_a = [&](int kt, int si) {
     const int so = kt * BK * (int)sizeof(T);
-    uint8_t* dst = stage[si] + wave * 8192;
+    uint8_t* dst = stage[si] + wave * (kStage / 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < RT; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(dst + j * 1024), 16, a_off[j], so, 0, 0);
   };
   auto load_b = [&](int kt, BRaw& b) {
@@ -576,11 +592,11 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     }
   };
 
-  f32x16 acc[2][8];
+  f32x16 acc[2][RT];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][i][v] = 0.f;
 
@@ -604,27 +620,37 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
     const BRaw& rnext = raw[1 - rs];
     float se = 0.f;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const int u = q >> 3, i = q & 7;
+    for (int q = 0; q < NQ; ++q) {
+      const int u = q / RT, i = q % RT;
       const V8 a = ar[q & 3];
       {
         const int q3 = q + 3;
-        if (q3 < 32)
-          ar[q3 & 3] = *reinterpret_cast<const V8*>(la + a_rd[q3 >> 3] + (q3 & 7) * 4096);
+        if (q3 < NQ)
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(la + a_rd[q3 / RT] + (q3 % RT) * 4096);
         else
-          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd[0] + (q3 - 32) * 4096);
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd[0] + (q3 - NQ) * 4096);
       }
-      // decode: column tile dt = q / 16, sub-step du = (q / 4) % 4, dword q % 4
-      const int dt = q >> 4, du = (q >> 2) & 3, dp = q & 3;
-      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][0][u]), a, acc[0][i]);
+      // decode: dword d of step kt + 1's 32 is column tile d / 16, sub-step
+      // (d / 4) % 4, dword d % 4; DPQ of them ride on each fragment pair
+      uint32_t part[DPQ];
+#pragma unroll
+      for (int j = 0; j < DPQ; ++j) {
+        const int d = q * DPQ + j, dt = d >> 4, du = (d >> 2) & 3, dp = d & 3;
+        if (j == 0) Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][0][u]), a, acc[0][i]);
+        if (DPQ > 1 && j == DPQ / 2) Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][1][u]), a, acc[1][i]);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((d & 7) == 0) se = scale_of(rnext, dt, du >> 1);
+        part[j] = decode_part(rnext, dt, du, dp, se);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (DPQ == 1) Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][1][u]), a, acc[1][i]);
       __builtin_amdgcn_sched_barrier(0);
-      if ((q & 7) == 0) se = scale_of(rnext, dt, du >> 1);
-      const uint32_t part = decode_part(rnext, dt, du, dp, se);
-      __builtin_amdgcn_sched_barrier(0);
-      Mfma32<DT>::run_agpr(__builtin_bit_cast(V8, bf[rs][1][u]), a, acc[1][i]);
-      __builtin_amdgcn_sched_barrier(0);
-      bf[1 - rs][dt][du][dp] = part;
-      if (q == 15) {
+#pragma unroll
+      for (int j = 0; j < DPQ; ++j) {
+        const int d = q * DPQ + j;
+        bf[1 - rs][d >> 4][(d >> 2) & 3][d & 3] = part[j];
+      }
+      if (q == NQ / 2 - 1) {
         a_stage_barrier();
         load_a(min(kt + 2, KT - 1), nw);
       }
@@ -652,14 +678,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa0 + a_rd[0] + q * 4096);
+  for (int q = 0; q < 3; ++q) ar[q] = *reinterpret_cast<const V8*>(sa0 + a_rd[q / RT] + (q % RT) * 4096);
 
   // ---------------------------------------------------------------- main loop
   // the zeroed accumulators are materialised in AGPRs before the fence
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+a"(acc[t][i]));
+    for (int i = 0; i < RT; ++i) asm volatile("" : "+a"(acc[t][i]));
   mfma32_fence();
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -687,21 +713,21 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
   // acc[t][i][v]: tile row 32 i + fr, tile column 64 w + 32 t + 8 (v / 4) +
   // 4 fh + v % 4.  Each lane holds 4 consecutive columns of 16 rows, so the
   // block goes through LDS (the A stages are free now) to leave as whole
-  // rows: per half of the tile's rows, wave w writes its 128 x 64 block
-  // (16 KB, 16-byte chunk c of row r in slot c ^ (r & 7)) and reads it back
-  // with lane l on row 8 j + l / 8, chunk l % 8, so that one store
-  // instruction writes 8 full 128-byte row segments.
+  // rows: per half of the tile's rows, wave w writes its 16 RT x 64 block
+  // (16-byte chunk c of row r in slot c ^ (r & 7)) and reads it back with
+  // lane l on row 8 j + l / 8, chunk l % 8, so that one store instruction
+  // writes 8 full 128-byte row segments.
   // this wave's discarded last stage load has landed and every wave is done
   // with the stages
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   lds_barrier();
   T* O = reinterpret_cast<T*>(out);
-  uint8_t* const eb = ((wave >> 1) ? sa1 : sa0) + (wave & 1) * 16384;
+  uint8_t* const eb = ((wave >> 1) ? sa1 : sa0) + (wave & 1) * (kStage / 2);
   const int col0 = bn + wave * 64;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RT / 2; ++i)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -710,14 +736,14 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
           typedef T T4 __attribute__((ext_vector_type(4)));
           T4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = from_f32<DT>(acc[t][4 * h + i][4 * g + e]);
+          for (int e = 0; e < 4; ++e) v[e] = from_f32<DT>(acc[t][(RT / 2) * h + i][4 * g + e]);
           *reinterpret_cast<T4*>(eb + r * 128 + ((c ^ (r & 7)) << 4) + 8 * fh) = v;
         }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 2 * RT; ++j) {
       const int r = 8 * j + (lane >> 3), c = lane & 7;
       const u32x4 d = *reinterpret_cast<const u32x4*>(eb + r * 128 + ((c ^ (r & 7)) << 4));
-      const int orow = out_rows[128 * h + r];
+      const int orow = out_rows[(TM / 2) * h + r];
       const int col = col0 + 8 * c;
       if (orow >= 0) {
         T* op = O + (int64_t)orow * N + col;
@@ -733,6 +759,27 @@ mfma_gemm_fast_kernel(const void* __restrict__ a_base, int64_t a_rows,
       }
     }
   }
+}
+
+#define NVFP4_FAST_ARGS                                                                        \
+  const void* __restrict__ a_base, int64_t a_rows, const uint8_t* __restrict__ wc,             \
+      const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,       \
+      void* __restrict__ out, const int32_t* __restrict__ offsets,                             \
+      const int32_t* __restrict__ perm, int top_k, int E, int tiles_m
+#define NVFP4_FAST_PASS a_base, a_rows, wc, ws, gw, M, N, K, out, offsets, perm, top_k, E, tiles_m
+
+// 256-row tiles: one workgroup (four waves, 256 accumulators each) per CU
+template <int DT, bool GATHER, bool PACKED>
+__global__ void __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_gemm_fast_kernel(NVFP4_FAST_ARGS) {
+  mfma_gemm_fast_body<DT, GATHER, PACKED, 8>(NVFP4_FAST_PASS);
+}
+
+// 128-row tiles: two workgroups per CU (two waves of 128 accumulators per SIMD)
+template <int DT, bool GATHER, bool PACKED>
+__global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_gemm_fast2_kernel(NVFP4_FAST_ARGS) {
+  mfma_gemm_fast_body<DT, GATHER, PACKED, 4>(NVFP4_FAST_PASS);
 }
 
 // ------------------------------------------------------------------ packed weight layout
@@ -978,6 +1025,48 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
 
 // ------------------------------------------------------------------ launchers
 
+template <bool GATHER, bool PACKED, int RT>
+hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
+                          const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
+                          const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
+                          hipStream_t s_stream) {
+  constexpr int TM = 32 * RT;
+  const int64_t tiles_m = (rows + TM - 1) / TM + (GATHER ? e : 0);
+  const int64_t blocks = tiles_m * ((n + BN - 1) / BN);
+#define NVFP4_LAUNCH(KER, D)                                                                     \
+  KER<D, GATHER, PACKED><<<(int)blocks, kGemmThreads, 0, s_stream>>>(                              \
+      a, a_rows, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e,    \
+      (int)tiles_m)
+  if constexpr (RT == 8) {
+    if (dt == kF16)
+      NVFP4_LAUNCH(mfma_gemm_fast_kernel, kF16);
+    else
+      NVFP4_LAUNCH(mfma_gemm_fast_kernel, kBF16);
+  } else {
+    if (dt == kF16)
+      NVFP4_LAUNCH(mfma_gemm_fast2_kernel, kF16);
+    else
+      NVFP4_LAUNCH(mfma_gemm_fast2_kernel, kBF16);
+  }
+#undef NVFP4_LAUNCH
+  return hipGetLastError();
+}
+
+template <bool GATHER, bool PACKED>
+hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
+                       const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
+                       const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
+                       hipStream_t s) {
+  // up to 128 rows (routed pairs) the 128-row tiles skip the half of a
+  // 256-row tile that would multiply padding; above that the 256-row tiles
+  // are faster (each weight element is decoded for twice as many rows)
+  if (rows <= 128)
+    return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
+                                             top_k, e, s);
+  return launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
+                                           top_k, e, s);
+}
+
 hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                             uint8_t* pc, uint8_t* ps, hipStream_t s) {
   const int64_t pieces = ((rows + 31) / 32) * (k / BK) * 64;
@@ -989,31 +1078,14 @@ hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t
 hipError_t launch_qqmm_gemm_packed(const void* xhat, int dt, const uint8_t* pc, const uint8_t* ps,
                                    const float* gw, int64_t m, int64_t n, int64_t k, void* out,
                                    hipStream_t s) {
-  const int64_t blocks = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const int tiles_m = (int)((m + BM - 1) / BM);
-  if (dt == kF16)
-    mfma_gemm_fast_kernel<kF16, false, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        xhat, m, pc, ps, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
-  else
-    mfma_gemm_fast_kernel<kBF16, false, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        xhat, m, pc, ps, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
-  return hipGetLastError();
+  return launch_fast<false, true>(dt, xhat, m, pc, ps, gw, m, n, k, out, nullptr, nullptr, 1, 1, s);
 }
 
 hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, const uint8_t* ps,
                                      const float* gw, const int32_t* offsets, const int32_t* perm,
                                      int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
                                      void* out, hipStream_t s) {
-  const int64_t pairs = t * top_k;
-  const int64_t mt = (pairs + BM - 1) / BM + e;
-  const int64_t blocks = mt * ((n + BN - 1) / BN);
-  if (dt == kF16)
-    mfma_gemm_fast_kernel<kF16, true, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        x, t, pc, ps, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
-  else
-    mfma_gemm_fast_kernel<kBF16, true, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        x, t, pc, ps, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
-  return hipGetLastError();
+  return launch_fast<true, true>(dt, x, t, pc, ps, gw, t * top_k, n, k, out, offsets, perm, top_k, e, s);
 }
 
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
@@ -1027,16 +1099,8 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
     return hipGetLastError();
   }
   int64_t blocks = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  if (k % BK == 0 && n % 4 == 0) {
-    const int tiles_m = (int)((m + BM - 1) / BM);
-    if (dt == kF16)
-      mfma_gemm_fast_kernel<kF16, false, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
-    else
-      mfma_gemm_fast_kernel<kBF16, false, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          xhat, m, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, tiles_m);
-    return hipGetLastError();
-  }
+  if (k % BK == 0 && n % 4 == 0)
+    return launch_fast<false, false>(dt, xhat, m, wc, ws, gw, m, n, k, out, nullptr, nullptr, 1, 1, s);
   if (dt == kF16)
     mfma_gemm_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
         xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1);
@@ -1067,15 +1131,8 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
   }
   int64_t mt = (pairs + BM - 1) / BM + e;
   int64_t blocks = mt * ((n + BN - 1) / BN);
-  if (k % BK == 0 && n % 4 == 0) {
-    if (dt == kF16)
-      mfma_gemm_fast_kernel<kF16, true, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
-    else
-      mfma_gemm_fast_kernel<kBF16, true, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-          x, t, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, (int)mt);
-    return hipGetLastError();
-  }
+  if (k % BK == 0 && n % 4 == 0)
+    return launch_fast<true, false>(dt, x, t, wc, ws, gw, pairs, n, k, out, offsets, perm, top_k, e, s);
   if (dt == kF16)
     mfma_gemm_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
         x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e);
