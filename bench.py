@@ -48,7 +48,7 @@ M, N, K = 2048, 14336, 4096
 # source it was measured on (sha256 prefix of the file), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "6454c3ec9bf973f8", 360599224),
+    "gemm": ("gemm.hip", "6b150f63ea5f1623", 367316285),
     "qmv": ("qmv.hip", "09301831f4c6ad9f", 33246960),
 }
 
