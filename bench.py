@@ -16,6 +16,9 @@ Beside it, on the same run:
   qmv         decode x bf16 [1, 4096] @ the same w: algorithmic bytes per
               launch / kernel time, vs 8 TB/s, with the weight rotated over
               copies totalling > 512 MB so the Infinity Cache cannot serve it;
+  small_batch_qqmm  qqmm with x bf16 [m, 4096], m = 2, 4, 8, 16, @ the same w,
+              row-major and packed (cold weights as for qmv), GB/s of
+              algorithmic bytes;
   quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
               outliers (also rotated), GB/s each;
   gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
@@ -186,6 +189,46 @@ def bench_qmv(args, nv, torch, W):
                 gbs_warm=nbytes / ms_warm / 1e6)
 
 
+def bench_small(args, nv, torch, W):
+    """qqmm with a few rows of x (the decode shape batched): x bf16 [m, 4096]
+    Normal(0, 1) with its round trip inside the kernel, cold weights rotated
+    as for qmv, row-major and packed; bytes = weight codes + scales + x + out."""
+    _, w = W.qmv_inputs(device="cuda")
+    gw = nv.nvfp4_tensor_amax(w)
+    wc, ws = nv.nvfp4_quantize(w, gw)
+    del w
+    per = wc.numel() + ws.numel()
+    copies = max(2, -(-600_000_000 // per))
+    wcs = [wc.clone() for _ in range(copies)]
+    wss = [ws.clone() for _ in range(copies)]
+    wps = [nv.nvfp4_mfma_pack(wc, ws) for _ in range(copies)]
+    r = {}
+    for m in (2, 4, 8, 16):
+        x = W.normal((m, K), 1.0, 100 + m, "bf16", device="cuda")
+        gx = nv.nvfp4_tensor_amax(x)
+        out = torch.empty(m, N, dtype=torch.bfloat16, device="cuda")
+        wsp, _ = nv.qqmm_workspace(m, N, K, torch.bfloat16, "cuda")
+        state = {"i": 0}
+
+        def row_major():
+            i = state["i"] % copies
+            state["i"] += 1
+            nv.nvfp4_qqmm(x, wcs[i], wss[i], gx, gw, out=out, workspace=wsp)
+
+        def packed():
+            i = state["i"] % copies
+            state["i"] += 1
+            nv.nvfp4_qqmm_packed(x, wps[i], gx, gw, out=out, workspace=wsp)
+
+        nbytes = per + m * K * 2 + m * N * 2
+        r[m] = {}
+        for name, fn in (("row_major", row_major), ("packed", packed)):
+            settle(fn, 0.05)
+            ms = timed(fn, copies * 4, copies, graph=True)
+            r[m][name] = dict(ms=ms, gbs=nbytes / ms / 1e6, bytes=nbytes)
+    return r
+
+
 def bench_quantize(args, nv, torch, W):
     w = W.quantize_weight(device="cuda")
     rows, k = w.shape
@@ -303,7 +346,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "quantize", "gather", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "quantize", "gather", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +374,12 @@ def main():
         res["qmv"] = bench_qmv(args, nv, torch, W)
         log(f"  {res['qmv']['ms'] * 1e3:.2f} us/launch, {res['qmv']['gbs']:.0f} GB/s "
             f"(warm {res['qmv']['gbs_warm']:.0f} GB/s)")
+    if args.only in ("all", "small"):
+        log("small-batch qqmm (m rows @ the decode weight) ...")
+        res["small"] = bench_small(args, nv, torch, W)
+        for m_, d in res["small"].items():
+            log("  m=%d: " % m_ + ", ".join(f"{k_} {v['ms'] * 1e3:.2f} us ({v['gbs']:.0f} GB/s)"
+                                            for k_, v in d.items()))
     if args.only in ("all", "quantize"):
         log("quantize / dequantize ...")
         res["quantize"] = bench_quantize(args, nv, torch, W)
@@ -374,6 +423,14 @@ def main():
                        "weight_copies_rotated": v["copies"],
                        "warm_cache_GBps": round(v["gbs_warm"], 1),
                        "workload": "qmv decode: x bf16 [1,4096] @ NVFP4 w [14336,4096]^T"}
+    if "small" in res:
+        line["small_batch_qqmm"] = {
+            f"m={m_}": {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["gbs"] / PEAK_HBM_GBS, 4),
+                             "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}
+                        for k_, v in d.items()}
+            for m_, d in res["small"].items()}
+        line["small_batch_qqmm"]["workload"] = ("qqmm x bf16 [m,4096] (round trip in the kernel) "
+                                                "@ NVFP4 w [14336,4096]^T, cold weights")
     if "quantize" in res:
         line["quantize"] = {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["frac"], 4),
                                  "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}

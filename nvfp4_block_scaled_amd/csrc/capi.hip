@@ -264,6 +264,9 @@ nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm] workspace must be 256-byte aligned.");
   if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4::small_m_ok(dt, false, m, n, k))  // x's round trip happens inside the kernel
+    return launched(op, nvfp4::launch_small_m(x, dt, true, global_scale_x, w_codes, w_scales,
+                                              false, global_scale_w, m, n, k, out, stream));
   hipError_t e = nvfp4::launch_quant_dequant(x, dt, m, k, global_scale_x, workspace, stream);
   if (e != hipSuccess) return launched(op, e);
   return launched(op, nvfp4::launch_qqmm_gemm(workspace, dt, w_codes, w_scales, global_scale_w, m,
@@ -278,6 +281,9 @@ nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
                                      m, n, k, out))
     return st;
   if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4::small_m_ok(dt, false, m, n, k))
+    return launched(op, nvfp4::launch_small_m(x, dt, false, nullptr, w_codes, w_scales, false,
+                                              global_scale_w, m, n, k, out, stream));
   return launched(op, nvfp4::launch_qqmm_gemm(x, dt, w_codes, w_scales, global_scale_w, m, n, k,
                                                out, stream));
 }
@@ -421,6 +427,10 @@ nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* globa
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_packed] workspace must be 256-byte aligned.");
   if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4::small_m_ok(dt, true, m, n, k))
+    return launched(op, nvfp4::launch_small_m(x, dt, true, global_scale_x, packed_codes,
+                                              packed_scales, true, global_scale_w, m, n, k, out,
+                                              stream));
   hipError_t e = nvfp4::launch_quant_dequant(x, dt, m, k, global_scale_x, workspace, stream);
   if (e != hipSuccess) return launched(op, e);
   return launched(op, nvfp4::launch_qqmm_gemm_packed(workspace, dt, packed_codes, packed_scales,
@@ -436,6 +446,9 @@ nvfp4_status nvfp4_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* pack
     return st;
   if (nvfp4_status st = check_packed(op, dt, n, k)) return st;
   if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4::small_m_ok(dt, true, m, n, k))
+    return launched(op, nvfp4::launch_small_m(x, dt, false, nullptr, packed_codes, packed_scales,
+                                              true, global_scale_w, m, n, k, out, stream));
   return launched(op, nvfp4::launch_qqmm_gemm_packed(x, dt, packed_codes, packed_scales,
                                                       global_scale_w, m, n, k, out, stream));
 }

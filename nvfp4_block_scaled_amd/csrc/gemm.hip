@@ -351,7 +351,6 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     allocator keeps every accumulator in place (left to itself it splits
 //     them between the two files and moves them around every k-step).
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit data format
 constexpr int kBLoadsPerStep = 4;          // weight loads issued per k-step and wave
 constexpr int kPackCodeBlock = 1024;       // packed codes per 32-column tile and k-step
 constexpr int kPackScaleBlock = 128;       // packed scales per 32-column tile and k-step
@@ -374,13 +373,6 @@ __device__ __forceinline__ void mfma32_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// LDS barrier without a memory fence: finish this wave's LDS operations, then
-// meet the other waves.  The "memory" clobber keeps the compiler from moving
-// memory accesses across it; outstanding global loads stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // The main loop's barrier: this wave's global-to-LDS load of the A stage
 // needed next has landed -- it was issued a step ago and only the
 // kBLoadsPerStep weight loads of this step are younger -- then meet the other
@@ -388,36 +380,6 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void a_stage_barrier() {
   static_assert(kBLoadsPerStep == 4, "the wait count below is the number of weight loads per step");
   asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
-  const int n = bytes >= 0xFFFFFFFFull ? -1 : (int)(uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
-}
-
-// Two 16-bit values (element 2j low) from two floats.
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  using T = typename Elem<DT>::T;
-  typedef T T2 __attribute__((ext_vector_type(2)));
-  T2 v;
-  v[0] = from_f32<DT>(a);
-  v[1] = from_f32<DT>(b);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Dword P of a decoded weight fragment: the two codes of byte P of the code
-// word, times the effective block scale, as two 16-bit values.
-template <int DT, int P>
-__device__ __forceinline__ uint32_t decode_dword(uint32_t codes, float se) {
-  const f32x2 v = e2m1_decode2_f32<P>(codes);
-  float a, b;
-  {
-#pragma clang fp contract(off)
-    a = v.x * se;
-    b = v.y * se;
-  }
-  return pack2<DT>(a, b);
 }
 
 // Raw weights of one k-step for one lane: for each of its 2 column tiles, the

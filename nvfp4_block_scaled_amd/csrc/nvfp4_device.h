@@ -231,4 +231,108 @@ __device__ __forceinline__ float wave_sum_uniform(float v) {
   return (a + b) + (c + d);
 }
 
+// ----------------------------------------------------------------- x round trip
+
+// Load 8 consecutive elements (half group h, elements 8h .. 8h + 7) of x as floats.
+// 8 16-bit values (4 dwords, element 2i in the low half of dword i) as floats.
+template <int DT>
+__device__ __forceinline__ void unpack8(u32x4 w, float (&v)[8]) {
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (DT == kBF16) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+    } else {
+      f16x2 hv = __builtin_bit_cast(f16x2, q[i]);
+      v[2 * i] = (float)hv.x;
+      v[2 * i + 1] = (float)hv.y;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void load8x(const void* base, int64_t h, float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * h;
+    f32x4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    unpack8<DT>(reinterpret_cast<const u32x4*>(base)[h], v);
+  }
+}
+
+// x_hat of one half group (8 values at element 8h), rounded to T, as floats.
+// The pair partner (lane ^ 1) holds the other half of the group.
+template <int DT>
+__device__ __forceinline__ void xhat_half_group(const float (&v)[8], float enc, float dec,
+                                                float (&o)[8]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  uint32_t byte;
+  uint32_t codes = encode_half_group(v, a, enc, byte);
+  float sc;
+  {
+#pragma clang fp contract(off)
+    sc = e4m3_decode(byte) * dec;
+  }
+  float q[8];
+  e2m1_decode8_f32(codes, q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    o[i] = to_f32<DT>(from_f32<DT>(q[i] * sc));
+  }
+}
+
+// ----------------------------------------------------------------- weight decode to 16-bit
+
+// Two 16-bit values (element 2j low) from two floats.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  using T = typename Elem<DT>::T;
+  typedef T T2 __attribute__((ext_vector_type(2)));
+  T2 v;
+  v[0] = from_f32<DT>(a);
+  v[1] = from_f32<DT>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Dword P of a decoded weight fragment: the two codes of byte P of the code
+// word, times the effective block scale, as two 16-bit values.
+template <int DT, int P>
+__device__ __forceinline__ uint32_t decode_dword(uint32_t codes, float se) {
+  const f32x2 v = e2m1_decode2_f32<P>(codes);
+  float a, b;
+  {
+#pragma clang fp contract(off)
+    a = v.x * se;
+    b = v.y * se;
+  }
+  return pack2<DT>(a, b);
+}
+
+// ----------------------------------------------------------------- buffer resources
+
+// A raw buffer resource over `bytes` bytes (32-bit data format, no swizzle,
+// range checked: loads past the end return zeros).
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0xFFFFFFFFull ? -1 : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
+// ----------------------------------------------------------------- barriers
+
+// LDS barrier without a memory fence: finish this wave's LDS operations, then
+// meet the other waves.  The "memory" clobber keeps the compiler from moving
+// memory accesses across it; outstanding global loads stay in flight (a
+// __syncthreads() would first wait for all of them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace nvfp4

@@ -48,4 +48,14 @@ hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, c
                                      int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
                                      void* out, hipStream_t s);
 
+// smallm.hip: 1 <= m <= kSmallMaxM rows of x, 16-bit x, k % 128 == 0, with x
+// and its padding in LDS (m (k + 8) 2 bytes plus 7 KB within kSmallMaxLds)
+// and the weight's codes below 2 GB
+constexpr int64_t kSmallMaxM = 16;
+constexpr size_t kSmallMaxLds = 160 * 1024;
+bool small_m_ok(int dt, bool packed, int64_t m, int64_t n, int64_t k);
+hipError_t launch_small_m(const void* x, int dt, bool quantize_x, const float* gx,
+                          const uint8_t* wc, const uint8_t* ws, bool packed, const float* gw,
+                          int64_t m, int64_t n, int64_t k, void* out, hipStream_t s);
+
 }  // namespace nvfp4

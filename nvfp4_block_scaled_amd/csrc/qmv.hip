@@ -35,55 +35,6 @@ constexpr int kWaves = 8;
 constexpr int kThreadsQ = kWaves * 64;
 constexpr int kMaxRows = 8;  // rows per wave on the register path
 
-template <int DT>
-__device__ __forceinline__ void load8x(const void* base, int64_t h, float (&v)[8]) {
-  if constexpr (DT == kF32) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * h;
-    f32x4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    u32x4 w = reinterpret_cast<const u32x4*>(base)[h];
-    uint32_t q[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == kBF16) {
-        v[2 * i] = __uint_as_float(q[i] << 16);
-        v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
-      } else {
-        f16x2 hv = __builtin_bit_cast(f16x2, q[i]);
-        v[2 * i] = (float)hv.x;
-        v[2 * i + 1] = (float)hv.y;
-      }
-    }
-  }
-}
-
-// x_hat of one half group (8 values at element 8h), rounded to T, as floats.
-// The pair partner (lane ^ 1) holds the other half of the group.
-template <int DT>
-__device__ __forceinline__ void xhat_half_group(const float (&v)[8], float enc, float dec,
-                                                float (&o)[8]) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
-  a = fmaxf(a, __shfl_xor(a, 1, 64));
-  uint32_t byte;
-  uint32_t codes = encode_half_group(v, a, enc, byte);
-  float sc;
-  {
-#pragma clang fp contract(off)
-    sc = e4m3_decode(byte) * dec;
-  }
-  float q[8];
-  e2m1_decode8_f32(codes, q);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-    o[i] = to_f32<DT>(from_f32<DT>(q[i] * sc));
-  }
-}
-
 // Partial dot product of one group of 16 (codes in dwords c0, c1) with
 // x_hat (16-bit pairs xp[0..7], or floats xf[0..15]).
 template <int DT>
@@ -200,7 +151,7 @@ qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
       }
     }
   }
-  __syncthreads();
+  lds_barrier();  // x_hat written; the weight loads stay in flight
 
   // 4. this lane's x_hat pieces into registers: 32 elements per piece
   uint32_t xp[CH][2][16];  // 16-bit pairs (16-bit T)
