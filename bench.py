@@ -48,20 +48,29 @@ M, N, K = 2048, 14336, 4096
 # HBM bytes per launch from two rocprofv3 counter runs (FETCH_SIZE, then
 # WRITE_SIZE), each scaled by what the same counter reads for a 512 MiB device
 # copy (fetch x 1.9999, write x 1.0000).  A figure holds only for the kernel
-# source it was measured on (sha256 prefix of the file), else it is reported
+# source it was measured on (sha256 prefix of the file and the two headers it
+# includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "6b150f63ea5f1623", 367316285),
-    "qmv": ("qmv.hip", "09301831f4c6ad9f", 33246960),
+    "gemm": ("gemm.hip", "44ead79dc070dff4", 367329054),
+    "qmv": ("qmv.hip", "82774d58538ec6ac", 33246753),
 }
 
 
-def measured_traffic(kernel):
+def source_hash(src):
+    """sha256[:16] of a kernel source together with the two headers it includes."""
     import hashlib
+    h = hashlib.sha256()
+    for f in (src, "nvfp4_device.h", "nvfp4_internal.h"):
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
     src, sha, nbytes = MEASURED_TRAFFIC[kernel]
-    path = os.path.join(ROOT, "nvfp4_block_scaled_amd", "csrc", src)
     try:
-        cur = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+        cur = source_hash(src)
     except OSError:
         return None
     return nbytes if cur == sha else None

@@ -147,7 +147,12 @@ size_t nvfp4_qqmm_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt
  * nvfp4_qqmm -- out = T( x_hat @ w^T ), x [m, k] and w NVFP4 [n, k] (diff
  * page 8, qqmm; diff page 7, QQMatmul::eval_gpu): x_hat is x after the NVFP4
  * round trip with global_scale_x, w is decoded with global_scale_w on the
- * block scale; float32 accumulation.  m == 1 runs the qmv kernel.
+ * block scale; float32 accumulation.  m == 1 runs the qmv kernel; 2 <= m
+ * <= 16 with 16-bit x, k % 128 == 0 and m (k + 8) 2 + 7168 <= 163840 runs
+ * the small-batch kernel, which does the x round trip itself (the workspace
+ * is then not touched); larger m go through the workspace and the
+ * matrix-core kernels.  The paths other than qmv round each decoded weight
+ * e2m1(q) * fp32(e4m3(s) * g_w/2688) to dt before the products.
  *   x               device [m, k] of type dt
  *   w_codes/scales  device [n, k/2] / [n, k/16]
  *   out             device [m, n] of type dt, written
@@ -166,7 +171,8 @@ nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale
  * NVFP4 decoded with global_scale_w on the block scale: the pages'
  * quantized_matmul (diff page 8, ops.cpp quantized_matmul; "mlx 0.30.7" diff
  * page 71, QuantizedMatmul::eval_gpu), i.e. the contraction of nvfp4_qqmm
- * without the activation round trip.  No workspace.
+ * without the activation round trip.  No workspace.  1 <= m <= 16 runs the
+ * small-batch kernel under the conditions given for nvfp4_qqmm.
  *   x               device [m, k] of type dt, 16-byte aligned
  *   w_codes/scales  device [n, k/2] / [n, k/16]
  *   global_scale_w  device float or NULL
@@ -263,11 +269,15 @@ nvfp4_status nvfp4_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_
 
 /*
  * nvfp4_qqmm_packed, nvfp4_qmm_packed, nvfp4_gather_qmm_packed -- nvfp4_qqmm,
- * nvfp4_qmm and nvfp4_gather_qmm with the weight given as its packed copy
- * (same results).  They run the matrix-core path only: x float16 or
- * bfloat16, k a multiple of 64, n a multiple of 4 (gather: of 32).  The
- * remaining arguments, workspaces and errors are those of the row-major
- * calls; any m >= 1 runs the matrix-core kernel.
+ * nvfp4_qmm and nvfp4_gather_qmm with the weight given as its packed copy.
+ * They run the matrix-core path only: x float16 or bfloat16, k a multiple of
+ * 64, n a multiple of 4 (gather: of 32).  The remaining arguments,
+ * workspaces and errors are those of the row-major calls; any m >= 1 runs a
+ * matrix-core kernel.  Above 16 rows (or outside the small-batch conditions
+ * of nvfp4_qqmm) the results equal the row-major calls' bit for bit; with
+ * 1 <= m <= 16 the packed small-batch kernel sums in another order than the
+ * row-major one (32-row instead of 16-row tiles), so the two agree to
+ * rounding, not bitwise.
  */
 nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* global_scale_x,
                                const uint8_t* packed_codes, const uint8_t* packed_scales,
