@@ -235,9 +235,45 @@ def moe_route(idx, e_count):
     return offsets, perm
 
 
+# ----------------------------------------------------------------- backward
+
+def quantize_columnwise(x, global_scale=None):
+    """Encode x [rows, cols] along its first axis: the rowwise encode of x^T,
+    codes [cols, rows/2] and scales [cols, rows/16] ("mlx 0.30.7.2 -> 0.30.7.6"
+    diff page 7, fp_quantize_columnwise: an M-major [M, K] tensor quantized in
+    groups along K, the scale and code steps those of fp_quantize_rowwise)."""
+    return quantize(np.ascontiguousarray(_f32(x).T), global_scale)
+
+
+def quant_dequant_columnwise(x, global_scale=None, dtype="bf16"):
+    """The round trip of x^T: [cols, rows] values of type T."""
+    return quant_dequant(np.ascontiguousarray(_f32(x).T), global_scale, dtype)
+
+
+def qqmm_vjp(x, w, dy, global_scale_x=None, global_scale_w=None, dtype="bf16", nthreads=None):
+    """Gradients of y = qqmm(x, w) for the cotangent dy ("mlx 0.30.7.2 ->
+    0.30.7.6" diff page 8, primitives.cpp QQMatmul::vjp):
+      g_dy = float32(max |dy|) when the primal global scales are given, else none;
+      dx = qqmm(dy, w^T)   with w^T [k, n] quantized along n under g_w;
+      dw = qqmm(dy^T, x^T) with x^T [k, m] quantized along m under g_x;
+    each qqmm round-trips its first operand under g_dy.  Returns (dx [m, k],
+    dw [n, k], g_dy)."""
+    x, w, dy = _f32(x), _f32(w), _f32(dy)
+    if (global_scale_x is None) != (global_scale_w is None):
+        raise ValueError("both global scales or neither")
+    g_dy = tensor_amax(dy) if global_scale_x is not None else None
+    wt_codes, wt_scales = quantize_columnwise(w, global_scale_w)   # w^T [k, n]
+    dx = qqmm(dy, wt_codes, wt_scales, g_dy, global_scale_w, dtype=dtype, nthreads=nthreads)
+    xt_codes, xt_scales = quantize_columnwise(x, global_scale_x)   # x^T [k, m]
+    dw = qqmm(np.ascontiguousarray(dy.T), xt_codes, xt_scales, g_dy, global_scale_x, dtype=dtype,
+              nthreads=nthreads)
+    return dx, dw, g_dy
+
+
 __all__ = [
     "F32", "F16", "BF16", "MUT_NONE", "MUT_DROP_GW", "MUT_DROP_GX", "MUT_GW_ON_SUM",
-    "MUT_AMAX6_BF16", "MUT_ENC_ORDER", "mutant", "e2m1_value", "e2m1_encode", "e4m3_value",
+    "MUT_AMAX6_BF16", "MUT_ENC_ORDER", "mutant", "quantize_columnwise", "quant_dequant_columnwise",
+    "qqmm_vjp", "e2m1_value", "e2m1_encode", "e4m3_value",
     "e4m3_encode", "round_ieee", "round_to", "tensor_amax", "quantize", "dequantize",
     "quant_dequant", "qqmm", "gather_qmm", "moe_route", "lib", "default_threads",
 ]

@@ -66,6 +66,28 @@ def grid_tensor(rows, k, seed, scale=1.0):
     return (x.view(rows, k) * scale).contiguous()
 
 
+def doubly_grid(rows, cols, seed, scale=1.0, col_exponent_period=0):
+    """float32 [rows, cols] on the e2m1 grid with a +6 and a -6 in every group
+    of 16 along each axis: +6 where (col - row) % 16 == 0 and -6 where
+    (col - row) % 16 == 1, the other values uniform over {0, +-0.5, .., +-6}.
+    With col_exponent_period p > 0 column c is also multiplied by
+    2^(c % p): every group along the rows then shares one power of two,
+    while a group along the columns mixes p of them."""
+    assert rows % 16 == 0 and cols % 16 == 0
+    g = _gen(seed)
+    levels = torch.tensor(E2M1_GRID[1:], dtype=torch.float32)
+    mags = levels[torch.randint(0, len(levels), (rows, cols), generator=g)]
+    zero = torch.rand(rows, cols, generator=g) < 1.0 / 15.0
+    sign = torch.where(torch.rand(rows, cols, generator=g) < 0.5, -1.0, 1.0)
+    x = torch.where(zero, torch.zeros_like(mags), mags * sign)
+    d = (torch.arange(cols)[None, :] - torch.arange(rows)[:, None]) % 16
+    x = torch.where(d == 0, torch.full_like(x, 6.0), x)
+    x = torch.where(d == 1, torch.full_like(x, -6.0), x)
+    if col_exponent_period > 0:
+        x = x * (2.0 ** (torch.arange(cols) % col_exponent_period)).to(torch.float32)[None, :]
+    return (x * scale).contiguous()
+
+
 def grid_case(name, seed=11):
     """The four exact-grid cases of osaurus-ai/mlx pull request 31 ("The test").
 
