@@ -19,6 +19,8 @@ Beside it, on the same run:
   small_batch_qqmm  qqmm with x bf16 [m, 4096], m = 2, 4, 8, 16, @ the same w,
               row-major and packed (cold weights as for qmv), GB/s of
               algorithmic bytes;
+  qqmm_backward  the vjp of the prefill qqmm (dx and dw, 2 x 2 M N K flop) and
+              its columnwise passes alone;
   quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
               outliers (also rotated), GB/s each;
   gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
@@ -238,6 +240,29 @@ def bench_small(args, nv, torch, W):
     return r
 
 
+def bench_backward(args, nv, torch, W):
+    """The vjp of the prefill qqmm: x bf16 [2048, 4096], w bf16 [14336, 4096],
+    dy bf16 [2048, 14336] Normal(0, 0.01); g_x = amax(x), g_w = amax(w);
+    dx and dw, 2 x 2 M N K flop, and the columnwise passes alone."""
+    x, w = W.qqmm_inputs(device="cuda")
+    dy = W.normal((M, N), 0.01, 7, "bf16", device="cuda")
+    gx, gw = nv.nvfp4_tensor_amax(x), nv.nvfp4_tensor_amax(w)
+    ws = torch.empty(nv.load_library().nvfp4_qqmm_vjp_workspace_size(M, N, K, 2), dtype=torch.uint8,
+                     device="cuda")
+    vjp = lambda: nv.nvfp4_qqmm_vjp(x, w, dy, gx, gw, workspace=ws)
+    settle(vjp, 0.1)
+    ms = timed(vjp, max(args.steps // 2, 5), 2)
+    wc = torch.empty(K, N // 2, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(K, N // 16, dtype=torch.uint8, device="cuda")
+    dyt = torch.empty(N, M, dtype=torch.bfloat16, device="cuda")
+    ms_wcol = timed(lambda: nv.nvfp4_quantize_columnwise(w, gw, codes=wc, scales=wsc), 20, 3, graph=True)
+    ms_dycol = timed(lambda: nv.nvfp4_quant_dequant_columnwise(dy, gx, out=dyt), 20, 3, graph=True)
+    flop = 2 * 2.0 * M * N * K
+    return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, ms_wcol=ms_wcol,
+                wcol_gbs=(N * K * 2 + N * K // 2 + N * K // 16) / ms_wcol / 1e6,
+                ms_dycol=ms_dycol, dycol_gbs=(M * N * 4) / ms_dycol / 1e6)
+
+
 def bench_quantize(args, nv, torch, W):
     w = W.quantize_weight(device="cuda")
     rows, k = w.shape
@@ -355,7 +380,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "quantize", "gather", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "backward", "quantize", "gather", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -389,6 +414,13 @@ def main():
         for m_, d in res["small"].items():
             log("  m=%d: " % m_ + ", ".join(f"{k_} {v['ms'] * 1e3:.2f} us ({v['gbs']:.0f} GB/s)"
                                             for k_, v in d.items()))
+    if args.only in ("all", "backward"):
+        log("qqmm backward (dx and dw of the prefill shape) ...")
+        res["backward"] = bench_backward(args, nv, torch, W)
+        b = res["backward"]
+        log(f"  {b['ms']:.3f} ms, {b['tflops']:.1f} TFLOP/s; columnwise quantize of w "
+            f"{b['ms_wcol'] * 1e3:.1f} us ({b['wcol_gbs']:.0f} GB/s), columnwise round trip of dy "
+            f"{b['ms_dycol'] * 1e3:.1f} us ({b['dycol_gbs']:.0f} GB/s)")
     if args.only in ("all", "quantize"):
         log("quantize / dequantize ...")
         res["quantize"] = bench_quantize(args, nv, torch, W)
@@ -440,6 +472,14 @@ def main():
             for m_, d in res["small"].items()}
         line["small_batch_qqmm"]["workload"] = ("qqmm x bf16 [m,4096] (round trip in the kernel) "
                                                 "@ NVFP4 w [14336,4096]^T, cold weights")
+    if "backward" in res:
+        b = res["backward"]
+        line["qqmm_backward"] = {
+            "value": round(b["tflops"], 2), "unit": "TFLOP/s", "frac": round(b["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "ms": round(b["ms"], 4), "algorithmic_flop": b["flop"],
+            "columnwise_quantize_w": {"us": round(b["ms_wcol"] * 1e3, 2), "GBps": round(b["wcol_gbs"], 1)},
+            "columnwise_round_trip_dy": {"us": round(b["ms_dycol"] * 1e3, 2), "GBps": round(b["dycol_gbs"], 1)},
+            "workload": "vjp of qqmm x bf16 [2048,4096] @ w [14336,4096]^T: dx and dw for dy [2048,14336]"}
     if "quantize" in res:
         line["quantize"] = {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["frac"], 4),
                                  "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}

@@ -183,6 +183,60 @@ nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* global_scale_w, int64_t m, int64_t n,
                        int64_t k, void* out, hipStream_t stream);
 
+/* ---------------------------------------------------------------- backward
+ *
+ * nvfp4_quantize_columnwise -- quantize x [rows, cols] (row-major) along its
+ * first axis, i.e. encode the transpose x^T [cols, rows] row by row: the
+ * pages' columnwise quantize of an M-major tensor ("mlx 0.30.7.2 ->
+ * 0.30.7.6" diff page 7, fp_quantize_columnwise), with the same per-group
+ * arithmetic as nvfp4_quantize.
+ *   x            device [rows, cols] of type dt, 16-byte aligned
+ *   codes        device uint8 [cols, rows/2], 8-byte aligned, written
+ *   scales       device uint8 [cols, rows/16], written
+ * Errors: rows not a multiple of 16, cols not a multiple of 8 (16-bit) or 4
+ * (float32), NULL pointer, misalignment, bad dtype.
+ */
+nvfp4_status nvfp4_quantize_columnwise(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                       const float* global_scale, uint8_t* codes, uint8_t* scales,
+                                       hipStream_t stream);
+
+/*
+ * nvfp4_quant_dequant_columnwise -- the NVFP4 round trip of x^T: writes
+ * xhat_t [cols, rows] of type dt, the dequantized nvfp4_quantize_columnwise
+ * (what nvfp4_quant_dequant gives for the transpose).  xhat_t 16-byte
+ * aligned; errors as nvfp4_quantize_columnwise.
+ */
+nvfp4_status nvfp4_quant_dequant_columnwise(const void* x, nvfp4_dtype dt, int64_t rows,
+                                            int64_t cols, const float* global_scale, void* xhat_t,
+                                            hipStream_t stream);
+
+/*
+ * nvfp4_qqmm_vjp -- gradients of y = qqmm(x, w) for the cotangent dy
+ * ("mlx 0.30.7.2 -> 0.30.7.6" diff page 8, primitives.cpp QQMatmul::vjp):
+ *   g_dy = float32(max |dy|) when the global scales are given (none otherwise)
+ *   dx [m, k] = qqmm(dy, w^T): dy round-tripped under g_dy, w^T [k, n]
+ *               quantized along n under g_w;
+ *   dw [n, k] = qqmm(dy^T, x^T): dy^T round-tripped along m under g_dy, x^T
+ *               [k, m] quantized along m under g_x;
+ * float32 accumulation, outputs of type dt (the gradients of the global
+ * scales are zero and not produced).  Every step runs on the matrix-core or
+ * small-batch contraction kernels of nvfp4_qqmm / nvfp4_qmm.
+ *   x [m, k], w [n, k], dy [m, n]   device, type dt, 16-byte aligned
+ *   global_scale_x, global_scale_w  device floats, both or neither
+ *   dx, dw          device outputs; either may be NULL (not computed), not both
+ *   dy_amax         device float written with g_dy, or NULL
+ *   workspace       device, nvfp4_qqmm_vjp_workspace_size() bytes, 256-byte
+ *                   aligned; its contents afterwards are scratch
+ * Errors: m, n or k not a positive multiple of 16 (each is the quantized
+ * dimension of an operand), exactly one global scale, NULL or misaligned
+ * pointers, workspace too small, bad dtype.
+ */
+size_t nvfp4_qqmm_vjp_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt);
+nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_dtype dt,
+                            const float* global_scale_x, const float* global_scale_w, int64_t m,
+                            int64_t n, int64_t k, void* dx, void* dw, float* dy_amax,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * nvfp4_gather_qmm_workspace_size -- bytes of device workspace
  * nvfp4_gather_qmm needs (routing tables: expert offsets and the token order).

@@ -72,6 +72,10 @@ def load_library():
         "nvfp4_qqmm_packed": (I, [P, I, P, P, P, P, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_qmm_packed": (I, [P, I, P, P, P, I64, I64, I64, P, P]),
         "nvfp4_gather_qmm_packed": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_quantize_columnwise": (I, [P, I, I64, I64, P, P, P, P]),
+        "nvfp4_quant_dequant_columnwise": (I, [P, I, I64, I64, P, P, P]),
+        "nvfp4_qqmm_vjp_workspace_size": (SZ, [I64, I64, I64, I]),
+        "nvfp4_qqmm_vjp": (I, [P, P, P, I, P, P, I64, I64, I64, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -185,6 +189,72 @@ def nvfp4_quant_dequant(x, global_scale=None, out=None):
     _check(L.nvfp4_quant_dequant(_ptr(x), _dtype_code(x, "x"), rows, k, _ptr(g), _ptr(out),
                                  _stream()))
     return out
+
+
+# ------------------------------------------------------------------ backward
+
+def _rows_cols(x):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    return x.shape[0], x.shape[1]
+
+
+def nvfp4_quantize_columnwise(x, global_scale=None, codes=None, scales=None):
+    """Quantize x [rows, cols] along its first axis (the encode of x^T):
+    codes [cols, rows/2], scales [cols, rows/16]."""
+    L = load_library()
+    _dev(x, "x")
+    rows, cols = _rows_cols(x)
+    g = _gscale(global_scale, "global_scale")
+    if codes is None:
+        codes = torch.empty(cols, rows // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(cols, rows // 16, dtype=torch.uint8, device=x.device)
+    _check(L.nvfp4_quantize_columnwise(_ptr(x), _dtype_code(x, "x"), rows, cols, _ptr(g),
+                                       _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def nvfp4_quant_dequant_columnwise(x, global_scale=None, out=None):
+    """The NVFP4 round trip of x^T: [cols, rows] of x's dtype."""
+    L = load_library()
+    _dev(x, "x")
+    rows, cols = _rows_cols(x)
+    g = _gscale(global_scale, "global_scale")
+    if out is None:
+        out = torch.empty(cols, rows, dtype=x.dtype, device=x.device)
+    _check(L.nvfp4_quant_dequant_columnwise(_ptr(x), _dtype_code(x, "x"), rows, cols, _ptr(g),
+                                            _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_qqmm_vjp(x, w, dy, global_scale_x=None, global_scale_w=None, want_dx=True,
+                   want_dw=True, workspace=None):
+    """Gradients of y = nvfp4_qqmm(x, w) for the cotangent dy [m, n]:
+    returns (dx [m, k] or None, dw [n, k] or None, g_dy (device float, or
+    None without global scales))."""
+    L = load_library()
+    for t, name in ((x, "x"), (w, "w"), (dy, "dy")):
+        _dev(t, name)
+    m, k = _rows_cols(x)
+    n = w.shape[0]
+    if w.shape != (n, k) or dy.shape != (m, n):
+        raise ValueError(f"[qqmm_vjp] shapes x {tuple(x.shape)}, w {tuple(w.shape)}, dy {tuple(dy.shape)}")
+    if not (x.dtype == w.dtype == dy.dtype):
+        raise ValueError("[qqmm_vjp] x, w and dy must share one dtype")
+    gx, gw = _gscale(global_scale_x, "global_scale_x"), _gscale(global_scale_w, "global_scale_w")
+    dt = _dtype_code(x, "x")
+    dx = torch.empty(m, k, dtype=x.dtype, device=x.device) if want_dx else None
+    dw = torch.empty(n, k, dtype=x.dtype, device=x.device) if want_dw else None
+    gdy = torch.empty(1, dtype=torch.float32, device=x.device) if gx is not None else None
+    if workspace is None:
+        nbytes = L.nvfp4_qqmm_vjp_workspace_size(m, n, k, dt)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_qqmm_vjp(_ptr(x), _ptr(w), _ptr(dy), dt, _ptr(gx), _ptr(gw), m, n, k,
+                            _ptr(dx), _ptr(dw), _ptr(gdy), _ptr(workspace), nbytes, _stream()))
+    return dx, dw, gdy
 
 
 # ------------------------------------------------------------------ contractions

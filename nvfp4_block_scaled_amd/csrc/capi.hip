@@ -288,6 +288,170 @@ nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
                                                out, stream));
 }
 
+// ------------------------------------------------------------------ backward
+
+static nvfp4_status check_colwise(const char* op, const void* x, nvfp4_dtype dt, int64_t rows,
+                                  int64_t cols) {
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] Unsupported dtype code %d (float32, float16 and bfloat16 only).", op, (int)dt);
+  if (rows < 0 || rows % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] The quantized dimension (rows, %lld) must be a non-negative multiple of the "
+                "group size 16.", op, (long long)rows);
+  const int64_t cq = dt == NVFP4_F32 ? 4 : 8;
+  if (cols < 0 || cols % cq != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] cols (%lld) must be a non-negative multiple of %lld.",
+                op, (long long)cols, (long long)cq);
+  if (rows > INT32_MAX || cols > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Sizes too large.", op);
+  if (rows > 0 && cols > 0 && (x == nullptr || !aligned(x, 16)))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] input must be non-NULL and 16-byte aligned.", op);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_quantize_columnwise(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                       const float* global_scale, uint8_t* codes, uint8_t* scales,
+                                       hipStream_t stream) {
+  const char* op = "quantize_columnwise";
+  if (nvfp4_status st = check_colwise(op, x, dt, rows, cols)) return st;
+  if (rows > 0 && cols > 0) {
+    CHECK_PTR("quantize_columnwise", codes);
+    CHECK_PTR("quantize_columnwise", scales);
+    if (!aligned(codes, 8))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quantize_columnwise] codes must be 8-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0 || cols == 0) return ok();
+  return launched(op, nvfp4::launch_quantize_colwise(x, dt, rows, cols, global_scale, codes, scales,
+                                                     stream));
+}
+
+nvfp4_status nvfp4_quant_dequant_columnwise(const void* x, nvfp4_dtype dt, int64_t rows,
+                                            int64_t cols, const float* global_scale, void* xhat_t,
+                                            hipStream_t stream) {
+  const char* op = "quant_dequant_columnwise";
+  if (nvfp4_status st = check_colwise(op, x, dt, rows, cols)) return st;
+  if (rows > 0 && cols > 0 && (xhat_t == nullptr || !aligned(xhat_t, 16)))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[quant_dequant_columnwise] xhat_t must be non-NULL and 16-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0 || cols == 0) return ok();
+  return launched(op, nvfp4::launch_quant_dequant_colwise(x, dt, rows, cols, global_scale, xhat_t,
+                                                          stream));
+}
+
+// Workspace of the vjp, each region 256-byte aligned: the cotangent's amax,
+// w^T's codes and scales, dy_hat [m, n] (for dx), dy^T_hat [n, m] (for dw),
+// x^T's codes and scales.
+namespace {
+struct VjpLayout {
+  size_t g, wc, ws, dyh, dyth, xc, xs, total;
+};
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+VjpLayout vjp_layout(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt) {
+  VjpLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  L.g = take(sizeof(float));
+  L.wc = take((size_t)k * (size_t)n / 2);
+  L.ws = take((size_t)k * (size_t)n / 16);
+  L.dyh = take((size_t)m * (size_t)n * dtype_size(dt));
+  L.dyth = take((size_t)n * (size_t)m * dtype_size(dt));
+  L.xc = take((size_t)k * (size_t)m / 2);
+  L.xs = take((size_t)k * (size_t)m / 16);
+  L.total = off;
+  return L;
+}
+
+// out [rows, cols] = x_hat @ w^T over kc, x_hat the round trip of x under gx
+// (quantize_x) or x itself; w given as codes [cols, kc/2] and scales.
+hipError_t contract(const void* x, nvfp4_dtype dt, bool quantize_x, const float* gx,
+                    const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t rows,
+                    int64_t cols, int64_t kc, void* out, void* xhat_ws, hipStream_t s) {
+  if (nvfp4::small_m_ok(dt, false, rows, cols, kc))
+    return nvfp4::launch_small_m(x, dt, quantize_x, gx, wc, ws, false, gw, rows, cols, kc, out, s);
+  const void* a = x;
+  if (quantize_x) {
+    hipError_t e = nvfp4::launch_quant_dequant(x, dt, rows, kc, gx, xhat_ws, s);
+    if (e != hipSuccess) return e;
+    a = xhat_ws;
+  }
+  return nvfp4::launch_qqmm_gemm(a, dt, wc, ws, gw, rows, cols, kc, out, s);
+}
+}  // namespace
+
+size_t nvfp4_qqmm_vjp_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt) {
+  if (m <= 0 || n <= 0 || k <= 0 || !dtype_ok(dt)) return 0;
+  return vjp_layout(m, n, k, dt).total;
+}
+
+nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_dtype dt,
+                            const float* global_scale_x, const float* global_scale_w, int64_t m,
+                            int64_t n, int64_t k, void* dx, void* dw, float* dy_amax,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "qqmm_vjp";
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[qqmm_vjp] Unsupported dtype code %d (float32, float16 and bfloat16 only).", (int)dt);
+  if (m <= 0 || n <= 0 || k <= 0 || m % 16 != 0 || n % 16 != 0 || k % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[qqmm_vjp] m (%lld), n (%lld) and k (%lld) must be positive multiples of 16: each is "
+                "the quantized dimension of one operand.", (long long)m, (long long)n, (long long)k);
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX || m * n > (int64_t)1 << 46 ||
+      n * k > (int64_t)1 << 46 || m * k > (int64_t)1 << 46)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[qqmm_vjp] Sizes too large.");
+  if ((global_scale_x == nullptr) != (global_scale_w == nullptr))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[qqmm_vjp] For nvfp4 mode, either both global_scale_x and global_scale_w must be "
+                "provided, or neither.");
+  CHECK_PTR("qqmm_vjp", dy);
+  if (!dx && !dw) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_vjp] dx and dw are both NULL.");
+  if (dw) CHECK_PTR("qqmm_vjp", x);
+  if (dx) CHECK_PTR("qqmm_vjp", w);
+  if ((x && !aligned(x, 16)) || (w && !aligned(w, 16)) || !aligned(dy, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_vjp] x, w and dy must be 16-byte aligned.");
+  const VjpLayout L = vjp_layout(m, n, k, dt);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[qqmm_vjp] workspace of %zu bytes is smaller than %zu or not 256-byte aligned.",
+                workspace_bytes, L.total);
+  if (nvfp4_status st = check_device(op)) return st;
+  char* base = reinterpret_cast<char*>(workspace);
+  const bool has_g = global_scale_x != nullptr;
+  // the cotangent's global scale: its amax as float32 (none without global scales)
+  float* gdy = nullptr;
+  if (has_g) {
+    gdy = dy_amax ? dy_amax : reinterpret_cast<float*>(base + L.g);
+    if (hipError_t e = nvfp4::launch_tensor_amax(dy, dt, m * n, gdy, stream)) return launched(op, e);
+  }
+  uint8_t* wc = reinterpret_cast<uint8_t*>(base + L.wc);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(base + L.ws);
+  uint8_t* xc = reinterpret_cast<uint8_t*>(base + L.xc);
+  uint8_t* xs = reinterpret_cast<uint8_t*>(base + L.xs);
+  if (dx) {
+    // dx = qqmm(dy, w^T): w^T [k, n] quantized along n under g_w
+    if (hipError_t e = nvfp4::launch_quantize_colwise(w, dt, n, k, global_scale_w, wc, ws, stream))
+      return launched(op, e);
+    if (hipError_t e = contract(dy, dt, true, gdy, wc, ws, global_scale_w, m, k, n, dx,
+                                base + L.dyh, stream))
+      return launched(op, e);
+  }
+  if (dw) {
+    // dw = qqmm(dy^T, x^T): dy^T round-tripped along m under g_dy, x^T [k, m]
+    // quantized along m under g_x
+    void* dyth = base + L.dyth;
+    if (hipError_t e = nvfp4::launch_quant_dequant_colwise(dy, dt, m, n, gdy, dyth, stream))
+      return launched(op, e);
+    if (hipError_t e = nvfp4::launch_quantize_colwise(x, dt, m, k, global_scale_x, xc, xs, stream))
+      return launched(op, e);
+    if (hipError_t e = contract(dyth, dt, false, nullptr, xc, xs, global_scale_x, n, k, m, dw,
+                                nullptr, stream))
+      return launched(op, e);
+  }
+  return ok();
+}
+
 size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
                                        int64_t k) {
   (void)n;

@@ -170,6 +170,91 @@ quantize_kernel(const void* __restrict__ x, int64_t halves, const float* __restr
   }
 }
 
+// ------------------------------------------------------------------ columnwise
+//
+// Quantize x [R, C] (row-major) along its first axis: the encode of the
+// transpose, groups of 16 consecutive rows of one column, written as codes
+// [C, R/2] and scales [C, R/16] (MODE 0) or as x_hat of the transpose [C, R]
+// in the input type (MODE 1) -- the pages' columnwise quantize of an M-major
+// tensor ("mlx 0.30.7.2 -> 0.30.7.6" diff page 7, fp_quantize_columnwise),
+// used by the backward of qqmm.  The arithmetic per group is the rowwise one.
+//
+// Tile: 256 rows x 64 columns through LDS; loads of 16 bytes, 8 (16-bit) or
+// 4 (float32) columns each, coalesced along rows.  Wave w then takes groups
+// 4w .. 4w + 3 (tile rows 64w .. 64w + 63) of every column, lane = column,
+// reading one tile row per LDS instruction (64 consecutive values).
+constexpr int kColRows = 256, kColCols = 64;
+
+template <int DT, int MODE>
+__global__ void __launch_bounds__(kThreads)
+quantize_colwise_kernel(const void* __restrict__ x, int R, int C, const float* __restrict__ gscale,
+                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                        void* __restrict__ xhat_t) {
+  using T = typename Elem<DT>::T;
+  constexpr int kPerChunk = 16 / (int)sizeof(T);          // columns per 16-byte load
+  constexpr int kChunksPerRow = kColCols / kPerChunk;
+  __shared__ __attribute__((aligned(16))) T tile[kColRows][kColCols];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.y * kColRows, c0 = blockIdx.x * kColCols;
+
+  // load: chunk q = row q / kChunksPerRow, columns kPerChunk * (q % kChunksPerRow) ..
+  for (int q = tid; q < kColRows * kChunksPerRow; q += kThreads) {
+    const int r = q / kChunksPerRow, cc = kPerChunk * (q % kChunksPerRow);
+    if (r0 + r < R && c0 + cc < C)  // C % 8 == 0 (16-bit) or % 4 == 0: chunks are whole
+      *reinterpret_cast<u32x4*>(&tile[r][cc]) =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const T*>(x) + (int64_t)(r0 + r) * C + c0 + cc));
+  }
+  __syncthreads();
+
+  const int c = c0 + lane;
+  if (c >= C) return;
+  const float enc = global_encode(gscale);
+  const float dec = global_decode(gscale);
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    const int g = 4 * wave + gi;  // group within the tile
+    const int rg = r0 + 16 * g;   // its first row
+    if (rg >= R) break;           // R % 16 == 0: groups are whole
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = to_f32<DT>(tile[16 * g + i][lane]);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
+    const float(&lo)[8] = *reinterpret_cast<const float(*)[8]>(v);
+    const float(&hi)[8] = *reinterpret_cast<const float(*)[8]>(v + 8);
+    uint32_t byte;
+    const uint32_t w0 = encode_half_group(lo, a, enc, byte);
+    const uint32_t w1 = encode_half_group(hi, a, enc, byte);
+    if constexpr (MODE == 0) {
+      *reinterpret_cast<u32x2*>(codes + (int64_t)c * (R / 2) + rg / 2) = u32x2{w0, w1};
+      scales[(int64_t)c * (R / 16) + rg / 16] = (uint8_t)byte;
+    } else {
+      float sc;
+      {
+#pragma clang fp contract(off)
+        sc = e4m3_decode(byte) * dec;
+      }
+      float q0[8], q1[8], o[16];
+      e2m1_decode8_f32(w0, q0);
+      e2m1_decode8_f32(w1, q1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+        o[i] = q0[i] * sc;
+        o[8 + i] = q1[i] * sc;
+      }
+      T* dst = reinterpret_cast<T*>(xhat_t) + (int64_t)c * R + rg;
+      const float(&o0)[8] = *reinterpret_cast<const float(*)[8]>(o);
+      const float(&o1)[8] = *reinterpret_cast<const float(*)[8]>(o + 8);
+      store8<DT>(dst, 0, o0);
+      store8<DT>(dst, 1, o1);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dequantize
 
 template <int DT>
@@ -263,6 +348,35 @@ hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t k, const
 hipError_t launch_quant_dequant(const void* x, int dt, int64_t rows, int64_t k, const float* g,
                                 void* xhat, hipStream_t s) {
   return launch_quantize_mode<1>(x, dt, rows, k, g, nullptr, nullptr, xhat, s);
+}
+
+template <int MODE>
+static hipError_t launch_colwise_mode(const void* x, int dt, int64_t R, int64_t C, const float* g,
+                                      uint8_t* codes, uint8_t* scales, void* xhat_t, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + kColCols - 1) / kColCols), (unsigned)((R + kColRows - 1) / kColRows));
+  switch (dt) {
+    case kF32:
+      quantize_colwise_kernel<kF32, MODE><<<grid, kThreads, 0, s>>>(x, (int)R, (int)C, g, codes, scales, xhat_t);
+      break;
+    case kF16:
+      quantize_colwise_kernel<kF16, MODE><<<grid, kThreads, 0, s>>>(x, (int)R, (int)C, g, codes, scales, xhat_t);
+      break;
+    default:
+      quantize_colwise_kernel<kBF16, MODE><<<grid, kThreads, 0, s>>>(x, (int)R, (int)C, g, codes, scales, xhat_t);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_colwise(const void* x, int dt, int64_t rows, int64_t cols, const float* g,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  return launch_colwise_mode<0>(x, dt, rows, cols, g, codes, scales, nullptr, s);
+}
+
+hipError_t launch_quant_dequant_colwise(const void* x, int dt, int64_t rows, int64_t cols,
+                                        const float* g, void* xhat_t, hipStream_t s) {
+  return launch_colwise_mode<1>(x, dt, rows, cols, g, nullptr, nullptr, xhat_t, s);
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,

@@ -17,6 +17,13 @@ hipError_t launch_quant_dequant(const void* x, int dt, int64_t rows, int64_t k, 
                                 void* xhat, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                              const float* g, void* out, int dt, hipStream_t s);
+// quantize x [rows, cols] along rows (the transpose's encode): codes
+// [cols, rows/2] and scales [cols, rows/16], or x_hat of the transpose
+// [cols, rows]; rows % 16 == 0, cols % 8 == 0 (16-bit) / % 4 == 0 (float32)
+hipError_t launch_quantize_colwise(const void* x, int dt, int64_t rows, int64_t cols, const float* g,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_dequant_colwise(const void* x, int dt, int64_t rows, int64_t cols,
+                                        const float* g, void* xhat_t, hipStream_t s);
 
 // qmv.hip
 constexpr int64_t kQmvMaxK = 32768;

@@ -192,3 +192,38 @@ def test_packed_matmul_errors(L):
     bad = list(gok)
     bad[13] = gws - 4
     assert L.nvfp4_gather_qmm_packed(*bad) == INV and "workspace" in err(L)
+
+
+def test_columnwise_errors(L):
+    q = L.nvfp4_quantize_columnwise
+    assert q(A, BF16, 24, 16, None, B, C, None) == INV and "group size 16" in err(L)
+    assert q(A, BF16, 32, 12, None, B, C, None) == INV and "multiple of 8" in err(L)
+    assert q(A, F32, 32, 12, None, B, C, None) == UNSUP  # float32 needs cols % 4 only
+    assert q(A, BF16, 32, 16, None, B + 4, C, None) == INV and "aligned" in err(L)
+    assert q(None, BF16, 32, 16, None, B, C, None) == INV
+    assert q(A, BF16, 32, 16, None, B, C, None) == UNSUP
+    qd = L.nvfp4_quant_dequant_columnwise
+    assert qd(A, F16, 32, 16, None, None, None) == INV
+    assert qd(A, F16, 32, 16, None, C + 8, None) == INV
+    assert qd(A, F16, 32, 16, None, C, None) == UNSUP
+
+
+def test_vjp_errors(L):
+    ws = L.nvfp4_qqmm_vjp_workspace_size(32, 64, 48, BF16)
+    assert ws % 256 == 0 and ws >= 64 * 48 // 2 + 32 * 64 * 2 * 2 + 48 * 32 // 2
+    D = 0x70000
+    vjp = L.nvfp4_qqmm_vjp
+    ok = (A, W, B, BF16, G, G, 32, 64, 48, C, D, None, 0x80000, ws, None)
+    assert vjp(*ok) == UNSUP
+    bad_m = ok[:6] + (24,) + ok[7:]
+    assert vjp(*bad_m) == INV and "multiples of 16" in err(L)
+    one_g = ok[:4] + (G, None) + ok[6:]
+    assert vjp(*one_g) == INV and "both global_scale_x and global_scale_w" in err(L)
+    none_out = ok[:9] + (None, None) + ok[11:]
+    assert vjp(*none_out) == INV and "both NULL" in err(L)
+    small_ws = ok[:13] + (ws - 1,) + ok[14:]
+    assert vjp(*small_ws) == INV and "workspace" in err(L)
+    # dx alone needs no x, dw alone no w
+    assert vjp(None, W, B, BF16, G, G, 32, 64, 48, C, None, None, 0x80000, ws, None) == UNSUP
+    assert vjp(A, None, B, BF16, G, G, 32, 64, 48, None, D, None, 0x80000, ws, None) == UNSUP
+    assert vjp(None, W, B, BF16, G, G, 32, 64, 48, C, D, None, 0x80000, ws, None) == INV
