@@ -182,8 +182,13 @@ quantize_kernel(const void* __restrict__ x, int64_t halves, const float* __restr
 // Tile: 256 rows x 64 columns through LDS; loads of 16 bytes, 8 (16-bit) or
 // 4 (float32) columns each, coalesced along rows.  Wave w then takes groups
 // 4w .. 4w + 3 (tile rows 64w .. 64w + 63) of every column, lane = column,
-// reading one tile row per LDS instruction (64 consecutive values).
+// reading one tile row per LDS instruction (64 consecutive values).  The
+// outputs of the tile (per column: 128 code bytes and 16 scale bytes, or 256
+// values of x_hat) are staged in LDS and leave as 16-byte chunks along the
+// output rows, so that each store instruction writes whole row segments.
 constexpr int kColRows = 256, kColCols = 64;
+constexpr int kCodeStride = kColRows / 2 + 8;  // staged code bytes per column (+8: banks)
+constexpr int kXhStride = kColRows + 8;        // staged x_hat values per column (+8: banks)
 
 template <int DT, int MODE>
 __global__ void __launch_bounds__(kThreads)
@@ -193,33 +198,37 @@ quantize_colwise_kernel(const void* __restrict__ x, int R, int C, const float* _
   using T = typename Elem<DT>::T;
   constexpr int kPerChunk = 16 / (int)sizeof(T);          // columns per 16-byte load
   constexpr int kChunksPerRow = kColCols / kPerChunk;
-  __shared__ __attribute__((aligned(16))) T tile[kColRows][kColCols];
+  constexpr int kTileElems = kColRows * kColCols > kColCols * kXhStride ? kColRows * kColCols
+                                                                         : kColCols * kXhStride;
+  __shared__ __attribute__((aligned(16))) T buf[kTileElems];  // input tile, then staged x_hat
+  __shared__ __attribute__((aligned(16))) uint8_t code_st[MODE == 0 ? kColCols * kCodeStride : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t scale_st[MODE == 0 ? kColCols * 16 : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r0 = blockIdx.y * kColRows, c0 = blockIdx.x * kColCols;
+  const int rows_here = min(kColRows, R - r0);  // a multiple of 16
+  const int cols_here = min(kColCols, C - c0);
 
-  // load: chunk q = row q / kChunksPerRow, columns kPerChunk * (q % kChunksPerRow) ..
+  // load: chunk q = tile row q / kChunksPerRow, columns kPerChunk * (q % kChunksPerRow) ..
   for (int q = tid; q < kColRows * kChunksPerRow; q += kThreads) {
     const int r = q / kChunksPerRow, cc = kPerChunk * (q % kChunksPerRow);
-    if (r0 + r < R && c0 + cc < C)  // C % 8 == 0 (16-bit) or % 4 == 0: chunks are whole
-      *reinterpret_cast<u32x4*>(&tile[r][cc]) =
+    if (r < rows_here && cc < cols_here)  // C % 8 == 0 (16-bit) or % 4 == 0: chunks are whole
+      *reinterpret_cast<u32x4*>(&buf[r * kColCols + cc]) =
           __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
               reinterpret_cast<const T*>(x) + (int64_t)(r0 + r) * C + c0 + cc));
   }
   __syncthreads();
 
-  const int c = c0 + lane;
-  if (c >= C) return;
   const float enc = global_encode(gscale);
   const float dec = global_decode(gscale);
+  T xh[4][16];
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
     const int g = 4 * wave + gi;  // group within the tile
-    const int rg = r0 + 16 * g;   // its first row
-    if (rg >= R) break;           // R % 16 == 0: groups are whole
+    if (16 * g >= rows_here || lane >= cols_here) break;
     float v[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = to_f32<DT>(tile[16 * g + i][lane]);
+    for (int i = 0; i < 16; ++i) v[i] = to_f32<DT>(buf[(16 * g + i) * kColCols + lane]);
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, __builtin_fabsf(v[i]));
@@ -229,28 +238,81 @@ quantize_colwise_kernel(const void* __restrict__ x, int R, int C, const float* _
     const uint32_t w0 = encode_half_group(lo, a, enc, byte);
     const uint32_t w1 = encode_half_group(hi, a, enc, byte);
     if constexpr (MODE == 0) {
-      *reinterpret_cast<u32x2*>(codes + (int64_t)c * (R / 2) + rg / 2) = u32x2{w0, w1};
-      scales[(int64_t)c * (R / 16) + rg / 16] = (uint8_t)byte;
+      *reinterpret_cast<u32x2*>(&code_st[lane * kCodeStride + 8 * g]) = u32x2{w0, w1};
+      scale_st[lane * 16 + g] = (uint8_t)byte;
     } else {
       float sc;
       {
 #pragma clang fp contract(off)
         sc = e4m3_decode(byte) * dec;
       }
-      float q0[8], q1[8], o[16];
+      float q0[8], q1[8];
       e2m1_decode8_f32(w0, q0);
       e2m1_decode8_f32(w1, q1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
 #pragma clang fp contract(off)
-        o[i] = q0[i] * sc;
-        o[8 + i] = q1[i] * sc;
+        xh[gi][i] = from_f32<DT>(q0[i] * sc);
+        xh[gi][8 + i] = from_f32<DT>(q1[i] * sc);
       }
-      T* dst = reinterpret_cast<T*>(xhat_t) + (int64_t)c * R + rg;
-      const float(&o0)[8] = *reinterpret_cast<const float(*)[8]>(o);
-      const float(&o1)[8] = *reinterpret_cast<const float(*)[8]>(o + 8);
-      store8<DT>(dst, 0, o0);
-      store8<DT>(dst, 1, o1);
+    }
+  }
+  __syncthreads();  // every wave is done reading the input tile
+
+  if constexpr (MODE == 0) {
+    // codes of output row c0 + j: 16 * (rows_here / 16) * 8 / 16 chunks of 16 bytes
+    const int chunks = rows_here / 32;       // 16-byte chunks per output row (rows_here % 32 may be 16)
+    const bool half = (rows_here % 32) != 0;  // a last 8-byte piece
+    for (int q = tid; q < kColCols * 8; q += kThreads) {
+      const int j = q / 8, ch = q % 8;
+      if (j >= cols_here) continue;
+      uint8_t* dst = codes + (int64_t)(c0 + j) * (R / 2) + r0 / 2 + 16 * ch;
+      const uint8_t* src = &code_st[j * kCodeStride + 16 * ch];
+      if (ch < chunks) {
+        // staged rows are 8-byte aligned (stride 136): read the chunk as two halves
+        const u32x2 a2 = reinterpret_cast<const u32x2*>(src)[0];
+        const u32x2 b2 = reinterpret_cast<const u32x2*>(src)[1];
+        if (((R / 2) & 15) == 0) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{a2.x, a2.y, b2.x, b2.y};
+        } else {
+          reinterpret_cast<u32x2*>(dst)[0] = a2;
+          reinterpret_cast<u32x2*>(dst)[1] = b2;
+        }
+      } else if (ch == chunks && half) {
+        *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<const u32x2*>(src);
+      }
+    }
+    // scales of output row c0 + j: rows_here / 16 bytes
+    if (tid < cols_here) {
+      const int j = tid;
+      uint8_t* dst = scales + (int64_t)(c0 + j) * (R / 16) + r0 / 16;
+      const uint8_t* src = &scale_st[j * 16];
+      if (rows_here == kColRows && ((R / 16) & 15) == 0)
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      else
+        for (int i = 0; i < rows_here / 16; ++i) dst[i] = src[i];
+    }
+  } else {
+    // stage x_hat: column lane, tile rows 16 g .. 16 g + 15
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int g = 4 * wave + gi;
+      if (16 * g >= rows_here || lane >= cols_here) break;
+      typedef T T8 __attribute__((ext_vector_type(8)));
+      T8 a8, b8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { a8[i] = xh[gi][i]; b8[i] = xh[gi][8 + i]; }
+      *reinterpret_cast<T8*>(&buf[lane * kXhStride + 16 * g]) = a8;
+      *reinterpret_cast<T8*>(&buf[lane * kXhStride + 16 * g + 8]) = b8;
+    }
+    __syncthreads();
+    // output row c0 + j: rows_here values in chunks of kPerChunk
+    constexpr int kChunksOut = kColRows / kPerChunk;
+    for (int q = tid; q < kColCols * kChunksOut; q += kThreads) {
+      const int j = q / kChunksOut, ch = q % kChunksOut;
+      if (j >= cols_here || kPerChunk * ch >= rows_here) continue;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(xhat_t) + (int64_t)(c0 + j) * R + r0 + kPerChunk * ch) =
+          *reinterpret_cast<const u32x4*>(&buf[j * kXhStride + kPerChunk * ch]);
     }
   }
 }

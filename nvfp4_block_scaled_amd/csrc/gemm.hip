@@ -1021,8 +1021,12 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
                        hipStream_t s) {
   // up to 128 rows (routed pairs) the 128-row tiles skip the half of a
   // 256-row tile that would multiply padding; above that the 256-row tiles
-  // are faster (each weight element is decoded for twice as many rows)
-  if (rows <= 128)
+  // are faster (each weight element is decoded for twice as many rows),
+  // unless they are too few to give every CU a tile (a long k and few output
+  // columns, as in the backward's dx): then the 128-row tiles double the
+  // tile count.  Both compute every output element in the same order.
+  const int64_t tiles8 = ((rows + 255) / 256) * ((n + BN - 1) / BN);
+  if (rows <= 128 || (!GATHER && tiles8 < device_cu_count()))
     return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
                                              top_k, e, s);
   return launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,

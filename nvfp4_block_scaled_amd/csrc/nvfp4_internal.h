@@ -55,6 +55,9 @@ hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, c
                                      int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
                                      void* out, hipStream_t s);
 
+// compute units of the current device (cached per device)
+int device_cu_count();
+
 // smallm.hip: 1 <= m <= kSmallMaxM rows of x, 16-bit x, k % 128 == 0, with x
 // and its padding in LDS (m (k + 8) 2 bytes plus 7 KB within kSmallMaxLds)
 // and the weight's codes below 2 GB

@@ -404,19 +404,6 @@ smallm_pk_kernel(const void* __restrict__ x, const float* __restrict__ gx,
 
 // ---------------------------------------------------------------- launch
 
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 // LDS of a launch: the x rows and the k-part partial sums
 size_t rm_lds(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(k + 8) * 2 + (size_t)(kSmWaves - 1) * 64 * sizeof(f32x4);
@@ -484,6 +471,19 @@ hipError_t launch_small_q(int dt, const void* x, const float* gx, const uint8_t*
 }
 
 }  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
 
 bool small_m_ok(int dt, bool packed, int64_t m, int64_t n, int64_t k) {
   return (dt == kF16 || dt == kBF16) && m >= 1 && m <= kSmallMaxM && k % kSmChunk == 0 &&
