@@ -54,8 +54,8 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "44ead79dc070dff4", 367329054),
-    "qmv": ("qmv.hip", "82774d58538ec6ac", 33246753),
+    "gemm": ("gemm.hip", "27b1cade469aca21", 367356734),
+    "qmv": ("qmv.hip", "fc4ed5b793f7bb53", 33246692),
 }
 
 
