@@ -18,6 +18,9 @@
  *   [PR31]    osaurus-ai/mlx pull request 31 (CPU qqmm ignores nvfp4 global
  *             scales): sections "What fails", "The test", "The fix",
  *             "Verification".
+ *   [PR1772]  the pull request referenced from [PR4458]'s page, "fix(mlx):
+ *             bump MLX pin to 81ba1c6a so mxfp8 block scales round up"
+ *             (lablup/mlxcel 1772): sections "Why" and "Validation".
  *
  * Arithmetic rules (each restated where it is used):
  *   - every step the pages perform in float32 is done here in float32 with
@@ -42,6 +45,22 @@
  *   R6  decode factor is g/2688 everywhere ([DIFF-8] fp_dequantize fallback).
  *   R7  the global decode factor multiplies the block scale, not the sum
  *       ([PR4458] statement; [PR31] "The fix").
+ *   R19 mx modes ([DIFF-8] fp_quantize / fp_dequantize: group size 32 outside
+ *       nvfp4, 8 bits for mxfp8, 4 otherwise, scales converted to e8m0 and
+ *       decoded as 2^(s - 127); validate_global_scale: no global scale
+ *       outside nvfp4): mxfp4 = e2m1 codes packed as R1, mxfp8 = one e4m3
+ *       byte per element, one E8M0 byte per 32 consecutive elements.
+ *   R20 the E8M0 block scale is the smallest power of two >= amax / maxval
+ *       (maxval 6 or 448, the division in float32), clamped to the E8M0
+ *       range [2^-127, 2^127] ([PR1772] "Why": rounding log2 to nearest
+ *       saturated block maxima, the CUDA conversion rounds up).
+ *   R21 the element encode of R4 with enc = 1: enc_b = 1 / float(s), then
+ *       e2m1 / e4m3 of x * enc_b (R2, R5).
+ *   R22 decode T(value(q) * 2^(s - 127)); the product is exact in float32.
+ *   R23 mx qqmm: both operands go through their mx encode and the products
+ *       of the decoded values are summed without rounding either operand to
+ *       T first (the pages hand both operands' codes and scales to a
+ *       block-scaled product); only the sum is rounded to T.
  */
 #include <math.h>
 #include <stdint.h>
@@ -59,6 +78,7 @@
 #define MUT_GW_ON_SUM 3      /* (iii) g_w/2688 applied to a T-precision sum      */
 #define MUT_AMAX6_BF16 4     /* (iv)  amax/6 rounded to bfloat16 before * enc    */
 #define MUT_ENC_ORDER 5      /* (v)   q = e2m1((x*enc)/sf) instead of x*(enc/sf) */
+#define MUT_E8M0_NEAREST 6   /* (vi)  mx block scale rounded to nearest, not up  */
 
 static int g_mutant = MUT_NONE;
 
@@ -406,4 +426,150 @@ int orc_moe_route(const int32_t* idx, int64_t t_count, int64_t top_k, int64_t e_
     for (int64_t p = 0; p < total; ++p)
       if (idx[p] == e) perm[pos++] = (int32_t)p;
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MX modes: mxfp4 / mxfp8 (readings R19-R23)                               */
+/* ------------------------------------------------------------------------ */
+
+/* E8M0 (OCP Microscaling v1.0 scale type): byte b is 2^(b - 127); 0xFF is
+ * NaN.  No sign, no mantissa, no zero. */
+double orc_e8m0_value(unsigned b) {
+  if ((b & 0xFFu) == 0xFFu) return NAN;
+  return ldexp(1.0, (int)(b & 0xFFu) - 127);
+}
+
+/* Round-up conversion of v >= 0 to E8M0 (reading R20): the smallest byte b
+ * in 0..254 with 2^(b - 127) >= v, found by search over the bytes; values
+ * above 2^127 clamp to 254. */
+unsigned orc_e8m0_encode_up(float v) {
+  for (unsigned b = 0; b <= 254; ++b)
+    if (orc_e8m0_value(b) >= (double)v) return b;
+  return 254;
+}
+
+/* Value of a code of the mx element type: e2m1 (bits 4) or e4m3 (bits 8). */
+static double mx_code_value(unsigned q, int bits) {
+  return bits == 8 ? orc_e4m3_value(q) : orc_e2m1_value(q);
+}
+
+/* Encode one group of 32 contiguous values (readings R20, R21): the block
+ * amax, its float32 quotient by maxval rounded up to an E8M0 scale s, the
+ * encode factor 1/float(s), and each element's code of x * enc_b.  Writes 32
+ * codes and returns the scale byte. */
+static unsigned mx_encode_group(const float* xb, int bits, unsigned* q) {
+  float amax = 0.0f;
+  for (int i = 0; i < 32; ++i) {
+    float a = fabsf(xb[i]);
+    if (a > amax) amax = a;
+  }
+  volatile float maxval = bits == 8 ? 448.0f : 6.0f;
+  volatile float sd = amax / maxval;
+  unsigned s = orc_e8m0_encode_up(sd);
+  if (g_mutant == MUT_E8M0_NEAREST) {
+    /* the rejected encode: 2^round(log2(amax / maxval)), ties away */
+    s = sd > 0.0f ? (unsigned)lround(log2((double)sd) + 127.0) : 0u;
+  }
+  volatile float sf = (float)orc_e8m0_value(s);
+  float enc_b = 1.0f / sf;
+  for (int i = 0; i < 32; ++i) {
+    float y = xb[i] * enc_b;
+    q[i] = bits == 8 ? orc_e4m3_encode(y) : orc_e2m1_encode(y);
+  }
+  return s;
+}
+
+static int64_t mx_row_bytes(int64_t k, int bits) { return bits == 8 ? k : k / 2; }
+
+static unsigned mx_code_at(const uint8_t* codes_row, int64_t i, int bits) {
+  return bits == 8 ? (unsigned)codes_row[i] : code_at(codes_row, i);
+}
+
+/* mx quantize: x [rows, k] (k % 32 == 0) -> codes [rows, k/2] (mxfp4, R1
+ * nibble order) or [rows, k] (mxfp8), E8M0 scales [rows, k/32]
+ * ([DIFF-8] fp_quantize; [DIFF-7] fp_quantize_rowwise with use_mx_scale). */
+void orc_mx_quantize(const float* x, int64_t rows, int64_t k, int bits, uint8_t* codes,
+                     uint8_t* scales) {
+  unsigned q[32];
+  int64_t rb = mx_row_bytes(k, bits);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < k / 32; ++b) {
+      scales[r * (k / 32) + b] = (uint8_t)mx_encode_group(x + r * k + b * 32, bits, q);
+      uint8_t* out = codes + r * rb + (bits == 8 ? b * 32 : b * 16);
+      if (bits == 8)
+        for (int j = 0; j < 32; ++j) out[j] = (uint8_t)q[j];
+      else
+        for (int j = 0; j < 16; ++j) out[j] = (uint8_t)(q[2 * j] | (q[2 * j + 1] << 4));
+    }
+  }
+}
+
+/* Decoded value of element i of a quantized mx row in float32 (exact,
+ * reading R22). */
+static float mx_value(const uint8_t* codes_row, const uint8_t* scales_row, int64_t i, int bits) {
+  return (float)(mx_code_value(mx_code_at(codes_row, i, bits), bits) *
+                 orc_e8m0_value(scales_row[i / 32]));
+}
+
+/* mx dequantize: T(value(q) * 2^(s - 127)) ([DIFF-8] fp_dequantize: e8m0
+ * scales decoded as a power of two; reading R22). */
+void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                       int bits, int out_dtype, float* out) {
+  int64_t rb = mx_row_bytes(k, bits);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < k; ++i)
+      out[r * k + i] = orc_round_to(mx_value(codes + r * rb, scales + r * (k / 32), i, bits),
+                                    out_dtype);
+}
+
+/* mx quant_dequant: the encode then the decode, result in type T
+ * ([DIFF-7] fp_quantize_dequantize with use_mx_scale). */
+void orc_mx_quant_dequant(const float* x, int64_t rows, int64_t k, int bits, int dtype,
+                          float* xhat) {
+  unsigned q[32];
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < k / 32; ++b) {
+      unsigned s = mx_encode_group(x + r * k + b * 32, bits, q);
+      double sc = orc_e8m0_value(s);
+      for (int i = 0; i < 32; ++i)
+        xhat[r * k + b * 32 + i] = orc_round_to((float)(mx_code_value(q[i], bits) * sc), dtype);
+    }
+  }
+}
+
+/* mx qqmm / qmv on a subset of the output (rows mi of x, columns ni of w):
+ * out = T( sum_k x_hat[m, k] * w_hat[n, k] ), with x_hat the float32 decode
+ * of x's own mx encode and w_hat that of the given codes and scales, summed
+ * in double (reading R23; [DIFF-8] qqmm, where the mode selects the group
+ * size and scale type for both operands). */
+void orc_mx_qqmm_subset(const float* x, int dtype, int64_t m, int64_t k, int bits,
+                        const uint8_t* wcodes, const uint8_t* wscales, int64_t n,
+                        const int64_t* mi, int64_t nm, const int64_t* ni, int64_t nn, float* out,
+                        int nthreads) {
+  (void)m;
+  (void)n;
+  int64_t rb = mx_row_bytes(k, bits);
+  float* xh = (float*)malloc(sizeof(float) * (size_t)(nm * k));
+  float* wr = (float*)malloc(sizeof(float) * (size_t)(nn * k));
+  uint8_t* xc = (uint8_t*)malloc((size_t)rb);
+  uint8_t* xs = (uint8_t*)malloc((size_t)(k / 32));
+  for (int64_t a = 0; a < nm; ++a) {
+    orc_mx_quantize(x + mi[a] * k, 1, k, bits, xc, xs);
+    for (int64_t i = 0; i < k; ++i) xh[a * k + i] = mx_value(xc, xs, i, bits);
+  }
+  for (int64_t b = 0; b < nn; ++b)
+    for (int64_t i = 0; i < k; ++i)
+      wr[b * k + i] = mx_value(wcodes + ni[b] * rb, wscales + ni[b] * (k / 32), i, bits);
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+  for (int64_t a = 0; a < nm; ++a) {
+    for (int64_t b = 0; b < nn; ++b) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < k; ++i) acc += (double)xh[a * k + i] * (double)wr[b * k + i];
+      out[a * nn + b] = orc_round_to((float)acc, dtype);
+    }
+  }
+  free(xh);
+  free(wr);
+  free(xc);
+  free(xs);
 }

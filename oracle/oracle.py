@@ -20,6 +20,9 @@ MUT_DROP_GX = 2
 MUT_GW_ON_SUM = 3
 MUT_AMAX6_BF16 = 4
 MUT_ENC_ORDER = 5
+MUT_E8M0_NEAREST = 6
+
+MX_BITS = {"mxfp4": 4, "mxfp8": 8}
 
 _lib = None
 _P = ctypes.c_void_p
@@ -62,6 +65,19 @@ def lib():
                                             _P, _I64, _P, _P, _I64, _P, _I64, _P, _INT]
         L.orc_moe_route.restype = _INT
         L.orc_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [ctypes.c_uint]
+        L.orc_e8m0_encode_up.restype = ctypes.c_uint
+        L.orc_e8m0_encode_up.argtypes = [_F]
+        L.orc_mx_quantize.restype = None
+        L.orc_mx_quantize.argtypes = [_P, _I64, _I64, _INT, _P, _P]
+        L.orc_mx_dequantize.restype = None
+        L.orc_mx_dequantize.argtypes = [_P, _P, _I64, _I64, _INT, _INT, _P]
+        L.orc_mx_quant_dequant.restype = None
+        L.orc_mx_quant_dequant.argtypes = [_P, _I64, _I64, _INT, _INT, _P]
+        L.orc_mx_qqmm_subset.restype = None
+        L.orc_mx_qqmm_subset.argtypes = [_P, _INT, _I64, _I64, _INT, _P, _P, _I64, _P, _I64,
+                                         _P, _I64, _P, _INT]
         L.orc_set_mutant.restype = None
         L.orc_set_mutant.argtypes = [_INT]
         L.orc_get_mutant.restype = _INT
@@ -270,7 +286,85 @@ def qqmm_vjp(x, w, dy, global_scale_x=None, global_scale_w=None, dtype="bf16", n
     return dx, dw, g_dy
 
 
+# ----------------------------------------------------------------- mx modes
+
+def _bits(mode):
+    if mode not in MX_BITS:
+        raise ValueError(f"mx mode must be 'mxfp4' or 'mxfp8', not {mode!r}")
+    return MX_BITS[mode]
+
+
+def e8m0_value(b):
+    return lib().orc_e8m0_value(int(b))
+
+
+def e8m0_encode_up(v):
+    return lib().orc_e8m0_encode_up(float(v))
+
+
+def mx_code_bytes(k, mode):
+    """Bytes of one quantized row of k elements."""
+    return k if _bits(mode) == 8 else k // 2
+
+
+def mx_quantize(x, mode):
+    """x [rows, k] (k % 32 == 0) -> (codes uint8 [rows, k/2] for mxfp4 or [rows, k]
+    for mxfp8, E8M0 scales uint8 [rows, k/32])."""
+    bits = _bits(mode)
+    x = _f32(x)
+    rows, k = x.shape
+    assert k % 32 == 0
+    codes = np.empty((rows, mx_code_bytes(k, mode)), np.uint8)
+    scales = np.empty((rows, k // 32), np.uint8)
+    lib().orc_mx_quantize(_ptr(x), rows, k, bits, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mx_dequantize(codes, scales, mode, dtype="bf16"):
+    bits = _bits(mode)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows = codes.shape[0]
+    k = scales.shape[1] * 32
+    assert codes.shape[1] == mx_code_bytes(k, mode)
+    out = np.empty((rows, k), np.float32)
+    lib().orc_mx_dequantize(_ptr(codes), _ptr(scales), rows, k, bits, _dt(dtype), _ptr(out))
+    return out
+
+
+def mx_quant_dequant(x, mode, dtype="bf16"):
+    bits = _bits(mode)
+    x = _f32(x)
+    rows, k = x.shape
+    assert k % 32 == 0
+    out = np.empty((rows, k), np.float32)
+    lib().orc_mx_quant_dequant(_ptr(x), rows, k, bits, _dt(dtype), _ptr(out))
+    return out
+
+
+def mx_qqmm(x, w_codes, w_scales, mode, dtype="bf16", rows=None, cols=None, nthreads=None):
+    """out[rows][:, cols] of T(x_hat @ w_hat^T) in an mx mode: x goes through
+    its own mx encode, w is given quantized; products of the float32 decodes
+    summed in double, one rounding to T."""
+    bits = _bits(mode)
+    x = _f32(x)
+    m, k = x.shape
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    w_scales = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    n = w_codes.shape[0]
+    assert w_codes.shape[1] == mx_code_bytes(k, mode) and w_scales.shape[1] * 32 == k
+    mi = np.arange(m, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    ni = np.arange(n, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+    out = np.empty((mi.size, ni.size), np.float32)
+    lib().orc_mx_qqmm_subset(_ptr(x), _dt(dtype), m, k, bits, _ptr(w_codes), _ptr(w_scales), n,
+                             _ptr(mi), mi.size, _ptr(ni), ni.size, _ptr(out),
+                             int(nthreads or default_threads()))
+    return out
+
+
 __all__ = [
+    "MUT_E8M0_NEAREST", "MX_BITS", "e8m0_value", "e8m0_encode_up", "mx_code_bytes",
+    "mx_quantize", "mx_dequantize", "mx_quant_dequant", "mx_qqmm",
     "F32", "F16", "BF16", "MUT_NONE", "MUT_DROP_GW", "MUT_DROP_GX", "MUT_GW_ON_SUM",
     "MUT_AMAX6_BF16", "MUT_ENC_ORDER", "mutant", "quantize_columnwise", "quant_dequant_columnwise",
     "qqmm_vjp", "e2m1_value", "e2m1_encode", "e4m3_value",
