@@ -348,6 +348,113 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
                                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The mx modes: mxfp4 and mxfp8 ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8,
+ * fp_quantize / fp_dequantize: group size 32 outside nvfp4, 8 bits for mxfp8
+ * and 4 otherwise, scales converted to E8M0 and decoded as 2^(s - 127);
+ * validate_global_scale: no global scale outside nvfp4).
+ *
+ * Format of a quantized tensor [rows, k], k a multiple of 32:
+ *   codes   mxfp4: [rows, k/2], e2m1, element 2j in the low nibble of byte j;
+ *           mxfp8: [rows, k], one e4m3 byte per element
+ *   scales  [rows, k/32], one E8M0 byte per 32 consecutive elements of a row
+ * Encode per group of 32 (page 7, fp_quantize_rowwise with use_mx_scale):
+ * the group amax, s = the smallest power of two >= amax / maxval (maxval 6 or
+ * 448; the float32 quotient rounded UP, clamped to 2^-127 .. 2^127 -- the pull
+ * request referenced from the "[Metal] global scale for qmm" page, "mxfp8
+ * block scales round up", section "Why"), then each code the nearest value
+ * (ties to even, saturating) of x * 2^-s.  Decode T(value(code) * 2^s),
+ * exact in float32 before the rounding to T.
+ */
+typedef enum { NVFP4_MXFP4 = 4, NVFP4_MXFP8 = 8 } nvfp4_mx_mode;
+
+/*
+ * nvfp4_mx_quantize -- codes and scales of x [rows, k] in an mx mode.
+ *   x        device [rows, k] of type dt, 16-byte aligned
+ *   codes    device, written, 16-byte aligned; scales device, written
+ * Errors: bad dtype or mode, rows < 0, k not a positive multiple of 32, NULL
+ * or misaligned pointer (rows > 0).
+ */
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode, int64_t rows,
+                               int64_t k, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * nvfp4_mx_dequantize -- T(value(code) * 2^(s - 127)) as [rows, k] of out_dt
+ * (16-byte aligned); the codes 16-byte aligned.  Errors as nvfp4_mx_quantize.
+ */
+nvfp4_status nvfp4_mx_dequantize(const uint8_t* codes, const uint8_t* scales, nvfp4_mx_mode mode,
+                                 int64_t rows, int64_t k, void* out, nvfp4_dtype out_dt,
+                                 hipStream_t stream);
+
+/*
+ * nvfp4_mx_quant_dequant -- the round trip of x in x's type (page 7,
+ * fp_quantize_dequantize with use_mx_scale); x_hat 16-byte aligned.
+ */
+nvfp4_status nvfp4_mx_quant_dequant(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                    int64_t rows, int64_t k, void* x_hat, hipStream_t stream);
+
+/*
+ * Packed mx operands for the block-scaled matrix-core product (gfx950's
+ * v_mfma_scale_f32_32x32x64_f8f6f4 consumes the codes and E8M0 scales
+ * directly).  Rows in tiles of 32; k in steps of 64, the step count padded to
+ * a multiple of 4.  For tile T and step s, P = 2 (mxfp4) or 4 (mxfp8) blocks
+ * of 512 bytes; block p holds bytes 16p .. 16p + 15 of the step's row-major
+ * codes of rows 32T .. 32T + 31, in row order.  For tile T and quad q of
+ * steps, a 256-byte scale block whose byte 4l + j is the scale of row
+ * 32T + l % 32, group 2 (4q + j) + l / 32.  Blocks in (T, s) / (T, q) order;
+ * padding rows and steps are zero.
+ */
+
+/*
+ * nvfp4_mx_pack_size -- bytes of the packed codes and scales of a [rows, k]
+ * mx operand.  Errors: NULL pointer, bad mode, rows <= 0, k not a positive
+ * multiple of 32 (the outputs are then 0).
+ */
+nvfp4_status nvfp4_mx_pack_size(nvfp4_mx_mode mode, int64_t rows, int64_t k, size_t* codes_bytes,
+                                size_t* scales_bytes);
+
+/*
+ * nvfp4_mx_pack -- write the packed copy of row-major mx codes and scales.
+ * codes and packed_codes 16-byte aligned.  Errors as nvfp4_mx_pack_size, NULL
+ * or misaligned pointers.
+ */
+nvfp4_status nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, nvfp4_mx_mode mode,
+                           int64_t rows, int64_t k, uint8_t* packed_codes, uint8_t* packed_scales,
+                           hipStream_t stream);
+
+/*
+ * nvfp4_mx_qqmm_workspace_size -- bytes of workspace nvfp4_mx_qqmm (packed_w
+ * = 0) or nvfp4_mx_qqmm_packed (packed_w = 1) needs: x's packed codes and
+ * scales, and for a row-major weight its packed copy, each 256-byte aligned.
+ * 0 for invalid sizes.
+ */
+size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k,
+                                    int packed_w);
+
+/*
+ * nvfp4_mx_qqmm -- out [m, n] = T( sum_k x_hat[m, k] * w_hat[n, k] ) in an mx
+ * mode: x [m, k] of type dt (float32, float16, bfloat16) is quantized in the
+ * same mode (page 8, qqmm: the mode selects both operands' group size and
+ * scale type), w is given quantized [n, k]; the products of the two decodes
+ * are exact in float32 and summed in float32 by the matrix cores; out of
+ * type dt.  nvfp4_mx_qqmm_packed takes the weight as its packed copy.
+ *   x        device, 16-byte aligned
+ *   w_codes  device, 16-byte aligned (row-major) / packed copy
+ *   out      device [m, n], 16-byte aligned
+ *   workspace  device, nvfp4_mx_qqmm_workspace_size() bytes, 256-byte aligned
+ * Errors: bad dtype or mode, m, n <= 0, k not a positive multiple of 32, NULL
+ * or misaligned pointer, workspace too small, operands too large (a packed
+ * operand of 2 GB or more).
+ */
+nvfp4_status nvfp4_mx_qqmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t m, int64_t n,
+                           int64_t k, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                  const uint8_t* packed_codes, const uint8_t* packed_scales,
+                                  int64_t m, int64_t n, int64_t k, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Test hook: treat every device as having this gcnArchName (NULL restores the
  * real query).  Lets host-only tests reach the unsupported-device error.
  */

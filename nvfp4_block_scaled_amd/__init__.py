@@ -19,6 +19,8 @@ The functions carry the C entry points' names (see include/nvfp4.h):
     nvfp4_mfma_pack(w_codes, w_scales)                -> MfmaPacked (packed copy)
     nvfp4_qqmm_packed / nvfp4_qmm_packed / nvfp4_gather_qmm_packed
                                                       (same, on the packed copy)
+    nvfp4_mx_quantize / _dequantize / _quant_dequant / _pack / _qqmm / _qqmm_packed
+                                                      (the mxfp4 / mxfp8 modes)
 Global scales are float32 device tensors with one element (per expert: e
 elements, any shape such as [e, 1, 1]), as the pages' validate_global_scale
 requires ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8).
@@ -76,6 +78,14 @@ def load_library():
         "nvfp4_quant_dequant_columnwise": (I, [P, I, I64, I64, P, P, P]),
         "nvfp4_qqmm_vjp_workspace_size": (SZ, [I64, I64, I64, I]),
         "nvfp4_qqmm_vjp": (I, [P, P, P, I, P, P, I64, I64, I64, P, P, P, P, SZ, P]),
+        "nvfp4_mx_quantize": (I, [P, I, I, I64, I64, P, P, P]),
+        "nvfp4_mx_dequantize": (I, [P, P, I, I64, I64, P, I, P]),
+        "nvfp4_mx_quant_dequant": (I, [P, I, I, I64, I64, P, P]),
+        "nvfp4_mx_pack_size": (I, [I, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+        "nvfp4_mx_pack": (I, [P, P, I, I64, I64, P, P, P]),
+        "nvfp4_mx_qqmm_workspace_size": (SZ, [I, I64, I64, I64, I]),
+        "nvfp4_mx_qqmm": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_mx_qqmm_packed": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -467,27 +477,183 @@ def nvfp4_gather_qmm_packed(x, w, expert_idx, global_scale_w=None, out=None, wor
     return out
 
 
+# ------------------------------------------------------------------ mx modes
+
+MX_MODES = {"mxfp4": 4, "mxfp8": 8}
+
+
+def _mx_mode(mode):
+    if mode not in MX_MODES:
+        raise ValueError(f"mx mode must be 'mxfp4' or 'mxfp8', not {mode!r}")
+    return MX_MODES[mode]
+
+
+def _mx_code_cols(k, mode):
+    return k if MX_MODES[mode] == 8 else k // 2
+
+
+def nvfp4_mx_quantize(x, mode, codes=None, scales=None):
+    """(codes uint8 [..., k/2] (mxfp4) or [..., k] (mxfp8), E8M0 scales uint8 [..., k/32])."""
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(x, "x")
+    rows, k = _rows_k(x)
+    if codes is None:
+        codes = torch.empty(tuple(x.shape[:-1]) + (_mx_code_cols(k, mode),), dtype=torch.uint8,
+                            device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]) + (k // 32,), dtype=torch.uint8, device=x.device)
+    _check(L.nvfp4_mx_quantize(_ptr(x), _dtype_code(x, "x"), bits, rows, k, _ptr(codes), _ptr(scales),
+                               _stream()))
+    return codes, scales
+
+
+def nvfp4_mx_dequantize(codes, scales, mode, dtype=torch.bfloat16, out=None):
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(codes, "codes")
+    _dev(scales, "scales")
+    k = scales.shape[-1] * 32
+    if codes.shape[-1] != _mx_code_cols(k, mode) or codes.shape[:-1] != scales.shape[:-1]:
+        raise ValueError("codes and scales describe different shapes")
+    rows = scales.numel() // scales.shape[-1] if scales.shape[-1] else 0
+    if out is None:
+        out = torch.empty(tuple(codes.shape[:-1]) + (k,), dtype=dtype, device=codes.device)
+    _check(L.nvfp4_mx_dequantize(_ptr(codes), _ptr(scales), bits, rows, k, _ptr(out),
+                                 _dtype_code(out, "out"), _stream()))
+    return out
+
+
+def nvfp4_mx_quant_dequant(x, mode, out=None):
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(x, "x")
+    rows, k = _rows_k(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(L.nvfp4_mx_quant_dequant(_ptr(x), _dtype_code(x, "x"), bits, rows, k, _ptr(out), _stream()))
+    return out
+
+
+class MxPacked:
+    """The packed copy of an mx weight [rows, k] for the block-scaled
+    matrix-core product: flat uint8 device tensors in the order include/nvfp4.h
+    describes."""
+
+    def __init__(self, codes, scales, shape, mode):
+        self.codes, self.scales, self.shape, self.mode = codes, scales, tuple(shape), mode
+
+    @property
+    def k(self):
+        return self.shape[-1]
+
+
+def nvfp4_mx_pack(w_codes, w_scales, mode):
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    k = w_scales.shape[-1] * 32
+    if w_codes.shape[-1] != _mx_code_cols(k, mode) or w_codes.shape[:-1] != w_scales.shape[:-1]:
+        raise ValueError("w_codes and w_scales describe different shapes")
+    rows = w_scales.numel() // w_scales.shape[-1]
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(L.nvfp4_mx_pack_size(bits, rows, k, ctypes.byref(cb), ctypes.byref(sb)))
+    pc = torch.empty(cb.value, dtype=torch.uint8, device=w_codes.device)
+    ps = torch.empty(sb.value, dtype=torch.uint8, device=w_codes.device)
+    _check(L.nvfp4_mx_pack(_ptr(w_codes), _ptr(w_scales), bits, rows, k, _ptr(pc), _ptr(ps),
+                           _stream()))
+    return MxPacked(pc, ps, tuple(w_codes.shape[:-1]) + (k,), mode)
+
+
+def mx_qqmm_workspace(mode, m, n, k, packed_w, device):
+    nbytes = load_library().nvfp4_mx_qqmm_workspace_size(_mx_mode(mode), m, n, k, int(bool(packed_w)))
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
+
+
+def nvfp4_mx_qqmm(x, w_codes, w_scales, mode, out=None, workspace=None):
+    """out [m, n] = x_hat @ w_hat^T in an mx mode (x quantized in the kernel
+    path; w given quantized, row-major)."""
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(x, "x")
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    if x.dim() > 2 or w_codes.dim() != 2:
+        raise ValueError("[qqmm] Only 2D inputs are supported.")
+    m, k = x.shape if x.dim() == 2 else (1, x.shape[0])
+    n = w_codes.shape[0]
+    if w_scales.shape != (n, k // 32) or w_codes.shape[1] != _mx_code_cols(k, mode):
+        raise ValueError("w_codes / w_scales do not match x's inner size")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = mx_qqmm_workspace(mode, m, n, k, False, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_mx_qqmm(_ptr(x), _dtype_code(x, "x"), bits, _ptr(w_codes), _ptr(w_scales), m, n, k,
+                           _ptr(out), _ptr(workspace), nbytes, _stream()))
+    return out
+
+
+def nvfp4_mx_qqmm_packed(x, w, out=None, workspace=None):
+    """nvfp4_mx_qqmm with w an MxPacked [n, k]."""
+    L = load_library()
+    bits = _mx_mode(w.mode)
+    _dev(x, "x")
+    if x.dim() > 2 or len(w.shape) != 2:
+        raise ValueError("[qqmm] Only 2D inputs are supported.")
+    m, k = x.shape if x.dim() == 2 else (1, x.shape[0])
+    n = w.shape[0]
+    if w.k != k:
+        raise ValueError(f"weights of inner size {w.k} do not match x's {k}")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (n,), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = mx_qqmm_workspace(w.mode, m, n, k, True, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_mx_qqmm_packed(_ptr(x), _dtype_code(x, "x"), bits, _ptr(w.codes), _ptr(w.scales), m,
+                                  n, k, _ptr(out), _ptr(workspace), nbytes, _stream()))
+    return out
+
+
 # ------------------------------------------------------------------ MLX-style names
 
-def _mode_check(group_size, bits, mode):
-    if mode != "nvfp4" or group_size not in (None, 16) or bits not in (None, 4):
-        raise ValueError("[quantize] only mode='nvfp4' with group_size=16 and bits=4 is supported")
+def _mode_check(group_size, bits, mode, global_scales=()):
+    """The pages' mode table: nvfp4 = group 16, bits 4; mxfp4 = 32, 4; mxfp8 =
+    32, 8; global scales only with nvfp4 ("mlx 0.30.7.2 -> 0.30.7.6" diff page
+    8, fp_quantize and validate_global_scale)."""
+    want = {"nvfp4": (16, 4), "mxfp4": (32, 4), "mxfp8": (32, 8)}
+    if mode not in want:
+        raise ValueError(f"[quantize] unsupported mode {mode!r} (nvfp4, mxfp4, mxfp8)")
+    gs, b = want[mode]
+    if group_size not in (None, gs) or bits not in (None, b):
+        raise ValueError(f"[quantize] mode {mode!r} needs group_size={gs} and bits={b}")
+    if mode != "nvfp4" and any(g is not None for g in global_scales):
+        raise ValueError("[quantize] Global scale is only supported for 'nvfp4' quantization mode.")
 
 
 def quantize(w, group_size=None, bits=None, mode="nvfp4", global_scale=None):
-    _mode_check(group_size, bits, mode)
+    _mode_check(group_size, bits, mode, (global_scale,))
+    if mode != "nvfp4":
+        return nvfp4_mx_quantize(w, mode)
     return nvfp4_quantize(w, global_scale)
 
 
 def dequantize(w, scales, group_size=None, bits=None, mode="nvfp4", global_scale=None,
                dtype=torch.bfloat16):
-    _mode_check(group_size, bits, mode)
+    _mode_check(group_size, bits, mode, (global_scale,))
+    if mode != "nvfp4":
+        return nvfp4_mx_dequantize(w, scales, mode, dtype)
     return nvfp4_dequantize(w, scales, global_scale, dtype)
 
 
 def qqmm(x, w, scales, group_size=None, bits=None, mode="nvfp4", global_scale_x=None,
          global_scale_w=None):
-    _mode_check(group_size, bits, mode)
+    _mode_check(group_size, bits, mode, (global_scale_x, global_scale_w))
+    if mode != "nvfp4":
+        return nvfp4_mx_qqmm(x, w, scales, mode)
     return nvfp4_qqmm(x, w, scales, global_scale_x, global_scale_w)
 
 
@@ -499,4 +665,6 @@ __all__ = [
     "load_library", "NVFP4Error", "nvfp4_tensor_amax", "nvfp4_quantize", "nvfp4_dequantize",
     "nvfp4_quant_dequant", "nvfp4_qmv", "nvfp4_qqmm", "nvfp4_qmm", "nvfp4_gather_qmm", "nvfp4_moe_route",
     "qqmm_workspace", "gather_workspace", "quantize", "dequantize", "qqmm", "gather_qmm",
+    "MX_MODES", "MxPacked", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_quant_dequant",
+    "nvfp4_mx_pack", "mx_qqmm_workspace", "nvfp4_mx_qqmm", "nvfp4_mx_qqmm_packed",
 ]

@@ -657,4 +657,206 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
                                                        n, k, out, stream));
 }
 
+// ------------------------------------------------------------------ mx modes
+
+static bool mx_mode_ok(int mode) { return mode == NVFP4_MXFP4 || mode == NVFP4_MXFP8; }
+
+static nvfp4_status check_mx(const char* op, const void* x, nvfp4_dtype dt, int mode, int64_t rows,
+                             int64_t k) {
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] Unsupported dtype code %d (float32, float16 and bfloat16 only).", op, (int)dt);
+  if (!mx_mode_ok(mode))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] Unsupported mx mode %d (4: mxfp4, 8: mxfp8).", op,
+                mode);
+  if (rows < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] rows (%lld) must be >= 0.", op, (long long)rows);
+  if (k <= 0 || k % 32 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[%s] The last dimension (%lld) must be a positive multiple of the group size 32.",
+                op, (long long)k);
+  if (rows > 0 && x == nullptr) return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] input must not be NULL.", op);
+  if (rows > 0 && !aligned(x, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] input must be 16-byte aligned.", op);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode, int64_t rows,
+                               int64_t k, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const char* op = "mx_quantize";
+  if (nvfp4_status st = check_mx(op, x, dt, mode, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("mx_quantize", codes);
+    CHECK_PTR("mx_quantize", scales);
+    if (!aligned(codes, 16))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quantize] codes must be 16-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_mx_quantize(x, dt, mode, rows, k, codes, scales, stream));
+}
+
+nvfp4_status nvfp4_mx_dequantize(const uint8_t* codes, const uint8_t* scales, nvfp4_mx_mode mode,
+                                 int64_t rows, int64_t k, void* out, nvfp4_dtype out_dt,
+                                 hipStream_t stream) {
+  const char* op = "mx_dequantize";
+  if (nvfp4_status st = check_mx(op, out, out_dt, mode, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("mx_dequantize", codes);
+    CHECK_PTR("mx_dequantize", scales);
+    if (!aligned(codes, 16))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_dequantize] codes must be 16-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_mx_dequantize(codes, scales, mode, rows, k, out, out_dt, stream));
+}
+
+nvfp4_status nvfp4_mx_quant_dequant(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                    int64_t rows, int64_t k, void* x_hat, hipStream_t stream) {
+  const char* op = "mx_quant_dequant";
+  if (nvfp4_status st = check_mx(op, x, dt, mode, rows, k)) return st;
+  if (rows > 0) {
+    CHECK_PTR("mx_quant_dequant", x_hat);
+    if (!aligned(x_hat, 16))
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quant_dequant] x_hat must be 16-byte aligned.");
+  }
+  if (nvfp4_status st = check_device(op)) return st;
+  if (rows == 0) return ok();
+  return launched(op, nvfp4::launch_mx_quant_dequant(x, dt, mode, rows, k, x_hat, stream));
+}
+
+nvfp4_status nvfp4_mx_pack_size(nvfp4_mx_mode mode, int64_t rows, int64_t k, size_t* codes_bytes,
+                                size_t* scales_bytes) {
+  CHECK_PTR("mx_pack_size", codes_bytes);
+  CHECK_PTR("mx_pack_size", scales_bytes);
+  *codes_bytes = 0;
+  *scales_bytes = 0;
+  if (!mx_mode_ok(mode))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_pack_size] Unsupported mx mode %d (4: mxfp4, 8: mxfp8).",
+                (int)mode);
+  if (rows <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_pack_size] rows (%lld) must be positive.", (long long)rows);
+  if (k <= 0 || k % 32 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mx_pack_size] k (%lld) must be a positive multiple of 32.", (long long)k);
+  *codes_bytes = nvfp4::mx_packed_code_bytes(rows, k, mode);
+  *scales_bytes = nvfp4::mx_packed_scale_bytes(rows, k);
+  return ok();
+}
+
+nvfp4_status nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, nvfp4_mx_mode mode,
+                           int64_t rows, int64_t k, uint8_t* packed_codes, uint8_t* packed_scales,
+                           hipStream_t stream) {
+  const char* op = "mx_pack";
+  size_t cb = 0, sb = 0;
+  if (nvfp4_status st = nvfp4_mx_pack_size(mode, rows, k, &cb, &sb)) {
+    g_last_error.replace(0, std::strlen("[mx_pack_size]"), "[mx_pack]");
+    return st;
+  }
+  CHECK_PTR("mx_pack", codes);
+  CHECK_PTR("mx_pack", scales);
+  CHECK_PTR("mx_pack", packed_codes);
+  CHECK_PTR("mx_pack", packed_scales);
+  if (!aligned(codes, 16) || !aligned(packed_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_pack] codes and packed_codes must be 16-byte aligned.");
+  if (rows > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mx_pack] Sizes too large.");
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_mx_pack(codes, scales, mode, rows, k, packed_codes, packed_scales,
+                                            stream));
+}
+
+namespace {
+// workspace of the mx contractions: x's packed codes and scales, then (for a
+// row-major weight) the weight's packed codes and scales, each 256-aligned
+struct MxLayout {
+  size_t xc, xs, wc, ws, total;
+};
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+MxLayout mx_layout(int mode, int64_t m, int64_t n, int64_t k, bool packed_w) {
+  MxLayout l;
+  l.xc = 0;
+  l.xs = align256(nvfp4::mx_packed_code_bytes(m, k, mode));
+  l.wc = l.xs + align256(nvfp4::mx_packed_scale_bytes(m, k));
+  if (packed_w) {
+    l.ws = l.wc;
+    l.total = l.wc;
+  } else {
+    l.ws = l.wc + align256(nvfp4::mx_packed_code_bytes(n, k, mode));
+    l.total = l.ws + align256(nvfp4::mx_packed_scale_bytes(n, k));
+  }
+  return l;
+}
+}  // namespace
+
+size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k,
+                                    int packed_w) {
+  if (!mx_mode_ok(mode) || m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return 0;
+  return mx_layout(mode, m, n, k, packed_w != 0).total;
+}
+
+static nvfp4_status mx_qqmm_common(const char* op, const void* x, nvfp4_dtype dt, int mode,
+                                   const uint8_t* wc, const uint8_t* ws, int64_t m, int64_t n,
+                                   int64_t k, void* out, void* workspace, size_t workspace_bytes) {
+  if (nvfp4_status st = check_mx(op, x, dt, mode, m, k)) return st;
+  if (m <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] m and n must be positive.", op);
+  if (!x || !wc || !ws || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] x, the weight's codes and scales and out must not be NULL.", op);
+  if (!aligned(wc, 16) || !aligned(out, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] the weight's codes and out must be 16-byte aligned.", op);
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX ||
+      nvfp4::mx_packed_code_bytes(m, k, mode) >= nvfp4::kMxMaxPackedBytes ||
+      nvfp4::mx_packed_code_bytes(n, k, mode) >= nvfp4::kMxMaxPackedBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Sizes too large (a packed operand of 2 GB or more).", op);
+  if (workspace == nullptr || !aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] workspace must be a 256-byte aligned device buffer.", op);
+  (void)workspace_bytes;
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_mx_qqmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t m, int64_t n,
+                           int64_t k, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* op = "mx_qqmm";
+  if (nvfp4_status st =
+          mx_qqmm_common(op, x, dt, mode, w_codes, w_scales, m, n, k, out, workspace, workspace_bytes))
+    return st;
+  const MxLayout l = mx_layout(mode, m, n, k, false);
+  if (workspace_bytes < l.total)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_qqmm] workspace of %zu bytes is smaller than %zu.",
+                workspace_bytes, l.total);
+  if (nvfp4_status st = check_device(op)) return st;
+  uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
+  hipError_t e = nvfp4::launch_mx_pack(w_codes, w_scales, mode, n, k, base + l.wc, base + l.ws, stream);
+  if (e == hipSuccess)
+    e = nvfp4::launch_mx_quantize_packed(x, dt, mode, m, k, base + l.xc, base + l.xs, stream);
+  if (e == hipSuccess)
+    e = nvfp4::launch_mx_gemm(base + l.xc, base + l.xs, base + l.wc, base + l.ws, mode, m, n, k, out,
+                              dt, stream);
+  return launched(op, e);
+}
+
+nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                  const uint8_t* packed_codes, const uint8_t* packed_scales,
+                                  int64_t m, int64_t n, int64_t k, void* out, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "mx_qqmm_packed";
+  if (nvfp4_status st = mx_qqmm_common(op, x, dt, mode, packed_codes, packed_scales, m, n, k, out,
+                                       workspace, workspace_bytes))
+    return st;
+  const MxLayout l = mx_layout(mode, m, n, k, true);
+  if (workspace_bytes < l.total)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mx_qqmm_packed] workspace of %zu bytes is smaller than %zu.", workspace_bytes, l.total);
+  if (nvfp4_status st = check_device(op)) return st;
+  uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
+  hipError_t e = nvfp4::launch_mx_quantize_packed(x, dt, mode, m, k, base + l.xc, base + l.xs, stream);
+  if (e == hipSuccess)
+    e = nvfp4::launch_mx_gemm(base + l.xc, base + l.xs, packed_codes, packed_scales, mode, m, n, k,
+                              out, dt, stream);
+  return launched(op, e);
+}
+
 }  // extern "C"

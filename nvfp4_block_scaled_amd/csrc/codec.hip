@@ -17,49 +17,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Loads 8 consecutive elements of type DT starting at element 8*h.
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t h, float (&v)[8]) {
-  if constexpr (DT == kF32) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * h;
-    f32x4 a = __builtin_nontemporal_load(p);
-    f32x4 b = __builtin_nontemporal_load(p + 1);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + h);
-    uint32_t q[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (DT == kBF16) {
-        v[2 * i] = __uint_as_float(q[i] << 16);
-        v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
-      } else {
-        f16x2 hv = __builtin_bit_cast(f16x2, q[i]);
-        v[2 * i] = (float)hv.x;
-        v[2 * i + 1] = (float)hv.y;
-      }
-    }
-  }
-}
-
-// Stores 8 consecutive elements (already float) as type DT at element 8*h.
-template <int DT>
-__device__ __forceinline__ void store8(void* base, int64_t h, const float (&v)[8]) {
-  if constexpr (DT == kF32) {
-    f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * h;
-    p[0] = f32x4{v[0], v[1], v[2], v[3]};
-    p[1] = f32x4{v[4], v[5], v[6], v[7]};
-  } else {
-    using T = typename Elem<DT>::T;
-    typedef T T8 __attribute__((ext_vector_type(8)));
-    T8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = from_f32<DT>(v[i]);
-    reinterpret_cast<T8*>(base)[h] = o;
-  }
-}
-
 // ------------------------------------------------------------------ amax
 
 constexpr int kAmaxBlocks = 256;    // one workgroup per CU

@@ -263,6 +263,50 @@ __device__ __forceinline__ void load8x(const void* base, int64_t h, float (&v)[8
   }
 }
 
+// Streaming load of 8 consecutive elements of type DT (element 8h ..) as
+// floats (nontemporal: the data is read once).
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t h, float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * h;
+    f32x4 a = __builtin_nontemporal_load(p);
+    f32x4 b = __builtin_nontemporal_load(p + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + h);
+    uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kBF16) {
+        v[2 * i] = __uint_as_float(q[i] << 16);
+        v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+      } else {
+        f16x2 hv = __builtin_bit_cast(f16x2, q[i]);
+        v[2 * i] = (float)hv.x;
+        v[2 * i + 1] = (float)hv.y;
+      }
+    }
+  }
+}
+
+// Store 8 floats as type DT at element 8h.
+template <int DT>
+__device__ __forceinline__ void store8(void* base, int64_t h, const float (&v)[8]) {
+  if constexpr (DT == kF32) {
+    f32x4* p = reinterpret_cast<f32x4*>(base) + 2 * h;
+    p[0] = f32x4{v[0], v[1], v[2], v[3]};
+    p[1] = f32x4{v[4], v[5], v[6], v[7]};
+  } else {
+    using T = typename Elem<DT>::T;
+    typedef T T8 __attribute__((ext_vector_type(8)));
+    T8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = from_f32<DT>(v[i]);
+    reinterpret_cast<T8*>(base)[h] = o;
+  }
+}
+
 // x_hat of one half group (8 values at element 8h), rounded to T, as floats.
 // The pair partner (lane ^ 1) holds the other half of the group.
 template <int DT>
@@ -313,6 +357,41 @@ __device__ __forceinline__ uint32_t decode_dword(uint32_t codes, float se) {
     b = v.y * se;
   }
   return pack2<DT>(a, b);
+}
+
+// ----------------------------------------------------------------- E8M0 (mx modes)
+//
+// The mx modes' block scale: byte b stands for 2^(b - 127), 0xFF for NaN
+// ("mlx 0.30.7.2 -> 0.30.7.6" diff page 8, fp_dequantize fallback).  The
+// encode rounds up: the smallest power of two >= v (the pull request
+// referenced from the "[Metal] global scale for qmm" page, "mxfp8 block
+// scales round up", section "Why"), clamped to 2^-127 .. 2^127.
+
+// v >= 0 (finite): the biased exponent, plus one when any fraction bit is
+// set; 2^-127 and below (zero included) give byte 0.
+__device__ __forceinline__ uint32_t e8m0_encode_up(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if (u <= 0x00400000u) return 0u;
+  const uint32_t b = (u >> 23) + ((u & 0x7FFFFFu) ? 1u : 0u);
+  return b > 254u ? 254u : b;
+}
+
+// 2^(b - 127) for b in 0..254 (2^-127 is the float32 subnormal 0x00400000),
+// NaN for 255.
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return b == 0u ? __uint_as_float(0x00400000u)
+                 : (b == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(b << 23));
+}
+
+// 1 / 2^(b - 127) = 2^(127 - b), exact, for b in 0..254.
+__device__ __forceinline__ float e8m0_inverse(uint32_t b) {
+  return b == 254u ? __uint_as_float(0x00400000u) : __uint_as_float((254u - b) << 23);
+}
+
+// e4m3 code of a float32 of either sign (nearest, ties to even, saturating at
+// +-448, the sign bit kept, also for zero).
+__device__ __forceinline__ uint32_t e4m3_encode_signed(float y) {
+  return e4m3_encode_nonneg(__builtin_fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
 // ----------------------------------------------------------------- buffer resources

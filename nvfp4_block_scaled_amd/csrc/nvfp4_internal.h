@@ -68,4 +68,27 @@ hipError_t launch_small_m(const void* x, int dt, bool quantize_x, const float* g
                           const uint8_t* wc, const uint8_t* ws, bool packed, const float* gw,
                           int64_t m, int64_t n, int64_t k, void* out, hipStream_t s);
 
+// mx_codec.hip / mx_gemm.hip: the mx modes (bits 4 = mxfp4, 8 = mxfp8), k % 32
+// == 0.  Packed operand layout: rows padded to tiles of 32, k to quads of
+// four 64-wide steps (mx_packed_quads quads).
+int64_t mx_packed_quads(int64_t k);
+size_t mx_packed_code_bytes(int64_t rows, int64_t k, int bits);
+size_t mx_packed_scale_bytes(int64_t rows, int64_t k);
+hipError_t launch_mx_quantize(const void* x, int dt, int bits, int64_t rows, int64_t k,
+                              uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_quant_dequant(const void* x, int dt, int bits, int64_t rows, int64_t k,
+                                   void* xhat, hipStream_t s);
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int bits, int64_t rows,
+                                int64_t k, void* out, int dt, hipStream_t s);
+hipError_t launch_mx_quantize_packed(const void* x, int dt, int bits, int64_t rows, int64_t k,
+                                     uint8_t* pc, uint8_t* ps, hipStream_t s);
+hipError_t launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int bits, int64_t rows,
+                          int64_t k, uint8_t* pc, uint8_t* ps, hipStream_t s);
+// y [m, n] of type dt from the packed x (m rows) and w (n rows); the packed
+// operands must be below kMxMaxPackedBytes
+constexpr size_t kMxMaxPackedBytes = 0x7F000000u;
+hipError_t launch_mx_gemm(const uint8_t* xpc, const uint8_t* xps, const uint8_t* wpc,
+                          const uint8_t* wps, int bits, int64_t m, int64_t n, int64_t k, void* out,
+                          int dt, hipStream_t s);
+
 }  // namespace nvfp4

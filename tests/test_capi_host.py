@@ -146,7 +146,50 @@ def test_python_binding_rejects_host_tensors_and_bad_modes():
     with pytest.raises(ValueError):
         nv.quantize(x, group_size=32, mode="nvfp4")
     with pytest.raises(ValueError):
-        nv.quantize(x, mode="mxfp4")
+        nv.quantize(x, mode="mxfp6")
+    with pytest.raises(ValueError):
+        nv.quantize(x, mode="mxfp4", global_scale=torch.ones(1))
+    with pytest.raises(ValueError):
+        nv.quantize(x, group_size=16, mode="mxfp8")
+    with pytest.raises(ValueError):
+        nv.nvfp4_mx_quantize(x, "mxfp4")  # host tensor
+
+
+def test_mx_argument_errors(L):
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    # 100 rows -> 4 tiles; k = 96 -> 2 steps, padded to one quad of 4
+    assert L.nvfp4_mx_pack_size(4, 100, 96, ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 4 * 4 * 2 * 512 and sb.value == 4 * 1 * 256
+    assert L.nvfp4_mx_pack_size(8, 100, 320, ctypes.byref(cb), ctypes.byref(sb)) == 0
+    assert cb.value == 4 * 8 * 4 * 512 and sb.value == 4 * 2 * 256
+    assert L.nvfp4_mx_pack_size(6, 100, 96, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert "mx mode" in err(L) and cb.value == 0
+    assert L.nvfp4_mx_pack_size(4, 100, 48, ctypes.byref(cb), ctypes.byref(sb)) == INV
+    assert "multiple of 32" in err(L)
+    assert L.nvfp4_mx_quantize(A, BF16, 4, 4, 48, B, C, None) == INV and "group size 32" in err(L)
+    assert L.nvfp4_mx_quantize(A, BF16, 5, 4, 64, B, C, None) == INV and "[mx_quantize]" in err(L)
+    assert L.nvfp4_mx_quantize(A + 8, BF16, 8, 4, 64, B, C, None) == INV and "aligned" in err(L)
+    assert L.nvfp4_mx_quantize(A, 7, 8, 4, 64, B, C, None) == INV
+    assert L.nvfp4_mx_quantize(A, BF16, 8, 4, 64, B, C, None) == UNSUP  # validation passed
+    assert L.nvfp4_mx_dequantize(A, B, 4, 4, 64, None, BF16, None) == INV
+    assert L.nvfp4_mx_quant_dequant(A, F16, 4, 4, 64, B + 4, None) == INV and "aligned" in err(L)
+    need = L.nvfp4_mx_qqmm_workspace_size(4, 300, 520, 192, 0)
+    need_p = L.nvfp4_mx_qqmm_workspace_size(4, 300, 520, 192, 1)
+    assert need > need_p > 0 and need % 256 == 0 and need_p % 256 == 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 300, 520, 100, 0) == 0
+    assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 300, 520, 192, G, W, need - 1, None) == INV
+    assert "workspace" in err(L)
+    assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 300, 520, 192, G, W + 16, need, None) == INV
+    assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 0, 520, 192, G, W, need, None) == INV
+    assert L.nvfp4_mx_qqmm(A, BF16, 4, None, C, 300, 520, 192, G, W, need, None) == INV
+    assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 300, 520, 192, G, W, need, None) == UNSUP
+    need_p8 = L.nvfp4_mx_qqmm_workspace_size(8, 300, 520, 192, 1)
+    assert need_p8 > need_p  # mxfp8 codes take twice the bytes
+    assert L.nvfp4_mx_qqmm_packed(A, BF16, 8, B, C, 300, 520, 192, G, W, need_p8 - 1, None) == INV
+    assert L.nvfp4_mx_qqmm_packed(A, BF16, 8, B, C, 300, 520, 192, G, W, need_p8, None) == UNSUP
+    # a packed operand of 2 GB or more is refused before the device
+    assert L.nvfp4_mx_qqmm_packed(A, BF16, 8, B, C, 2048, 1 << 21, 1024, G, W, 1 << 40, None) == UNSUP
+    assert "too large" in err(L)
 
 
 def test_mfma_pack_sizes_and_errors(L):
