@@ -21,6 +21,9 @@ Beside it, on the same run:
               algorithmic bytes;
   qqmm_backward  the vjp of the prefill qqmm (dx and dw, 2 x 2 M N K flop) and
               its columnwise passes alone;
+  mx_qqmm     the prefill shape in the mxfp4 / mxfp8 modes on the block-scaled
+              matrix cores: the whole qqmm, the product alone (vs the dense
+              fp4 10.1 / fp8 5.0 PFLOP/s peaks) and the x pre-pass;
   quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
               outliers (also rotated), GB/s each;
   gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
@@ -263,6 +266,39 @@ def bench_backward(args, nv, torch, W):
                 ms_dycol=ms_dycol, dycol_gbs=(M * N * 4) / ms_dycol / 1e6)
 
 
+PEAK_MX_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0}  # dense fp4 / fp8 matrix-core peaks
+
+
+def bench_mx(args, nv, torch, W):
+    """The prefill shape in the mx modes: x bf16 [2048, 4096] quantized in the
+    mode (x pre-pass straight into the packed layout), w [14336, 4096]
+    quantized and packed once (untimed), the block-scaled product; the whole
+    qqmm, the product alone and the pre-pass alone."""
+    x, w = W.qqmm_inputs(device="cuda")
+    out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    flop = 2.0 * M * N * K
+    r = {}
+    for mode in ("mxfp4", "mxfp8"):
+        wc, ws = nv.nvfp4_mx_quantize(w, mode)
+        wp = nv.nvfp4_mx_pack(wc, ws, mode)
+        del wc, ws
+        wsp, _ = nv.mx_qqmm_workspace(mode, M, N, K, True, "cuda")
+        step = lambda: nv.nvfp4_mx_qqmm_packed(x, wp, out=out, workspace=wsp)
+        settle(step, 0.1)
+        ms = timed(step, args.steps, 2)
+        xp = nv.nvfp4_mx_quantize_packed(x, mode)
+        gemm = lambda: nv.nvfp4_mx_mm_packed(xp, wp, out=out)
+        settle(gemm, 0.05)
+        ms_gemm = timed(gemm, args.steps, 2)
+        ms_pre = timed(lambda: nv.nvfp4_mx_quantize_packed(x, mode, out=xp), args.steps, 2, graph=True)
+        peak = PEAK_MX_TFLOPS[mode]
+        r[mode] = dict(ms=ms, tflops=flop / ms / 1e9, ms_gemm=ms_gemm, gemm_tflops=flop / ms_gemm / 1e9,
+                       frac=flop / ms_gemm / 1e9 / peak, peak=peak, ms_prepass=ms_pre, flop=flop)
+        del wp, wsp, xp
+        torch.cuda.synchronize()
+    return r
+
+
 def bench_quantize(args, nv, torch, W):
     w = W.quantize_weight(device="cuda")
     rows, k = w.shape
@@ -380,7 +416,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "backward", "quantize", "gather", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "backward", "mx", "quantize",
+                                                      "gather", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -421,6 +458,13 @@ def main():
         log(f"  {b['ms']:.3f} ms, {b['tflops']:.1f} TFLOP/s; columnwise quantize of w "
             f"{b['ms_wcol'] * 1e3:.1f} us ({b['wcol_gbs']:.0f} GB/s), columnwise round trip of dy "
             f"{b['ms_dycol'] * 1e3:.1f} us ({b['dycol_gbs']:.0f} GB/s)")
+    if args.only in ("all", "mx"):
+        log("mx modes: qqmm prefill in mxfp4 / mxfp8 (block-scaled matrix cores) ...")
+        res["mx"] = bench_mx(args, nv, torch, W)
+        for mode, d in res["mx"].items():
+            log(f"  {mode}: qqmm {d['ms'] * 1e3:.1f} us ({d['tflops']:.0f} TFLOP/s); product alone "
+                f"{d['ms_gemm'] * 1e3:.1f} us ({d['gemm_tflops']:.0f} TFLOP/s, {100 * d['frac']:.1f} % of "
+                f"{d['peak'] / 1000:.1f} PFLOP/s); x pre-pass {d['ms_prepass'] * 1e3:.1f} us")
     if args.only in ("all", "quantize"):
         log("quantize / dequantize ...")
         res["quantize"] = bench_quantize(args, nv, torch, W)
@@ -480,6 +524,16 @@ def main():
             "columnwise_quantize_w": {"us": round(b["ms_wcol"] * 1e3, 2), "GBps": round(b["wcol_gbs"], 1)},
             "columnwise_round_trip_dy": {"us": round(b["ms_dycol"] * 1e3, 2), "GBps": round(b["dycol_gbs"], 1)},
             "workload": "vjp of qqmm x bf16 [2048,4096] @ w [14336,4096]^T: dx and dw for dy [2048,14336]"}
+    if "mx" in res:
+        line["mx_qqmm"] = {mode: {"value": round(d["tflops"], 2), "unit": "TFLOP/s", "us": round(d["ms"] * 1e3, 2),
+                                  "product_alone": {"TFLOPs": round(d["gemm_tflops"], 2),
+                                                    "us": round(d["ms_gemm"] * 1e3, 2),
+                                                    "peak": d["peak"], "frac": round(d["frac"], 4),
+                                                    "kernel": f"mx_gemm_kernel<bf16, {4 if mode == 'mxfp4' else 8}>"},
+                                  "x_prepass_us": round(d["ms_prepass"] * 1e3, 2)}
+                           for mode, d in res["mx"].items()}
+        line["mx_qqmm"]["workload"] = ("qqmm x bf16 [2048,4096] (quantized in the mode) @ w [14336,4096]^T "
+                                       "in mxfp4 / mxfp8 (packed once), bf16 out")
     if "quantize" in res:
         line["quantize"] = {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["frac"], 4),
                                  "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}

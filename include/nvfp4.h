@@ -422,6 +422,30 @@ nvfp4_status nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, nvfp4_mx
                            hipStream_t stream);
 
 /*
+ * nvfp4_mx_quantize_packed -- quantize x [rows, k] (type dt, 16-byte aligned)
+ * in an mx mode straight into the packed layout (the same bytes as
+ * nvfp4_mx_quantize followed by nvfp4_mx_pack); packed_codes 16-byte aligned,
+ * sizes from nvfp4_mx_pack_size.  Errors as nvfp4_mx_quantize, rows <= 0.
+ */
+nvfp4_status nvfp4_mx_quantize_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                      int64_t rows, int64_t k, uint8_t* packed_codes,
+                                      uint8_t* packed_scales, hipStream_t stream);
+
+/*
+ * nvfp4_mx_mm_packed -- out [m, n] (type out_dt, 16-byte aligned) = the
+ * block-scaled product of two packed mx operands, x [m, k] and w [n, k] in
+ * the same mode: out = T( sum_k x_hat[m, k] * w_hat[n, k] ), the products of
+ * the decodes exact in float32, summed in float32.  nvfp4_mx_qqmm_packed is
+ * nvfp4_mx_quantize_packed of x followed by this call.
+ * Errors: bad mode or dtype, m, n <= 0, k not a positive multiple of 32, NULL
+ * or misaligned pointer, a packed operand of 2 GB or more.
+ */
+nvfp4_status nvfp4_mx_mm_packed(const uint8_t* x_packed_codes, const uint8_t* x_packed_scales,
+                                const uint8_t* w_packed_codes, const uint8_t* w_packed_scales,
+                                nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k, void* out,
+                                nvfp4_dtype out_dt, hipStream_t stream);
+
+/*
  * nvfp4_mx_qqmm_workspace_size -- bytes of workspace nvfp4_mx_qqmm (packed_w
  * = 0) or nvfp4_mx_qqmm_packed (packed_w = 1) needs: x's packed codes and
  * scales, and for a row-major weight its packed copy, each 256-byte aligned.

@@ -83,6 +83,8 @@ def load_library():
         "nvfp4_mx_quant_dequant": (I, [P, I, I, I64, I64, P, P]),
         "nvfp4_mx_pack_size": (I, [I, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "nvfp4_mx_pack": (I, [P, P, I, I64, I64, P, P, P]),
+        "nvfp4_mx_quantize_packed": (I, [P, I, I, I64, I64, P, P, P]),
+        "nvfp4_mx_mm_packed": (I, [P, P, P, P, I, I64, I64, I64, P, I, P]),
         "nvfp4_mx_qqmm_workspace_size": (SZ, [I, I64, I64, I64, I]),
         "nvfp4_mx_qqmm": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_mx_qqmm_packed": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
@@ -566,6 +568,39 @@ def nvfp4_mx_pack(w_codes, w_scales, mode):
     return MxPacked(pc, ps, tuple(w_codes.shape[:-1]) + (k,), mode)
 
 
+def nvfp4_mx_quantize_packed(x, mode, out=None):
+    """x [rows, k] quantized in an mx mode straight into the packed layout
+    (into `out`, an MxPacked of the same shape and mode, when given)."""
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(x, "x")
+    rows, k = _rows_k(x)
+    if out is None:
+        cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(L.nvfp4_mx_pack_size(bits, rows, k, ctypes.byref(cb), ctypes.byref(sb)))
+        out = MxPacked(torch.empty(cb.value, dtype=torch.uint8, device=x.device),
+                       torch.empty(sb.value, dtype=torch.uint8, device=x.device), (rows, k), mode)
+    elif out.mode != mode or out.shape != (rows, k):
+        raise ValueError("out has another mode or shape")
+    _check(L.nvfp4_mx_quantize_packed(_ptr(x), _dtype_code(x, "x"), bits, rows, k, _ptr(out.codes),
+                                      _ptr(out.scales), _stream()))
+    return out
+
+
+def nvfp4_mx_mm_packed(x, w, dtype=torch.bfloat16, out=None):
+    """out [m, n] = x_hat @ w_hat^T for two MxPacked operands of one mode."""
+    L = load_library()
+    if x.mode != w.mode or x.k != w.k:
+        raise ValueError("the packed operands differ in mode or inner size")
+    m, n, k = x.shape[0], w.shape[0], x.k
+    if out is None:
+        out = torch.empty(m, n, dtype=dtype, device=x.codes.device)
+    _check(L.nvfp4_mx_mm_packed(_ptr(x.codes), _ptr(x.scales), _ptr(w.codes), _ptr(w.scales),
+                                _mx_mode(x.mode), m, n, k, _ptr(out), _dtype_code(out, "out"),
+                                _stream()))
+    return out
+
+
 def mx_qqmm_workspace(mode, m, n, k, packed_w, device):
     nbytes = load_library().nvfp4_mx_qqmm_workspace_size(_mx_mode(mode), m, n, k, int(bool(packed_w)))
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device), nbytes
@@ -667,4 +702,5 @@ __all__ = [
     "qqmm_workspace", "gather_workspace", "quantize", "dequantize", "qqmm", "gather_qmm",
     "MX_MODES", "MxPacked", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_quant_dequant",
     "nvfp4_mx_pack", "mx_qqmm_workspace", "nvfp4_mx_qqmm", "nvfp4_mx_qqmm_packed",
+    "nvfp4_mx_quantize_packed", "nvfp4_mx_mm_packed",
 ]

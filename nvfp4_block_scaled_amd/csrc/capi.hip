@@ -766,6 +766,46 @@ nvfp4_status nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, nvfp4_mx
                                             stream));
 }
 
+nvfp4_status nvfp4_mx_quantize_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                      int64_t rows, int64_t k, uint8_t* packed_codes,
+                                      uint8_t* packed_scales, hipStream_t stream) {
+  const char* op = "mx_quantize_packed";
+  if (nvfp4_status st = check_mx(op, x, dt, mode, rows, k)) return st;
+  if (rows <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quantize_packed] rows (%lld) must be positive.",
+                (long long)rows);
+  CHECK_PTR("mx_quantize_packed", packed_codes);
+  CHECK_PTR("mx_quantize_packed", packed_scales);
+  if (!aligned(packed_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quantize_packed] packed_codes must be 16-byte aligned.");
+  if (rows > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mx_quantize_packed] Sizes too large.");
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_mx_quantize_packed(x, dt, mode, rows, k, packed_codes,
+                                                       packed_scales, stream));
+}
+
+nvfp4_status nvfp4_mx_mm_packed(const uint8_t* x_packed_codes, const uint8_t* x_packed_scales,
+                                const uint8_t* w_packed_codes, const uint8_t* w_packed_scales,
+                                nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k, void* out,
+                                nvfp4_dtype out_dt, hipStream_t stream) {
+  const char* op = "mx_mm_packed";
+  if (nvfp4_status st = check_mx(op, out, out_dt, mode, m, k)) return st;
+  if (m <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_mm_packed] m and n must be positive.");
+  if (!x_packed_codes || !x_packed_scales || !w_packed_codes || !w_packed_scales)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_mm_packed] the packed operands must not be NULL.");
+  if (!aligned(x_packed_codes, 16) || !aligned(w_packed_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_mm_packed] packed codes must be 16-byte aligned.");
+  if (m > INT32_MAX || n > INT32_MAX || k > INT32_MAX ||
+      nvfp4::mx_packed_code_bytes(m, k, mode) >= nvfp4::kMxMaxPackedBytes ||
+      nvfp4::mx_packed_code_bytes(n, k, mode) >= nvfp4::kMxMaxPackedBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mx_mm_packed] Sizes too large (a packed operand of 2 GB or more).");
+  if (nvfp4_status st = check_device(op)) return st;
+  return launched(op, nvfp4::launch_mx_gemm(x_packed_codes, x_packed_scales, w_packed_codes,
+                                            w_packed_scales, mode, m, n, k, out, out_dt, stream));
+}
+
 namespace {
 // workspace of the mx contractions: x's packed codes and scales, then (for a
 // row-major weight) the weight's packed codes and scales, each 256-aligned

@@ -128,6 +128,20 @@ def test_mx_pack_layout(mode, rows, k):
     assert_bytes_equal(packed.scales.cpu().numpy(), rs, "packed scales")
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,k", [(40, 96), (300, 512)])
+def test_mx_quantize_packed_equals_pack_of_quantize(mode, dtype, rows, k):
+    say(f"mx quantize_packed {mode} {dtype} {rows}x{k}")
+    x = W.normal((rows, k), 1.0, 530 + rows, oracle_dtype(dtype), outlier_frac=0.01,
+                 outlier_mult=30.0).cuda()
+    xp = nv.nvfp4_mx_quantize_packed(x, mode)
+    c, s_ = nv.nvfp4_mx_quantize(x, mode)
+    ref = nv.nvfp4_mx_pack(c, s_, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(xp.codes, ref.codes) and torch.equal(xp.scales, ref.scales)
+
+
 # ------------------------------------------------------------------ qqmm
 
 def _grid(rows, k, mode, seed, exps):
@@ -179,9 +193,12 @@ def test_mx_qqmm_general(mode, dtype, m, n, k):
     x = W.normal((m, k), 1.0, 520 + m, od)
     w = W.normal((n, k), 0.02, 521 + n, od)
     oc, os_ = O.mx_quantize(host(w), mode)
+    wp = nv.nvfp4_mx_pack(dev(oc), dev(os_), mode)
     y = nv.nvfp4_mx_qqmm(x.cuda(), dev(oc), dev(os_), mode)
-    yp = nv.nvfp4_mx_qqmm_packed(x.cuda(), nv.nvfp4_mx_pack(dev(oc), dev(os_), mode))
+    yp = nv.nvfp4_mx_qqmm_packed(x.cuda(), wp)
+    ymm = nv.nvfp4_mx_mm_packed(nv.nvfp4_mx_quantize_packed(x.cuda(), mode), wp, dtype=dtype)
     torch.cuda.synchronize()
+    assert torch.equal(yp, ymm)
     ref = O.mx_qqmm(host(x), oc, os_, mode, dtype=od)
     fro, _ = assert_close(host(y), ref, what=f"mx qqmm {mode}")
     assert fro <= MX_FRO_GUARD
