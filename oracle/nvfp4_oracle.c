@@ -408,6 +408,58 @@ void orc_gather_qmm_subset(const float* x, int dtype, int64_t t_count, int64_t k
   }
 }
 
+/* gather_qmm in its general indexed form, on a subset of output rows and
+ * columns ([PR4458] statement and test loops: every dtype, transpose True and
+ * False, per-expert global scales; the op's lhs_indices / rhs_indices):
+ *   x is [b, mr, k]: b batch entries of mr rows; pair p (0 <= p < L) takes x
+ *   entry lhs[p] (p when lhs is NULL) and expert rhs[p]; output row
+ *   q = p * mr + r is T( sum_k x[lhs[p], r, k] * w_e[n, k] ), e = rhs[p].
+ *   transpose = 1: expert e's weight is [n, k] quantized along k (codes
+ *   [e, n, k/2], scales [e, n, k/16]), the product x @ w_e^T;
+ *   transpose = 0: it is [k, n] quantized along n (codes [e, k, n/2], scales
+ *   [e, k, n/16]), the product x @ w_e, whose element (n, k) is the decoded
+ *   [k, n] weight at row k, column n.
+ * x is used as given (reading R10); the global scale g[e] / 2688 multiplies
+ * the block scale (R7); products summed in double, one rounding to T. */
+void orc_gather_qmm_indexed_subset(const float* x, int dtype, int64_t b, int64_t mr, int64_t k,
+                                   const uint8_t* wcodes, const uint8_t* wscales, const float* g,
+                                   int64_t e_count, int64_t n, int transpose, const int32_t* lhs,
+                                   const int32_t* rhs, int64_t L, const int64_t* qi, int64_t nq,
+                                   const int64_t* ni, int64_t nn, float* out, int nthreads) {
+  (void)b;
+  (void)L;
+  (void)e_count;
+#pragma omp parallel num_threads(nthreads)
+  {
+    float* wr = (float*)malloc(sizeof(float) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < nq; ++a) {
+      const int64_t q = qi[a], p = q / mr, r = q % mr;
+      const int64_t ent = lhs ? (int64_t)lhs[p] : p;
+      const int64_t e = rhs[p];
+      const float* xr = x + (ent * mr + r) * k;
+      float dec = (g && g_mutant != MUT_DROP_GW) ? global_dec(1, g[e]) : 1.0f;
+      for (int64_t c = 0; c < nn; ++c) {
+        const int64_t col = ni[c];
+        if (transpose) {
+          weight_row_f32(wcodes + (e * n + col) * (k / 2), wscales + (e * n + col) * (k / 16), k, dec,
+                         wr);
+        } else {
+          for (int64_t i = 0; i < k; ++i) {
+            const uint8_t* crow = wcodes + (e * k + i) * (n / 2);
+            const uint8_t* srow = wscales + (e * k + i) * (n / 16);
+            wr[i] = (float)orc_e2m1_value(code_at(crow, col)) * block_scale(srow[col / 16], dec);
+          }
+        }
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; ++i) acc += (double)xr[i] * (double)wr[i];
+        out[a * nn + c] = orc_round_to((float)acc, dtype);
+      }
+    }
+    free(wr);
+  }
+}
+
 /* Routing reference: tokens grouped by expert, stable (ascending t, then j).
  * offsets [e_count + 1] is the exclusive prefix sum of the per-expert counts;
  * perm [t_count * top_k] lists flat pair ids t*top_k + j in that order.

@@ -63,6 +63,9 @@ def lib():
         L.orc_gather_qmm_subset.restype = None
         L.orc_gather_qmm_subset.argtypes = [_P, _INT, _I64, _I64, _P, _P, _P, _I64, _I64,
                                             _P, _I64, _P, _P, _I64, _P, _I64, _P, _INT]
+        L.orc_gather_qmm_indexed_subset.restype = None
+        L.orc_gather_qmm_indexed_subset.argtypes = [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _I64, _I64,
+                                                    _INT, _P, _P, _I64, _P, _I64, _P, _I64, _P, _INT]
         L.orc_moe_route.restype = _INT
         L.orc_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
         L.orc_e8m0_value.restype = ctypes.c_double
@@ -240,6 +243,41 @@ def gather_qmm(x, w_codes, w_scales, idx, global_scale=None, dtype="bf16", pairs
     return out
 
 
+def gather_qmm_indexed(x, w_codes, w_scales, rhs, lhs=None, global_scale=None, transpose=True,
+                       dtype="bf16", rows=None, cols=None, nthreads=None):
+    """gather_qmm in its indexed form: x [b, mr, k] (or [b, k], mr = 1),
+    pair p takes x entry lhs[p] (p if lhs is None) and expert rhs[p]; returns
+    out rows q = p * mr + r ([len(rhs) * mr, n], or the `rows` / `cols`
+    subset).  transpose=True: w_codes [e, n, k/2] (quantized along k);
+    transpose=False: w_codes [e, k, n/2] (quantized along n), out = x @ w."""
+    x = _f32(x)
+    if x.ndim == 2:
+        x = x[:, None, :]
+    b, mr, k = x.shape
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    w_scales = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    e_count = w_codes.shape[0]
+    if transpose:
+        n = w_codes.shape[1]
+        assert w_codes.shape[2] * 2 == k and w_scales.shape[2] * 16 == k
+    else:
+        n = w_codes.shape[2] * 2
+        assert w_codes.shape[1] == k and w_scales.shape[2] * 16 == n
+    rhs = np.ascontiguousarray(np.reshape(rhs, (-1,)), dtype=np.int32)
+    L = rhs.size
+    lhs_a = None if lhs is None else np.ascontiguousarray(np.reshape(lhs, (-1,)), dtype=np.int32)
+    g = None if global_scale is None else _f32(np.reshape(global_scale, (-1,)))
+    qi = np.arange(L * mr, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    ni = np.arange(n, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+    out = np.empty((qi.size, ni.size), np.float32)
+    lib().orc_gather_qmm_indexed_subset(_ptr(x), _dt(dtype), b, mr, k, _ptr(w_codes), _ptr(w_scales),
+                                        None if g is None else _ptr(g), e_count, n, int(bool(transpose)),
+                                        None if lhs_a is None else _ptr(lhs_a), _ptr(rhs), L, _ptr(qi),
+                                        qi.size, _ptr(ni), ni.size, _ptr(out),
+                                        int(nthreads or default_threads()))
+    return out
+
+
 def moe_route(idx, e_count):
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     t_count, top_k = idx.shape
@@ -367,7 +405,7 @@ __all__ = [
     "mx_quantize", "mx_dequantize", "mx_quant_dequant", "mx_qqmm",
     "F32", "F16", "BF16", "MUT_NONE", "MUT_DROP_GW", "MUT_DROP_GX", "MUT_GW_ON_SUM",
     "MUT_AMAX6_BF16", "MUT_ENC_ORDER", "mutant", "quantize_columnwise", "quant_dequant_columnwise",
-    "qqmm_vjp", "e2m1_value", "e2m1_encode", "e4m3_value",
+    "qqmm_vjp", "gather_qmm_indexed", "e2m1_value", "e2m1_encode", "e4m3_value",
     "e4m3_encode", "round_ieee", "round_to", "tensor_amax", "quantize", "dequantize",
     "quant_dequant", "qqmm", "gather_qmm", "moe_route", "lib", "default_threads",
 ]
