@@ -27,6 +27,9 @@ Beside it, on the same run:
   quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
               outliers (also rotated), GB/s each;
   gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
+  gather_qmm_indexed  the same MoE shape through the indexed form: weights
+              stored [k, n] (transpose = False), and the routed and
+              sorted_indices paths of transpose = True;
   cpu_baseline  the oracle (plain C, double accumulation) on a bounded row
               sample of the headline workload, on this host's cores.
 Inputs are synthetic and already resident in device memory when timing starts.
@@ -299,6 +302,57 @@ def bench_mx(args, nv, torch, W):
     return r
 
 
+def bench_gather_ex(args, nv, torch, W):
+    """The MoE shape (4096 tokens, top-2 of 8 experts, n 14336, k 4096) in the
+    indexed form: transpose = False (each expert's [k, n] weight quantized
+    along n) and the sorted_indices path of transpose = True (pairs already
+    grouped by expert) beside the routed one."""
+    T, E, Nn, Kk, top_k = 4096, 8, N, K, 2
+    x = W.normal((T, Kk), 1.0, 5, "bf16", device="cuda")
+    idx = W.expert_indices(T, E, top_k, 205, device="cuda")
+    g = torch.empty(E, dtype=torch.float32, device="cuda")
+    flop = 2.0 * T * top_k * Nn * Kk
+    r = {}
+    # transpose = False
+    wc = torch.empty(E, Kk, Nn // 2, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, Kk, Nn // 16, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        wt = W.normal((Kk, Nn), 0.02, 300 + e, "bf16", device="cuda")
+        nv.nvfp4_tensor_amax(wt, out=g[e:e + 1])
+        nv.nvfp4_quantize(wt, g[e:e + 1], codes=wc[e], scales=wsc[e])
+        del wt
+    lhs = (torch.arange(T * top_k, device="cuda", dtype=torch.int32) // top_k).to(torch.int32)
+    rhs = idx.reshape(-1).contiguous()
+    out = torch.empty(T * top_k, Nn, dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty(nv.load_library().nvfp4_gather_qmm_indexed_workspace_size(T * top_k, 1, E, 1),
+                      dtype=torch.uint8, device="cuda")
+    f = lambda: nv.nvfp4_gather_qmm_indexed(x, wc, wsc, rhs, lhs, g, transpose=False, out=out, workspace=wsp)
+    settle(f, 0.1)
+    ms = timed(f, max(3, args.steps // 4), 2)
+    r["transpose_false"] = dict(ms=ms, tflops=flop / ms / 1e9)
+    del wc, wsc
+    torch.cuda.synchronize()
+    # transpose = True, routed vs sorted_indices (the same pairs sorted by expert)
+    wc = torch.empty(E, Nn, Kk // 2, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, Nn, Kk // 16, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        w = W.normal((Nn, Kk), 0.02, 400 + e, "bf16", device="cuda")
+        nv.nvfp4_tensor_amax(w, out=g[e:e + 1])
+        nv.nvfp4_quantize(w, g[e:e + 1], codes=wc[e], scales=wsc[e])
+        del w
+    order = torch.argsort(rhs.to(torch.int64), stable=True)
+    rhs_s = rhs[order].contiguous()
+    lhs_s = lhs[order].contiguous()
+    for name, srt, rr, ll in (("routed", False, rhs, lhs), ("sorted_indices", True, rhs_s, lhs_s)):
+        f = lambda: nv.nvfp4_gather_qmm_indexed(x, wc, wsc, rr, ll, g, transpose=True,
+                                                sorted_indices=srt, out=out, workspace=wsp)
+        settle(f, 0.1)
+        ms = timed(f, max(3, args.steps // 4), 2)
+        r[name] = dict(ms=ms, tflops=flop / ms / 1e9)
+    torch.cuda.synchronize()
+    return r
+
+
 def bench_quantize(args, nv, torch, W):
     w = W.quantize_weight(device="cuda")
     rows, k = w.shape
@@ -417,7 +471,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "backward", "mx", "quantize",
-                                                      "gather", "copy"])
+                                                      "gather", "gather_ex", "copy"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -474,6 +528,12 @@ def main():
         log("gather_qmm MoE ...")
         res["gather"] = bench_gather(args, nv, torch, W)
         log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s")
+
+    if args.only in ("all", "gather_ex"):
+        log("gather_qmm indexed forms (transpose = False; sorted_indices) ...")
+        res["gather_ex"] = bench_gather_ex(args, nv, torch, W)
+        for k_, v in res["gather_ex"].items():
+            log(f"  {k_}: {v['ms']:.3f} ms, {v['tflops']:.1f} TFLOP/s")
 
     if args.only == "copy":
         c = bench_copy(args, torch)
@@ -543,6 +603,14 @@ def main():
         line["gather_qmm"] = {"value": round(gq["tflops"], 2), "unit": "TFLOP/s",
                               "frac": round(gq["frac"], 4), "ms": round(gq["ms"], 4),
                               "workload": "4096 tokens x top-2 of 8 experts, NVFP4 w [8,14336,4096]"}
+    if "gather_ex" in res:
+        line["gather_qmm_indexed"] = {k_: {"value": round(v["tflops"], 2), "unit": "TFLOP/s",
+                                           "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                           "ms": round(v["ms"], 4)}
+                                      for k_, v in res["gather_ex"].items()}
+        line["gather_qmm_indexed"]["workload"] = (
+            "4096 tokens x top-2 of 8 experts, n 14336, k 4096, lhs_indices = pair // 2: transpose=False "
+            "(weights [8,4096,14336] quantized along n); transpose=True routed vs sorted_indices")
     if "qqmm" in res and not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(res["qqmm"]["data"])

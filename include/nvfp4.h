@@ -348,6 +348,48 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
                                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gather_qmm in its indexed form -- the cells of the pages' gather_qmm test
+ * loops ("[Metal] global scale for qmm" (ml-explore/mlx PR 4458): float32,
+ * float16 and bfloat16; transpose True and False; per-expert global scales
+ * [E, 1, 1]) and the op's lhs_indices, rhs_indices and sorted_indices.
+ *   x            device [entries, rows_per_entry, k] of type dt, 16-byte aligned
+ *   w_codes      transpose = 1: [e, n, k/2] with scales [e, n, k/16] (each
+ *                expert's [n, k] weight quantized along k, out = x @ w^T);
+ *                transpose = 0: [e, k, n/2] with scales [e, k, n/16] (each
+ *                expert's [k, n] weight quantized along n, out = x @ w)
+ *   global_scale_w  device float32 [e] or NULL
+ *   lhs_indices  device int32 [pairs] in [0, entries), or NULL: pair p uses
+ *                x entry p (then pairs <= entries)
+ *   rhs_indices  device int32 [pairs], the expert of each pair
+ *   out          device [pairs, rows_per_entry, n] of type dt: rows
+ *                p * rows_per_entry + r = x[lhs[p], r] times expert rhs[p]
+ *   sorted_indices  1 asserts that rhs_indices is non-decreasing: the pairs
+ *                are then grouped by binary search instead of the routing
+ *                sort (same results; an unsorted array gives undefined values)
+ *   workspace    nvfp4_gather_qmm_indexed_workspace_size(pairs,
+ *                rows_per_entry, e, lhs_indices != NULL) bytes, 256-byte aligned
+ * x is used as given; the global scale multiplies the block scale.  Pairs
+ * with an expert outside [0, e) are skipped (their output rows are not
+ * written); an lhs index outside [0, entries) is a precondition violation.
+ * transpose = 1 runs the matrix-core kernels of nvfp4_gather_qmm (float16 /
+ * bfloat16) or the float32 kernel; transpose = 0 a matrix-core kernel that
+ * decodes each weight tile into LDS (float32: the float32 kernel).
+ * Errors: bad dtype, non-positive sizes, k (transpose = 1) or n (transpose =
+ * 0) not a multiple of 16, k % 8 != 0 with transpose = 0, pairs > entries
+ * without lhs_indices, NULL or misaligned pointers, workspace too small,
+ * sizes too large, e > 1024.
+ */
+size_t nvfp4_gather_qmm_indexed_workspace_size(int64_t pairs, int64_t rows_per_entry, int64_t e,
+                                               int with_lhs);
+nvfp4_status nvfp4_gather_qmm_indexed(const void* x, nvfp4_dtype dt, int64_t entries,
+                                      int64_t rows_per_entry, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, const float* global_scale_w,
+                                      const int32_t* lhs_indices, const int32_t* rhs_indices,
+                                      int64_t pairs, int64_t e, int64_t n, int64_t k, int transpose,
+                                      int sorted_indices, void* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The mx modes: mxfp4 and mxfp8 ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8,
  * fp_quantize / fp_dequantize: group size 32 outside nvfp4, 8 bits for mxfp8
  * and 4 otherwise, scales converted to E8M0 and decoded as 2^(s - 127);

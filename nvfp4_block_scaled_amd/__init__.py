@@ -78,6 +78,9 @@ def load_library():
         "nvfp4_quant_dequant_columnwise": (I, [P, I, I64, I64, P, P, P]),
         "nvfp4_qqmm_vjp_workspace_size": (SZ, [I64, I64, I64, I]),
         "nvfp4_qqmm_vjp": (I, [P, P, P, I, P, P, I64, I64, I64, P, P, P, P, SZ, P]),
+        "nvfp4_gather_qmm_indexed_workspace_size": (SZ, [I64, I64, I64, I]),
+        "nvfp4_gather_qmm_indexed": (I, [P, I, I64, I64, P, P, P, P, P, I64, I64, I64, I64, I, I, P, P,
+                                         SZ, P]),
         "nvfp4_mx_quantize": (I, [P, I, I, I64, I64, P, P, P]),
         "nvfp4_mx_dequantize": (I, [P, P, I, I64, I64, P, I, P]),
         "nvfp4_mx_quant_dequant": (I, [P, I, I, I64, I64, P, P]),
@@ -369,6 +372,53 @@ def nvfp4_gather_qmm(x, w_codes, w_scales, expert_idx, global_scale_w=None, out=
     _check(L.nvfp4_gather_qmm(_ptr(x), _dtype_code(x, "x"), _ptr(w_codes), _ptr(w_scales), _ptr(g),
                               _ptr(expert_idx), t, top_k, e, n, k, _ptr(out), _ptr(workspace),
                               nbytes, _stream()))
+    return out
+
+
+def nvfp4_gather_qmm_indexed(x, w_codes, w_scales, rhs_indices, lhs_indices=None,
+                             global_scale_w=None, transpose=True, sorted_indices=False, out=None,
+                             workspace=None):
+    """Indexed gather_qmm: x [entries, rows_per_entry, k] (or [entries, k]);
+    pair p multiplies x entry lhs_indices[p] (p without lhs_indices) by expert
+    rhs_indices[p]; out [pairs, rows_per_entry, n] (or [pairs, n]).
+    transpose=True: w_codes [e, n, k/2] (x @ w^T); transpose=False: w_codes
+    [e, k, n/2] quantized along n (x @ w)."""
+    L = load_library()
+    _dev(x, "x")
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    _dev(rhs_indices, "rhs_indices")
+    if x.dim() not in (2, 3) or w_codes.dim() != 3:
+        raise ValueError("x must be [entries, k] or [entries, rows, k] and w_codes [e, ., .]")
+    entries, mr, k = (x.shape[0], 1, x.shape[1]) if x.dim() == 2 else tuple(x.shape)
+    e = w_codes.shape[0]
+    if transpose:
+        n = w_codes.shape[1]
+        if w_codes.shape[2] * 2 != k or tuple(w_scales.shape) != (e, n, k // 16):
+            raise ValueError("w_codes / w_scales do not match x's inner size (transpose=True)")
+    else:
+        n = w_codes.shape[2] * 2
+        if w_codes.shape[1] != k or tuple(w_scales.shape) != (e, k, n // 16):
+            raise ValueError("w_codes / w_scales do not match x's inner size (transpose=False)")
+    if rhs_indices.dtype != torch.int32:
+        raise ValueError("rhs_indices must be int32")
+    pairs = rhs_indices.numel()
+    if lhs_indices is not None:
+        _dev(lhs_indices, "lhs_indices")
+        if lhs_indices.dtype != torch.int32 or lhs_indices.numel() != pairs:
+            raise ValueError("lhs_indices must be int32 with one entry per pair")
+    g = _gscale(global_scale_w, "global_scale", numel=e)
+    if out is None:
+        shape = (pairs, n) if x.dim() == 2 else (pairs, mr, n)
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    if workspace is None:
+        nbytes = L.nvfp4_gather_qmm_indexed_workspace_size(pairs, mr, e, int(lhs_indices is not None))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_gather_qmm_indexed(_ptr(x), _dtype_code(x, "x"), entries, mr, _ptr(w_codes),
+                                      _ptr(w_scales), _ptr(g), _ptr(lhs_indices), _ptr(rhs_indices), pairs,
+                                      e, n, k, int(bool(transpose)), int(bool(sorted_indices)), _ptr(out),
+                                      _ptr(workspace), nbytes, _stream()))
     return out
 
 
@@ -692,8 +742,15 @@ def qqmm(x, w, scales, group_size=None, bits=None, mode="nvfp4", global_scale_x=
     return nvfp4_qqmm(x, w, scales, global_scale_x, global_scale_w)
 
 
-def gather_qmm(x, w, scales, rhs_indices, global_scale=None):
-    return nvfp4_gather_qmm(x, w, scales, rhs_indices, global_scale)
+def gather_qmm(x, w, scales, rhs_indices, global_scale=None, lhs_indices=None, transpose=True,
+               sorted_indices=False):
+    """The MoE form (x [t, k], rhs_indices [t, top_k]) by default; with
+    lhs_indices, transpose=False or sorted_indices the indexed form."""
+    if lhs_indices is None and transpose and not sorted_indices and x.dim() == 2 \
+            and rhs_indices.dim() == 2 and rhs_indices.shape[0] == x.shape[0]:
+        return nvfp4_gather_qmm(x, w, scales, rhs_indices, global_scale)
+    return nvfp4_gather_qmm_indexed(x, w, scales, rhs_indices.reshape(-1), lhs_indices, global_scale,
+                                    transpose, sorted_indices)
 
 
 __all__ = [
@@ -702,5 +759,5 @@ __all__ = [
     "qqmm_workspace", "gather_workspace", "quantize", "dequantize", "qqmm", "gather_qmm",
     "MX_MODES", "MxPacked", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_quant_dequant",
     "nvfp4_mx_pack", "mx_qqmm_workspace", "nvfp4_mx_qqmm", "nvfp4_mx_qqmm_packed",
-    "nvfp4_mx_quantize_packed", "nvfp4_mx_mm_packed",
+    "nvfp4_mx_quantize_packed", "nvfp4_mx_mm_packed", "nvfp4_gather_qmm_indexed",
 ]

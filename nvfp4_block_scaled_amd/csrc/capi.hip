@@ -476,7 +476,7 @@ nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k
   CHECK_PTR("moe_route", offsets);
   CHECK_PTR("moe_route", perm);
   if (nvfp4_status st = check_device(op)) return st;
-  return launched(op, nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream));
+  return launched(op, nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream));
 }
 
 nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
@@ -510,10 +510,11 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
   int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
   size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
-  hipError_t he = nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream);
   if (he != hipSuccess) return launched(op, he);
   return launched(op, nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets,
-                                                perm, t, top_k, e, n, k, out, stream));
+                                                 perm, t, t * top_k, top_k, nullptr, e, n, k, out,
+                                                 stream));
 }
 
 // ------------------------------------------------------------------ packed weights
@@ -650,11 +651,107 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
   int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
   size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
-  hipError_t he = nvfp4::launch_moe_route(expert_idx, t, top_k, e, offsets, perm, stream);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream);
   if (he != hipSuccess) return launched(op, he);
   return launched(op, nvfp4::launch_gather_gemm_packed(x, dt, packed_codes, packed_scales,
-                                                       global_scale_w, offsets, perm, t, top_k, e,
-                                                       n, k, out, stream));
+                                                       global_scale_w, offsets, perm, t, t * top_k,
+                                                       top_k, nullptr, e, n, k, out, stream));
+}
+
+// ------------------------------------------------------------------ indexed gather_qmm
+
+namespace {
+struct GatherIxLayout {
+  size_t offsets, perm, amap, total;
+};
+GatherIxLayout gather_ix_layout(int64_t pairs, int64_t mr, int64_t e, bool with_lhs) {
+  GatherIxLayout l;
+  const size_t rows = (size_t)(pairs * mr);
+  l.offsets = 0;
+  l.perm = ((size_t)(e + 1) * 4 + 255) & ~(size_t)255;
+  l.amap = l.perm + ((rows * 4 + 255) & ~(size_t)255);
+  l.total = with_lhs ? l.amap + ((rows * 4 + 255) & ~(size_t)255) : l.amap;
+  return l;
+}
+}  // namespace
+
+size_t nvfp4_gather_qmm_indexed_workspace_size(int64_t pairs, int64_t rows_per_entry, int64_t e,
+                                               int with_lhs) {
+  if (pairs <= 0 || rows_per_entry <= 0 || e <= 0) return 0;
+  return gather_ix_layout(pairs, rows_per_entry, e, with_lhs != 0).total;
+}
+
+nvfp4_status nvfp4_gather_qmm_indexed(const void* x, nvfp4_dtype dt, int64_t entries,
+                                      int64_t rows_per_entry, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, const float* global_scale_w,
+                                      const int32_t* lhs_indices, const int32_t* rhs_indices,
+                                      int64_t pairs, int64_t e, int64_t n, int64_t k, int transpose,
+                                      int sorted_indices, void* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "gather_qmm_indexed";
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] Unsupported dtype code %d (float32, float16 and bfloat16 only).",
+                (int)dt);
+  if (entries <= 0 || rows_per_entry <= 0 || pairs <= 0 || e <= 0 || n <= 0 || k <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] entries, rows_per_entry, pairs, e, n and k must be positive.");
+  if (transpose) {
+    if (nvfp4_status st = check_k(op, k)) return st;
+  } else {
+    if (n % 16 != 0)
+      return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                  "[gather_qmm_indexed] With transpose = 0 the weights are quantized along n, which "
+                  "(%lld) must be a multiple of the group size 16.",
+                  (long long)n);
+    if (k % 8 != 0)
+      return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                  "[gather_qmm_indexed] With transpose = 0, k (%lld) must be a multiple of 8.",
+                  (long long)k);
+  }
+  if (!lhs_indices && pairs > entries)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] Without lhs_indices pair p uses x entry p: pairs (%lld) must not "
+                "exceed entries (%lld).",
+                (long long)pairs, (long long)entries);
+  if (!x || !w_codes || !w_scales || !rhs_indices || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] x, w_codes, w_scales, rhs_indices and out must not be NULL.");
+  if (!aligned(x, 16) || !aligned(w_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] x and w_codes must be 16-byte aligned.");
+  if (pairs * rows_per_entry >= ((int64_t)1 << 31) || entries * rows_per_entry >= ((int64_t)1 << 31) ||
+      n > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_indexed] Sizes too large.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_indexed] at most 1024 experts are supported.");
+  const GatherIxLayout l = gather_ix_layout(pairs, rows_per_entry, e, lhs_indices != nullptr);
+  if (workspace == nullptr || workspace_bytes < l.total)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_indexed] workspace of %zu bytes is smaller than %zu.", workspace_bytes,
+                l.total);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_indexed] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op)) return st;
+  char* base = reinterpret_cast<char*>(workspace);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + l.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + l.perm);
+  int32_t* amap = lhs_indices ? reinterpret_cast<int32_t*>(base + l.amap) : nullptr;
+  const int64_t rows = pairs * rows_per_entry;
+  hipError_t he = sorted_indices
+                      ? nvfp4::launch_sorted_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm, stream)
+                      : nvfp4::launch_moe_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm, stream);
+  if (he == hipSuccess && amap)
+    he = nvfp4::launch_amap(perm, lhs_indices, rows, rows_per_entry, amap, stream);
+  if (he == hipSuccess) {
+    if (transpose)
+      he = nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets, perm,
+                                     entries * rows_per_entry, rows, 1, amap, e, n, k, out, stream);
+    else
+      he = nvfp4::launch_gather_gemm_t(x, dt, w_codes, w_scales, global_scale_w, offsets, perm, rows, 1,
+                                       amap, e, n, k, out, stream);
+  }
+  return launched(op, he);
 }
 
 // ------------------------------------------------------------------ mx modes

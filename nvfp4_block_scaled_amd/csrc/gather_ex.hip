@@ -1,0 +1,257 @@
+// gather_ex.hip -- the indexed forms of gather_qmm on gfx950: routing of
+// already sorted expert indices, the x-row map of lhs indices, and the
+// contraction with weights stored [K, N] (transpose = False).
+//
+// The op ("[Metal] global scale for qmm" (ml-explore/mlx PR 4458): statement
+// and test loops over float32 / float16 / bfloat16 and transpose True /
+// False, per-expert global scales [E, 1, 1]; the op's lhs_indices /
+// rhs_indices / sorted_indices): x is [b, mr, k]; pair p multiplies x entry
+// lhs[p] (p without lhs) by expert rhs[p]; output rows p * mr .. p * mr +
+// mr - 1.  With transpose = False expert e's weight is [K, N] quantized along
+// N, and the output is x @ w_e.
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+// Sorted expert indices: the rows of expert e are [mr lb(e), mr lb(e + 1))
+// with lb(e) the number of pairs whose expert is below e (a binary search),
+// and the permutation is the identity.
+__global__ void __launch_bounds__(256)
+sorted_route_kernel(const int32_t* __restrict__ rhs, int pairs, int mr, int E,
+                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid <= E) {
+    int lo = 0, hi = pairs;  // first pair with rhs >= tid
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (rhs[mid] < tid) lo = mid + 1; else hi = mid;
+    }
+    offsets[tid] = lo * mr;
+  }
+  const int rows = pairs * mr;
+  for (int q = tid; q < rows; q += gridDim.x * blockDim.x) perm[q] = q;
+}
+
+// x row of each routed row: amap[s] = lhs[q / mr] mr + q % mr, q = perm[s].
+__global__ void __launch_bounds__(256)
+amap_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ lhs, int rows, int mr,
+            int32_t* __restrict__ amap) {
+  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < rows; s += gridDim.x * blockDim.x) {
+    const int q = perm[s];
+    amap[s] = lhs[q / mr] * mr + q % mr;
+  }
+}
+
+// ------------------------------------------------------------------ transpose = False
+
+// 128 x 128 output tiles, k steps of 32.  The weight tile (32 rows of k, 128
+// columns of n: 64 code bytes and 8 scales per row) is decoded once per
+// workgroup -- each thread 16 consecutive columns of one row, which share
+// one block scale -- and written transposed into LDS as [n][k], so that both
+// operand fragments of the 32x32x16 MFMA are 16-byte LDS reads (8 k values of
+// one row).  The A rows are gathered through perm / amap as in the other
+// gather kernels.
+constexpr int kTT = 128;
+constexpr int kTK = 32;
+constexpr int kPitch = kTK + 8;  // LDS row pitch in elements (80 bytes)
+
+template <int DT> struct MfmaT;
+template <> struct MfmaT<kBF16> {
+  typedef __bf16 V8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 run(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MfmaT<kF16> {
+  typedef _Float16 V8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ f32x16 run(V8 a, V8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ wc,
+                const uint8_t* __restrict__ ws, const float* __restrict__ gw, int N,
+                void* __restrict__ out, const int32_t* __restrict__ offsets,
+                const int32_t* __restrict__ perm, int top_k, int E, const int32_t* __restrict__ amap) {
+  using T = typename Elem<DT>::T;
+  using V8 = typename MfmaT<DT>::V8;
+  __shared__ __attribute__((aligned(16))) T la[kTT * kPitch];
+  __shared__ __attribute__((aligned(16))) T lb[kTT * kPitch];
+  __shared__ int64_t arow_s[kTT];
+  __shared__ int orow_s[kTT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // the expert and rows of this tile (tiles of all experts in order)
+  const int n_tiles = (N + kTT - 1) / kTT;
+  const int tile_n = blockIdx.x % n_tiles;
+  int tile_m = blockIdx.x / n_tiles;
+  int expert = -1, row_lo = 0, row_count = 0;
+  {
+    int acc_tiles = 0;
+    for (int e = 0; e < E; ++e) {
+      const int cnt = offsets[e + 1] - offsets[e];
+      const int tiles = (cnt + kTT - 1) / kTT;
+      if (tile_m < acc_tiles + tiles) {
+        expert = e;
+        tile_m -= acc_tiles;
+        row_lo = offsets[e];
+        row_count = cnt;
+        break;
+      }
+      acc_tiles += tiles;
+    }
+  }
+  if (expert < 0) return;
+  const int bm = tile_m * kTT, bn = tile_n * kTT;
+  const float dec_w = gw ? gw[expert] / (kE4M3Max * kE2M1Max) : 1.0f;
+  if (tid < kTT) {
+    const int r = bm + tid;
+    if (r < row_count) {
+      const int p = perm[row_lo + r];
+      arow_s[tid] = amap ? amap[row_lo + r] : p / top_k;
+      orow_s[tid] = p;
+    } else {
+      arow_s[tid] = -1;
+      orow_s[tid] = -1;
+    }
+  }
+  __syncthreads();
+
+  const uint8_t* wce = wc + (int64_t)expert * K * (N / 2);
+  const uint8_t* wse = ws + (int64_t)expert * K * (N / 16);
+  // A: thread t loads tile row t / 2, k 16 (t % 2) .. + 15 (two 16-byte pieces)
+  const int ar = tid >> 1, ah = tid & 1;
+  const int64_t arow = arow_s[ar];
+  // B: thread t decodes weight row k0 + t / 8, columns bn + 16 (t % 8) .. + 15
+  const int bk = tid >> 3, bc = tid & 7;
+  const int bcol = bn + 16 * bc;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  for (int k0 = 0; k0 < K; k0 += kTK) {
+    // A tile rows (zeros past the tile's rows or past k; K % 8 == 0)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + 16 * ah + 8 * h;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (arow >= 0 && k < K)
+        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
+      *reinterpret_cast<u32x4*>(&la[ar * kPitch + 16 * ah + 8 * h]) = v;
+    }
+    // B tile: 16 decoded weights of row k, written to column k of rows n
+    {
+      const int k = k0 + bk;
+      float wv[16];
+      if (k < K && bcol < N) {
+        const u32x2 codes = *reinterpret_cast<const u32x2*>(wce + (int64_t)k * (N / 2) + bcol / 2);
+        float se;
+        {
+#pragma clang fp contract(off)
+          se = e4m3_decode(wse[(int64_t)k * (N / 16) + bcol / 16]) * dec_w;
+        }
+        float q[8];
+        e2m1_decode8_f32(codes.x, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+          wv[i] = q[i] * se;
+        }
+        e2m1_decode8_f32(codes.y, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+          wv[8 + i] = q[i] * se;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wv[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lb[(16 * bc + i) * kPitch + bk] = from_f32<DT>(wv[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {  // two 16-wide k sub-steps
+      V8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const V8*>(&la[(64 * wm + 32 * i + (lane & 31)) * kPitch + 16 * u + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const V8*>(&lb[(64 * wn + 32 * j + (lane & 31)) * kPitch + 16 * u + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = MfmaT<DT>::run(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][j][v]: tile row 64 wm + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4,
+  // column 64 wn + 32 j + lane % 32
+  T* O = reinterpret_cast<T*>(out);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int tr = 64 * wm + 32 * i + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+      const int orow = orow_s[tr];
+      if (orow < 0) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = bn + 64 * wn + 32 * j + (lane & 31);
+        if (col < N) O[(int64_t)orow * N + col] = from_f32<DT>(acc[i][j][v]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sorted_route(const int32_t* rhs, int64_t pairs, int64_t mr, int64_t e,
+                               int32_t* offsets, int32_t* perm, hipStream_t s) {
+  const int64_t rows = pairs * mr;
+  const int64_t work = rows > e + 1 ? rows : e + 1;
+  int blocks = (int)((work + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  sorted_route_kernel<<<blocks, 256, 0, s>>>(rhs, (int)pairs, (int)mr, (int)e, offsets, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_amap(const int32_t* perm, const int32_t* lhs, int64_t rows, int64_t mr, int32_t* amap,
+                       hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  int blocks = (int)((rows + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  amap_kernel<<<blocks, 256, 0, s>>>(perm, lhs, (int)rows, (int)mr, amap);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_gemm_t(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
+                                const float* gw, const int32_t* offsets, const int32_t* perm,
+                                int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
+                                int64_t n, int64_t k, void* out, hipStream_t s) {
+  if (dt == kF32)
+    return launch_gather_gemm_t_f32(reinterpret_cast<const float*>(x), wc, ws, gw, offsets, perm, rows,
+                                    top_k, amap, e, n, k, reinterpret_cast<float*>(out), s);
+  const int64_t mt = (rows + kTT - 1) / kTT + e;
+  const int64_t blocks = mt * ((n + kTT - 1) / kTT);
+  if (dt == kF16)
+    gather_t_kernel<kF16><<<(int)blocks, 256, 0, s>>>(x, (int)k, wc, ws, gw, (int)n, out, offsets, perm,
+                                                       (int)top_k, (int)e, amap);
+  else
+    gather_t_kernel<kBF16><<<(int)blocks, 256, 0, s>>>(x, (int)k, wc, ws, gw, (int)n, out, offsets, perm,
+                                                        (int)top_k, (int)e, amap);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

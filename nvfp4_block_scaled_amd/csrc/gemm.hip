@@ -95,7 +95,8 @@ __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc,
                  const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
                  void* __restrict__ out, const int32_t* __restrict__ offsets,
-                 const int32_t* __restrict__ perm, int top_k, int E) {
+                 const int32_t* __restrict__ perm, int top_k, int E,
+                 const int32_t* __restrict__ amap) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileElems];  // [buf][A,B]
@@ -137,7 +138,8 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
   // ---------------------------------------------------------------- A rows of this thread
   // Dense: tile row r is row r of x_hat and of out.  Gather: tile row r is the
   // pair p = perm[row_lo + r] routed to this expert; its A row is x[p / top_k]
-  // and its output row is row p of out viewed as [t * top_k, n].
+  // (or amap[row_lo + r] when an x-row map is given) and its output row is row
+  // p of out viewed as [t * top_k, n].
   // A chunk q = tid + 256 i (i < 8): tile row (tid >> 3) + 32 i, chunk tid & 7
   const int a_chunk = tid & 7;
   int64_t a_row[8];
@@ -147,7 +149,7 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
     if (r < row_count) {
       if constexpr (GATHER) {
         int p = perm[row_lo + r];
-        a_row[i] = p / top_k;
+        a_row[i] = amap ? amap[row_lo + r] : p / top_k;
       } else {
         a_row[i] = r;
       }
@@ -401,7 +403,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
                     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                     const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                    int top_k, int E, int tiles_m) {
+                    int top_k, int E, int tiles_m, const int32_t* __restrict__ amap) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
   constexpr int TM = 32 * RT;              // tile rows
@@ -486,7 +488,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
     const int rr = (bm + r < row_count) ? r : 0;  // rows past the count re-read row 0
     int64_t arow;
     if constexpr (GATHER)
-      arow = perm[row_lo + bm + rr] / top_k;
+      arow = amap ? amap[row_lo + bm + rr] : perm[row_lo + bm + rr] / top_k;
     else
       arow = bm + rr;
     a_off[j] = (uint32_t)((arow * K + c * 8) * (int64_t)sizeof(T));
@@ -727,8 +729,9 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   const void* __restrict__ a_base, int64_t a_rows, const uint8_t* __restrict__ wc,             \
       const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,       \
       void* __restrict__ out, const int32_t* __restrict__ offsets,                             \
-      const int32_t* __restrict__ perm, int top_k, int E, int tiles_m
-#define NVFP4_FAST_PASS a_base, a_rows, wc, ws, gw, M, N, K, out, offsets, perm, top_k, E, tiles_m
+      const int32_t* __restrict__ perm, int top_k, int E, int tiles_m,                          \
+      const int32_t* __restrict__ amap
+#define NVFP4_FAST_PASS a_base, a_rows, wc, ws, gw, M, N, K, out, offsets, perm, top_k, E, tiles_m, amap
 
 // 256-row tiles: one workgroup (four waves, 256 accumulators each) per CU
 template <int DT, bool GATHER, bool PACKED>
@@ -786,12 +789,15 @@ constexpr int FT = 64, FK = 16;
 
 // out tile 64 x 64, 256 threads with 4 x 4 outputs each; the weight tile is
 // decoded to float32 e2m1(q) * (e4m3(s) * g/2688) while staged in LDS.
-template <bool GATHER>
+// TRANS: each expert's weight is [K, N] quantized along N (gather_qmm with
+// transpose = False, out = x @ w): element (n, k) is row k, column n.
+template <bool GATHER, bool TRANS = false>
 __global__ void __launch_bounds__(256)
 f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
                 const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
                 float* __restrict__ out, const int32_t* __restrict__ offsets,
-                const int32_t* __restrict__ perm, int top_k, int E) {
+                const int32_t* __restrict__ perm, int top_k, int E,
+                const int32_t* __restrict__ amap) {
   __shared__ float la[FK][FT + 1];
   __shared__ float lb[FK][FT + 1];
   __shared__ int64_t arow[FT];
@@ -825,7 +831,7 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
     if (r < row_count) {
       if constexpr (GATHER) {
         int p = perm[row_lo + r];
-        arow[tid] = p / top_k;
+        arow[tid] = amap ? amap[row_lo + r] : p / top_k;
         orow_s[tid] = p;
       } else {
         arow[tid] = r;
@@ -853,13 +859,22 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
       float wv = 0.f;
       int n = bn + r;
       if (n < N && k < K) {
-        int64_t row = wbase + n;
-        uint32_t byte = wc[row * (K >> 1) + (k >> 1)];
-        uint32_t code = (k & 1) ? (byte >> 4) : (byte & 15u);
+        uint32_t code, sbyte;
+        if constexpr (TRANS) {
+          const int64_t row = (int64_t)expert * K + k;
+          const uint32_t byte = wc[row * (N >> 1) + (n >> 1)];
+          code = (n & 1) ? (byte >> 4) : (byte & 15u);
+          sbyte = ws[row * (N >> 4) + (n >> 4)];
+        } else {
+          const int64_t row = wbase + n;
+          const uint32_t byte = wc[row * (K >> 1) + (k >> 1)];
+          code = (k & 1) ? (byte >> 4) : (byte & 15u);
+          sbyte = ws[row * (K >> 4) + (k >> 4)];
+        }
         float se;
         {
 #pragma clang fp contract(off)
-          se = e4m3_decode(ws[row * (K >> 4) + (k >> 4)]) * dec_w;
+          se = e4m3_decode(sbyte) * dec_w;
           wv = e2m1_decode(code) * se;
         }
       }
@@ -925,7 +940,7 @@ __device__ __forceinline__ uint64_t match_experts(int e, bool valid, F on_group)
 // expert.  Out-of-range experts are skipped.
 __global__ void __launch_bounds__(kRouteThreads)
 moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __restrict__ offsets,
-                 int32_t* __restrict__ perm) {
+                 int32_t* __restrict__ perm, int mr) {
   __shared__ int base[kRouteMaxE];
   __shared__ int scan[kRouteThreads];
   __shared__ int wcnt[kRouteWaves * kRouteMaxE];
@@ -936,7 +951,7 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
   __syncthreads();
   for (int c0 = 0; c0 < total; c0 += kRouteThreads) {
     const int p = c0 + tid;
-    const int e = (p < total) ? idx[p] : -1;
+    const int e = (p < total) ? idx[p / mr] : -1;
     const bool valid = (e >= 0 && e < E);
     match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
   }
@@ -963,7 +978,7 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
     __syncthreads();
     const int p = c0 + tid;
-    const int e = (p < total) ? idx[p] : -1;
+    const int e = (p < total) ? idx[p / mr] : -1;
     const bool valid = (e >= 0 && e < E);
     const uint64_t same =
         match_experts(e, valid, [&](int le, int cnt) { wcnt[wave * E + le] = cnt; });
@@ -991,14 +1006,14 @@ template <bool GATHER, bool PACKED, int RT>
 hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
                           const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
                           const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
-                          hipStream_t s_stream) {
+                          const int32_t* amap, hipStream_t s_stream) {
   constexpr int TM = 32 * RT;
   const int64_t tiles_m = (rows + TM - 1) / TM + (GATHER ? e : 0);
   const int64_t blocks = tiles_m * ((n + BN - 1) / BN);
 #define NVFP4_LAUNCH(KER, D)                                                                     \
   KER<D, GATHER, PACKED><<<(int)blocks, kGemmThreads, 0, s_stream>>>(                              \
       a, a_rows, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e,    \
-      (int)tiles_m)
+      (int)tiles_m, amap)
   if constexpr (RT == 8) {
     if (dt == kF16)
       NVFP4_LAUNCH(mfma_gemm_fast_kernel, kF16);
@@ -1018,7 +1033,7 @@ template <bool GATHER, bool PACKED>
 hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
                        const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
                        const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
-                       hipStream_t s) {
+                       const int32_t* amap, hipStream_t s) {
   // up to 128 rows (routed pairs) the 128-row tiles skip the half of a
   // 256-row tile that would multiply padding; above that the 256-row tiles
   // are faster (each weight element is decoded for twice as many rows),
@@ -1028,9 +1043,9 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
   const int64_t tiles8 = ((rows + 255) / 256) * ((n + BN - 1) / BN);
   if (rows <= 128 || (!GATHER && tiles8 < device_cu_count()))
     return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                             top_k, e, s);
+                                             top_k, e, amap, s);
   return launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                           top_k, e, s);
+                                           top_k, e, amap, s);
 }
 
 hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
@@ -1044,14 +1059,16 @@ hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t
 hipError_t launch_qqmm_gemm_packed(const void* xhat, int dt, const uint8_t* pc, const uint8_t* ps,
                                    const float* gw, int64_t m, int64_t n, int64_t k, void* out,
                                    hipStream_t s) {
-  return launch_fast<false, true>(dt, xhat, m, pc, ps, gw, m, n, k, out, nullptr, nullptr, 1, 1, s);
+  return launch_fast<false, true>(dt, xhat, m, pc, ps, gw, m, n, k, out, nullptr, nullptr, 1, 1,
+                                  nullptr, s);
 }
 
 hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, const uint8_t* ps,
                                      const float* gw, const int32_t* offsets, const int32_t* perm,
-                                     int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
-                                     void* out, hipStream_t s) {
-  return launch_fast<true, true>(dt, x, t, pc, ps, gw, t * top_k, n, k, out, offsets, perm, top_k, e, s);
+                                     int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                                     int64_t e, int64_t n, int64_t k, void* out, hipStream_t s) {
+  return launch_fast<true, true>(dt, x, x_rows, pc, ps, gw, rows, n, k, out, offsets, perm, top_k, e,
+                                 amap, s);
 }
 
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
@@ -1061,50 +1078,63 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
     int64_t blocks = ((m + FT - 1) / FT) * ((n + FT - 1) / FT);
     f32_gemm_kernel<false><<<(int)blocks, 256, 0, s>>>(
         reinterpret_cast<const float*>(xhat), wc, ws, gw, (int)m, (int)n, (int)k,
-        reinterpret_cast<float*>(out), nullptr, nullptr, 1, 1);
+        reinterpret_cast<float*>(out), nullptr, nullptr, 1, 1, nullptr);
     return hipGetLastError();
   }
   int64_t blocks = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   if (k % BK == 0 && n % 4 == 0)
-    return launch_fast<false, false>(dt, xhat, m, wc, ws, gw, m, n, k, out, nullptr, nullptr, 1, 1, s);
+    return launch_fast<false, false>(dt, xhat, m, wc, ws, gw, m, n, k, out, nullptr, nullptr, 1, 1,
+                                     nullptr, s);
   if (dt == kF16)
     mfma_gemm_kernel<kF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-        xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1);
+        xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, nullptr);
   else
     mfma_gemm_kernel<kBF16, false><<<(int)blocks, kGemmThreads, 0, s>>>(
-        xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1);
+        xhat, wc, ws, gw, (int)m, (int)n, (int)k, out, nullptr, nullptr, 1, 1, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_moe_route(const int32_t* idx, int64_t t, int64_t top_k, int64_t e,
+hipError_t launch_moe_route(const int32_t* idx, int64_t entries, int64_t rows_per_entry, int64_t e,
                             int32_t* offsets, int32_t* perm, hipStream_t s) {
-  moe_route_kernel<<<1, kRouteThreads, 0, s>>>(idx, (int)(t * top_k), (int)e, offsets, perm);
+  moe_route_kernel<<<1, kRouteThreads, 0, s>>>(idx, (int)(entries * rows_per_entry), (int)e, offsets, perm,
+                                               (int)rows_per_entry);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_gemm_t_f32(const float* x, const uint8_t* wc, const uint8_t* ws,
+                                   const float* gw, const int32_t* offsets, const int32_t* perm,
+                                   int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
+                                   int64_t n, int64_t k, float* out, hipStream_t s) {
+  const int64_t mt = (rows + FT - 1) / FT + e;
+  const int64_t blocks = mt * ((n + FT - 1) / FT);
+  f32_gemm_kernel<true, true><<<(int)blocks, 256, 0, s>>>(x, wc, ws, gw, (int)rows, (int)n, (int)k, out,
+                                                        offsets, perm, (int)top_k, (int)e, amap);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
                               const float* gw, const int32_t* offsets, const int32_t* perm,
-                              int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
-                              void* out, hipStream_t s) {
-  const int64_t pairs = t * top_k;
+                              int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                              int64_t e, int64_t n, int64_t k, void* out, hipStream_t s) {
   if (dt == kF32) {
-    int64_t mt = (pairs + FT - 1) / FT + e;
+    int64_t mt = (rows + FT - 1) / FT + e;
     int64_t blocks = mt * ((n + FT - 1) / FT);
     f32_gemm_kernel<true><<<(int)blocks, 256, 0, s>>>(
-        reinterpret_cast<const float*>(x), wc, ws, gw, (int)pairs, (int)n, (int)k,
-        reinterpret_cast<float*>(out), offsets, perm, (int)top_k, (int)e);
+        reinterpret_cast<const float*>(x), wc, ws, gw, (int)rows, (int)n, (int)k,
+        reinterpret_cast<float*>(out), offsets, perm, (int)top_k, (int)e, amap);
     return hipGetLastError();
   }
-  int64_t mt = (pairs + BM - 1) / BM + e;
+  int64_t mt = (rows + BM - 1) / BM + e;
   int64_t blocks = mt * ((n + BN - 1) / BN);
   if (k % BK == 0 && n % 4 == 0)
-    return launch_fast<true, false>(dt, x, t, wc, ws, gw, pairs, n, k, out, offsets, perm, top_k, e, s);
+    return launch_fast<true, false>(dt, x, x_rows, wc, ws, gw, rows, n, k, out, offsets, perm, top_k, e,
+                                    amap, s);
   if (dt == kF16)
     mfma_gemm_kernel<kF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e);
+        x, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, amap);
   else
     mfma_gemm_kernel<kBF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
-        x, wc, ws, gw, (int)pairs, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e);
+        x, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, amap);
   return hipGetLastError();
 }
 

@@ -35,12 +35,20 @@ hipError_t launch_qmv(const void* x, int dt, const float* gx, const uint8_t* wc,
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
                             const float* gw, int64_t m, int64_t n, int64_t k, void* out,
                             hipStream_t s);
-hipError_t launch_moe_route(const int32_t* idx, int64_t t, int64_t top_k, int64_t e,
+// routing: row q (of entries * rows_per_entry) goes to expert idx[q / rows_per_entry]
+hipError_t launch_moe_route(const int32_t* idx, int64_t entries, int64_t rows_per_entry, int64_t e,
                             int32_t* offsets, int32_t* perm, hipStream_t s);
+// gather contraction over `rows` routed rows: the A row of routed row s is
+// amap[s] when amap is given, else perm[s] / top_k; its output row perm[s];
+// x holds x_rows rows
 hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
                               const float* gw, const int32_t* offsets, const int32_t* perm,
-                              int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
-                              void* out, hipStream_t s);
+                              int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                              int64_t e, int64_t n, int64_t k, void* out, hipStream_t s);
+hipError_t launch_gather_gemm_t_f32(const float* x, const uint8_t* wc, const uint8_t* ws,
+                                   const float* gw, const int32_t* offsets, const int32_t* perm,
+                                   int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
+                                   int64_t n, int64_t k, float* out, hipStream_t s);
 // the packed weight layout of the matrix-core path (gemm.hip, mfma_pack_kernel)
 constexpr int64_t kPackK = 64;             // k must be a multiple of this
 constexpr int64_t kPackCodeBytes = 1024;   // per 32-row tile and 64-wide k-step
@@ -52,8 +60,20 @@ hipError_t launch_qqmm_gemm_packed(const void* xhat, int dt, const uint8_t* pc, 
                                    hipStream_t s);
 hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, const uint8_t* ps,
                                      const float* gw, const int32_t* offsets, const int32_t* perm,
-                                     int64_t t, int64_t top_k, int64_t e, int64_t n, int64_t k,
-                                     void* out, hipStream_t s);
+                                     int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                                     int64_t e, int64_t n, int64_t k, void* out, hipStream_t s);
+
+// gather_ex.hip: routing of sorted expert indices (offsets by binary search,
+// identity permutation), the x-row map of lhs indices, and the contraction
+// with weights [e, K, N] quantized along N (transpose = False; K % 8 == 0)
+hipError_t launch_sorted_route(const int32_t* rhs, int64_t pairs, int64_t mr, int64_t e,
+                               int32_t* offsets, int32_t* perm, hipStream_t s);
+hipError_t launch_amap(const int32_t* perm, const int32_t* lhs, int64_t rows, int64_t mr, int32_t* amap,
+                       hipStream_t s);
+hipError_t launch_gather_gemm_t(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
+                                const float* gw, const int32_t* offsets, const int32_t* perm,
+                                int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
+                                int64_t n, int64_t k, void* out, hipStream_t s);
 
 // compute units of the current device (cached per device)
 int device_cu_count();

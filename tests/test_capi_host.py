@@ -270,3 +270,26 @@ def test_vjp_errors(L):
     assert vjp(None, W, B, BF16, G, G, 32, 64, 48, C, None, None, 0x80000, ws, None) == UNSUP
     assert vjp(A, None, B, BF16, G, G, 32, 64, 48, None, D, None, 0x80000, ws, None) == UNSUP
     assert vjp(None, W, B, BF16, G, G, 32, 64, 48, C, D, None, 0x80000, ws, None) == INV
+
+
+def test_gather_indexed_errors(L):
+    need = L.nvfp4_gather_qmm_indexed_workspace_size(70, 1, 4, 1)
+    assert need > L.nvfp4_gather_qmm_indexed_workspace_size(70, 1, 4, 0) > 0 and need % 256 == 0
+    assert L.nvfp4_gather_qmm_indexed_workspace_size(0, 1, 4, 1) == 0
+    args = lambda **kw: dict(dict(x=A, dt=BF16, entries=40, mr=1, wc=B, ws=C, g=None, lhs=G, rhs=W,
+                                  pairs=70, e=4, n=160, k=96, tr=1, srt=0, out=A, wsp=W + 0x1000,
+                                  nb=need), **kw)
+    call = lambda a: L.nvfp4_gather_qmm_indexed(a["x"], a["dt"], a["entries"], a["mr"], a["wc"], a["ws"],
+                                                a["g"], a["lhs"], a["rhs"], a["pairs"], a["e"], a["n"],
+                                                a["k"], a["tr"], a["srt"], a["out"], a["wsp"], a["nb"], None)
+    assert call(args()) == UNSUP  # validation passed
+    assert call(args(k=100)) == INV and "group size 16" in err(L)
+    assert call(args(tr=0, k=96, n=100)) == INV and "quantized along n" in err(L)
+    assert call(args(tr=0, k=100)) == INV and "multiple of 8" in err(L)
+    assert call(args(tr=0, k=100, n=160)) == INV
+    assert call(args(lhs=None)) == INV and "must not exceed entries" in err(L)
+    assert call(args(rhs=None)) == INV
+    assert call(args(x=A + 8)) == INV and "aligned" in err(L)
+    assert call(args(nb=need - 1)) == INV and "workspace" in err(L)
+    assert call(args(e=2000)) == UNSUP
+    assert call(args(dt=7)) == INV
