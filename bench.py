@@ -26,7 +26,8 @@ Beside it, on the same run:
               fp4 10.1 / fp8 5.0 PFLOP/s peaks) and the x pre-pass;
   quantize    amax / quantize / dequantize of w bf16 [4096, 4096] with 0.1 %
               outliers (also rotated), GB/s each;
-  gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096], top-2, TFLOP/s;
+  gather_qmm  MoE: 4096 tokens, 8 experts of [14336, 4096] (packed once,
+              untimed; the row-major weight beside it), top-2, TFLOP/s;
   gather_qmm_indexed  the same MoE shape through the indexed form: weights
               stored [k, n] (transpose = False), and the routed and
               sorted_indices paths of transpose = True;
@@ -402,14 +403,20 @@ def bench_gather(args, nv, torch, W):
         nv.nvfp4_tensor_amax(w[e], out=g[e:e + 1])
         nv.nvfp4_quantize(w[e], g[e:e + 1], codes=wc[e], scales=wsc[e])
     del w
+    # the experts' packed copy for the matrix-core kernel, made once (untimed)
+    wp = nv.nvfp4_mfma_pack(wc, wsc)
     torch.cuda.synchronize()
     out = torch.empty(T, top_k, Nn, dtype=torch.bfloat16, device="cuda")
     wsp, _ = nv.gather_workspace(T, top_k, E, Nn, Kk, "cuda")
-    gq = lambda: nv.nvfp4_gather_qmm(x, wc, wsc, idx, g, out=out, workspace=wsp)
+    gq = lambda: nv.nvfp4_gather_qmm_packed(x, wp, idx, g, out=out, workspace=wsp)
     settle(gq)
     ms = timed(gq, max(3, args.steps // 4), 2)
+    gq_rm = lambda: nv.nvfp4_gather_qmm(x, wc, wsc, idx, g, out=out, workspace=wsp)
+    settle(gq_rm, 0.05)
+    ms_rm = timed(gq_rm, max(3, args.steps // 4), 2)
     flop = 2.0 * T * top_k * Nn * Kk
-    return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS)
+    return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS,
+                ms_rm=ms_rm, tflops_rm=flop / ms_rm / 1e9)
 
 
 def bench_copy(args, torch):
@@ -527,7 +534,8 @@ def main():
     if args.only in ("all", "gather"):
         log("gather_qmm MoE ...")
         res["gather"] = bench_gather(args, nv, torch, W)
-        log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s")
+        log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s (row-major weight "
+            f"{res['gather']['ms_rm']:.3f} ms, {res['gather']['tflops_rm']:.1f} TFLOP/s)")
 
     if args.only in ("all", "gather_ex"):
         log("gather_qmm indexed forms (transpose = False; sorted_indices) ...")
@@ -602,7 +610,10 @@ def main():
         gq = res["gather"]
         line["gather_qmm"] = {"value": round(gq["tflops"], 2), "unit": "TFLOP/s",
                               "frac": round(gq["frac"], 4), "ms": round(gq["ms"], 4),
-                              "workload": "4096 tokens x top-2 of 8 experts, NVFP4 w [8,14336,4096]"}
+                              "row_major_weight": {"value": round(gq["tflops_rm"], 2),
+                                                   "ms": round(gq["ms_rm"], 4)},
+                              "workload": "4096 tokens x top-2 of 8 experts, NVFP4 w [8,14336,4096] "
+                                          "(packed once for the matrix cores)"}
     if "gather_ex" in res:
         line["gather_qmm_indexed"] = {k_: {"value": round(v["tflops"], 2), "unit": "TFLOP/s",
                                            "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4),

@@ -403,7 +403,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
                     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                     const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
-                    int top_k, int E, int tiles_m, const int32_t* __restrict__ amap) {
+                    int top_k, int E, int tiles_m, const int32_t* __restrict__ amap, int seg) {
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
   constexpr int TM = 32 * RT;              // tile rows
@@ -427,15 +427,19 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   int tile_m = L % tiles_m;
   int expert = 0, row_lo = 0, row_count = M;
   if constexpr (GATHER) {
+    // seg 0: all of each expert's rows; 1: its whole 256-row tiles only; 2:
+    // the rows past them (fewer than 256, on 128-row tiles)
     int acc_tiles = 0;
     expert = -1;
     for (int e = 0; e < E; ++e) {
-      const int cnt = offsets[e + 1] - offsets[e];
+      const int all = offsets[e + 1] - offsets[e];
+      const int lo = seg == 2 ? all - all % 256 : 0;
+      const int cnt = seg == 1 ? all - all % 256 : all - lo;
       const int tiles = (cnt + TM - 1) / TM;
       if (tile_m < acc_tiles + tiles) {
         expert = e;
         tile_m -= acc_tiles;
-        row_lo = offsets[e];
+        row_lo = offsets[e] + lo;
         row_count = cnt;
         break;
       }
@@ -730,8 +734,8 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
       const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,       \
       void* __restrict__ out, const int32_t* __restrict__ offsets,                             \
       const int32_t* __restrict__ perm, int top_k, int E, int tiles_m,                          \
-      const int32_t* __restrict__ amap
-#define NVFP4_FAST_PASS a_base, a_rows, wc, ws, gw, M, N, K, out, offsets, perm, top_k, E, tiles_m, amap
+      const int32_t* __restrict__ amap, int seg
+#define NVFP4_FAST_PASS a_base, a_rows, wc, ws, gw, M, N, K, out, offsets, perm, top_k, E, tiles_m, amap, seg
 
 // 256-row tiles: one workgroup (four waves, 256 accumulators each) per CU
 template <int DT, bool GATHER, bool PACKED>
@@ -1006,14 +1010,18 @@ template <bool GATHER, bool PACKED, int RT>
 hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
                           const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
                           const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
-                          const int32_t* amap, hipStream_t s_stream) {
+                          const int32_t* amap, int seg, hipStream_t s_stream) {
   constexpr int TM = 32 * RT;
-  const int64_t tiles_m = (rows + TM - 1) / TM + (GATHER ? e : 0);
+  // tile rows: an upper bound for the gather (per-expert counts live on the
+  // device; surplus workgroups return at once)
+  const int64_t tiles_m = seg == 1 ? rows / 256 + 1
+                        : seg == 2 ? 2 * e
+                                   : (rows + TM - 1) / TM + (GATHER ? e : 0);
   const int64_t blocks = tiles_m * ((n + BN - 1) / BN);
 #define NVFP4_LAUNCH(KER, D)                                                                     \
   KER<D, GATHER, PACKED><<<(int)blocks, kGemmThreads, 0, s_stream>>>(                              \
       a, a_rows, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e,    \
-      (int)tiles_m, amap)
+      (int)tiles_m, amap, seg)
   if constexpr (RT == 8) {
     if (dt == kF16)
       NVFP4_LAUNCH(mfma_gemm_fast_kernel, kF16);
@@ -1043,9 +1051,19 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
   const int64_t tiles8 = ((rows + 255) / 256) * ((n + BN - 1) / BN);
   if (rows <= 128 || (!GATHER && tiles8 < device_cu_count()))
     return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                             top_k, e, amap, s);
+                                             top_k, e, amap, 0, s);
+  if constexpr (GATHER) {
+    // each expert's whole 256-row tiles, then its remaining rows on 128-row
+    // tiles: a nearly empty 256-row tile per expert would cost a whole tile
+    // (same summation order for every output either way)
+    if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out,
+                                                           offsets, perm, top_k, e, amap, 1, s))
+      return err;
+    return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
+                                             top_k, e, amap, 2, s);
+  }
   return launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                           top_k, e, amap, s);
+                                           top_k, e, amap, 0, s);
 }
 
 hipError_t launch_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
