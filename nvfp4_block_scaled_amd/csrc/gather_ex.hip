@@ -47,16 +47,17 @@ amap_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ lhs, i
 
 // ------------------------------------------------------------------ transpose = False
 
-// 128 x 128 output tiles, k steps of 32.  The weight tile (32 rows of k, 128
+// 128 x 128 output tiles, k steps of 64.  The weight tile (64 rows of k, 128
 // columns of n: 64 code bytes and 8 scales per row) is decoded once per
-// workgroup -- each thread 16 consecutive columns of one row, which share
-// one block scale -- and written transposed into LDS as [n][k], so that both
-// operand fragments of the 32x32x16 MFMA are 16-byte LDS reads (8 k values of
-// one row).  The A rows are gathered through perm / amap as in the other
-// gather kernels.
+// workgroup -- each thread 16 consecutive columns of two rows, 16 columns
+// sharing one block scale -- and written transposed into LDS as [n][k], so
+// that both operand fragments of the 32x32x16 MFMA are 16-byte LDS reads (8 k
+// values of one row).  The next step's raw operands are fetched into
+// registers before this step's MFMAs.  The A rows are gathered through perm /
+// amap as in the other gather kernels.
 constexpr int kTT = 128;
-constexpr int kTK = 32;
-constexpr int kPitch = kTK + 8;  // LDS row pitch in elements (80 bytes)
+constexpr int kTK = 64;
+constexpr int kPitch = kTK + 8;  // LDS row pitch in elements (144 bytes)
 
 template <int DT> struct MfmaT;
 template <> struct MfmaT<kBF16> {
@@ -125,12 +126,41 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
 
   const uint8_t* wce = wc + (int64_t)expert * K * (N / 2);
   const uint8_t* wse = ws + (int64_t)expert * K * (N / 16);
-  // A: thread t loads tile row t / 2, k 16 (t % 2) .. + 15 (two 16-byte pieces)
+  // A: thread t loads tile row t / 2, k 32 (t % 2) .. + 31 (four 16-byte pieces)
   const int ar = tid >> 1, ah = tid & 1;
   const int64_t arow = arow_s[ar];
-  // B: thread t decodes weight row k0 + t / 8, columns bn + 16 (t % 8) .. + 15
+  // B: thread t decodes weight rows k0 + t / 8 and k0 + 32 + t / 8, columns
+  // bn + 16 (t % 8) .. + 15
   const int bk = tid >> 3, bc = tid & 7;
   const int bcol = bn + 16 * bc;
+  // LDS slot of B element (n, k): 16-byte chunk k / 8 of row n in slot
+  // (k / 8) ^ ((n / 16) % 8), so that the decode's writes (16 rows n = 16 c +
+  // i of one column k across the threads' c) spread over the banks
+  auto lb_at = [](int n, int k) { return n * kPitch + (((k >> 3) ^ ((n >> 4) & 7)) << 3) + (k & 7); };
+
+  // the next step's raw operands, fetched before this step's MFMAs
+  u32x4 ra[4];
+  u32x2 rcode[2];
+  uint32_t rscale[2];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int k = k0 + 32 * ah + 8 * h;
+      ra[h] = u32x4{0u, 0u, 0u, 0u};
+      if (arow >= 0 && k < K)
+        ra[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int k = k0 + bk + 32 * r;
+      rcode[r] = u32x2{0u, 0u};
+      rscale[r] = 0u;
+      if (k < K && bcol < N) {
+        rcode[r] = *reinterpret_cast<const u32x2*>(wce + (int64_t)k * (N / 2) + bcol / 2);
+        rscale[r] = wse[(int64_t)k * (N / 16) + bcol / 16];
+      }
+    }
+  };
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -138,57 +168,44 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
+  fetch(0);
   for (int k0 = 0; k0 < K; k0 += kTK) {
-    // A tile rows (zeros past the tile's rows or past k; K % 8 == 0)
+    // stage this step: A as loaded, B decoded (zeros past k or n decode to 0)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = k0 + 16 * ah + 8 * h;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (arow >= 0 && k < K)
-        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
-      *reinterpret_cast<u32x4*>(&la[ar * kPitch + 16 * ah + 8 * h]) = v;
-    }
-    // B tile: 16 decoded weights of row k, written to column k of rows n
-    {
-      const int k = k0 + bk;
-      float wv[16];
-      if (k < K && bcol < N) {
-        const u32x2 codes = *reinterpret_cast<const u32x2*>(wce + (int64_t)k * (N / 2) + bcol / 2);
-        float se;
+    for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4*>(&la[ar * kPitch + 32 * ah + 8 * h]) = ra[h];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float se;
+      {
+#pragma clang fp contract(off)
+        se = e4m3_decode(rscale[r]) * dec_w;
+      }
+      float q[16];
+      e2m1_decode8_f32(rcode[r].x, *reinterpret_cast<float(*)[8]>(q));
+      e2m1_decode8_f32(rcode[r].y, *reinterpret_cast<float(*)[8]>(q + 8));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v;
         {
 #pragma clang fp contract(off)
-          se = e4m3_decode(wse[(int64_t)k * (N / 16) + bcol / 16]) * dec_w;
+          v = q[i] * se;
         }
-        float q[8];
-        e2m1_decode8_f32(codes.x, q);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-          wv[i] = q[i] * se;
-        }
-        e2m1_decode8_f32(codes.y, q);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma clang fp contract(off)
-          wv[8 + i] = q[i] * se;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) wv[i] = 0.0f;
+        lb[lb_at(16 * bc + i, bk + 32 * r)] = from_f32<DT>(v);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lb[(16 * bc + i) * kPitch + bk] = from_f32<DT>(wv[i]);
     }
     __syncthreads();
+    if (k0 + kTK < K) fetch(k0 + kTK);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {  // two 16-wide k sub-steps
+    for (int u = 0; u < kTK / 16; ++u) {  // 16-wide k sub-steps
       V8 a[2], b[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         a[i] = *reinterpret_cast<const V8*>(&la[(64 * wm + 32 * i + (lane & 31)) * kPitch + 16 * u + 8 * (lane >> 5)]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const V8*>(&lb[(64 * wn + 32 * j + (lane & 31)) * kPitch + 16 * u + 8 * (lane >> 5)]);
+      for (int j = 0; j < 2; ++j) {
+        const int n = 64 * wn + 32 * j + (lane & 31);
+        b[j] = *reinterpret_cast<const V8*>(&lb[lb_at(n, 16 * u + 8 * (lane >> 5))]);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
