@@ -224,3 +224,25 @@ def test_mx_qqmm_prefill_14336x4096(mode):
     ref = O.mx_qqmm(host(x), oc, os_, mode, dtype="bf16", rows=rows, cols=cols)
     fro, _ = assert_close(host(y)[rows][:, cols], ref, what=f"mx prefill {mode}")
     assert fro <= MX_FRO_GUARD
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mlx_style_names_dispatch_the_mx_modes(mode):
+    """quantize / dequantize / qqmm with mode="mxfp4" / "mxfp8" (group size 32,
+    bits 4 / 8) run the mx kernels; a global scale with an mx mode is refused
+    as the pages' validate_global_scale does."""
+    say(f"mlx-style names {mode}")
+    x = W.normal((64, 256), 1.0, 540, "bf16").cuda()
+    w = W.normal((96, 256), 0.02, 541, "bf16").cuda()
+    bits = 8 if mode == "mxfp8" else 4
+    c, s_ = nv.quantize(w, group_size=32, bits=bits, mode=mode)
+    c2, s2 = nv.nvfp4_mx_quantize(w, mode)
+    d = nv.dequantize(c, s_, group_size=32, bits=bits, mode=mode)
+    y = nv.qqmm(x, c, s_, mode=mode)
+    y2 = nv.nvfp4_mx_qqmm(x, c, s_, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c2) and torch.equal(s_, s2)
+    assert torch.equal(d, nv.nvfp4_mx_dequantize(c, s_, mode))
+    assert torch.equal(y, y2)
+    with pytest.raises(ValueError):
+        nv.quantize(w, mode=mode, global_scale=torch.ones(1, device="cuda"))
