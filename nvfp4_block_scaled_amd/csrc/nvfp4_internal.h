@@ -30,6 +30,12 @@ constexpr int64_t kQmvMaxK = 32768;
 hipError_t launch_qmv(const void* x, int dt, const float* gx, const uint8_t* wc,
                       const uint8_t* ws, const float* gw, int64_t n, int64_t k, void* out,
                       hipStream_t s);
+// 1 <= m <= 2 rows of 16-bit x, k = 4096, row-major weight: x_hat [m, k] @ w^T
+// with x_hat x's round trip under gx (quantize_x) or x as given
+bool qmv_rows_ok(int dt, int64_t m, int64_t n, int64_t k);
+hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, const float* gx,
+                           const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t n,
+                           void* out, hipStream_t s);
 
 // gemm.hip
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,

@@ -24,6 +24,16 @@
 //   * a DPP row reduction plus four lane reads give the row sum.
 // Generic path (any k % 16 == 0 up to 32768): one group per lane per sweep,
 // x_hat in LDS as float32 padded to 17 words per group (conflict-free reads).
+//
+// A few rows (qmv_rows_kernel, 1 <= m <= 2 rows of 16-bit x, k = 4096): the
+// register path with one accumulator per x row.  The weight stream is the
+// same; each decoded code pair feeds m v_dot2 products, so the VALU work per
+// weight element grows as 0.5 + 0.5 m instructions while the bytes stay put
+// (past two rows it outgrows the stream, and the matrix-core kernels of
+// smallm.hip do better).
+// x_hat is x's round trip under g_x (qqmm) or x as given (quantized_matmul).
+// With m = 1 and the round trip of x done beforehand the sums are qmv's,
+// operation for operation.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -269,6 +279,197 @@ qmv_generic_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
 }
 
+// ------------------------------------------------------------------ a few x rows
+
+constexpr int kRowsMaxM = 2;
+
+template <int DT> struct Dot2;
+template <> struct Dot2<kBF16> {
+  using V = bf16x2;
+  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_bf16<B>(w); }
+  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
+  }
+};
+template <> struct Dot2<kF16> {
+  using V = f16x2;
+  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_f16<B>(w); }
+  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2, b), c, false);
+  }
+};
+
+// Rows of x past m are never computed; their loads read zeros (buffer range).
+template <int DT, int R>
+__global__ void __launch_bounds__(kThreadsQ)
+qmv_rows_kernel(const void* __restrict__ x, int m, bool qx, const float* __restrict__ gx,
+                const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                const float* __restrict__ gw, int n, void* __restrict__ out) {
+  constexpr int K = 4096;
+  constexpr int HPR = K / 8;  // half groups per x row: one per thread
+  using T = typename Elem<DT>::T;
+  using D = Dot2<DT>;
+  __shared__ __attribute__((aligned(16))) u32x4 xs[kRowsMaxM * HPR];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // 1. half group tid of every x row, first in the load queue
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)m * K * 2);
+  u32x4 xr[kRowsMaxM];
+#pragma unroll
+  for (int j = 0; j < kRowsMaxM; ++j)
+    xr[j] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(j * HPR + tid) * 16u, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. every weight load of this wave's R rows (rows past n re-read row n - 1)
+  const int r0 = (blockIdx.x * kWaves + wave) * R;
+  RowPiece wp[R][2];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int r = min(r0 + i, n - 1);
+    const uint8_t* crow = wc + (int64_t)r * (K / 2);
+    const uint8_t* srow = ws + (int64_t)r * (K / 16);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int e0 = hh * 2048 + 32 * lane;
+      wp[i][hh].code = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + e0 / 2));
+      wp[i][hh].scale =
+          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(srow + ((e0 / 16) & ~3)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 3. the x_hat rows into LDS
+  {
+    const float enc = global_encode(gx);
+    const float dec = global_decode(gx);
+#pragma unroll
+    for (int j = 0; j < kRowsMaxM; ++j) {
+      if (j < m) {
+        u32x4 v = xr[j];
+        if (qx) {
+          float f[8], o[8];
+          unpack8<DT>(v, f);
+          xhat_half_group<DT>(f, enc, dec, o);  // lane pairs hold the two halves of a group
+          typedef T T8 __attribute__((ext_vector_type(8)));
+          T8 t;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) t[i] = from_f32<DT>(o[i]);
+          v = __builtin_bit_cast(u32x4, t);
+        }
+        xs[j * HPR + tid] = v;
+      }
+    }
+  }
+  lds_barrier();  // the weight loads stay in flight
+
+  // 4. this lane's x_hat pieces (elements 2048 hh + 32 lane .. + 31 of each row)
+  uint32_t xp[kRowsMaxM][2][16];
+#pragma unroll
+  for (int j = 0; j < kRowsMaxM; ++j) {
+    if (j < m) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 t = xs[j * HPR + (hh * 2048 + 32 * lane) / 8 + q];
+          xp[j][hh][4 * q] = t.x; xp[j][hh][4 * q + 1] = t.y;
+          xp[j][hh][4 * q + 2] = t.z; xp[j][hh][4 * q + 3] = t.w;
+        }
+      }
+    }
+  }
+
+  // 5. rows: per group, the 8 decoded pairs dotted with each x row, the
+  //    partial sums times e4m3(s) * g_w/2688; lane i keeps row r0 + i
+  const float dec_w = global_decode(gw);
+  const int sshift = 8 * ((2 * lane) & 3);
+  float mine[kRowsMaxM];
+#pragma unroll
+  for (int j = 0; j < kRowsMaxM; ++j) mine[j] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float acc[kRowsMaxM];
+#pragma unroll
+    for (int j = 0; j < kRowsMaxM; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const RowPiece& pc = wp[i][hh];
+      float se0, se1;
+      {
+#pragma clang fp contract(off)
+        const uint32_t sc = pc.scale >> sshift;
+        se0 = e4m3_decode_byte<0>(sc) * dec_w;
+        se1 = e4m3_decode_byte<1>(sc) * dec_w;
+      }
+      const uint32_t cw[4] = {pc.code.x, pc.code.y, pc.code.z, pc.code.w};
+      typename D::V d[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        d[4 * u] = D::template dec<0>(cw[u]);
+        d[4 * u + 1] = D::template dec<1>(cw[u]);
+        d[4 * u + 2] = D::template dec<2>(cw[u]);
+        d[4 * u + 3] = D::template dec<3>(cw[u]);
+      }
+#pragma unroll
+      for (int j = 0; j < kRowsMaxM; ++j) {
+        if (j < m) {
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) p0 = D::dot(d[t], xp[j][hh][t], p0);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) p1 = D::dot(d[8 + t], xp[j][hh][8 + t], p1);
+          acc[j] = __builtin_fmaf(p0, se0, acc[j]);
+          acc[j] = __builtin_fmaf(p1, se1, acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsMaxM; ++j) {
+      if (j < m) {
+        const float v = wave_sum_uniform(acc[j]);
+        mine[j] = (lane == i) ? v : mine[j];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // consume rows in load order
+  }
+  // 6. lane i stores row r0 + i of every output row
+  if (lane < R && r0 + lane < n) {
+#pragma unroll
+    for (int j = 0; j < kRowsMaxM; ++j)
+      if (j < m) reinterpret_cast<T*>(out)[(int64_t)j * n + r0 + lane] = from_f32<DT>(mine[j]);
+  }
+}
+
+template <int DT, int R>
+void launch_rows(const void* x, int m, bool qx, const float* gx, const uint8_t* wc,
+                 const uint8_t* ws, const float* gw, int64_t n, void* out, int64_t blocks,
+                 hipStream_t s) {
+  qmv_rows_kernel<DT, R><<<(int)blocks, kThreadsQ, 0, s>>>(x, m, qx, gx, wc, ws, gw, (int)n, out);
+}
+
+template <int DT>
+hipError_t launch_rows_t(const void* x, int m, bool qx, const float* gx, const uint8_t* wc,
+                         const uint8_t* ws, const float* gw, int64_t n, void* out, hipStream_t s) {
+  int64_t blocks = (n + kWaves * kMaxRows - 1) / (kWaves * kMaxRows);
+  if (blocks < 256) blocks = 256;
+  const int rpw = (int)((n + blocks * kWaves - 1) / (blocks * kWaves));
+  blocks = (n + (int64_t)kWaves * rpw - 1) / ((int64_t)kWaves * rpw);
+  switch (rpw) {
+    case 1: launch_rows<DT, 1>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 2: launch_rows<DT, 2>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 3: launch_rows<DT, 3>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 4: launch_rows<DT, 4>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 5: launch_rows<DT, 5>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 6: launch_rows<DT, 6>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    case 7: launch_rows<DT, 7>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+    default: launch_rows<DT, 8>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
+  }
+  return hipGetLastError();
+}
+
 template <int DT, int CH, int R>
 void launch_reg(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                 const float* gw, int64_t n, void* out, int64_t blocks, hipStream_t s) {
@@ -325,6 +526,18 @@ hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const
 }
 
 }  // namespace
+
+bool qmv_rows_ok(int dt, int64_t m, int64_t n, int64_t k) {
+  return (dt == kBF16 || dt == kF16) && m >= 1 && m <= kRowsMaxM && k == 4096 && n >= 1 &&
+         n < 0x7FFFFFFF;
+}
+
+hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, const float* gx,
+                           const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t n,
+                           void* out, hipStream_t s) {
+  return dt == kF16 ? launch_rows_t<kF16>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s)
+                    : launch_rows_t<kBF16>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s);
+}
 
 hipError_t launch_qmv(const void* x, int dt, const float* gx, const uint8_t* wc,
                       const uint8_t* ws, const float* gw, int64_t n, int64_t k, void* out,

@@ -28,6 +28,11 @@
 //     tile as the first operand and the x rows (padded by repeating the last
 //     row, whose products are never stored) as the second;
 //   * the k parts of a tile are summed through LDS in a fixed order.
+// Packed weight with k = 2048 / 4096 and m <= 8 (smallm_px_kernel): the codes
+// decoded exactly, one block of 16 per matrix-core product, each block's
+// partial sums scaled in float32 (described at the kernel).  Row-major weight
+// with k = 4096 and m <= 2: qmv's register kernel with one accumulator per row
+// (qmv.hip).  Otherwise:
 // Row-major weight: v_mfma_f32_16x16x32 over strips of 16 rows; per 128-wide
 // k chunk a lane loads 16 code bytes of its row (four lanes cover 64
 // contiguous bytes) and two scale bytes.  Packed weight (mfma_pack_kernel):
@@ -92,33 +97,34 @@ __device__ __forceinline__ typename SmMfma<DT>::V8 decode_word(uint32_t w, float
 
 // ---------------------------------------------------------------- x rows in LDS
 //
-// x rows [M][K + 8] of T in LDS: 16 bytes of padding per row put the fragment
-// reads of different rows in different banks.  Half group h = elements
-// 8 h .. 8 h + 7 of x (row h / (K / 8)); thread t takes h = t + 512 r.
+// x rows [M][ldr] of T in LDS (ldr = K + 8: 16 bytes of padding per row put
+// the fragment reads of different rows in different banks).  Half group h =
+// elements 8 h .. 8 h + 7 of x (row h / (K / 8)); thread t of NT takes
+// h = t + NT r.
 
+template <int NT>
 __device__ __forceinline__ void issue_x_loads(const void* x, int H, int tid,
                                               u32x4 (&xr)[kSmXRounds]) {
   const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (uint64_t)H * 16);
 #pragma unroll
   for (int r = 0; r < kSmXRounds; ++r)  // past the end of x: zeros
     xr[r] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, (uint32_t)(tid + kSmThreads * r) * 16u, 0, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, (uint32_t)(tid + NT * r) * 16u, 0, 0));
 }
 
-template <int DT, bool QX>
+template <int DT, bool QX, int NT>
 __device__ __forceinline__ void write_x_rows(const u32x4 (&xr)[kSmXRounds], const float* gx, int M,
-                                             int K, int tid, typename Elem<DT>::T* xs) {
+                                             int K, int ldr, int tid, typename Elem<DT>::T* xs) {
   using T = typename Elem<DT>::T;
   const int hpr = K / 8;  // half groups per row
   const int H = M * hpr;  // even: pair partners (h, h ^ 1) share a round
-  const int rounds = (H + kSmThreads - 1) / kSmThreads;
-  const int ldr = K + 8;
+  const int rounds = (H + NT - 1) / NT;
   const float enc = global_encode(gx);
   const float dec = global_decode(gx);
 #pragma unroll
   for (int r = 0; r < kSmXRounds; ++r) {
     if (r < rounds) {
-      const int h = tid + kSmThreads * r;
+      const int h = tid + NT * r;
       T* dst = xs + (h / hpr) * ldr + 8 * (h % hpr);
       if constexpr (QX) {
         float v[8], o[8];
@@ -215,7 +221,7 @@ smallm_rm_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   };
 
   u32x4 xr[kSmXRounds];
-  issue_x_loads(x, M * (K / 8), tid, xr);
+  issue_x_loads<kSmThreads>(x, M * (K / 8), tid, xr);
   __builtin_amdgcn_sched_barrier(0);  // x loads ahead of the weight loads
   const int64_t pass_rows = (int64_t)gridDim.x * RW;
   int64_t r0 = (int64_t)blockIdx.x * RW;
@@ -224,7 +230,7 @@ smallm_rm_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   load_batch(bufA, oc, os, c0);
   load_batch(bufB, oc, os, c0 + kSmBatch);
   __builtin_amdgcn_sched_barrier(0);
-  write_x_rows<DT, QX>(xr, gx, M, K, tid, xs);
+  write_x_rows<DT, QX, kSmThreads>(xr, gx, M, K, ldr, tid, xs);
   lds_barrier();  // x rows written; the weight loads stay in flight
 
   for (; r0 < N; r0 += pass_rows) {
@@ -347,7 +353,7 @@ smallm_pk_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   };
 
   u32x4 xr[kSmXRounds];
-  issue_x_loads(x, M * (K / 8), tid, xr);
+  issue_x_loads<kSmThreads>(x, M * (K / 8), tid, xr);
   __builtin_amdgcn_sched_barrier(0);
   const int pass_tiles = gridDim.x * TPW;
   int t0 = blockIdx.x * TPW;
@@ -356,7 +362,7 @@ smallm_pk_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   load_batch(bufA, oc, os, s0);
   load_batch(bufB, oc, os, s0 + kSmBatch);
   __builtin_amdgcn_sched_barrier(0);
-  write_x_rows<DT, QX>(xr, gx, M, K, tid, xs);
+  write_x_rows<DT, QX, kSmThreads>(xr, gx, M, K, ldr, tid, xs);
   lds_barrier();
 
   for (; t0 < tiles; t0 += pass_tiles) {
@@ -402,12 +408,160 @@ smallm_pk_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
 }
 
+// ---------------------------------------------------------------- packed weight, exact decode
+//
+// Up to kPxMaxM rows of x against the packed weight (K = 2048 or 4096), one
+// or two 32-row tiles per workgroup, 4 waves per tile, each wave a quarter of
+// the tile's k steps (K = 256 SW), all of its weight loads issued before
+// anything else.  The codes are decoded exactly
+// (e2m1 to T, one conversion per two codes), each 16-wide block is contracted
+// on the matrix cores on its own, and its partial sums are scaled by
+// e4m3(s) * g_w/2688 in float32, as qmv does per group -- no rounding of the
+// decoded weight.
+//
+// One v_mfma_f32_32x32x16 contracts two blocks at once, block-diagonally.  The
+// second operand is the weight: lane (n = l % 32, h = l / 32) holds dword j of
+// its codes, codes 32 h + 8 j .. + 7 of the step (block 2 h + j / 2).  The
+// first operand is x: in lane half h its row i carries x row i - 16 h, and
+// zeros (an all-zero LDS row) outside 0 <= i - 16 h < M.  So output rows
+// i < 16 see only the block of lane half 0 and rows i >= 16 only that of lane
+// half 1: with dwords 0, 1 the MFMA pair gives block 0 in rows i and block 2 in
+// rows 16 + i, with dwords 2, 3 blocks 1 and 3.  Output lane l holds rows
+// 8 (v / 4) + 4 h + v % 4 of column n, so x row m = 4 h + v (v < 4) sits in
+// elements v (blocks 0 / 1) and 8 + v (blocks 2 / 3) of one lane.
+
+constexpr int kPxWaves = 4;  // waves per tile: its k quarters
+constexpr int kPxMaxM = 8;
+
+template <int DT, bool QX, int SW, int TPW>
+__global__ void __launch_bounds__(64 * kPxWaves * TPW)
+smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+                 const uint8_t* __restrict__ pc, const uint8_t* __restrict__ ps,
+                 const float* __restrict__ gw, int M, int N, void* __restrict__ out) {
+  using T = typename Elem<DT>::T;
+  using V8 = typename SmMfma<DT>::V8;
+  constexpr int K = kPkStep * kPxWaves * SW;
+  constexpr int KT = K / kPkStep;
+  constexpr int ldr = K + 16;  // 32 bytes of padding per row
+  constexpr int NT = 64 * kPxWaves * TPW;
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm_lds[];
+  T* const xs = reinterpret_cast<T*>(sm_lds);  // M rows of x_hat, then a zero row
+  f32x4* const red = reinterpret_cast<f32x4*>(sm_lds + (size_t)(M + 1) * ldr * sizeof(T));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int li = lane & 31;
+  const int tiles = (N + 31) / 32;
+  const int tile = TPW * blockIdx.x + wave / kPxWaves;
+  const int quarter = wave % kPxWaves;
+
+  // 1. x first, then every weight load of this wave's SW steps (a tile past
+  //    the last one reads zeros and stores nothing)
+  u32x4 xr[kSmXRounds];
+  issue_x_loads<NT>(x, M * (K / 8), tid, xr);
+  __builtin_amdgcn_sched_barrier(0);
+  const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(pc, (uint64_t)tiles * KT * kPackCodeBytes);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ps, (uint64_t)tiles * KT * kPackScaleBytes);
+  const uint32_t blk0 = (uint32_t)tile * (uint32_t)KT + (uint32_t)(quarter * SW);
+  SmPiece wp[SW];
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    wp[s].code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rs_c, (blk0 + s) * (uint32_t)kPackCodeBytes + 16u * lane, 0, 0));
+    wp[s].scale = __builtin_amdgcn_raw_buffer_load_b32(
+        rs_s, (blk0 + s) * (uint32_t)kPackScaleBytes + 4u * li, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. x_hat rows and the zero row into LDS; the weight loads stay in flight
+  write_x_rows<DT, QX, NT>(xr, gx, M, K, ldr, tid, xs);
+  for (int e = tid; e < ldr / 8; e += NT)
+    reinterpret_cast<u32x4*>(xs + (size_t)M * ldr)[e] = u32x4{0u, 0u, 0u, 0u};
+  lds_barrier();
+
+  // 3. the steps
+  const float dec_w = global_decode(gw);
+  const int xi = li - 16 * h;  // x row of this lane's first-operand slots
+  const T* const xrow = xs + (size_t)((xi >= 0 && xi < M) ? xi : M) * ldr + 32 * h;
+  const f32x16 zero = {};
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < SW; ++s) {
+    const T* xp = xrow + kPkStep * (quarter * SW + s);
+    const uint32_t cw[4] = {wp[s].code.x, wp[s].code.y, wp[s].code.z, wp[s].code.w};
+    V8 xa[4], wb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xa[j] = *reinterpret_cast<const V8*>(xp + 8 * j);
+      u32x4 d;
+      if constexpr (DT == kBF16) {
+        d.x = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<0>(cw[j]));
+        d.y = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<1>(cw[j]));
+        d.z = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<2>(cw[j]));
+        d.w = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<3>(cw[j]));
+      } else {
+        d.x = __builtin_bit_cast(uint32_t, e2m1_decode2_f16<0>(cw[j]));
+        d.y = __builtin_bit_cast(uint32_t, e2m1_decode2_f16<1>(cw[j]));
+        d.z = __builtin_bit_cast(uint32_t, e2m1_decode2_f16<2>(cw[j]));
+        d.w = __builtin_bit_cast(uint32_t, e2m1_decode2_f16<3>(cw[j]));
+      }
+      wb[j] = __builtin_bit_cast(V8, d);
+    }
+    f32x16 pa = SmMfma<DT>::run32(xa[0], wb[0], zero);
+    pa = SmMfma<DT>::run32(xa[1], wb[1], pa);  // rows < 16: block 0, rows >= 16: block 2
+    f32x16 pb = SmMfma<DT>::run32(xa[2], wb[2], zero);
+    pb = SmMfma<DT>::run32(xa[3], wb[3], pb);  // blocks 1 and 3
+    float se[4];
+    {
+#pragma clang fp contract(off)
+      se[0] = e4m3_decode_byte<0>(wp[s].scale) * dec_w;
+      se[1] = e4m3_decode_byte<1>(wp[s].scale) * dec_w;
+      se[2] = e4m3_decode_byte<2>(wp[s].scale) * dec_w;
+      se[3] = e4m3_decode_byte<3>(wp[s].scale) * dec_w;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc[v] = __builtin_fmaf(pa[v], se[0], acc[v]);
+      acc[v] = __builtin_fmaf(pb[v], se[1], acc[v]);
+      acc[v] = __builtin_fmaf(pa[8 + v], se[2], acc[v]);
+      acc[v] = __builtin_fmaf(pb[8 + v], se[3], acc[v]);
+    }
+  }
+
+  // 4. the four k quarters of a tile summed in order; lane (n, h) holds x
+  //    rows 4 h .. + 3
+  const int slot = (wave / kPxWaves) * (kPxWaves - 1);
+  if (quarter > 0) red[(slot + quarter - 1) * 64 + lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  lds_barrier();
+  if (quarter == 0) {
+#pragma unroll
+    for (int p = 0; p < kPxWaves - 1; ++p) {
+      const f32x4 r = red[(slot + p) * 64 + lane];
+      acc[0] += r.x; acc[1] += r.y; acc[2] += r.z; acc[3] += r.w;
+    }
+    const int n = 32 * tile + li;
+    if (n < N) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * h + v;
+        if (m < M) reinterpret_cast<T*>(out)[(int64_t)m * N + n] = from_f32<DT>(acc[v]);
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launch
 
 // LDS of a launch: the x rows and the k-part partial sums
 size_t rm_lds(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(k + 8) * 2 + (size_t)(kSmWaves - 1) * 64 * sizeof(f32x4);
 }
+size_t px_lds(int64_t m, int64_t k, int tpw) {
+  return (size_t)(m + 1) * (size_t)(k + 16) * 2 + (size_t)tpw * (kPxWaves - 1) * 64 * sizeof(f32x4);
+}
+bool px_ok(int64_t m, int64_t k) { return m >= 1 && m <= kPxMaxM && (k == 2048 || k == 4096); }
 size_t pk_lds(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(k + 8) * 2 + (size_t)(kSmWaves - 1) * 64 * sizeof(f32x16);
 }
@@ -459,10 +613,38 @@ hipError_t launch_pk(const void* x, const float* gx, const uint8_t* pc, const ui
   return hipGetLastError();
 }
 
+template <int DT, bool QX, int SW, int TPW>
+hipError_t launch_px_t(const void* x, const float* gx, const uint8_t* pc, const uint8_t* ps,
+                       const float* gw, int64_t m, int64_t n, void* out, hipStream_t s) {
+  if (hipError_t e = allow_lds(smallm_px_kernel<DT, QX, SW, TPW>)) return e;
+  const int64_t tiles = (n + 31) / 32;
+  smallm_px_kernel<DT, QX, SW, TPW><<<(int)((tiles + TPW - 1) / TPW), 64 * kPxWaves * TPW,
+                                      px_lds(m, 256 * SW, TPW), s>>>(x, gx, pc, ps, gw, (int)m,
+                                                                      (int)n, out);
+  return hipGetLastError();
+}
+
+template <int DT, bool QX>
+hipError_t launch_px(const void* x, const float* gx, const uint8_t* pc, const uint8_t* ps,
+                     const float* gw, int64_t m, int64_t n, int64_t k, void* out, hipStream_t s) {
+  // Every workgroup rebuilds x_hat for its own use: with the round trip in
+  // the kernel and more than one row, two tiles per workgroup halve that work
+  // per CU (measured faster from m = 2 on); x used as given runs fastest with
+  // one tile per workgroup (more workgroups to spread over the CUs).
+  if (QX && m >= 2)
+    return k == 2048 ? launch_px_t<DT, QX, 8, 2>(x, gx, pc, ps, gw, m, n, out, s)
+                     : launch_px_t<DT, QX, 16, 2>(x, gx, pc, ps, gw, m, n, out, s);
+  return k == 2048 ? launch_px_t<DT, QX, 8, 1>(x, gx, pc, ps, gw, m, n, out, s)
+                   : launch_px_t<DT, QX, 16, 1>(x, gx, pc, ps, gw, m, n, out, s);
+}
+
 template <bool QX>
 hipError_t launch_small_q(int dt, const void* x, const float* gx, const uint8_t* wc,
                           const uint8_t* ws, bool packed, const float* gw, int64_t m, int64_t n,
                           int64_t k, void* out, hipStream_t s) {
+  if (packed && px_ok(m, k))
+    return dt == kF16 ? launch_px<kF16, QX>(x, gx, wc, ws, gw, m, n, k, out, s)
+                      : launch_px<kBF16, QX>(x, gx, wc, ws, gw, m, n, k, out, s);
   if (packed)
     return dt == kF16 ? launch_pk<kF16, QX>(x, gx, wc, ws, gw, m, n, k, out, s)
                       : launch_pk<kBF16, QX>(x, gx, wc, ws, gw, m, n, k, out, s);
@@ -494,6 +676,8 @@ bool small_m_ok(int dt, bool packed, int64_t m, int64_t n, int64_t k) {
 hipError_t launch_small_m(const void* x, int dt, bool quantize_x, const float* gx,
                           const uint8_t* wc, const uint8_t* ws, bool packed, const float* gw,
                           int64_t m, int64_t n, int64_t k, void* out, hipStream_t s) {
+  if (!packed && qmv_rows_ok(dt, m, n, k))  // qmv's register design, one accumulator per row
+    return launch_qmv_rows(x, dt, m, quantize_x, gx, wc, ws, gw, n, out, s);
   return quantize_x ? launch_small_q<true>(dt, x, gx, wc, ws, packed, gw, m, n, k, out, s)
                     : launch_small_q<false>(dt, x, gx, wc, ws, packed, gw, m, n, k, out, s);
 }

@@ -3,8 +3,10 @@ x, k % 128 == 0): qqmm with x's NVFP4 round trip done inside the kernel, and
 qmm with x used as given, on the row-major and the packed weight.
 
 Bars: exact-grid operands bit for bit; general data within the norm-wise
-1e-2 bar and the matrix-core regression guard (the decoded weight is rounded
-to the 16-bit type before the products, as in the large matrix-core kernels);
+1e-2 bar and the matrix-core regression guard (the general kernels round the
+decoded weight to the 16-bit type before the products, as the large
+matrix-core kernels do; at k = 2048 / 4096 the packed path for m <= 8 and the
+row-major path for m <= 2 take exact products and scale each block's sum);
 the in-kernel round trip of x bit-identical to the separate quant-dequant
 pass, for the row-major and the packed kernel."""
 import numpy as np
@@ -147,3 +149,76 @@ def test_small_no_global_scales_and_zero_rows():
     fro, _ = assert_close(host(y), ref, what="small no g")
     assert fro <= MFMA_FRO_GUARD
     assert np.all(host(y)[3] == 0)
+
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("k", [2048, 4096])
+def test_k4096_grid_bit_exact_row_major_and_packed(dtype, m, k):
+    """k = 2048 / 4096, the decode's width: exact-grid x [m, k] and w [300, k]
+    under g_x = 2688, g_w = 336 give the float64 product rounded once, for
+    qqmm and qmm, on the row-major weight (the v_dot2 register path up to two
+    rows) and on the packed weight (the exact-decode block-diagonal kernel up
+    to eight rows; n = 300 ends in a partial 32-row tile)."""
+    say(f"k={k} grid m={m} {dtype}")
+    x = W.grid_tensor(m, k, seed=170 + m)
+    w = W.grid_tensor(300, k, seed=171)
+    od = oracle_dtype(dtype)
+    xd = x.to(dtype).cuda()
+    wc, ws = nv.nvfp4_quantize(w.to(dtype).cuda(), scalar(336.0))
+    packed = nv.nvfp4_mfma_pack(wc, ws)
+    got = {"qmm": nv.nvfp4_qmm(xd, wc, ws, scalar(336.0)),
+           "qmm packed": nv.nvfp4_qmm_packed(xd, packed, scalar(336.0))}
+    if m > 1:
+        got["qqmm"] = nv.nvfp4_qqmm(xd, wc, ws, scalar(2688.0), scalar(336.0))
+    got["qqmm packed"] = nv.nvfp4_qqmm_packed(xd, packed, scalar(2688.0), scalar(336.0))
+    torch.cuda.synchronize()
+    ref = _exact(x.numpy(), w.numpy(), od)
+    for what, y in got.items():
+        assert_values_equal(host(y), ref, f"k={k} grid {what}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("m,n", [(1, 1000), (2, 33), (2, 2049), (3, 300), (5, 14336), (8, 4100)])
+def test_k4096_general(dtype, m, n):
+    """General data at k = 4096 over ragged n: qqmm and qmm against the
+    oracle, row-major and packed; qqmm equals qmm on the separately computed
+    x_hat bit for bit; up to two rows the row-major path gives, row by row,
+    the bits of qmv (the same register design and summation order)."""
+    say(f"k=4096 general m={m} n={n} {dtype}")
+    od = oracle_dtype(dtype)
+    x = W.normal((m, 4096), 1.0, 180 + m, od)
+    w = W.normal((n, 4096), 0.02, 181 + n, od)
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    xd, gx, gw = x.cuda(), scalar(gxh), scalar(gwh)
+    wc, ws = dev(oc), dev(os_)
+    xhat = nv.nvfp4_quant_dequant(xd, gx)
+    y_qmm = nv.nvfp4_qmm(xd, wc, ws, gw)
+    y_xhat = nv.nvfp4_qmm(xhat, wc, ws, gw)
+    y_qqmm = nv.nvfp4_qqmm(xd, wc, ws, gx, gw) if m > 1 else None
+    y_rows = [nv.nvfp4_qmv(xd[i:i + 1], wc, ws, gx, gw) for i in range(m)] if m <= 2 else []
+    packed = nv.nvfp4_mfma_pack(wc, ws) if n % 4 == 0 else None
+    if packed is not None:
+        yp_qqmm = nv.nvfp4_qqmm_packed(xd, packed, gx, gw)
+        yp_qmm = nv.nvfp4_qmm_packed(xd, packed, gw)
+        yp_xhat = nv.nvfp4_qmm_packed(xhat, packed, gw)
+    torch.cuda.synchronize()
+    qmm_ref = _qmm_ref(host(x), oc, os_, gwh, od)
+    qqmm_ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od)
+    fro, _ = assert_close(host(y_qmm), qmm_ref, what="k=4096 qmm")
+    assert fro <= MFMA_FRO_GUARD
+    for i, yr in enumerate(y_rows):
+        assert torch.equal(y_xhat[i:i + 1].view(torch.int16), yr.reshape(1, -1).view(torch.int16)), \
+            f"row {i}: differs from qmv"
+    if m > 1:
+        fro, _ = assert_close(host(y_qqmm), qqmm_ref, what="k=4096 qqmm")
+        assert fro <= MFMA_FRO_GUARD
+        assert torch.equal(y_qqmm.view(torch.int16), y_xhat.view(torch.int16))
+    if packed is not None:
+        fro, _ = assert_close(host(yp_qqmm), qqmm_ref, what="k=4096 qqmm packed")
+        assert fro <= MFMA_FRO_GUARD
+        fro, _ = assert_close(host(yp_qmm), qmm_ref, what="k=4096 qmm packed")
+        assert fro <= MFMA_FRO_GUARD
+        assert torch.equal(yp_qqmm.view(torch.int16), yp_xhat.view(torch.int16))
