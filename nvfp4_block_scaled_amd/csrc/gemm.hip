@@ -427,14 +427,17 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   int tile_m = L % tiles_m;
   int expert = 0, row_lo = 0, row_count = M;
   if constexpr (GATHER) {
-    // seg 0: all of each expert's rows; 1: its whole 256-row tiles only; 2:
-    // the rows past them (fewer than 256, on 128-row tiles)
+    // seg 0: all of each expert's rows; 1: its whole 256-row tiles, plus a
+    // remainder of more than 128 rows on one more (partial) 256-row tile; 2:
+    // a remainder of at most 128 rows, on one 128-row tile
     int acc_tiles = 0;
     expert = -1;
     for (int e = 0; e < E; ++e) {
       const int all = offsets[e + 1] - offsets[e];
-      const int lo = seg == 2 ? all - all % 256 : 0;
-      const int cnt = seg == 1 ? all - all % 256 : all - lo;
+      const int rem = all % 256;
+      const int head = rem > 128 ? all : all - rem;  // the rows of seg 1
+      const int lo = seg == 2 ? head : 0;
+      const int cnt = seg == 1 ? head : all - lo;
       const int tiles = (cnt + TM - 1) / TM;
       if (tile_m < acc_tiles + tiles) {
         expert = e;
@@ -1014,8 +1017,8 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
   constexpr int TM = 32 * RT;
   // tile rows: an upper bound for the gather (per-expert counts live on the
   // device; surplus workgroups return at once)
-  const int64_t tiles_m = seg == 1 ? rows / 256 + 1
-                        : seg == 2 ? 2 * e
+  const int64_t tiles_m = seg == 1 ? rows / 256 + std::min<int64_t>(e, rows / 129)
+                        : seg == 2 ? e
                                    : (rows + TM - 1) / TM + (GATHER ? e : 0);
   const int64_t blocks = tiles_m * ((n + BN - 1) / BN);
 #define NVFP4_LAUNCH(KER, D)                                                                     \
@@ -1053,8 +1056,11 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
     return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
                                              top_k, e, amap, 0, s);
   if constexpr (GATHER) {
-    // each expert's whole 256-row tiles, then its remaining rows on 128-row
-    // tiles: a nearly empty 256-row tile per expert would cost a whole tile
+    // each expert's whole 256-row tiles and any remainder of more than 128
+    // rows on 256-row tiles, then the remainders of at most 128 rows on
+    // 128-row tiles: a nearly empty 256-row tile per expert would cost a
+    // whole tile, while a remainder above 128 rows costs the same MFMA work
+    // either way and, in the first launch, fills the last round of tiles
     // (same summation order for every output either way)
     if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out,
                                                            offsets, perm, top_k, e, amap, 1, s))
