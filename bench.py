@@ -300,6 +300,30 @@ def bench_mx(args, nv, torch, W):
                        frac=flop / ms_gemm / 1e9 / peak, peak=peak, ms_prepass=ms_pre, flop=flop)
         del wp, wsp, xp
         torch.cuda.synchronize()
+        # the decode shape in the mode: one row of x (the streaming kernel),
+        # cold weights rotated as for qmv
+        x1 = W.normal((1, K), 1.0, 3, "bf16", device="cuda")
+        wc, ws = nv.nvfp4_mx_quantize(w, mode)
+        per = wc.numel() + ws.numel()
+        copies = max(2, -(-600_000_000 // per))
+        wcs = [wc.clone() for _ in range(copies)]
+        wss = [ws.clone() for _ in range(copies)]
+        del wc, ws
+        o1 = torch.empty(1, N, dtype=torch.bfloat16, device="cuda")
+        wsp1, _ = nv.mx_qqmm_workspace(mode, 1, N, K, False, "cuda")
+        state = {"i": 0}
+
+        def call():
+            i = state["i"] % copies
+            state["i"] += 1
+            nv.nvfp4_mx_qqmm(x1, wcs[i], wss[i], mode, out=o1, workspace=wsp1)
+
+        settle(call, 0.05)
+        ms_qmv = timed(call, copies * 4, copies, graph=True)
+        nbytes = per + K * 2 + N * 2
+        r[mode]["qmv"] = dict(ms=ms_qmv, gbs=nbytes / ms_qmv / 1e6, bytes=nbytes, copies=copies)
+        del wcs, wss, wsp1
+        torch.cuda.synchronize()
     return r
 
 
@@ -525,7 +549,8 @@ def main():
         for mode, d in res["mx"].items():
             log(f"  {mode}: qqmm {d['ms'] * 1e3:.1f} us ({d['tflops']:.0f} TFLOP/s); product alone "
                 f"{d['ms_gemm'] * 1e3:.1f} us ({d['gemm_tflops']:.0f} TFLOP/s, {100 * d['frac']:.1f} % of "
-                f"{d['peak'] / 1000:.1f} PFLOP/s); x pre-pass {d['ms_prepass'] * 1e3:.1f} us")
+                f"{d['peak'] / 1000:.1f} PFLOP/s); x pre-pass {d['ms_prepass'] * 1e3:.1f} us; "
+                f"qmv {d['qmv']['ms'] * 1e3:.2f} us ({d['qmv']['gbs']:.0f} GB/s)")
     if args.only in ("all", "quantize"):
         log("quantize / dequantize ...")
         res["quantize"] = bench_quantize(args, nv, torch, W)
@@ -598,10 +623,17 @@ def main():
                                                     "us": round(d["ms_gemm"] * 1e3, 2),
                                                     "peak": d["peak"], "frac": round(d["frac"], 4),
                                                     "kernel": f"mx_gemm_kernel<bf16, {4 if mode == 'mxfp4' else 8}>"},
-                                  "x_prepass_us": round(d["ms_prepass"] * 1e3, 2)}
+                                  "x_prepass_us": round(d["ms_prepass"] * 1e3, 2),
+                                  "qmv": {"GBps": round(d["qmv"]["gbs"], 1), "unit": "GB/s",
+                                          "frac": round(d["qmv"]["gbs"] / PEAK_HBM_GBS, 4),
+                                          "us_per_launch": round(d["qmv"]["ms"] * 1e3, 3),
+                                          "algorithmic_bytes_per_launch": d["qmv"]["bytes"],
+                                          "weight_copies_rotated": d["qmv"]["copies"],
+                                          "kernel": f"mx_qmv_kernel<bf16, {4 if mode == 'mxfp4' else 8}>"}}
                            for mode, d in res["mx"].items()}
         line["mx_qqmm"]["workload"] = ("qqmm x bf16 [2048,4096] (quantized in the mode) @ w [14336,4096]^T "
-                                       "in mxfp4 / mxfp8 (packed once), bf16 out")
+                                       "in mxfp4 / mxfp8 (packed once), bf16 out; qmv: x bf16 [1,4096] "
+                                       "@ the row-major mx weight, cold weights")
     if "quantize" in res:
         line["quantize"] = {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["frac"], 4),
                                  "us": round(v["ms"] * 1e3, 3), "bytes": v["bytes"]}

@@ -491,7 +491,8 @@ nvfp4_status nvfp4_mx_mm_packed(const uint8_t* x_packed_codes, const uint8_t* x_
  * nvfp4_mx_qqmm_workspace_size -- bytes of workspace nvfp4_mx_qqmm (packed_w
  * = 0) or nvfp4_mx_qqmm_packed (packed_w = 1) needs: x's packed codes and
  * scales, and for a row-major weight its packed copy, each 256-byte aligned.
- * 0 for invalid sizes.
+ * 0 for invalid sizes, and 0 for nvfp4_mx_qqmm with m = 1 and k = 4096 (the
+ * matrix-vector kernel uses none).
  */
 size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k,
                                     int packed_w);
@@ -502,11 +503,15 @@ size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, in
  * same mode (page 8, qqmm: the mode selects both operands' group size and
  * scale type), w is given quantized [n, k]; the products of the two decodes
  * are exact in float32 and summed in float32 by the matrix cores; out of
- * type dt.  nvfp4_mx_qqmm_packed takes the weight as its packed copy.
+ * type dt.  nvfp4_mx_qqmm_packed takes the weight as its packed copy.  With
+ * one row of x (m = 1) and k = 4096, nvfp4_mx_qqmm runs a matrix-vector
+ * kernel on the row-major weight instead: per group of 32 the code values'
+ * dot product (exact products, float32 sums) times both groups' scales.
  *   x        device, 16-byte aligned
  *   w_codes  device, 16-byte aligned (row-major) / packed copy
  *   out      device [m, n], 16-byte aligned
  *   workspace  device, nvfp4_mx_qqmm_workspace_size() bytes, 256-byte aligned
+ *            (may be NULL when that size is 0)
  * Errors: bad dtype or mode, m, n <= 0, k not a positive multiple of 32, NULL
  * or misaligned pointer, workspace too small, operands too large (a packed
  * operand of 2 GB or more).

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["codec.hip", "qmv.hip", "gemm.hip", "smallm.hip", "mx_codec.hip", "mx_gemm.hip", "gather_ex.hip", "capi.hip"]
+SOURCES = ["codec.hip", "qmv.hip", "gemm.hip", "smallm.hip", "mx_codec.hip", "mx_gemm.hip", "mx_qmv.hip", "gather_ex.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

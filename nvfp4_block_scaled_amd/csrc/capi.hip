@@ -929,6 +929,7 @@ MxLayout mx_layout(int mode, int64_t m, int64_t n, int64_t k, bool packed_w) {
 size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k,
                                     int packed_w) {
   if (!mx_mode_ok(mode) || m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return 0;
+  if (!packed_w && nvfp4::mx_qmv_ok(m, n, k)) return 0;  // the matrix-vector kernel needs none
   return mx_layout(mode, m, n, k, packed_w != 0).total;
 }
 
@@ -946,9 +947,16 @@ static nvfp4_status mx_qqmm_common(const char* op, const void* x, nvfp4_dtype dt
       nvfp4::mx_packed_code_bytes(m, k, mode) >= nvfp4::kMxMaxPackedBytes ||
       nvfp4::mx_packed_code_bytes(n, k, mode) >= nvfp4::kMxMaxPackedBytes)
     return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Sizes too large (a packed operand of 2 GB or more).", op);
+  return NVFP4_OK;
+}
+
+static nvfp4_status mx_workspace_ok(const char* op, void* workspace, size_t workspace_bytes, size_t need) {
+  if (need == 0) return NVFP4_OK;
   if (workspace == nullptr || !aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] workspace must be a 256-byte aligned device buffer.", op);
-  (void)workspace_bytes;
+  if (workspace_bytes < need)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] workspace of %zu bytes is smaller than %zu.", op,
+                workspace_bytes, need);
   return NVFP4_OK;
 }
 
@@ -960,11 +968,11 @@ nvfp4_status nvfp4_mx_qqmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
   if (nvfp4_status st =
           mx_qqmm_common(op, x, dt, mode, w_codes, w_scales, m, n, k, out, workspace, workspace_bytes))
     return st;
+  const bool qmv = nvfp4::mx_qmv_ok(m, n, k);  // one row of x: the streaming matrix-vector kernel
   const MxLayout l = mx_layout(mode, m, n, k, false);
-  if (workspace_bytes < l.total)
-    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_qqmm] workspace of %zu bytes is smaller than %zu.",
-                workspace_bytes, l.total);
+  if (nvfp4_status st = mx_workspace_ok(op, workspace, workspace_bytes, qmv ? 0 : l.total)) return st;
   if (nvfp4_status st = check_device(op)) return st;
+  if (qmv) return launched(op, nvfp4::launch_mx_qmv(x, dt, mode, w_codes, w_scales, n, out, stream));
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   hipError_t e = nvfp4::launch_mx_pack(w_codes, w_scales, mode, n, k, base + l.wc, base + l.ws, stream);
   if (e == hipSuccess)
@@ -984,9 +992,7 @@ nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode m
                                        workspace, workspace_bytes))
     return st;
   const MxLayout l = mx_layout(mode, m, n, k, true);
-  if (workspace_bytes < l.total)
-    return fail(NVFP4_ERR_INVALID_ARGUMENT,
-                "[mx_qqmm_packed] workspace of %zu bytes is smaller than %zu.", workspace_bytes, l.total);
+  if (nvfp4_status st = mx_workspace_ok(op, workspace, workspace_bytes, l.total)) return st;
   if (nvfp4_status st = check_device(op)) return st;
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   hipError_t e = nvfp4::launch_mx_quantize_packed(x, dt, mode, m, k, base + l.xc, base + l.xs, stream);

@@ -1,0 +1,221 @@
+// mx_qmv.hip -- the mx modes' matrix-vector product for gfx950: qqmm in
+// mxfp4 / mxfp8 with one row of x,
+//     out[n] = T( sum_k x_hat[k] * w_hat[n, k] ),
+// x_hat the mx round trip of x (its own E8M0 scale per group of 32) and w_hat
+// the decode of the mx weight, both kept as float32 values, not rounded to T
+// ("mlx 0.30.7.2 -> 0.30.7.6" diff, page 8, qqmm with the fp modes; page 7,
+// QQMatmul::eval_gpu and the matrix-vector path of the fp modes).
+//
+// HBM-bound like the NVFP4 qmv, with the same design (k = 4096): every wave
+// owns up to R consecutive weight rows and issues all of their loads first;
+// meanwhile the workgroup quantizes x into LDS; then each lane keeps its
+// pieces of x in registers.  Load j of a wave reads bytes 1024 j .. + 1023 of
+// a row's codes, 16 per lane: a whole group of 32 (mxfp4) or half of one
+// (mxfp8).  Within a piece both operands carry one power-of-two scale each,
+// so the piece's partial sum runs over the unscaled code values (exact bf16
+// values -- e2m1 or e4m3 -- in v_dot2_f32_bf16, whose products are exact,
+// float32 sums) and is then multiplied by 2^(s_w - 127) and by 2^(s_x - 127),
+// both exact scalings of a float32.
+#include "mx_device.h"
+#include "nvfp4_device.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kMxqWaves = 8;
+constexpr int kMxqThreads = 64 * kMxqWaves;
+constexpr int kMxqMaxRows = 8;
+constexpr int kMxqK = 4096;
+
+// Per row and lane: NP pieces of 16 code bytes, EP = 128 / BITS elements
+// each (32 = a group for mxfp4, 16 = half a group for mxfp8), and the
+// piece's scale byte.
+template <int BITS> struct MxqShape {
+  static constexpr int NP = kMxqK * BITS / 8 / 1024;  // pieces per row and lane
+  static constexpr int EP = 128 / BITS;               // elements per piece
+  static constexpr int PP = EP / 2;                   // bf16 pairs per piece
+};
+struct MxqPiece {
+  u32x4 c;
+  uint32_t s;
+};
+
+// The bf16 pairs of a piece's codes, element order.
+template <int BITS>
+__device__ __forceinline__ void mxq_pairs(u32x4 cv, bf16x2 (&d)[MxqShape<BITS>::PP]) {
+  const uint32_t c[4] = {cv.x, cv.y, cv.z, cv.w};
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d[4 * i] = e2m1_decode2_bf16<0>(c[i]);
+      d[4 * i + 1] = e2m1_decode2_bf16<1>(c[i]);
+      d[4 * i + 2] = e2m1_decode2_bf16<2>(c[i]);
+      d[4 * i + 3] = e2m1_decode2_bf16<3>(c[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false);
+      d[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true);
+    }
+  }
+}
+
+template <int DT, int BITS, int R>
+__global__ void __launch_bounds__(kMxqThreads)
+mx_qmv_kernel(const void* __restrict__ x, const uint8_t* __restrict__ wc,
+              const uint8_t* __restrict__ ws, int n, void* __restrict__ out) {
+  constexpr int K = kMxqK;
+  constexpr int kRowCodeBytes = K * BITS / 8;
+  constexpr int NP = MxqShape<BITS>::NP, EP = MxqShape<BITS>::EP, PP = MxqShape<BITS>::PP;
+  __shared__ __attribute__((aligned(16))) u32x4 xq[K / 8];  // x's code values as bf16, 8 per entry
+  __shared__ float xsc[K / 32];                              // x's group scales 2^(s - 127)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // 1. this thread's 8 elements of x (a quarter group), first in the queue
+  float xv[8];
+  load8x<DT>(x, tid, xv);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. every weight load of this wave's R rows (rows past n re-read row n - 1)
+  const int r0 = (blockIdx.x * kMxqWaves + wave) * R;
+  MxqPiece wp[R][NP];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int r = min(r0 + i, n - 1);
+    const uint8_t* crow = wc + (int64_t)r * kRowCodeBytes;
+    const uint8_t* srow = ws + (int64_t)r * (K / 32);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int e0 = EP * (64 * j + lane);  // first element of the piece
+      wp[i][j].c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + 1024 * j + 16 * lane));
+      wp[i][j].s = __builtin_nontemporal_load(srow + e0 / 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // rows arrive in the order they are used
+  }
+
+  // 3. the mx round trip of x: the group amax over the four lanes of a group,
+  //    the E8M0 scale, the codes; their values (unscaled) into LDS as bf16
+  {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, __builtin_fabsf(xv[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    float enc_b;
+    const uint32_t s = mx_scale<BITS>(a, enc_b);
+    u32x4 t;
+    if constexpr (BITS == 4) {
+      const uint32_t w = mx_codes4(xv, enc_b);
+      t.x = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<0>(w));
+      t.y = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<1>(w));
+      t.z = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<2>(w));
+      t.w = __builtin_bit_cast(uint32_t, e2m1_decode2_bf16<3>(w));
+    } else {
+      const u32x2 w = mx_codes8(xv, enc_b);
+      t.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+      t.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+      t.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+      t.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+    }
+    xq[tid] = t;
+    if ((tid & 3) == 0) xsc[tid >> 2] = e8m0_value(s);
+  }
+  lds_barrier();  // the weight loads stay in flight
+
+  // 4. this lane's pieces of x: code values and scales
+  uint32_t xp[NP][PP];
+  float sx[NP];
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int e0 = EP * (64 * j + lane);
+#pragma unroll
+    for (int q = 0; q < EP / 8; ++q) {
+      const u32x4 t = xq[e0 / 8 + q];
+      xp[j][4 * q] = t.x;
+      xp[j][4 * q + 1] = t.y;
+      xp[j][4 * q + 2] = t.z;
+      xp[j][4 * q + 3] = t.w;
+    }
+    sx[j] = xsc[e0 / 32];
+  }
+
+  // 5. rows: per group the code-value dot product, times 2^(s_w - 127) and
+  //    2^(s_x - 127); lane i keeps row r0 + i
+  float mine = 0.0f;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      bf16x2 d[PP];
+      mxq_pairs<BITS>(wp[i][j].c, d);
+      float p = 0.0f;
+#pragma unroll
+      for (int u = 0; u < PP; ++u)
+        p = __builtin_amdgcn_fdot2_f32_bf16(d[u], __builtin_bit_cast(bf16x2, xp[j][u]), p, false);
+      float t;
+      {
+#pragma clang fp contract(off)
+        t = p * e8m0_value(wp[i][j].s & 0xFFu);
+      }
+      acc = __builtin_fmaf(t, sx[j], acc);
+    }
+    const float v = wave_sum_uniform(acc);
+    mine = (lane == i) ? v : mine;
+    __builtin_amdgcn_sched_barrier(0);  // consume rows in load order
+  }
+  if (lane < R && r0 + lane < n) reinterpret_cast<typename Elem<DT>::T*>(out)[r0 + lane] = from_f32<DT>(mine);
+}
+
+template <int DT, int BITS, int R>
+void launch_r(const void* x, const uint8_t* wc, const uint8_t* ws, int64_t n, void* out,
+              int64_t blocks, hipStream_t s) {
+  mx_qmv_kernel<DT, BITS, R><<<(int)blocks, kMxqThreads, 0, s>>>(x, wc, ws, (int)n, out);
+}
+
+template <int DT, int BITS>
+hipError_t launch_t(const void* x, const uint8_t* wc, const uint8_t* ws, int64_t n, void* out,
+                    hipStream_t s) {
+  // at least one workgroup per CU, at most kMxqMaxRows rows per wave
+  int64_t blocks = (n + kMxqWaves * kMxqMaxRows - 1) / (kMxqWaves * kMxqMaxRows);
+  if (blocks < 256) blocks = 256;
+  const int rpw = (int)((n + blocks * kMxqWaves - 1) / (blocks * kMxqWaves));
+  blocks = (n + (int64_t)kMxqWaves * rpw - 1) / ((int64_t)kMxqWaves * rpw);
+  switch (rpw) {
+    case 1: launch_r<DT, BITS, 1>(x, wc, ws, n, out, blocks, s); break;
+    case 2: launch_r<DT, BITS, 2>(x, wc, ws, n, out, blocks, s); break;
+    case 3: launch_r<DT, BITS, 3>(x, wc, ws, n, out, blocks, s); break;
+    case 4: launch_r<DT, BITS, 4>(x, wc, ws, n, out, blocks, s); break;
+    case 5: launch_r<DT, BITS, 5>(x, wc, ws, n, out, blocks, s); break;
+    case 6: launch_r<DT, BITS, 6>(x, wc, ws, n, out, blocks, s); break;
+    case 7: launch_r<DT, BITS, 7>(x, wc, ws, n, out, blocks, s); break;
+    default: launch_r<DT, BITS, 8>(x, wc, ws, n, out, blocks, s); break;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const void* x, int dt, const uint8_t* wc, const uint8_t* ws, int64_t n,
+                       void* out, hipStream_t s) {
+  switch (dt) {
+    case kF32: return launch_t<kF32, BITS>(x, wc, ws, n, out, s);
+    case kF16: return launch_t<kF16, BITS>(x, wc, ws, n, out, s);
+    default: return launch_t<kBF16, BITS>(x, wc, ws, n, out, s);
+  }
+}
+
+}  // namespace
+
+bool mx_qmv_ok(int64_t m, int64_t n, int64_t k) { return m == 1 && k == kMxqK && n >= 1 && n < 0x7FFFFFFF; }
+
+hipError_t launch_mx_qmv(const void* x, int dt, int mode, const uint8_t* wc, const uint8_t* ws,
+                         int64_t n, void* out, hipStream_t s) {
+  return mode == 8 ? launch_bits<8>(x, dt, wc, ws, n, out, s) : launch_bits<4>(x, dt, wc, ws, n, out, s);
+}
+
+}  // namespace nvfp4

@@ -207,6 +207,49 @@ def test_mx_qqmm_general(mode, dtype, m, n, k):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("n", [300, 1000])
+def test_mx_qmv_exact_on_grid_operands(mode, dtype, n):
+    """One row of x at k = 4096 (the matrix-vector kernel): grid operands
+    round-trip exactly and every partial sum is exact in float32 (mxfp8: x
+    nonzero in 8 groups only, so that the sum stays within 24 bits), so the
+    product equals the float64 product rounded once."""
+    say(f"mx qmv grid {mode} {dtype} n={n}")
+    x = _grid(1, 4096, mode, 41, [0, -1])
+    if mode == "mxfp8":
+        keep = np.zeros(128, bool)
+        keep[np.random.default_rng(42).choice(128, 8, replace=False)] = True
+        x = (x.reshape(1, 128, 32) * keep[None, :, None]).reshape(1, 4096).astype(np.float32)
+    w = _grid(n, 4096, mode, 43, [-2, -1])
+    oc, os_ = O.mx_quantize(w, mode)
+    y = nv.nvfp4_mx_qqmm(torch.from_numpy(x).to(dtype).cuda(), dev(oc), dev(os_), mode)
+    torch.cuda.synchronize()
+    od = oracle_dtype(dtype)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    ref = np.array([[O.round_to(float(v), od) for v in row] for row in exact], np.float32)
+    assert_values_equal(host(y), ref, f"mx qmv grid {dtype}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype,n", [(torch.bfloat16, 1), (torch.bfloat16, 14336), (torch.float16, 77),
+                                     (torch.float16, 1000), (torch.float32, 77), (torch.float32, 1000)])
+def test_mx_qmv_general(mode, dtype, n):
+    """One row of x at k = 4096, general data (x N(0, 1), w N(0, 0.02)):
+    the oracle's bar and the float32-summation guard, n from one row to the
+    decode shape's 14336 (several rows per wave, a partial last wave)."""
+    say(f"mx qmv {mode} {dtype} n={n}")
+    od = oracle_dtype(dtype)
+    x = W.normal((1, 4096), 1.0, 550 + n, od)
+    w = W.normal((n, 4096), 0.02, 551 + n, od)
+    oc, os_ = O.mx_quantize(host(w), mode)
+    y = nv.nvfp4_mx_qqmm(x.cuda(), dev(oc), dev(os_), mode)
+    torch.cuda.synchronize()
+    ref = O.mx_qqmm(host(x), oc, os_, mode, dtype=od)
+    fro, _ = assert_close(host(y), ref, what=f"mx qmv {mode}")
+    assert fro <= MX_FRO_GUARD
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_mx_qqmm_prefill_14336x4096(mode):
     """The prefill shape x bf16 [2048, 4096] N(0, 1), w [14336, 4096] from
     N(0, 0.02), both in the mx mode; every 97th column and every 7th row
