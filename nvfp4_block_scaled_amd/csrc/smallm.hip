@@ -28,7 +28,7 @@
 //     tile as the first operand and the x rows (padded by repeating the last
 //     row, whose products are never stored) as the second;
 //   * the k parts of a tile are summed through LDS in a fixed order.
-// Packed weight with k = 2048 / 4096 and m <= 8 (smallm_px_kernel): the codes
+// Packed weight with k = 2048 / 4096 and m <= 16 (smallm_px_kernel): the codes
 // decoded exactly, one block of 16 per matrix-core product, each block's
 // partial sums scaled in float32 (described at the kernel).  Row-major weight
 // with k = 4096 and m <= 2: qmv's register kernel with one accumulator per row
@@ -427,13 +427,14 @@ smallm_pk_kernel(const void* __restrict__ x, const float* __restrict__ gx,
 // i < 16 see only the block of lane half 0 and rows i >= 16 only that of lane
 // half 1: with dwords 0, 1 the MFMA pair gives block 0 in rows i and block 2 in
 // rows 16 + i, with dwords 2, 3 blocks 1 and 3.  Output lane l holds rows
-// 8 (v / 4) + 4 h + v % 4 of column n, so x row m = 4 h + v (v < 4) sits in
-// elements v (blocks 0 / 1) and 8 + v (blocks 2 / 3) of one lane.
+// 8 (v / 4) + 4 h + v % 4 of column n, so x row m = 8 (v / 4) + 4 h + v % 4
+// (v < MV: 4 accumulators cover m < 8, 8 cover m < 16) sits in elements v
+// (blocks 0 / 1) and 8 + v (blocks 2 / 3) of one lane.
 
 constexpr int kPxWaves = 4;  // waves per tile: its k quarters
-constexpr int kPxMaxM = 8;
+constexpr int kPxMaxM = 16;
 
-template <int DT, bool QX, int SW, int TPW>
+template <int DT, bool QX, int SW, int TPW, int MV>
 __global__ void __launch_bounds__(64 * kPxWaves * TPW)
 smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
                  const uint8_t* __restrict__ pc, const uint8_t* __restrict__ ps,
@@ -447,6 +448,7 @@ smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   extern __shared__ __attribute__((aligned(16))) uint8_t sm_lds[];
   T* const xs = reinterpret_cast<T*>(sm_lds);  // M rows of x_hat, then a zero row
   f32x4* const red = reinterpret_cast<f32x4*>(sm_lds + (size_t)(M + 1) * ldr * sizeof(T));
+  constexpr int NV4 = MV / 4;  // f32x4 per lane in the k-quarter reduction
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -486,7 +488,9 @@ smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   const int xi = li - 16 * h;  // x row of this lane's first-operand slots
   const T* const xrow = xs + (size_t)((xi >= 0 && xi < M) ? xi : M) * ldr + 32 * h;
   const f32x16 zero = {};
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[MV];
+#pragma unroll
+  for (int v = 0; v < MV; ++v) acc[v] = 0.0f;
 #pragma unroll
   for (int s = 0; s < SW; ++s) {
     const T* xp = xrow + kPkStep * (quarter * SW + s);
@@ -522,7 +526,7 @@ smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
       se[3] = e4m3_decode_byte<3>(wp[s].scale) * dec_w;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < MV; ++v) {
       acc[v] = __builtin_fmaf(pa[v], se[0], acc[v]);
       acc[v] = __builtin_fmaf(pb[v], se[1], acc[v]);
       acc[v] = __builtin_fmaf(pa[8 + v], se[2], acc[v]);
@@ -531,21 +535,29 @@ smallm_px_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
 
   // 4. the four k quarters of a tile summed in order; lane (n, h) holds x
-  //    rows 4 h .. + 3
+  //    rows 8 (v / 4) + 4 h + v % 4
   const int slot = (wave / kPxWaves) * (kPxWaves - 1);
-  if (quarter > 0) red[(slot + quarter - 1) * 64 + lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  if (quarter > 0) {
+#pragma unroll
+    for (int c = 0; c < NV4; ++c)
+      red[((slot + quarter - 1) * NV4 + c) * 64 + lane] =
+          f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+  }
   lds_barrier();
   if (quarter == 0) {
 #pragma unroll
     for (int p = 0; p < kPxWaves - 1; ++p) {
-      const f32x4 r = red[(slot + p) * 64 + lane];
-      acc[0] += r.x; acc[1] += r.y; acc[2] += r.z; acc[3] += r.w;
+#pragma unroll
+      for (int c = 0; c < NV4; ++c) {
+        const f32x4 r = red[((slot + p) * NV4 + c) * 64 + lane];
+        acc[4 * c] += r.x; acc[4 * c + 1] += r.y; acc[4 * c + 2] += r.z; acc[4 * c + 3] += r.w;
+      }
     }
     const int n = 32 * tile + li;
     if (n < N) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * h + v;
+      for (int v = 0; v < MV; ++v) {
+        const int m = 8 * (v / 4) + 4 * h + v % 4;
         if (m < M) reinterpret_cast<T*>(out)[(int64_t)m * N + n] = from_f32<DT>(acc[v]);
       }
     }
@@ -559,9 +571,12 @@ size_t rm_lds(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(k + 8) * 2 + (size_t)(kSmWaves - 1) * 64 * sizeof(f32x4);
 }
 size_t px_lds(int64_t m, int64_t k, int tpw) {
-  return (size_t)(m + 1) * (size_t)(k + 16) * 2 + (size_t)tpw * (kPxWaves - 1) * 64 * sizeof(f32x4);
+  const int64_t nv4 = m > 8 ? 2 : 1;
+  return (size_t)(m + 1) * (size_t)(k + 16) * 2 + (size_t)(tpw * nv4) * (kPxWaves - 1) * 64 * sizeof(f32x4);
 }
-bool px_ok(int64_t m, int64_t k) { return m >= 1 && m <= kPxMaxM && (k == 2048 || k == 4096); }
+bool px_ok(int64_t m, int64_t k) {
+  return m >= 1 && m <= kPxMaxM && (k == 2048 || k == 4096) && px_lds(m, k, 2) <= kSmallMaxLds;
+}
 size_t pk_lds(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(k + 8) * 2 + (size_t)(kSmWaves - 1) * 64 * sizeof(f32x16);
 }
@@ -613,14 +628,14 @@ hipError_t launch_pk(const void* x, const float* gx, const uint8_t* pc, const ui
   return hipGetLastError();
 }
 
-template <int DT, bool QX, int SW, int TPW>
+template <int DT, bool QX, int SW, int TPW, int MV>
 hipError_t launch_px_t(const void* x, const float* gx, const uint8_t* pc, const uint8_t* ps,
                        const float* gw, int64_t m, int64_t n, void* out, hipStream_t s) {
-  if (hipError_t e = allow_lds(smallm_px_kernel<DT, QX, SW, TPW>)) return e;
+  if (hipError_t e = allow_lds(smallm_px_kernel<DT, QX, SW, TPW, MV>)) return e;
   const int64_t tiles = (n + 31) / 32;
-  smallm_px_kernel<DT, QX, SW, TPW><<<(int)((tiles + TPW - 1) / TPW), 64 * kPxWaves * TPW,
-                                      px_lds(m, 256 * SW, TPW), s>>>(x, gx, pc, ps, gw, (int)m,
-                                                                      (int)n, out);
+  smallm_px_kernel<DT, QX, SW, TPW, MV><<<(int)((tiles + TPW - 1) / TPW), 64 * kPxWaves * TPW,
+                                          px_lds(m, 256 * SW, TPW), s>>>(x, gx, pc, ps, gw, (int)m,
+                                                                          (int)n, out);
   return hipGetLastError();
 }
 
@@ -631,11 +646,16 @@ hipError_t launch_px(const void* x, const float* gx, const uint8_t* pc, const ui
   // the kernel and more than one row, two tiles per workgroup halve that work
   // per CU (measured faster from m = 2 on); x used as given runs fastest with
   // one tile per workgroup (more workgroups to spread over the CUs).
+  // Above 8 rows x fills most of the LDS (one workgroup per CU): two tiles
+  // per workgroup keep the grid within one round of the CUs.
+  if (m > 8)
+    return k == 2048 ? launch_px_t<DT, QX, 8, 2, 8>(x, gx, pc, ps, gw, m, n, out, s)
+                     : launch_px_t<DT, QX, 16, 2, 8>(x, gx, pc, ps, gw, m, n, out, s);
   if (QX && m >= 2)
-    return k == 2048 ? launch_px_t<DT, QX, 8, 2>(x, gx, pc, ps, gw, m, n, out, s)
-                     : launch_px_t<DT, QX, 16, 2>(x, gx, pc, ps, gw, m, n, out, s);
-  return k == 2048 ? launch_px_t<DT, QX, 8, 1>(x, gx, pc, ps, gw, m, n, out, s)
-                   : launch_px_t<DT, QX, 16, 1>(x, gx, pc, ps, gw, m, n, out, s);
+    return k == 2048 ? launch_px_t<DT, QX, 8, 2, 4>(x, gx, pc, ps, gw, m, n, out, s)
+                     : launch_px_t<DT, QX, 16, 2, 4>(x, gx, pc, ps, gw, m, n, out, s);
+  return k == 2048 ? launch_px_t<DT, QX, 8, 1, 4>(x, gx, pc, ps, gw, m, n, out, s)
+                   : launch_px_t<DT, QX, 16, 1, 4>(x, gx, pc, ps, gw, m, n, out, s);
 }
 
 template <bool QX>

@@ -5,7 +5,7 @@ qmm with x used as given, on the row-major and the packed weight.
 Bars: exact-grid operands bit for bit; general data within the norm-wise
 1e-2 bar and the matrix-core regression guard (the general kernels round the
 decoded weight to the 16-bit type before the products, as the large
-matrix-core kernels do; at k = 2048 / 4096 the packed path for m <= 8 and the
+matrix-core kernels do; at k = 2048 / 4096 the packed path for m <= 16 and the
 row-major path for m <= 2 take exact products and scale each block's sum);
 the in-kernel round trip of x bit-identical to the separate quant-dequant
 pass, for the row-major and the packed kernel."""
@@ -153,14 +153,14 @@ def test_small_no_global_scales_and_zero_rows():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16])
 @pytest.mark.parametrize("k", [2048, 4096])
 def test_k4096_grid_bit_exact_row_major_and_packed(dtype, m, k):
     """k = 2048 / 4096, the decode's width: exact-grid x [m, k] and w [300, k]
     under g_x = 2688, g_w = 336 give the float64 product rounded once, for
     qqmm and qmm, on the row-major weight (the v_dot2 register path up to two
     rows) and on the packed weight (the exact-decode block-diagonal kernel up
-    to eight rows; n = 300 ends in a partial 32-row tile)."""
+    to sixteen rows; n = 300 ends in a partial 32-row tile)."""
     say(f"k={k} grid m={m} {dtype}")
     x = W.grid_tensor(m, k, seed=170 + m)
     w = W.grid_tensor(300, k, seed=171)
@@ -180,7 +180,8 @@ def test_k4096_grid_bit_exact_row_major_and_packed(dtype, m, k):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("m,n", [(1, 1000), (2, 33), (2, 2049), (3, 300), (5, 14336), (8, 4100)])
+@pytest.mark.parametrize("m,n", [(1, 1000), (2, 33), (2, 2049), (3, 300), (5, 14336), (8, 4100), (12, 300),
+                                 (16, 14336)])
 def test_k4096_general(dtype, m, n):
     """General data at k = 4096 over ragged n: qqmm and qmm against the
     oracle, row-major and packed; qqmm equals qmm on the separately computed
