@@ -61,8 +61,8 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "944a32d3f0be4b70", 367361007),
-    "qmv": ("qmv.hip", "398791562fdfbd6a", 33246725),
+    "gemm": ("gemm.hip", "f3c48a52033310bd", 367367363),
+    "qmv": ("qmv.hip", "fa66de6e5e1bafa1", 33246727),
 }
 
 
