@@ -49,10 +49,10 @@ amap_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ lhs, i
 
 // 128 x 128 output tiles, k steps of 64.  The weight tile (64 rows of k, 128
 // columns of n: 64 code bytes and 8 scales per row) is decoded once per
-// workgroup -- each thread 16 consecutive columns of two rows, 16 columns
-// sharing one block scale -- and written transposed into LDS as [n][k], so
-// that both operand fragments of the 32x32x16 MFMA are 16-byte LDS reads (8 k
-// values of one row).  The next step's raw operands are fetched into
+// workgroup -- each thread 8 consecutive columns (one block scale per row) of
+// 4 consecutive rows -- and written transposed into LDS as [n][k], 4 k values
+// of a column per 8-byte store, so that both operand fragments of the
+// 32x32x16 MFMA are 16-byte LDS reads (8 k values of one row).  The next step's raw operands are fetched into
 // registers before this step's MFMAs.  The A rows are gathered through perm /
 // amap as in the other gather kernels.
 constexpr int kTT = 128;
@@ -129,19 +129,19 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
   // A: thread t loads tile row t / 2, k 32 (t % 2) .. + 31 (four 16-byte pieces)
   const int ar = tid >> 1, ah = tid & 1;
   const int64_t arow = arow_s[ar];
-  // B: thread t decodes weight rows k0 + t / 8 and k0 + 32 + t / 8, columns
-  // bn + 16 (t % 8) .. + 15
-  const int bk = tid >> 3, bc = tid & 7;
-  const int bcol = bn + 16 * bc;
+  // B: thread t decodes weight rows k0 + 4 (t / 16) .. + 3, columns
+  // bn + 8 (t % 16) .. + 7 (whole 8-column groups: n is a multiple of 16)
+  const int bk = 4 * (tid >> 4), bc = tid & 15;
+  const int bcol = bn + 8 * bc;
   // LDS slot of B element (n, k): 16-byte chunk k / 8 of row n in slot
-  // (k / 8) ^ ((n / 16) % 8), so that the decode's writes (16 rows n = 16 c +
-  // i of one column k across the threads' c) spread over the banks
+  // (k / 8) ^ ((n / 16) % 8), so that the decode's writes (rows n = 8 c + i
+  // across the threads' c) spread over the banks
   auto lb_at = [](int n, int k) { return n * kPitch + (((k >> 3) ^ ((n >> 4) & 7)) << 3) + (k & 7); };
 
   // the next step's raw operands, fetched before this step's MFMAs
   u32x4 ra[4];
-  u32x2 rcode[2];
-  uint32_t rscale[2];
+  uint32_t rcode[4];
+  uint32_t rscale[4];
   auto fetch = [&](int k0) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -151,12 +151,12 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
         ra[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int k = k0 + bk + 32 * r;
-      rcode[r] = u32x2{0u, 0u};
+    for (int r = 0; r < 4; ++r) {
+      const int k = k0 + bk + r;
+      rcode[r] = 0u;
       rscale[r] = 0u;
       if (k < K && bcol < N) {
-        rcode[r] = *reinterpret_cast<const u32x2*>(wce + (int64_t)k * (N / 2) + bcol / 2);
+        rcode[r] = *reinterpret_cast<const uint32_t*>(wce + (int64_t)k * (N / 2) + bcol / 2);
         rscale[r] = wse[(int64_t)k * (N / 16) + bcol / 16];
       }
     }
@@ -173,25 +173,30 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
     // stage this step: A as loaded, B decoded (zeros past k or n decode to 0)
 #pragma unroll
     for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4*>(&la[ar * kPitch + 32 * ah + 8 * h]) = ra[h];
+    {
+      typedef T T4 __attribute__((ext_vector_type(4)));
+      T4 col[8];  // column i: rows bk .. bk + 3
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      float se;
-      {
-#pragma clang fp contract(off)
-        se = e4m3_decode(rscale[r]) * dec_w;
-      }
-      float q[16];
-      e2m1_decode8_f32(rcode[r].x, *reinterpret_cast<float(*)[8]>(q));
-      e2m1_decode8_f32(rcode[r].y, *reinterpret_cast<float(*)[8]>(q + 8));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v;
+      for (int r = 0; r < 4; ++r) {
+        float se;
         {
 #pragma clang fp contract(off)
-          v = q[i] * se;
+          se = e4m3_decode(rscale[r]) * dec_w;
         }
-        lb[lb_at(16 * bc + i, bk + 32 * r)] = from_f32<DT>(v);
+        float q[8];
+        e2m1_decode8_f32(rcode[r], q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float v;
+          {
+#pragma clang fp contract(off)
+            v = q[i] * se;
+          }
+          col[i][r] = from_f32<DT>(v);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<T4*>(&lb[lb_at(8 * bc + i, bk)]) = col[i];
     }
     __syncthreads();
     if (k0 + kTK < K) fetch(k0 + kTK);
