@@ -74,6 +74,10 @@ int nvfp4_version(void);
  * cotangent amax of QQMatmul::vjp, diff page 8, is the same reduction).
  *   x         device, n elements of type dt
  *   amax_out  device, 1 float; written (n == 0 gives 0)
+ * One kernel launch; its workgroups reduce through one of 64 library-owned
+ * device words, taken in turn per call, so up to 64 calls may be in flight at
+ * once on different streams (a captured graph keeps its word: do not replay
+ * one graph on two streams at once).
  * Errors: NULL pointer, n < 0, bad dtype.
  */
 nvfp4_status nvfp4_tensor_amax(const void* x, nvfp4_dtype dt, int64_t n, float* amax_out,

@@ -8,6 +8,8 @@
 // loading 8 consecutive elements (16 B for 16-bit types), which keeps every
 // wave's loads and stores contiguous; the pair exchanges its half-block
 // amax with one lane swap.
+#include <atomic>
+
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -22,16 +24,28 @@ constexpr int kThreads = 256;
 constexpr int kAmaxBlocks = 256;    // one workgroup per CU
 constexpr int kAmaxThreads = 1024;
 
-__global__ void amax_zero_kernel(float* out) { *out = 0.0f; }
+// The workgroup maxima of one launch meet in a slot of a small ring in device
+// memory: an atomic max on the slot's word (non-negative floats order like
+// their unsigned bits), then, once that atomic has returned, a ticket.  The
+// workgroup that draws the last ticket takes the word and clears it (one
+// atomic exchange), writes out and clears the ticket counter, so nothing has
+// to be cleared before a launch and no cache flush is needed: device-scope
+// atomics meet at one point for every XCD.  Launches take the slots in turn:
+// launches that overlap in time (on different streams) use different slots
+// while fewer than kAmaxSlots of them overlap.  Both arrays start at zero
+// with the module.
+constexpr int kAmaxSlots = 64;
+__device__ unsigned int amax_tickets[kAmaxSlots];
+__device__ unsigned int amax_words[kAmaxSlots];
 
 // max |x| over n elements: one 1024-thread workgroup per CU, a grid-stride
 // loop over 8-element chunks with four chunks in flight per lane (a whole
 // 16.8 MB activation is one round of loads), a scalar tail, a wave max, a
-// workgroup max through LDS and one atomicMax per workgroup on the float's
-// bit pattern (non-negative floats order like their unsigned bits).
+// workgroup max through LDS, then the last workgroup's reduction of the
+// workgroup maxima (above).
 template <int DT>
 __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restrict__ x, int64_t n,
-                                                            float* __restrict__ out) {
+                                                            float* __restrict__ out, int slot) {
   __shared__ float part[kAmaxThreads / 64];
   const int64_t chunks = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -64,7 +78,17 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restri
     float b = part[0];
 #pragma unroll
     for (int w = 1; w < kAmaxThreads / 64; ++w) b = fmaxf(b, part[w]);
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(b));
+    __hip_atomic_fetch_max(amax_words + slot, __float_as_uint(b), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the max has landed
+    const unsigned int t =
+        __hip_atomic_fetch_add(amax_tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == gridDim.x - 1) {  // every other workgroup's max landed before its ticket
+      const unsigned int w =
+          __hip_atomic_exchange(amax_words + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *out = __uint_as_float(w);
+      __hip_atomic_store(amax_tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -325,14 +349,14 @@ int grid_for(int64_t work, int per_block, int max_blocks) {
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipStream_t s) {
-  amax_zero_kernel<<<1, 1, 0, s>>>(out);
-  if (n > 0) {
-    int blocks = grid_for(n / 8 + 1, kAmaxThreads * 4, kAmaxBlocks);
-    switch (dt) {
-      case kF32: amax_kernel<kF32><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
-      case kF16: amax_kernel<kF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
-      default: amax_kernel<kBF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out); break;
-    }
+  static std::atomic<unsigned int> next_slot{0};
+  const int slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % kAmaxSlots);
+  // n == 0 still runs one workgroup, which writes 0
+  const int blocks = grid_for(n / 8 + 1, kAmaxThreads * 4, kAmaxBlocks);
+  switch (dt) {
+    case kF32: amax_kernel<kF32><<<blocks, kAmaxThreads, 0, s>>>(x, n, out, slot); break;
+    case kF16: amax_kernel<kF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out, slot); break;
+    default: amax_kernel<kBF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out, slot); break;
   }
   return hipGetLastError();
 }

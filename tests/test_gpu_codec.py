@@ -36,6 +36,27 @@ def test_tensor_amax(shape, dtype):
     assert float(got.item()) == ref
 
 
+def test_tensor_amax_many_launches_on_two_streams():
+    """The workgroup maxima of each launch live in a slot of a ring that the
+    last workgroup resets: 200 launches (the ring wraps), issued alternately
+    on two streams without waiting, each into its own output, all equal the
+    oracle's amax of their input; the same tensor read again gives the same
+    bits."""
+    say("tensor_amax 200 launches on two streams")
+    xs = [W.normal((257 + 97 * i,), 1.0 + i, 900 + i, "bf16", device="cuda") for i in range(8)]
+    outs = torch.empty(200, dtype=torch.float32, device="cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for j in range(200):
+        with torch.cuda.stream(streams[j % 2]):
+            nv.nvfp4_tensor_amax(xs[j % 8], out=outs[j:j + 1])
+    torch.cuda.synchronize()
+    refs = [O.tensor_amax(host(x)) for x in xs]
+    got = outs.cpu().numpy()
+    for j in range(200):
+        assert float(got[j]) == refs[j % 8], j
+
+
 def _quantize_both(x_host, g, dtype):
     """GPU and oracle quantize of the same values; returns both code/scale pairs."""
     xd = x_host.to(dtype).cuda()
