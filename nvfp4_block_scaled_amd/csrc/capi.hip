@@ -748,8 +748,8 @@ nvfp4_status nvfp4_gather_qmm_indexed(const void* x, nvfp4_dtype dt, int64_t ent
       he = nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets, perm,
                                      entries * rows_per_entry, rows, 1, amap, e, n, k, out, stream);
     else
-      he = nvfp4::launch_gather_gemm_t(x, dt, w_codes, w_scales, global_scale_w, offsets, perm, rows, 1,
-                                       amap, e, n, k, out, stream);
+      he = nvfp4::launch_gather_gemm_t(x, dt, w_codes, w_scales, global_scale_w, offsets, perm,
+                                       entries * rows_per_entry, rows, 1, amap, e, n, k, out, stream);
   }
   return launched(op, he);
 }

@@ -52,9 +52,13 @@ amap_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ lhs, i
 // workgroup -- each thread 8 consecutive columns (one block scale per row) of
 // 4 consecutive rows -- and written transposed into LDS as [n][k], 4 k values
 // of a column per 8-byte store, so that both operand fragments of the
-// 32x32x16 MFMA are 16-byte LDS reads (8 k values of one row).  The next step's raw operands are fetched into
-// registers before this step's MFMAs.  The A rows are gathered through perm /
-// amap as in the other gather kernels.
+// 32x32x16 MFMA are 16-byte LDS reads (8 k values of one row).  The next
+// step's raw weights are fetched into registers before this step's MFMAs.
+// The A rows are gathered through perm / amap as in the other gather kernels;
+// they go from global memory straight into two alternating LDS stages
+// (buffer_load ... lds: no registers, no LDS store instructions), each tile
+// row 128 bytes with its 16-byte k chunks XOR-swizzled by the row.  An x of
+// 2 GB or more (beyond 32-bit offsets) takes them through registers instead.
 constexpr int kTT = 128;
 constexpr int kTK = 64;
 constexpr int kPitch = kTK + 8;  // LDS row pitch in elements (144 bytes)
@@ -73,15 +77,23 @@ template <> struct MfmaT<kF16> {
   }
 };
 
-template <int DT>
+typedef __attribute__((address_space(3))) void* lds_ptr_g;
+constexpr uint32_t kGxOutside = 0x7FF00000u;  // a load offset past the end of x
+
+__device__ __forceinline__ void gx_fetch16(__amdgpu_buffer_rsrc_t rs, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_g)dst, 16, voff, 0, 0, 0);
+}
+
+template <int DT, bool DMA>
 __global__ void __launch_bounds__(256)
-gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ wc,
+gather_t_kernel(const void* __restrict__ x, int64_t x_rows, int K, const uint8_t* __restrict__ wc,
                 const uint8_t* __restrict__ ws, const float* __restrict__ gw, int N,
                 void* __restrict__ out, const int32_t* __restrict__ offsets,
                 const int32_t* __restrict__ perm, int top_k, int E, const int32_t* __restrict__ amap) {
   using T = typename Elem<DT>::T;
   using V8 = typename MfmaT<DT>::V8;
-  __shared__ __attribute__((aligned(16))) T la[kTT * kPitch];
+  // A: padded rows (register path) or two swizzled stages (DMA path)
+  __shared__ __attribute__((aligned(1024))) T la[DMA ? 2 * kTT * kTK : kTT * kPitch];
   __shared__ __attribute__((aligned(16))) T lb[kTT * kPitch];
   __shared__ int64_t arow_s[kTT];
   __shared__ int orow_s[kTT];
@@ -126,9 +138,26 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
 
   const uint8_t* wce = wc + (int64_t)expert * K * (N / 2);
   const uint8_t* wse = ws + (int64_t)expert * K * (N / 16);
-  // A: thread t loads tile row t / 2, k 32 (t % 2) .. + 31 (four 16-byte pieces)
+  // A, register path: thread t loads tile row t / 2, k 32 (t % 2) .. + 31
+  // (four 16-byte pieces)
   const int ar = tid >> 1, ah = tid & 1;
   const int64_t arow = arow_s[ar];
+  // A, DMA path: load j of wave w fills tile rows 32 w + 8 j .. + 7 (1 KB);
+  // lane l writes slot l % 8 of row 32 w + 8 j + l / 8, i.e. fetches the row's
+  // k chunk (l % 8) ^ swz(row); rows past the count read zeros
+  auto swz = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
+  const __amdgpu_buffer_rsrc_t rs_x = make_rsrc(x, (uint64_t)x_rows * K * sizeof(T));
+  uint32_t a_off[4] = {0u, 0u, 0u, 0u};
+  int a_chunk[4] = {0, 0, 0, 0};
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 8 * j + (lane >> 3);
+      a_chunk[j] = (lane & 7) ^ swz(r);
+      const int64_t xr = arow_s[r];
+      a_off[j] = xr >= 0 ? (uint32_t)((xr * K + 8 * a_chunk[j]) * (int64_t)sizeof(T)) : kGxOutside;
+    }
+  }
   // B: thread t decodes weight rows k0 + 4 (t / 16) .. + 3, columns
   // bn + 8 (t % 16) .. + 7 (whole 8-column groups: n is a multiple of 16)
   const int bk = 4 * (tid >> 4), bc = tid & 15;
@@ -142,13 +171,23 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
   u32x4 ra[4];
   uint32_t rcode[4];
   uint32_t rscale[4];
-  auto fetch = [&](int k0) {
+  auto fetch = [&](int k0, int stage) {
+    if constexpr (DMA) {
+      T* const dst = la + stage * kTT * kTK;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int k = k0 + 32 * ah + 8 * h;
-      ra[h] = u32x4{0u, 0u, 0u, 0u};
-      if (arow >= 0 && k < K)
-        ra[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
+      for (int j = 0; j < 4; ++j) {
+        const bool in = k0 + 8 * a_chunk[j] < K;  // k % 8 == 0: a chunk is whole or past the end
+        gx_fetch16(rs_x, dst + (32 * wave + 8 * j) * kTK,
+                   in ? a_off[j] + (uint32_t)(k0 * (int)sizeof(T)) : kGxOutside);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int k = k0 + 32 * ah + 8 * h;
+        ra[h] = u32x4{0u, 0u, 0u, 0u};
+        if (arow >= 0 && k < K)
+          ra[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(x) + arow * K + k);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -168,11 +207,14 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += kTK) {
+  fetch(0, 0);
+  int stage = 0;
+  for (int k0 = 0; k0 < K; k0 += kTK, stage ^= 1) {
     // stage this step: A as loaded, B decoded (zeros past k or n decode to 0)
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4*>(&la[ar * kPitch + 32 * ah + 8 * h]) = ra[h];
+      for (int h = 0; h < 4; ++h) *reinterpret_cast<u32x4*>(&la[ar * kPitch + 32 * ah + 8 * h]) = ra[h];
+    }
     {
       typedef T T4 __attribute__((ext_vector_type(4)));
       T4 col[8];  // column i: rows bk .. bk + 3
@@ -198,14 +240,19 @@ gather_t_kernel(const void* __restrict__ x, int K, const uint8_t* __restrict__ w
 #pragma unroll
       for (int i = 0; i < 8; ++i) *reinterpret_cast<T4*>(&lb[lb_at(8 * bc + i, bk)]) = col[i];
     }
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): this step's A stage landed
     __syncthreads();
-    if (k0 + kTK < K) fetch(k0 + kTK);
+    if (k0 + kTK < K) fetch(k0 + kTK, stage ^ 1);
+    const T* const las = DMA ? la + stage * kTT * kTK : la;
 #pragma unroll
     for (int u = 0; u < kTK / 16; ++u) {  // 16-wide k sub-steps
       V8 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const V8*>(&la[(64 * wm + 32 * i + (lane & 31)) * kPitch + 16 * u + 8 * (lane >> 5)]);
+      for (int i = 0; i < 2; ++i) {
+        const int tr = 64 * wm + 32 * i + (lane & 31), q = 2 * u + (lane >> 5);  // row, k chunk
+        a[i] = DMA ? *reinterpret_cast<const V8*>(&las[tr * kTK + ((q ^ swz(tr)) << 3)])
+                   : *reinterpret_cast<const V8*>(&las[tr * kPitch + 8 * q]);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = 64 * wn + 32 * j + (lane & 31);
@@ -260,19 +307,24 @@ hipError_t launch_amap(const int32_t* perm, const int32_t* lhs, int64_t rows, in
 
 hipError_t launch_gather_gemm_t(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
                                 const float* gw, const int32_t* offsets, const int32_t* perm,
-                                int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
-                                int64_t n, int64_t k, void* out, hipStream_t s) {
+                                int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                                int64_t e, int64_t n, int64_t k, void* out, hipStream_t s) {
   if (dt == kF32)
     return launch_gather_gemm_t_f32(reinterpret_cast<const float*>(x), wc, ws, gw, offsets, perm, rows,
                                     top_k, amap, e, n, k, reinterpret_cast<float*>(out), s);
   const int64_t mt = (rows + kTT - 1) / kTT + e;
   const int64_t blocks = mt * ((n + kTT - 1) / kTT);
-  if (dt == kF16)
-    gather_t_kernel<kF16><<<(int)blocks, 256, 0, s>>>(x, (int)k, wc, ws, gw, (int)n, out, offsets, perm,
-                                                       (int)top_k, (int)e, amap);
-  else
-    gather_t_kernel<kBF16><<<(int)blocks, 256, 0, s>>>(x, (int)k, wc, ws, gw, (int)n, out, offsets, perm,
-                                                        (int)top_k, (int)e, amap);
+  // the DMA path's 32-bit offsets: x below 2 GB, k well below 2^31
+  const bool dma = (uint64_t)x_rows * (uint64_t)k * 2u < 0x7F000000ull && k <= 65536;
+#define NVFP4_GT(D, M)                                                                             \
+  gather_t_kernel<D, M><<<(int)blocks, 256, 0, s>>>(x, x_rows, (int)k, wc, ws, gw, (int)n, out, offsets, \
+                                                    perm, (int)top_k, (int)e, amap)
+  if (dt == kF16) {
+    if (dma) NVFP4_GT(kF16, true); else NVFP4_GT(kF16, false);
+  } else {
+    if (dma) NVFP4_GT(kBF16, true); else NVFP4_GT(kBF16, false);
+  }
+#undef NVFP4_GT
   return hipGetLastError();
 }
 

@@ -78,8 +78,8 @@ hipError_t launch_amap(const int32_t* perm, const int32_t* lhs, int64_t rows, in
                        hipStream_t s);
 hipError_t launch_gather_gemm_t(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
                                 const float* gw, const int32_t* offsets, const int32_t* perm,
-                                int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
-                                int64_t n, int64_t k, void* out, hipStream_t s);
+                                int64_t x_rows, int64_t rows, int64_t top_k, const int32_t* amap,
+                                int64_t e, int64_t n, int64_t k, void* out, hipStream_t s);
 
 // compute units of the current device (cached per device)
 int device_cu_count();

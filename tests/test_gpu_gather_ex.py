@@ -102,6 +102,30 @@ def test_indexed_general(dtype, transpose, variant):
         assert fro <= MFMA_FRO_GUARD
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("k", [8, 200, 1000])
+def test_transpose_false_k_tails(dtype, k):
+    """transpose = False with k not a multiple of the kernel's 64-wide steps
+    (the last step's x chunks past k read zeros): k = 8, 200, 1000, against
+    the oracle."""
+    say(f"gather indexed transpose=False k={k} {dtype}")
+    E, N, pairs, entries = 3, 48, 50, 30
+    od = oracle_dtype(dtype)
+    rng = np.random.default_rng(95 + k)
+    wfull = W.normal((E, N, k), 0.02, 96 + k, "f32").numpy()
+    gs = np.array([O.tensor_amax(wfull[e]) for e in range(E)], np.float32)
+    codes, scales = _quantize_experts(list(wfull), gs, False)
+    x = W.normal((entries, k), 1.0, 97 + k, od)
+    rhs = rng.integers(0, E, pairs).astype(np.int32)
+    lhs = rng.integers(0, entries, pairs).astype(np.int32)
+    y = nv.nvfp4_gather_qmm_indexed(x.cuda(), dev(codes), dev(scales), dev(rhs), dev(lhs), dev(gs),
+                                    transpose=False)
+    torch.cuda.synchronize()
+    ref = O.gather_qmm_indexed(host(x)[:, None, :], codes, scales, rhs, lhs, gs, transpose=False, dtype=od)
+    fro, _ = assert_close(host(y).reshape(-1, N), ref, what=f"transpose=False k={k}")
+    assert fro <= MFMA_FRO_GUARD
+
+
 @pytest.mark.parametrize("transpose", [True, False])
 def test_sorted_path_equals_routed_path(transpose):
     say(f"gather indexed sorted == routed, transpose={transpose}")
