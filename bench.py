@@ -61,8 +61,8 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "f3c48a52033310bd", 367367363),
-    "qmv": ("qmv.hip", "fa66de6e5e1bafa1", 33246727),
+    "gemm": ("gemm.hip", "b4e1cee22d6446eb", 367350872),
+    "qmv": ("qmv.hip", "4d9257b6f81472aa", 33246761),
 }
 
 
