@@ -507,7 +507,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
-              "the kernels run on one MI355X and this build has no multi-GPU path.", file=sys.stderr)
+              "the kernels run on one MI355X and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
