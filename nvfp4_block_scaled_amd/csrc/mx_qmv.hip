@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kMxqWaves = 8;
 constexpr int kMxqThreads = 64 * kMxqWaves;
-constexpr int kMxqMaxRows = 8;
+constexpr int kMxqMaxRows = 2;  // rows per wave: more, shorter waves (as the NVFP4 qmv)
 constexpr int kMxqK = 4096;
 
 // Per row and lane: NP pieces of 16 code bytes, EP = 128 / BITS elements
