@@ -367,7 +367,10 @@ static hipError_t launch_quantize_mode(const void* x, int dt, int64_t rows, int6
                                        void* xhat, hipStream_t s) {
   const int64_t halves = rows * k / 8;
   if (halves == 0) return hipSuccess;
-  int blocks = grid_for(halves, kThreads * 2, 1 << 20);
+  // four half groups per thread (two iterations of two in flight): measured
+  // 10.4 us for a 4096 x 4096 bf16 weight, against 11.0 with two and 11.8
+  // with eight
+  int blocks = grid_for(halves, kThreads * 4, 1 << 20);
   uint32_t* c32 = reinterpret_cast<uint32_t*>(codes);
   switch (dt) {
     case kF32:
