@@ -919,6 +919,7 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxE = 1024;
+constexpr int kRouteCache = 8;  // chunks of kRouteThreads pairs kept in registers
 
 // Groups of equal experts inside one wave: returns the lanes (bit mask) that
 // share this lane's expert; the lowest lane of each group also records the
@@ -955,10 +956,27 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
   const int lane = tid & 63;
   const int wave = tid >> 6;
   for (int e = tid; e < E; e += kRouteThreads) base[e] = 0;
+  // the experts of the first kRouteCache chunks, all loads in flight at once
+  // and kept for both passes (one load latency instead of one per chunk)
+  int ev[kRouteCache];
+#pragma unroll
+  for (int c = 0; c < kRouteCache; ++c) {
+    const int p = c * kRouteThreads + tid;
+    ev[c] = (p < total) ? idx[p / mr] : -1;
+  }
+  auto expert_of = [&](int c, int p) { return (p < total) ? idx[p / mr] : -1; };
   __syncthreads();
-  for (int c0 = 0; c0 < total; c0 += kRouteThreads) {
+#pragma unroll
+  for (int c = 0; c < kRouteCache; ++c) {
+    if (c * kRouteThreads < total) {  // uniform
+      const int e = ev[c];
+      const bool valid = (e >= 0 && e < E);
+      match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
+    }
+  }
+  for (int c0 = kRouteCache * kRouteThreads; c0 < total; c0 += kRouteThreads) {
     const int p = c0 + tid;
-    const int e = (p < total) ? idx[p / mr] : -1;
+    const int e = expert_of(c0 / kRouteThreads, p);
     const bool valid = (e >= 0 && e < E);
     match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
   }
@@ -985,7 +1003,14 @@ moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __r
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
     __syncthreads();
     const int p = c0 + tid;
-    const int e = (p < total) ? idx[p / mr] : -1;
+    const int c = c0 / kRouteThreads;
+    int e = -1;
+    if (c < kRouteCache) {  // uniform; the unrolled selects keep ev in registers
+#pragma unroll
+      for (int j = 0; j < kRouteCache; ++j) e = (c == j) ? ev[j] : e;
+    } else {
+      e = expert_of(c, p);
+    }
     const bool valid = (e >= 0 && e < E);
     const uint64_t same =
         match_experts(e, valid, [&](int le, int cnt) { wcnt[wave * E + le] = cnt; });
