@@ -61,8 +61,8 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "b4e1cee22d6446eb", 367380576),
-    "qmv": ("qmv.hip", "c90cac9378cc713f", 33185285),
+    "gemm": ("gemm.hip", "650c1c25433e7e46", 367338375),
+    "qmv": ("qmv.hip", "c90cac9378cc713f", 33185306),
 }
 
 
