@@ -40,6 +40,8 @@
  *     errors are detected on the host before any HIP call.
  *   - Element types: NVFP4_F32, NVFP4_F16, NVFP4_BF16 (float64 is rejected
  *     as in the pages' dispatch).
+ *   - The device behind `stream` (the current device for the null stream)
+ *     must be gfx950; otherwise NVFP4_ERR_UNSUPPORTED.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -163,7 +165,9 @@ size_t nvfp4_qqmm_workspace_size(int64_t m, int64_t n, int64_t k, nvfp4_dtype dt
  *   workspace       device, at least nvfp4_qqmm_workspace_size() bytes,
  *                   256-byte aligned; may be NULL when that size is 0
  * Errors: NULL pointer, m, n <= 0, k <= 0 or k % 16 != 0, exactly one global
- * scale, workspace too small or misaligned, bad dtype.
+ * scale, workspace too small or misaligned, bad dtype; UNSUPPORTED when m > 1
+ * and x (m * k elements) or the weight's codes (n * k / 2 bytes) reach 2 GB
+ * (the matrix-core kernels address them with 32-bit offsets).
  */
 nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale_x,
                         const uint8_t* w_codes, const uint8_t* w_scales,
@@ -181,7 +185,8 @@ nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale
  *   w_codes/scales  device [n, k/2] / [n, k/16]
  *   global_scale_w  device float or NULL
  *   out             device [m, n] of type dt, written
- * Errors: NULL pointer, m, n <= 0, k <= 0 or k % 16 != 0, bad dtype.
+ * Errors: NULL pointer, m, n <= 0, k <= 0 or k % 16 != 0, bad dtype; the 2 GB
+ * limits of nvfp4_qqmm for m > 1.
  */
 nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* global_scale_w, int64_t m, int64_t n,
@@ -243,7 +248,9 @@ nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_
 
 /*
  * nvfp4_gather_qmm_workspace_size -- bytes of device workspace
- * nvfp4_gather_qmm needs (routing tables: expert offsets and the token order).
+ * nvfp4_gather_qmm (and nvfp4_gather_qmm_packed) needs: the routing tables
+ * (expert offsets, the pair order) and the routing's per-chunk counts.
+ * 0 for non-positive sizes or t * top_k >= 2^31.
  */
 size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
                                        int64_t k);
@@ -259,13 +266,16 @@ size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int6
  *   x               device [t, k] of type dt
  *   w_codes         device uint8 [e, n, k/2];  w_scales uint8 [e, n, k/16]
  *   global_scale_w  device float [e] or NULL
- *   expert_idx      device int32 [t, top_k], each in [0, e) (not checked:
- *                   it lives on the device; out-of-range pairs are skipped
- *                   and their output rows left unwritten)
+ *   expert_idx      device int32 [t, top_k]; a pair whose index lies
+ *                   outside [0, e) multiplies no expert and its output row
+ *                   out[t, j, :] is written with zeros
  *   out             device [t, top_k, n] of type dt, written
- *   workspace       device, at least nvfp4_gather_qmm_workspace_size() bytes
+ *   workspace       device, at least nvfp4_gather_qmm_workspace_size() bytes,
+ *                   256-byte aligned
  * Errors: NULL pointer, t, top_k, e, n <= 0, k <= 0 or k % 16 != 0, workspace
- * too small, bad dtype.
+ * too small, bad dtype; UNSUPPORTED for more than 1024 experts, t * top_k >=
+ * 2^31, or x (t * k elements) or one expert's codes (n * k / 2 bytes) of 2 GB
+ * or more.
  */
 nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
                               const uint8_t* w_scales, const float* global_scale_w,
@@ -277,14 +287,20 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
  * nvfp4_moe_route -- the routing step of nvfp4_gather_qmm on its own:
  * offsets[0..e] = exclusive prefix sum of the per-expert pair counts,
  * perm[offsets[x] .. offsets[x+1]) = the flat pair ids t*top_k + j routed to
- * expert x, ascending.
+ * expert x, ascending; perm[offsets[e] .. t*top_k) = the pairs whose index
+ * lies outside [0, e), ascending.
  *   expert_idx  device int32 [t, top_k]
  *   offsets     device int32 [e + 1], written
  *   perm        device int32 [t * top_k], written
- * Errors: NULL pointer, t, top_k, e <= 0, t * top_k >= 2^31.
+ *   workspace   device, nvfp4_moe_route_workspace_size() bytes (the
+ *               counting sort's per-chunk counts), 256-byte aligned
+ * Errors: NULL pointer, t, top_k, e <= 0, workspace too small or misaligned;
+ * UNSUPPORTED for t * top_k >= 2^31 or more than 1024 experts.
  */
+size_t nvfp4_moe_route_workspace_size(int64_t t, int64_t top_k, int64_t e);
 nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
-                             int32_t* offsets, int32_t* perm, hipStream_t stream);
+                             int32_t* offsets, int32_t* perm, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Packed weights for the matrix-core contractions.
@@ -372,9 +388,10 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
  *                sort (same results; an unsorted array gives undefined values)
  *   workspace    nvfp4_gather_qmm_indexed_workspace_size(pairs,
  *                rows_per_entry, e, lhs_indices != NULL) bytes, 256-byte aligned
- * x is used as given; the global scale multiplies the block scale.  Pairs
- * with an expert outside [0, e) are skipped (their output rows are not
- * written); an lhs index outside [0, entries) is a precondition violation.
+ * x is used as given; the global scale multiplies the block scale.  The
+ * rows of a pair whose expert lies outside [0, e) are written with zeros (with
+ * sorted_indices such pairs can only sit at the two ends); an lhs index
+ * outside [0, entries) is a precondition violation.
  * transpose = 1 runs the matrix-core kernels of nvfp4_gather_qmm (float16 /
  * bfloat16) or the float32 kernel; transpose = 0 a matrix-core kernel that
  * decodes each weight tile into LDS (float32: the float32 kernel).

@@ -68,7 +68,8 @@ def load_library():
         "nvfp4_qmm": (I, [P, I, P, P, P, I64, I64, I64, P, P]),
         "nvfp4_gather_qmm_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "nvfp4_gather_qmm": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
-        "nvfp4_moe_route": (I, [P, I64, I64, I64, P, P, P]),
+        "nvfp4_moe_route_workspace_size": (SZ, [I64, I64, I64]),
+        "nvfp4_moe_route": (I, [P, I64, I64, I64, P, P, P, SZ, P]),
         "nvfp4_mfma_pack_size": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
         "nvfp4_mfma_pack": (I, [P, P, I64, I64, P, P, P]),
         "nvfp4_qqmm_packed": (I, [P, I, P, P, P, P, I64, I64, I64, P, P, SZ, P]),
@@ -428,8 +429,10 @@ def nvfp4_moe_route(expert_idx, num_experts):
     t, top_k = expert_idx.shape
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=expert_idx.device)
     perm = torch.empty(t * top_k, dtype=torch.int32, device=expert_idx.device)
+    nbytes = L.nvfp4_moe_route_workspace_size(t, top_k, num_experts)
+    workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=expert_idx.device)
     _check(L.nvfp4_moe_route(_ptr(expert_idx), t, top_k, num_experts, _ptr(offsets), _ptr(perm),
-                             _stream()))
+                             _ptr(workspace), nbytes, _stream()))
     return offsets, perm
 
 

@@ -44,6 +44,9 @@ size_t dtype_size(int dt) { return dt == NVFP4_F32 ? 4 : 2; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// operands the matrix-core kernels address with 32-bit buffer offsets
+constexpr int64_t kOffsetLimit = (int64_t)1 << 31;
+
 #define CHECK_PTR(op, p)                                                          \
   do {                                                                            \
     if ((p) == nullptr)                                                           \
@@ -67,9 +70,10 @@ nvfp4_status check_k(const char* op, int64_t k) {
   return NVFP4_OK;
 }
 
-// The device behind `stream` must be gfx950 (the analogue of the pages'
-// compute-capability gate in QQMatmul::eval_gpu).  Checked once per device.
-nvfp4_status check_device(const char* op) {
+// The device behind `stream` (the current device for the null stream) must be
+// gfx950 (the analogue of the pages' compute-capability gate in
+// QQMatmul::eval_gpu).  Checked once per device.
+nvfp4_status check_device(const char* op, hipStream_t stream) {
   {
     std::lock_guard<std::mutex> lk(g_arch_mu);
     if (g_has_override) {
@@ -80,9 +84,9 @@ nvfp4_status check_device(const char* op) {
     }
   }
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess)
-    return fail(NVFP4_ERR_DEVICE, "[%s] No HIP device: %s", op, hipGetErrorString(e));
+    return fail(NVFP4_ERR_DEVICE, "[%s] No HIP device behind the stream: %s", op, hipGetErrorString(e));
   std::lock_guard<std::mutex> lk(g_arch_mu);
   if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_DEVICE, "[%s] Device id %d out of range.", op, dev);
   if (g_arch_ok[dev] == 0) {
@@ -135,7 +139,7 @@ nvfp4_status nvfp4_tensor_amax(const void* x, nvfp4_dtype dt, int64_t n, float* 
   if (n > 0) CHECK_PTR("tensor_amax", x);
   if (n > 0 && !aligned(x, 16))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[tensor_amax] x must be 16-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_tensor_amax(x, dt, n, amax_out, stream));
 }
 
@@ -163,7 +167,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     if (!aligned(codes, 4))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quantize] codes must be 4-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_quantize(x, dt, rows, k, global_scale, codes, scales, stream));
 }
@@ -179,7 +183,7 @@ nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64
     if (!aligned(codes, 4))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[dequantize] codes must be 4-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_dequantize(codes, scales, rows, k, global_scale, out, out_dt, stream));
 }
@@ -193,7 +197,7 @@ nvfp4_status nvfp4_quant_dequant(const void* x, nvfp4_dtype dt, int64_t rows, in
     if (!aligned(x_hat, 16))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quant_dequant] x_hat must be 16-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_quant_dequant(x, dt, rows, k, global_scale, x_hat, stream));
 }
@@ -218,6 +222,13 @@ static nvfp4_status check_matmul(const char* op, const void* x, nvfp4_dtype dt, 
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[%s] x and w_codes must be 16-byte aligned.", op);
   if (m * n > (int64_t)1 << 46 || n > INT32_MAX || m > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[%s] Sizes too large.", op);
+  // the contraction kernels for m > 1 address x (or x_hat) and the weight's
+  // codes with 32-bit buffer offsets
+  if (m > 1 && (m * k * (int64_t)dtype_size(dt) >= kOffsetLimit || n * (k / 2) >= kOffsetLimit))
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[%s] x (%lld x %lld) and the weight's codes (%lld x %lld bytes) must each stay "
+                "below 2 GB for m > 1.", op, (long long)m, (long long)k, (long long)n,
+                (long long)(k / 2));
   return NVFP4_OK;
 }
 
@@ -232,7 +243,7 @@ nvfp4_status nvfp4_qmv(const void* x, nvfp4_dtype dt, const float* global_scale_
   if (k > nvfp4::kQmvMaxK)
     return fail(NVFP4_ERR_UNSUPPORTED, "[qmv] k (%lld) above the supported maximum %lld.",
                 (long long)k, (long long)nvfp4::kQmvMaxK);
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_qmv(x, dt, global_scale_x, w_codes, w_scales, global_scale_w,
                                         n, k, out, stream));
 }
@@ -253,7 +264,7 @@ nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale
                                      m, n, k, out))
     return st;
   if (m == 1 && k <= nvfp4::kQmvMaxK) {
-    if (nvfp4_status st = check_device(op)) return st;
+    if (nvfp4_status st = check_device(op, stream)) return st;
     return launched(op, nvfp4::launch_qmv(x, dt, global_scale_x, w_codes, w_scales,
                                           global_scale_w, n, k, out, stream));
   }
@@ -263,7 +274,7 @@ nvfp4_status nvfp4_qqmm(const void* x, nvfp4_dtype dt, const float* global_scale
                 workspace_bytes, need);
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm] workspace must be 256-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (nvfp4::small_m_ok(dt, false, m, n, k))  // x's round trip happens inside the kernel
     return launched(op, nvfp4::launch_small_m(x, dt, true, global_scale_x, w_codes, w_scales,
                                               false, global_scale_w, m, n, k, out, stream));
@@ -280,7 +291,7 @@ nvfp4_status nvfp4_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
   if (nvfp4_status st = check_matmul(op, x, dt, global_scale_w, w_codes, w_scales, global_scale_w,
                                      m, n, k, out))
     return st;
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (nvfp4::small_m_ok(dt, false, m, n, k))
     return launched(op, nvfp4::launch_small_m(x, dt, false, nullptr, w_codes, w_scales, false,
                                               global_scale_w, m, n, k, out, stream));
@@ -321,7 +332,7 @@ nvfp4_status nvfp4_quantize_columnwise(const void* x, nvfp4_dtype dt, int64_t ro
     if (!aligned(codes, 8))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[quantize_columnwise] codes must be 8-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0 || cols == 0) return ok();
   return launched(op, nvfp4::launch_quantize_colwise(x, dt, rows, cols, global_scale, codes, scales,
                                                      stream));
@@ -335,7 +346,7 @@ nvfp4_status nvfp4_quant_dequant_columnwise(const void* x, nvfp4_dtype dt, int64
   if (rows > 0 && cols > 0 && (xhat_t == nullptr || !aligned(xhat_t, 16)))
     return fail(NVFP4_ERR_INVALID_ARGUMENT,
                 "[quant_dequant_columnwise] xhat_t must be non-NULL and 16-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0 || cols == 0) return ok();
   return launched(op, nvfp4::launch_quant_dequant_colwise(x, dt, rows, cols, global_scale, xhat_t,
                                                           stream));
@@ -416,7 +427,7 @@ nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_
     return fail(NVFP4_ERR_INVALID_ARGUMENT,
                 "[qqmm_vjp] workspace of %zu bytes is smaller than %zu or not 256-byte aligned.",
                 workspace_bytes, L.total);
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   char* base = reinterpret_cast<char*>(workspace);
   const bool has_g = global_scale_x != nullptr;
   // the cotangent's global scale: its amax as float32 (none without global scales)
@@ -452,19 +463,38 @@ nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_
   return ok();
 }
 
+namespace {
+// the routing tables of a gather: offsets [e + 1], perm [rows] and the
+// routing's per-chunk counts, each 256-byte aligned
+struct RouteLayout {
+  size_t offsets, perm, scratch, total;
+};
+RouteLayout route_layout(int64_t rows, int64_t e) {
+  RouteLayout l;
+  l.offsets = 0;
+  l.perm = up256((size_t)(e + 1) * sizeof(int32_t));
+  l.scratch = l.perm + up256((size_t)rows * sizeof(int32_t));
+  l.total = l.scratch + up256(nvfp4::route_scratch_bytes(rows, e));
+  return l;
+}
+}  // namespace
+
 size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
                                        int64_t k) {
   (void)n;
   (void)k;
-  if (t <= 0 || top_k <= 0 || e <= 0) return 0;
-  size_t off = (size_t)(e + 1) * sizeof(int32_t);
-  off = (off + 255) & ~(size_t)255;
-  size_t perm = (size_t)t * (size_t)top_k * sizeof(int32_t);
-  return off + ((perm + 255) & ~(size_t)255);
+  if (t <= 0 || top_k <= 0 || e <= 0 || t * top_k >= ((int64_t)1 << 31)) return 0;
+  return route_layout(t * top_k, e).total;
+}
+
+size_t nvfp4_moe_route_workspace_size(int64_t t, int64_t top_k, int64_t e) {
+  if (t <= 0 || top_k <= 0 || e <= 0 || t * top_k >= ((int64_t)1 << 31)) return 0;
+  return up256(nvfp4::route_scratch_bytes(t * top_k, e));
 }
 
 nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
-                             int32_t* offsets, int32_t* perm, hipStream_t stream) {
+                             int32_t* offsets, int32_t* perm, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   const char* op = "moe_route";
   if (t <= 0 || top_k <= 0 || e <= 0)
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[moe_route] t, top_k and e must be positive.");
@@ -475,8 +505,15 @@ nvfp4_status nvfp4_moe_route(const int32_t* expert_idx, int64_t t, int64_t top_k
   CHECK_PTR("moe_route", expert_idx);
   CHECK_PTR("moe_route", offsets);
   CHECK_PTR("moe_route", perm);
-  if (nvfp4_status st = check_device(op)) return st;
-  return launched(op, nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream));
+  const size_t need = nvfp4_moe_route_workspace_size(t, top_k, e);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[moe_route] workspace of %zu bytes is smaller than %zu or not 256-byte aligned.",
+                workspace_bytes, need);
+  if (nvfp4_status st = check_device(op, stream)) return st;
+  return launched(op, nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
+                                              reinterpret_cast<int32_t*>(workspace), nullptr, 0,
+                                              stream));
 }
 
 nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
@@ -498,6 +535,9 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] x and w_codes must be 16-byte aligned.");
   if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm] Sizes too large.");
+  if (t * k * (int64_t)dtype_size(dt) >= kOffsetLimit || n * (k / 2) >= kOffsetLimit)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[gather_qmm] x and one expert's codes must each stay below 2 GB.");
   if (e > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm] at most 1024 experts are supported.");
   size_t need = nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k);
@@ -506,11 +546,14 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
                 workspace_bytes, need);
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm] workspace must be 256-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
-  int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
-  size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
-  int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
-  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream);
+  if (nvfp4_status st = check_device(op, stream)) return st;
+  const RouteLayout rl = route_layout(t * top_k, e);
+  char* wsb = reinterpret_cast<char*>(workspace);
+  int32_t* offsets = reinterpret_cast<int32_t*>(wsb + rl.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(wsb + rl.perm);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
+                                          reinterpret_cast<int32_t*>(wsb + rl.scratch), out,
+                                          n * (int64_t)dtype_size(dt), stream);
   if (he != hipSuccess) return launched(op, he);
   return launched(op, nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets,
                                                  perm, t, t * top_k, top_k, nullptr, e, n, k, out,
@@ -555,7 +598,7 @@ nvfp4_status nvfp4_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_
                 "[mfma_pack] codes must be 16-byte and scales 4-byte aligned.");
   if (rows > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[mfma_pack] Sizes too large.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_mfma_pack(codes, scales, rows, k, packed_codes, packed_scales,
                                               stream));
 }
@@ -591,7 +634,7 @@ nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* globa
                 workspace_bytes, need);
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[qqmm_packed] workspace must be 256-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (nvfp4::small_m_ok(dt, true, m, n, k))
     return launched(op, nvfp4::launch_small_m(x, dt, true, global_scale_x, packed_codes,
                                               packed_scales, true, global_scale_w, m, n, k, out,
@@ -610,7 +653,7 @@ nvfp4_status nvfp4_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_t* pack
                                      global_scale_w, m, n, k, out))
     return st;
   if (nvfp4_status st = check_packed(op, dt, n, k)) return st;
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (nvfp4::small_m_ok(dt, true, m, n, k))
     return launched(op, nvfp4::launch_small_m(x, dt, false, nullptr, packed_codes, packed_scales,
                                               true, global_scale_w, m, n, k, out, stream));
@@ -639,6 +682,9 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
                 "[gather_qmm_packed] x and packed_codes must be 16-byte aligned.");
   if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_packed] Sizes too large.");
+  if (t * k * (int64_t)dtype_size(dt) >= kOffsetLimit || n * (k / 2) >= kOffsetLimit)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[gather_qmm_packed] x and one expert's codes must each stay below 2 GB.");
   if (e > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_packed] at most 1024 experts are supported.");
   size_t need = nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k);
@@ -647,11 +693,14 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
                 "[gather_qmm_packed] workspace of %zu bytes is smaller than %zu.", workspace_bytes, need);
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_packed] workspace must be 256-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
-  int32_t* offsets = reinterpret_cast<int32_t*>(workspace);
-  size_t off = ((size_t)(e + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
-  int32_t* perm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + off);
-  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm, stream);
+  if (nvfp4_status st = check_device(op, stream)) return st;
+  const RouteLayout rl = route_layout(t * top_k, e);
+  char* wsb = reinterpret_cast<char*>(workspace);
+  int32_t* offsets = reinterpret_cast<int32_t*>(wsb + rl.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(wsb + rl.perm);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
+                                          reinterpret_cast<int32_t*>(wsb + rl.scratch), out,
+                                          n * (int64_t)dtype_size(dt), stream);
   if (he != hipSuccess) return launched(op, he);
   return launched(op, nvfp4::launch_gather_gemm_packed(x, dt, packed_codes, packed_scales,
                                                        global_scale_w, offsets, perm, t, t * top_k,
@@ -662,7 +711,7 @@ nvfp4_status nvfp4_gather_qmm_packed(const void* x, nvfp4_dtype dt, const uint8_
 
 namespace {
 struct GatherIxLayout {
-  size_t offsets, perm, amap, total;
+  size_t offsets, perm, amap, scratch, total;
 };
 GatherIxLayout gather_ix_layout(int64_t pairs, int64_t mr, int64_t e, bool with_lhs) {
   GatherIxLayout l;
@@ -670,7 +719,8 @@ GatherIxLayout gather_ix_layout(int64_t pairs, int64_t mr, int64_t e, bool with_
   l.offsets = 0;
   l.perm = ((size_t)(e + 1) * 4 + 255) & ~(size_t)255;
   l.amap = l.perm + ((rows * 4 + 255) & ~(size_t)255);
-  l.total = with_lhs ? l.amap + ((rows * 4 + 255) & ~(size_t)255) : l.amap;
+  l.scratch = with_lhs ? l.amap + ((rows * 4 + 255) & ~(size_t)255) : l.amap;
+  l.total = l.scratch + up256(nvfp4::route_scratch_bytes((int64_t)rows, e));
   return l;
 }
 }  // namespace
@@ -723,6 +773,11 @@ nvfp4_status nvfp4_gather_qmm_indexed(const void* x, nvfp4_dtype dt, int64_t ent
   if (pairs * rows_per_entry >= ((int64_t)1 << 31) || entries * rows_per_entry >= ((int64_t)1 << 31) ||
       n > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_indexed] Sizes too large.");
+  if (transpose && dt != NVFP4_F32 &&
+      (entries * rows_per_entry * k * (int64_t)dtype_size(dt) >= kOffsetLimit ||
+       n * (k / 2) >= kOffsetLimit))
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[gather_qmm_indexed] x and one expert's codes must each stay below 2 GB.");
   if (e > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_indexed] at most 1024 experts are supported.");
   const GatherIxLayout l = gather_ix_layout(pairs, rows_per_entry, e, lhs_indices != nullptr);
@@ -732,15 +787,19 @@ nvfp4_status nvfp4_gather_qmm_indexed(const void* x, nvfp4_dtype dt, int64_t ent
                 l.total);
   if (!aligned(workspace, 256))
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_indexed] workspace must be 256-byte aligned.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   char* base = reinterpret_cast<char*>(workspace);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + l.offsets);
   int32_t* perm = reinterpret_cast<int32_t*>(base + l.perm);
   int32_t* amap = lhs_indices ? reinterpret_cast<int32_t*>(base + l.amap) : nullptr;
   const int64_t rows = pairs * rows_per_entry;
+  const int64_t row_bytes = n * (int64_t)dtype_size(dt);
   hipError_t he = sorted_indices
-                      ? nvfp4::launch_sorted_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm, stream)
-                      : nvfp4::launch_moe_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm, stream);
+                      ? nvfp4::launch_sorted_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm,
+                                                   out, row_bytes, stream)
+                      : nvfp4::launch_moe_route(rhs_indices, pairs, rows_per_entry, e, offsets, perm,
+                                                reinterpret_cast<int32_t*>(base + l.scratch), out,
+                                                row_bytes, stream);
   if (he == hipSuccess && amap)
     he = nvfp4::launch_amap(perm, lhs_indices, rows, rows_per_entry, amap, stream);
   if (he == hipSuccess) {
@@ -787,7 +846,7 @@ nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode
     if (!aligned(codes, 16))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quantize] codes must be 16-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_mx_quantize(x, dt, mode, rows, k, codes, scales, stream));
 }
@@ -803,7 +862,7 @@ nvfp4_status nvfp4_mx_dequantize(const uint8_t* codes, const uint8_t* scales, nv
     if (!aligned(codes, 16))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_dequantize] codes must be 16-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_mx_dequantize(codes, scales, mode, rows, k, out, out_dt, stream));
 }
@@ -817,7 +876,7 @@ nvfp4_status nvfp4_mx_quant_dequant(const void* x, nvfp4_dtype dt, nvfp4_mx_mode
     if (!aligned(x_hat, 16))
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quant_dequant] x_hat must be 16-byte aligned.");
   }
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (rows == 0) return ok();
   return launched(op, nvfp4::launch_mx_quant_dequant(x, dt, mode, rows, k, x_hat, stream));
 }
@@ -858,7 +917,7 @@ nvfp4_status nvfp4_mx_pack(const uint8_t* codes, const uint8_t* scales, nvfp4_mx
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_pack] codes and packed_codes must be 16-byte aligned.");
   if (rows > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[mx_pack] Sizes too large.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_mx_pack(codes, scales, mode, rows, k, packed_codes, packed_scales,
                                             stream));
 }
@@ -877,7 +936,7 @@ nvfp4_status nvfp4_mx_quantize_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mo
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_quantize_packed] packed_codes must be 16-byte aligned.");
   if (rows > INT32_MAX || k > INT32_MAX)
     return fail(NVFP4_ERR_UNSUPPORTED, "[mx_quantize_packed] Sizes too large.");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_mx_quantize_packed(x, dt, mode, rows, k, packed_codes,
                                                        packed_scales, stream));
 }
@@ -898,7 +957,7 @@ nvfp4_status nvfp4_mx_mm_packed(const uint8_t* x_packed_codes, const uint8_t* x_
       nvfp4::mx_packed_code_bytes(m, k, mode) >= nvfp4::kMxMaxPackedBytes ||
       nvfp4::mx_packed_code_bytes(n, k, mode) >= nvfp4::kMxMaxPackedBytes)
     return fail(NVFP4_ERR_UNSUPPORTED, "[mx_mm_packed] Sizes too large (a packed operand of 2 GB or more).");
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   return launched(op, nvfp4::launch_mx_gemm(x_packed_codes, x_packed_scales, w_packed_codes,
                                             w_packed_scales, mode, m, n, k, out, out_dt, stream));
 }
@@ -971,7 +1030,7 @@ nvfp4_status nvfp4_mx_qqmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
   const bool qmv = nvfp4::mx_qmv_ok(m, n, k);  // one row of x: the streaming matrix-vector kernel
   const MxLayout l = mx_layout(mode, m, n, k, false);
   if (nvfp4_status st = mx_workspace_ok(op, workspace, workspace_bytes, qmv ? 0 : l.total)) return st;
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   if (qmv) return launched(op, nvfp4::launch_mx_qmv(x, dt, mode, w_codes, w_scales, n, out, stream));
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   hipError_t e = nvfp4::launch_mx_pack(w_codes, w_scales, mode, n, k, base + l.wc, base + l.ws, stream);
@@ -993,7 +1052,7 @@ nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode m
     return st;
   const MxLayout l = mx_layout(mode, m, n, k, true);
   if (nvfp4_status st = mx_workspace_ok(op, workspace, workspace_bytes, l.total)) return st;
-  if (nvfp4_status st = check_device(op)) return st;
+  if (nvfp4_status st = check_device(op, stream)) return st;
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   hipError_t e = nvfp4::launch_mx_quantize_packed(x, dt, mode, m, k, base + l.xc, base + l.xs, stream);
   if (e == hipSuccess)

@@ -21,7 +21,8 @@ namespace {
 // and the permutation is the identity.
 __global__ void __launch_bounds__(256)
 sorted_route_kernel(const int32_t* __restrict__ rhs, int pairs, int mr, int E,
-                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                    uint8_t* __restrict__ zero_out, int64_t row_bytes) {
   const int tid = blockIdx.x * blockDim.x + threadIdx.x;
   if (tid <= E) {
     int lo = 0, hi = pairs;  // first pair with rhs >= tid
@@ -32,7 +33,22 @@ sorted_route_kernel(const int32_t* __restrict__ rhs, int pairs, int mr, int E,
     offsets[tid] = lo * mr;
   }
   const int rows = pairs * mr;
-  for (int q = tid; q < rows; q += gridDim.x * blockDim.x) perm[q] = q;
+  const int stride = gridDim.x * blockDim.x;
+  for (int q = tid; q < rows; q += stride) perm[q] = q;
+  if (zero_out) {
+    // rows whose expert lies outside [0, E) (before offsets[0] or from
+    // offsets[E] on): no product touches them, so they get zeros here
+    for (int q0 = tid & ~63; q0 < rows; q0 += stride) {  // wave-uniform
+      const int q = q0 + (threadIdx.x & 63);
+      int x = 0;
+      if (q < rows) x = rhs[q / mr];
+      uint64_t bad = __ballot(q < rows && !(x >= 0 && x < E));
+      while (bad) {
+        zero_row_wave(zero_out, (int64_t)(q0 + __builtin_ctzll(bad)), row_bytes);
+        bad &= bad - 1ull;
+      }
+    }
+  }
 }
 
 // x row of each routed row: amap[s] = lhs[q / mr] mr + q % mr, q = perm[s].
@@ -287,12 +303,14 @@ gather_t_kernel(const void* __restrict__ x, int64_t x_rows, int K, const uint8_t
 }  // namespace
 
 hipError_t launch_sorted_route(const int32_t* rhs, int64_t pairs, int64_t mr, int64_t e,
-                               int32_t* offsets, int32_t* perm, hipStream_t s) {
+                               int32_t* offsets, int32_t* perm, void* zero_out, int64_t row_bytes,
+                               hipStream_t s) {
   const int64_t rows = pairs * mr;
   const int64_t work = rows > e + 1 ? rows : e + 1;
   int blocks = (int)((work + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  sorted_route_kernel<<<blocks, 256, 0, s>>>(rhs, (int)pairs, (int)mr, (int)e, offsets, perm);
+  sorted_route_kernel<<<blocks, 256, 0, s>>>(rhs, (int)pairs, (int)mr, (int)e, offsets, perm,
+                                             reinterpret_cast<uint8_t*>(zero_out), row_bytes);
   return hipGetLastError();
 }
 

@@ -915,11 +915,26 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
 }
 
 // ------------------------------------------------------------------ routing
+//
+// Routing sorts the routed rows by expert, stably (ascending row id within an
+// expert): row q of the entries * mr rows goes to expert idx[q / mr].  It is a
+// counting sort in three launches over chunks of rows (a multiple of 1024
+// rows, at most kRouteMaxChunks chunks):
+//   count    one workgroup per chunk: the chunk's per-expert counts;
+//   scan     one workgroup: offsets[x], the exclusive prefix of the experts'
+//            totals, and each chunk's first slot per expert;
+//   scatter  one workgroup per chunk, in steps of 1024 rows: a row's slot is
+//            its expert's running slot, plus the same-expert rows of earlier
+//            waves of the step, plus its rank among the same-expert lanes of
+//            its wave.
+// A row whose expert lies outside [0, E) goes to a last bucket: perm[offsets[E]
+// .. rows) holds those rows in ascending order, and when an output is given
+// the scatter writes zeros to their output rows (no product touches them).
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteMaxE = 1024;
-constexpr int kRouteCache = 8;  // chunks of kRouteThreads pairs kept in registers
+constexpr int kRouteMaxChunks = 256;
 
 // Groups of equal experts inside one wave: returns the lanes (bit mask) that
 // share this lane's expert; the lowest lane of each group also records the
@@ -939,95 +954,117 @@ __device__ __forceinline__ uint64_t match_experts(int e, bool valid, F on_group)
   return same;
 }
 
-// One workgroup of 1024 lanes.  Pass 1 counts pairs per expert (one LDS
-// atomic per expert group of a wave), then an exclusive scan gives the
-// expert offsets.  Pass 2 walks the pairs again in chunks of 1024 in order:
-// a pair's slot is its expert's running base, plus the same-expert pairs of
-// earlier waves of the chunk (a per-wave count table), plus its rank among
-// the same-expert lanes of its wave -- i.e. ascending pair id within each
-// expert.  Out-of-range experts are skipped.
+// the bucket of routed row q: its expert, or E when that lies outside [0, E)
+__device__ __forceinline__ int route_bucket(const int32_t* __restrict__ idx, int q, int mr, int E) {
+  const int x = idx[q / mr];
+  return (x >= 0 && x < E) ? x : E;
+}
+
 __global__ void __launch_bounds__(kRouteThreads)
-moe_route_kernel(const int32_t* __restrict__ idx, int total, int E, int32_t* __restrict__ offsets,
-                 int32_t* __restrict__ perm, int mr) {
-  __shared__ int base[kRouteMaxE];
-  __shared__ int scan[kRouteThreads];
-  __shared__ int wcnt[kRouteWaves * kRouteMaxE];
+route_count_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int chunk,
+                   int32_t* __restrict__ counts) {
+  __shared__ int hist[kRouteMaxE + 1];
+  const int tid = threadIdx.x;
+  for (int x = tid; x <= E; x += kRouteThreads) hist[x] = 0;
+  __syncthreads();
+  const int q0 = blockIdx.x * chunk;
+  const int q1 = min(rows, q0 + chunk);
+  for (int qb = q0; qb < q1; qb += kRouteThreads) {
+    const int q = qb + tid;
+    const bool have = q < q1;
+    const int b = have ? route_bucket(idx, q, mr, E) : -1;
+    match_experts(b, have, [&](int le, int cnt) { atomicAdd(&hist[le], cnt); });
+  }
+  __syncthreads();
+  for (int x = tid; x <= E; x += kRouteThreads) counts[blockIdx.x * (E + 1) + x] = hist[x];
+}
+
+// counts [chunks][E + 1] in, each chunk's first slot per bucket out
+__global__ void __launch_bounds__(kRouteThreads)
+route_scan_kernel(int32_t* __restrict__ counts, int chunks, int E, int32_t* __restrict__ offsets) {
+  __shared__ int tot[2 * kRouteThreads];
+  __shared__ int part[kRouteThreads];
+  const int tid = threadIdx.x;
+  for (int x = tid; x < 2 * kRouteThreads; x += kRouteThreads) {
+    int run = 0;
+    if (x <= E) {
+      for (int c = 0; c < chunks; ++c) {
+        const int v = counts[c * (E + 1) + x];
+        counts[c * (E + 1) + x] = run;  // the chunk's first slot, relative to the bucket
+        run += v;
+      }
+    }
+    tot[x] = run;
+  }
+  __syncthreads();
+  // exclusive prefix over buckets 0 .. E (thread t holds buckets 2t, 2t + 1)
+  const int mine = tot[2 * tid] + tot[2 * tid + 1];
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int excl = part[tid] - mine;
+  const int o0 = excl, o1 = excl + tot[2 * tid];
+  __syncthreads();
+  tot[2 * tid] = o0;
+  tot[2 * tid + 1] = o1;
+  __syncthreads();
+  for (int x = tid; x <= E; x += kRouteThreads) offsets[x] = tot[x];
+  for (int i = tid; i < chunks * (E + 1); i += kRouteThreads) counts[i] += tot[i % (E + 1)];
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_scatter_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int chunk,
+                     const int32_t* __restrict__ starts, int32_t* __restrict__ perm,
+                     uint8_t* __restrict__ zero_out, int64_t row_bytes) {
+  __shared__ int base[kRouteMaxE + 1];
+  __shared__ int wcnt[kRouteWaves * (kRouteMaxE + 1)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) base[e] = 0;
-  // the experts of the first kRouteCache chunks, all loads in flight at once
-  // and kept for both passes (one load latency instead of one per chunk)
-  int ev[kRouteCache];
-#pragma unroll
-  for (int c = 0; c < kRouteCache; ++c) {
-    const int p = c * kRouteThreads + tid;
-    ev[c] = (p < total) ? idx[p / mr] : -1;
-  }
-  auto expert_of = [&](int c, int p) { return (p < total) ? idx[p / mr] : -1; };
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < kRouteCache; ++c) {
-    if (c * kRouteThreads < total) {  // uniform
-      const int e = ev[c];
-      const bool valid = (e >= 0 && e < E);
-      match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
-    }
-  }
-  for (int c0 = kRouteCache * kRouteThreads; c0 < total; c0 += kRouteThreads) {
-    const int p = c0 + tid;
-    const int e = expert_of(c0 / kRouteThreads, p);
-    const bool valid = (e >= 0 && e < E);
-    match_experts(e, valid, [&](int le, int cnt) { atomicAdd(&base[le], cnt); });
-  }
-  __syncthreads();
-  // exclusive scan of the counts (E <= 1024, one entry per lane)
-  const int mycount = (tid < E) ? base[tid] : 0;
-  scan[tid] = mycount;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const int v = (tid >= off) ? scan[tid - off] : 0;
+  for (int x = tid; x <= E; x += kRouteThreads) base[x] = starts[blockIdx.x * (E + 1) + x];
+  const int q0 = blockIdx.x * chunk;
+  const int q1 = min(rows, q0 + chunk);
+  for (int qb = q0; qb < q1; qb += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * (E + 1); i += kRouteThreads) wcnt[i] = 0;
     __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  if (tid < E) {
-    const int excl = scan[tid] - mycount;
-    offsets[tid] = excl;
-    base[tid] = excl;
-  }
-  if (tid == kRouteThreads - 1) offsets[E] = scan[tid];
-  __syncthreads();
-
-  for (int c0 = 0; c0 < total; c0 += kRouteThreads) {
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
-    __syncthreads();
-    const int p = c0 + tid;
-    const int c = c0 / kRouteThreads;
-    int e = -1;
-    if (c < kRouteCache) {  // uniform; the unrolled selects keep ev in registers
-#pragma unroll
-      for (int j = 0; j < kRouteCache; ++j) e = (c == j) ? ev[j] : e;
-    } else {
-      e = expert_of(c, p);
-    }
-    const bool valid = (e >= 0 && e < E);
+    const int q = qb + tid;
+    const bool have = q < q1;
+    const int b = have ? route_bucket(idx, q, mr, E) : -1;
     const uint64_t same =
-        match_experts(e, valid, [&](int le, int cnt) { wcnt[wave * E + le] = cnt; });
+        match_experts(b, have, [&](int le, int cnt) { wcnt[wave * (E + 1) + le] = cnt; });
     __syncthreads();
-    if (valid) {
-      int pos = base[e] + __builtin_popcountll(same & ((1ull << lane) - 1ull));
-      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
-      perm[pos] = p;
+    if (have) {
+      int pos = base[b] + __builtin_popcountll(same & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * (E + 1) + b];
+      perm[pos] = q;
+    }
+    if (zero_out) {
+      uint64_t bad = __ballot(have && b == E);
+      while (bad) {
+        const int l = __builtin_ctzll(bad);
+        zero_row_wave(zero_out, (int64_t)(qb + wave * 64 + l), row_bytes);
+        bad &= bad - 1ull;
+      }
     }
     __syncthreads();
-    for (int x = tid; x < E; x += kRouteThreads) {
+    for (int x = tid; x <= E; x += kRouteThreads) {
       int add = 0;
-      for (int w = 0; w < kRouteWaves; ++w) add += wcnt[w * E + x];
+      for (int w = 0; w < kRouteWaves; ++w) add += wcnt[w * (E + 1) + x];
       base[x] += add;
     }
     __syncthreads();
   }
+}
+
+int64_t route_chunk_rows(int64_t rows) {
+  int64_t c = (rows + kRouteMaxChunks - 1) / kRouteMaxChunks;
+  c = (c + kRouteThreads - 1) / kRouteThreads * kRouteThreads;
+  return c < kRouteThreads ? kRouteThreads : c;
 }
 
 }  // namespace
@@ -1143,10 +1180,24 @@ hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const u
   return hipGetLastError();
 }
 
+size_t route_scratch_bytes(int64_t rows, int64_t e) {
+  if (rows <= 0 || e <= 0) return 0;
+  const int64_t chunks = (rows + route_chunk_rows(rows) - 1) / route_chunk_rows(rows);
+  return (size_t)chunks * (size_t)(e + 1) * sizeof(int32_t);
+}
+
 hipError_t launch_moe_route(const int32_t* idx, int64_t entries, int64_t rows_per_entry, int64_t e,
-                            int32_t* offsets, int32_t* perm, hipStream_t s) {
-  moe_route_kernel<<<1, kRouteThreads, 0, s>>>(idx, (int)(entries * rows_per_entry), (int)e, offsets, perm,
-                                               (int)rows_per_entry);
+                            int32_t* offsets, int32_t* perm, int32_t* scratch, void* zero_out,
+                            int64_t row_bytes, hipStream_t s) {
+  const int64_t rows = entries * rows_per_entry;
+  const int64_t chunk = route_chunk_rows(rows);
+  const int chunks = (int)((rows + chunk - 1) / chunk);
+  route_count_kernel<<<chunks, kRouteThreads, 0, s>>>(idx, (int)rows, (int)rows_per_entry, (int)e,
+                                                      (int)chunk, scratch);
+  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(scratch, chunks, (int)e, offsets);
+  route_scatter_kernel<<<chunks, kRouteThreads, 0, s>>>(idx, (int)rows, (int)rows_per_entry, (int)e,
+                                                        (int)chunk, scratch, perm,
+                                                        reinterpret_cast<uint8_t*>(zero_out), row_bytes);
   return hipGetLastError();
 }
 

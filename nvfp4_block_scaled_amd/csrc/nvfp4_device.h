@@ -404,6 +404,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
 }
 
+// ----------------------------------------------------------------- output rows
+
+// Zeros to output row q of `out` (row_bytes bytes per row), written by the
+// whole wave: the rows of gather pairs whose expert lies outside [0, e).
+__device__ __forceinline__ void zero_row_wave(uint8_t* __restrict__ out, int64_t q, int64_t row_bytes) {
+  uint8_t* row = out + q * row_bytes;
+  const int lane = threadIdx.x & 63;
+  if ((row_bytes & 15) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0) {
+    for (int64_t o = 16 * lane; o < row_bytes; o += 1024)
+      *reinterpret_cast<u32x4*>(row + o) = u32x4{0u, 0u, 0u, 0u};
+  } else {
+    for (int64_t o = 2 * lane; o < row_bytes; o += 128) *reinterpret_cast<uint16_t*>(row + o) = 0;
+  }
+}
+
 // ----------------------------------------------------------------- barriers
 
 // LDS barrier without a memory fence: finish this wave's LDS operations, then

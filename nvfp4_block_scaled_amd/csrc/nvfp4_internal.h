@@ -41,9 +41,14 @@ hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, co
 hipError_t launch_qqmm_gemm(const void* xhat, int dt, const uint8_t* wc, const uint8_t* ws,
                             const float* gw, int64_t m, int64_t n, int64_t k, void* out,
                             hipStream_t s);
-// routing: row q (of entries * rows_per_entry) goes to expert idx[q / rows_per_entry]
+// routing: row q (of entries * rows_per_entry) goes to expert idx[q / rows_per_entry];
+// offsets [e + 1], perm [rows] (rows with an expert outside [0, e) at
+// perm[offsets[e] ..]); scratch of route_scratch_bytes(rows, e); with zero_out,
+// zeros to row q (row_bytes bytes) of zero_out for every such row
+size_t route_scratch_bytes(int64_t rows, int64_t e);
 hipError_t launch_moe_route(const int32_t* idx, int64_t entries, int64_t rows_per_entry, int64_t e,
-                            int32_t* offsets, int32_t* perm, hipStream_t s);
+                            int32_t* offsets, int32_t* perm, int32_t* scratch, void* zero_out,
+                            int64_t row_bytes, hipStream_t s);
 // gather contraction over `rows` routed rows: the A row of routed row s is
 // amap[s] when amap is given, else perm[s] / top_k; its output row perm[s];
 // x holds x_rows rows
@@ -73,7 +78,8 @@ hipError_t launch_gather_gemm_packed(const void* x, int dt, const uint8_t* pc, c
 // identity permutation), the x-row map of lhs indices, and the contraction
 // with weights [e, K, N] quantized along N (transpose = False; K % 8 == 0)
 hipError_t launch_sorted_route(const int32_t* rhs, int64_t pairs, int64_t mr, int64_t e,
-                               int32_t* offsets, int32_t* perm, hipStream_t s);
+                               int32_t* offsets, int32_t* perm, void* zero_out, int64_t row_bytes,
+                               hipStream_t s);
 hipError_t launch_amap(const int32_t* perm, const int32_t* lhs, int64_t rows, int64_t mr, int32_t* amap,
                        hipStream_t s);
 hipError_t launch_gather_gemm_t(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,

@@ -8,7 +8,26 @@
 // The kernel is HBM-bound: the weight stream is 9/16 byte per element and
 // nothing is reused, so the design is about keeping enough bytes in flight.
 //
-// Register path (k = 4096 * CH, CH = 1 or 2 for 16-bit x, 1 for float32):
+// Streaming path (16-bit x, k = 4096; qmv_stream_kernel): one 16-wave
+// workgroup per compute unit, each wave up to kStreamRows consecutive rows.
+//   * the global scales and x are the first loads of every wave, and a
+//     barrier puts every such load of the workgroup ahead of its weight
+//     loads: a vector load issued behind a compute unit's weight stream
+//     returns only after most of that stream (measured: x_hat ready 3.5-4 us
+//     into a 7.5 us kernel when it was loaded after the weights);
+//   * each wave then issues one row, builds x_hat for its share of x (a
+//     quarter group of 4 elements per lane, the whole vector per workgroup),
+//     issues two more rows, and from then on computes a row and issues the
+//     row kStreamAhead further.  A compute unit accepts only so many weight
+//     loads in flight; a wave issuing beyond that stalls, so the row loads
+//     are spread over the loop instead of all issued up front, and x_hat is
+//     built while only one row per wave is in flight;
+//   * a row is 3 loads: two 1 KB code runs and its 256 scale bytes (one
+//     dword per lane; each lane's two scale bytes per piece come from the
+//     lane holding them, ds_bpermute);
+//   * the arithmetic per row is the register path's below, operation for
+//     operation, so both give the same bits.
+// Register path (float32 x with k = 4096, 16-bit x with k = 8192):
 //   * every wave owns up to R consecutive rows and issues the loads of all of
 //     them (per row and lane: CH x 32 code bytes + CH x 4 scale bytes, the
 //     lanes of a wave covering each 2 KB chunk of a row contiguously) before
@@ -228,6 +247,160 @@ qmv_reg_kernel(const void* __restrict__ x, const float* __restrict__ gx,
 #pragma unroll
   for (int i = 1; i < R; ++i) mine = (lane == i) ? rs[i] : mine;
   if (lane < R && r0 + lane < n) reinterpret_cast<typename Elem<DT>::T*>(out)[r0 + lane] = from_f32<DT>(mine);
+}
+
+
+// ------------------------------------------------------------------ streaming path
+
+constexpr int kStreamWaves = 16;
+constexpr int kStreamThreads = kStreamWaves * 64;
+constexpr int kStreamRows = 4;   // rows per wave at most
+constexpr int kStreamAhead = 3;  // rows in flight per wave in the loop
+
+// One row of the streaming path: lane l's 32 elements at 32 l and 2048 +
+// 32 l (two 1 KB runs per wave) and scale bytes 4 l .. 4 l + 3 of the row.
+struct StreamRow {
+  u32x4 code[2];
+  uint32_t scale;
+};
+
+template <int DT>
+__global__ void __launch_bounds__(kStreamThreads)
+qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+                  const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
+                  const float* __restrict__ gw, int n, int q, int rem, void* __restrict__ out) {
+  constexpr int K = 4096;
+  using T = typename Elem<DT>::T;
+  __shared__ __attribute__((aligned(16))) uint32_t xs[K / 2];  // x_hat, 16-bit
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gwv = blockIdx.x * kStreamWaves + wave;
+  const int r0 = gwv * q + min(gwv, rem);
+  const int cnt = q + (gwv < rem ? 1 : 0);  // this wave's rows, at most kStreamRows
+
+  // 1. the global scales (a NULL pointer gets an empty range and reads 0)
+  //    and x: quarter group tid, elements 4 tid .. 4 tid + 3
+  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(gx, gx ? 4 : 0);
+  const __amdgpu_buffer_rsrc_t rgw = make_rsrc(gw, gw ? 4 : 0);
+  const float gx_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgx, 0, 0, 0));
+  const float gw_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgw, 0, 0, 0));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * sizeof(T));
+  const u32x2 xr = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)tid * 8u, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");  // the workgroup's x and scale loads go first
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. this wave's rows: a buffer range over exactly them, so that loads of
+  //    rows past cnt read zeros and every load can be issued unconditionally
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(wc + (int64_t)r0 * (K / 2), (uint64_t)cnt * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(ws + (int64_t)r0 * (K / 16), (uint64_t)cnt * (K / 16));
+  StreamRow wr[kStreamRows];
+  auto issue = [&](int i) {
+    const uint32_t co = (uint32_t)(i * (K / 2)) + 16u * lane;
+    wr[i].code[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, co, 0, 2));
+    wr[i].code[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, co + 1024u, 0, 2));
+    wr[i].scale = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(i * (K / 16)) + 4u * lane, 0, 2);
+  };
+  issue(0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. the factors 2688/g_x, g_x/2688, g_w/2688: one division, three lanes
+  float enc, dec, dec_w;
+  {
+    const float gxs = gx ? gx_v : kE4M3Max * kE2M1Max;
+    const float gws = gw ? gw_v : kE4M3Max * kE2M1Max;
+    const float num = lane == 0 ? kE4M3Max * kE2M1Max : (lane == 1 ? gxs : gws);
+    const float den = lane == 0 ? gxs : kE4M3Max * kE2M1Max;
+    float qv;
+    {
+#pragma clang fp contract(off)
+      qv = num / den;
+    }
+    enc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 0));
+    dec = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 1));
+    dec_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 2));
+  }
+
+  // 4. x_hat of this quarter group (lanes 4j .. 4j + 3 hold one group of 16)
+  {
+    float v[8];
+    unpack8<DT>(u32x4{xr.x, xr.y, 0u, 0u}, v);
+    float a = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                    fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+    a = fmaxf(a, dpp_mov<0xB1>(a));  // quad_perm [1,0,3,2]
+    a = fmaxf(a, dpp_mov<0x4E>(a));  // quad_perm [2,3,0,1]
+    const GroupScale gs = group_scale_from_amax(a, enc);
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma clang fp contract(off)
+      y[i] = v[i] * gs.enc_b;
+    }
+    uint32_t cw = 0;
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[0], y[1], 1.0f, 0);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[2], y[3], 1.0f, 1);
+    float sc;
+    {
+#pragma clang fp contract(off)
+      sc = e4m3_decode(gs.byte) * dec;
+    }
+    const f32x2 d0 = e2m1_decode2_f32<0>(cw), d1 = e2m1_decode2_f32<1>(cw);
+    float o[4];
+    {
+#pragma clang fp contract(off)
+      o[0] = d0.x * sc; o[1] = d0.y * sc; o[2] = d1.x * sc; o[3] = d1.y * sc;
+    }
+    reinterpret_cast<u32x2*>(xs)[tid] = u32x2{pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+  }
+#pragma unroll
+  for (int i = 1; i < kStreamAhead; ++i) issue(i);
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();  // x_hat written; the row loads stay in flight
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 5. this lane's x_hat pieces: elements 32 lane .. + 31 and 2048 + 32 lane ..
+  uint32_t xp[2][16];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const u32x4 t = reinterpret_cast<const u32x4*>(xs)[(hh * 2048 + 32 * lane) / 8 + qd];
+      xp[hh][4 * qd] = t.x; xp[hh][4 * qd + 1] = t.y;
+      xp[hh][4 * qd + 2] = t.z; xp[hh][4 * qd + 3] = t.w;
+    }
+  }
+
+  // 6. rows: compute row i, then issue row i + kStreamAhead
+  const int sshift = 8 * ((2 * lane) & 3);
+  float mine = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kStreamRows; ++i) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // the two scale bytes of piece hh sit in lane 32 hh + lane / 2
+      const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((32 * hh + (lane >> 1)) * 4, (int)wr[i].scale);
+      float se0, se1;
+      {
+#pragma clang fp contract(off)
+        const uint32_t sb = sw >> sshift;
+        se0 = e4m3_decode_byte<0>(sb) * dec_w;
+        se1 = e4m3_decode_byte<1>(sb) * dec_w;
+      }
+      const u32x4 c = wr[i].code[hh];
+      const float p0 = group_dot16<DT>(c.x, c.y, &xp[hh][0], nullptr);
+      const float p1 = group_dot16<DT>(c.z, c.w, &xp[hh][8], nullptr);
+      acc = __builtin_fmaf(p0, se0, acc);
+      acc = __builtin_fmaf(p1, se1, acc);
+    }
+    const float v = wave_sum_uniform(acc);
+    mine = (lane == i) ? v : mine;
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + kStreamAhead < kStreamRows) issue(i + kStreamAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (lane < cnt) reinterpret_cast<T*>(out)[r0 + lane] = from_f32<DT>(mine);
 }
 
 // ------------------------------------------------------------------ generic path
@@ -482,25 +655,35 @@ void launch_reg(const void* x, const float* gx, const uint8_t* wc, const uint8_t
   qmv_reg_kernel<DT, CH, R><<<(int)blocks, kThreadsQ, 0, s>>>(x, gx, wc, ws, gw, (int)n, out);
 }
 
+// rows per wave r <= kMaxRows: the launcher takes at least ceil(n / (8 kMaxRows)) workgroups
 template <int DT, int CH>
 void launch_reg_r(int r, const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                   const float* gw, int64_t n, void* out, int64_t blocks, hipStream_t s) {
-  switch (r) {
-    case 1: launch_reg<DT, CH, 1>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 2: launch_reg<DT, CH, 2>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 3: launch_reg<DT, CH, 3>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 4: launch_reg<DT, CH, 4>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 5: launch_reg<DT, CH, 5>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 6: launch_reg<DT, CH, 6>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 7: launch_reg<DT, CH, 7>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-    default: launch_reg<DT, CH, 8>(x, gx, wc, ws, gw, n, out, blocks, s); break;
-  }
+  static_assert(kMaxRows == 2, "rows per wave");
+  if (r <= 1)
+    launch_reg<DT, CH, 1>(x, gx, wc, ws, gw, n, out, blocks, s);
+  else
+    launch_reg<DT, CH, 2>(x, gx, wc, ws, gw, n, out, blocks, s);
 }
 
 template <int DT>
 hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                         const float* gw, int64_t n, int64_t k, void* out, hipStream_t s) {
   const int chunks = (k % 4096 == 0) ? (int)(k / 4096) : 0;
+  if constexpr (DT != kF32) {
+    if (chunks == 1 && n < 0x7FFFFFFF) {
+      // one 16-wave workgroup per compute unit, more when a wave would get
+      // more than kStreamRows rows
+      const int64_t per_wg = (int64_t)kStreamWaves * kStreamRows;
+      int64_t blocks = (n + kStreamWaves - 1) / kStreamWaves;
+      if (blocks > device_cu_count()) blocks = device_cu_count();
+      if (blocks < (n + per_wg - 1) / per_wg) blocks = (n + per_wg - 1) / per_wg;
+      const int64_t waves = blocks * kStreamWaves;
+      qmv_stream_kernel<DT><<<(int)blocks, kStreamThreads, 0, s>>>(
+          x, gx, wc, ws, gw, (int)n, (int)(n / waves), (int)(n % waves), out);
+      return hipGetLastError();
+    }
+  }
   const bool reg_path = chunks == 1 || (chunks == 2 && DT != kF32);
   if (reg_path) {
     // at least one workgroup per CU, at most kMaxRows rows per wave

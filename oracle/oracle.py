@@ -304,23 +304,26 @@ def quant_dequant_columnwise(x, global_scale=None, dtype="bf16"):
     return quant_dequant(np.ascontiguousarray(_f32(x).T), global_scale, dtype)
 
 
-def qqmm_vjp(x, w, dy, global_scale_x=None, global_scale_w=None, dtype="bf16", nthreads=None):
+def qqmm_vjp(x, w, dy, global_scale_x=None, global_scale_w=None, dtype="bf16", nthreads=None,
+             dx_rows=None, dw_rows=None):
     """Gradients of y = qqmm(x, w) for the cotangent dy ("mlx 0.30.7.2 ->
     0.30.7.6" diff page 8, primitives.cpp QQMatmul::vjp):
       g_dy = float32(max |dy|) when the primal global scales are given, else none;
       dx = qqmm(dy, w^T)   with w^T [k, n] quantized along n under g_w;
       dw = qqmm(dy^T, x^T) with x^T [k, m] quantized along m under g_x;
     each qqmm round-trips its first operand under g_dy.  Returns (dx [m, k],
-    dw [n, k], g_dy)."""
+    dw [n, k], g_dy); with dx_rows / dw_rows, only those rows of dx / dw (the
+    same values, fewer of them)."""
     x, w, dy = _f32(x), _f32(w), _f32(dy)
     if (global_scale_x is None) != (global_scale_w is None):
         raise ValueError("both global scales or neither")
     g_dy = tensor_amax(dy) if global_scale_x is not None else None
     wt_codes, wt_scales = quantize_columnwise(w, global_scale_w)   # w^T [k, n]
-    dx = qqmm(dy, wt_codes, wt_scales, g_dy, global_scale_w, dtype=dtype, nthreads=nthreads)
+    dx = qqmm(dy, wt_codes, wt_scales, g_dy, global_scale_w, dtype=dtype, nthreads=nthreads,
+              rows=dx_rows)
     xt_codes, xt_scales = quantize_columnwise(x, global_scale_x)   # x^T [k, m]
     dw = qqmm(np.ascontiguousarray(dy.T), xt_codes, xt_scales, g_dy, global_scale_x, dtype=dtype,
-              nthreads=nthreads)
+              nthreads=nthreads, rows=dw_rows)
     return dx, dw, g_dy
 
 

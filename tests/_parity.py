@@ -84,9 +84,47 @@ def assert_values_equal(got, ref, what=""):
                              f"got {got[i]!r} want {ref[i]!r}")
 
 
+CANARY = 0xA5
+GUARD_BYTES = 4096
+
+
+class Guarded:
+    """A device buffer with canary bytes on both sides: `t` is the tensor the
+    kernel writes (shape, dtype), the GUARD_BYTES before and after it hold
+    CANARY; check() fails if a kernel wrote outside `t`."""
+
+    def __init__(self, shape, dtype, device="cuda"):
+        esz = torch.empty((), dtype=dtype).element_size()
+        n = 1
+        for d in shape:
+            n *= int(d)
+        self.nbytes = n * esz
+        self.buf = torch.full((self.nbytes + 2 * GUARD_BYTES,), CANARY, dtype=torch.uint8, device=device)
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes].view(dtype).view(*shape)
+
+    def check(self, what=""):
+        head = self.buf[:GUARD_BYTES].cpu().numpy()
+        tail = self.buf[GUARD_BYTES + self.nbytes:].cpu().numpy()
+        for side, a in (("before", head), ("after", tail)):
+            bad = np.flatnonzero(a != CANARY)
+            if bad.size:
+                raise AssertionError(f"{what}: {bad.size} guard bytes {side} the output were "
+                                     f"overwritten (first at offset {int(bad[0])})")
+
+
+def guarded(shape, dtype, device="cuda"):
+    return Guarded(shape, dtype, device)
+
+
+def guarded_workspace(nbytes, device="cuda"):
+    """A 256-byte aligned guarded workspace of nbytes (at least 1) bytes."""
+    return Guarded((max(int(nbytes), 1),), torch.uint8, device)
+
+
 def oracle_dtype(t):
     return {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[t]
 
 
 __all__ = ["O", "REL_TOL", "say", "host", "dev", "scalar", "rel_errors", "assert_close",
-           "ulp_fraction", "assert_bytes_equal", "assert_values_equal", "oracle_dtype"]
+           "ulp_fraction", "assert_bytes_equal", "assert_values_equal", "oracle_dtype", "Guarded",
+           "guarded", "guarded_workspace", "CANARY"]

@@ -25,7 +25,11 @@ def test_world_size_above_one_is_refused():
 
 
 def test_traffic_figures_follow_the_measured_sources():
+    """A traffic figure is reported while its kernel source is the one the
+    counters were taken on, and null after any change to it."""
     import bench
     for kernel, (src, sha, nbytes) in bench.MEASURED_TRAFFIC.items():
-        assert bench.source_hash(src) == sha, f"{kernel}: {src} changed since its counters were taken"
-        assert bench.measured_traffic(kernel) == nbytes
+        if bench.source_hash(src) == sha:
+            assert bench.measured_traffic(kernel) == nbytes
+        else:
+            assert bench.measured_traffic(kernel) is None

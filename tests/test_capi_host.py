@@ -127,8 +127,47 @@ def test_gather_qmm_errors(L):
     bad = list(ok)
     bad[8] = 2000
     assert L.nvfp4_gather_qmm(*bad) == UNSUP
-    assert L.nvfp4_moe_route(0x70000, 10, 2, 0, A, B, None) == INV
-    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, None) == UNSUP
+    rws = L.nvfp4_moe_route_workspace_size(10, 2, 4)
+    assert rws > 0 and rws % 256 == 0
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 0, A, B, 0x60000, rws, None) == INV
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, None, rws, None) == INV
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, 0x60000, rws - 1, None) == INV
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, 0x60010, rws, None) == INV
+    assert L.nvfp4_moe_route(0x70000, 10, 2, 4, A, B, 0x60000, rws, None) == UNSUP
+    # the gather workspace holds the routing's counts as well
+    assert ws >= 256 + 256 + rws
+
+
+def test_contraction_offset_limits(L):
+    """The matrix-core contractions address x and the weight's codes with
+    32-bit offsets: 2 GB or more of either is refused on the host (m > 1)."""
+    big = 1 << 40  # a workspace size that never limits
+    # x of 2^31 bytes: m * k * 2 = 2^31
+    m, k = 1 << 15, 1 << 15
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, m, 64, k, C, 0x60000, big, None) == UNSUP
+    assert "2 GB" in err(L)
+    assert L.nvfp4_qmm(A, BF16, W, B, G, m, 64, k, C, None) == UNSUP and "2 GB" in err(L)
+    # just below: validation passes and the architecture check stops the call
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, m - 1, 64, k, C, 0x60000, big, None) == UNSUP
+    assert "gfx950" in err(L)
+    # the weight's codes: n * k / 2 = 2^31
+    n = 1 << 17
+    assert L.nvfp4_qqmm(A, BF16, G, W, B, G, 64, n, k, C, 0x60000, big, None) == UNSUP
+    assert "2 GB" in err(L)
+    assert L.nvfp4_qqmm_packed(A, BF16, G, W, B, G, 64, n, k, C, 0x60000, big, None) == UNSUP
+    assert "2 GB" in err(L)
+    # one row of x streams with 64-bit addressing: no such limit
+    assert L.nvfp4_qmv(A, BF16, None, W, B, None, n, 32768, C, None) == UNSUP
+    assert "gfx950" in err(L)
+    # gather: x rows (t) and one expert's codes
+    gws = L.nvfp4_gather_qmm_workspace_size(1 << 16, 2, 8, 64, 1 << 14)
+    assert L.nvfp4_gather_qmm(A, BF16, W, B, G, 0x70000, 1 << 16, 2, 8, 64, 1 << 14, C, 0x60000, gws,
+                              None) == UNSUP and "2 GB" in err(L)
+    gws = L.nvfp4_gather_qmm_workspace_size(64, 2, 8, n, k)
+    assert L.nvfp4_gather_qmm(A, BF16, W, B, G, 0x70000, 64, 2, 8, n, k, C, 0x60000, gws,
+                              None) == UNSUP and "2 GB" in err(L)
+    assert L.nvfp4_gather_qmm_packed(A, BF16, W, B, G, 0x70000, 64, 2, 8, n, k, C, 0x60000, gws,
+                                     None) == UNSUP and "2 GB" in err(L)
 
 
 def test_tensor_amax_errors(L):
