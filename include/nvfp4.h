@@ -284,6 +284,28 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * nvfp4_gather_qmm_noalloc -- nvfp4_gather_qmm for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and results.  The routing tables live in a
+ * fixed 5 MiB device array of the library (one per GPU, held until the
+ * process ends), so the call allocates nothing.  Its contents are whatever
+ * the last call on that GPU left; every table the call reads it writes
+ * first.  Calls that overlap on one GPU (on different streams, or graph
+ * replays in flight together) share that array and race: serialize them.
+ * Limit: the tables (e + 1 + t * top_k ints plus the routing's per-chunk
+ * counts, each part rounded up to 256 bytes) must fit in 5 MiB -- e.g.
+ * t * top_k = 1,048,576 pairs with up to 256 experts; larger calls return
+ * NVFP4_ERR_UNSUPPORTED with a message naming the sizes.  Other errors as
+ * nvfp4_gather_qmm.
+ */
+nvfp4_status nvfp4_gather_qmm_noalloc(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, const float* global_scale_w,
+                                      const int32_t* expert_idx, int64_t t, int64_t top_k,
+                                      int64_t e, int64_t n, int64_t k, void* out,
+                                      hipStream_t stream);
+
+/*
  * nvfp4_moe_route -- the routing step of nvfp4_gather_qmm on its own:
  * offsets[0..e] = exclusive prefix sum of the per-expert pair counts,
  * perm[offsets[x] .. offsets[x+1]) = the flat pair ids t*top_k + j routed to

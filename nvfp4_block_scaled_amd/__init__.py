@@ -68,6 +68,7 @@ def load_library():
         "nvfp4_qmm": (I, [P, I, P, P, P, I64, I64, I64, P, P]),
         "nvfp4_gather_qmm_workspace_size": (SZ, [I64, I64, I64, I64, I64]),
         "nvfp4_gather_qmm": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_gather_qmm_noalloc": (I, [P, I, P, P, P, P, I64, I64, I64, I64, I64, P, P]),
         "nvfp4_moe_route_workspace_size": (SZ, [I64, I64, I64]),
         "nvfp4_moe_route": (I, [P, I64, I64, I64, P, P, P, SZ, P]),
         "nvfp4_mfma_pack_size": (I, [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
@@ -373,6 +374,29 @@ def nvfp4_gather_qmm(x, w_codes, w_scales, expert_idx, global_scale_w=None, out=
     _check(L.nvfp4_gather_qmm(_ptr(x), _dtype_code(x, "x"), _ptr(w_codes), _ptr(w_scales), _ptr(g),
                               _ptr(expert_idx), t, top_k, e, n, k, _ptr(out), _ptr(workspace),
                               nbytes, _stream()))
+    return out
+
+
+def nvfp4_gather_qmm_noalloc(x, w_codes, w_scales, expert_idx, global_scale_w=None, out=None):
+    """nvfp4_gather_qmm without a workspace: the routing tables live in the
+    library's fixed device scratch (overlapping calls on one GPU race)."""
+    L = load_library()
+    _dev(x, "x")
+    _dev(expert_idx, "expert_idx")
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2:
+        raise ValueError("expert_idx must be int32 [t, top_k]")
+    t, k = x.shape
+    top_k = expert_idx.shape[1]
+    if expert_idx.shape[0] != t:
+        raise ValueError("expert_idx rows must match x rows")
+    _w_shapes(w_codes, w_scales, k)
+    e, n = w_codes.shape[0], w_codes.shape[1]
+    g = _gscale(global_scale_w, "global_scale_w", numel=e)
+    if out is None:
+        out = torch.empty((t, top_k, n), dtype=x.dtype, device=x.device)
+    _check(L.nvfp4_gather_qmm_noalloc(_ptr(x), _dtype_code(x, "x"), _ptr(w_codes), _ptr(w_scales),
+                                      _ptr(g), _ptr(expert_idx), t, top_k, e, n, k, _ptr(out),
+                                      _stream()))
     return out
 
 

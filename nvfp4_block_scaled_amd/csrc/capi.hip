@@ -111,6 +111,38 @@ nvfp4_status launched(const char* op, hipError_t e) {
   return ok();
 }
 
+// Device scratch of nvfp4_gather_qmm_noalloc: the routing tables live here
+// instead of in a caller workspace.  Each GPU holds its own copy for the life
+// of the process; host code uses only the per-device address from
+// hipGetSymbolAddress, never the array's name (a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = (size_t)5 << 20;
+static __device__ __align__(256) uint8_t noalloc_scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// the address of `dev`'s copy, looked up once per device with `dev` current
+nvfp4_status noalloc_scratch_of(const char* op, int dev, void** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_DEVICE, "[%s] Device id %d out of range.", op, dev);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (cur != dev) {
+      hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr)
+      return fail(NVFP4_ERR_DEVICE, "[%s] hipGetSymbolAddress of the scratch array: %s", op,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,6 +586,57 @@ nvfp4_status nvfp4_gather_qmm(const void* x, nvfp4_dtype dt, const uint8_t* w_co
   hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
                                           reinterpret_cast<int32_t*>(wsb + rl.scratch), out,
                                           n * (int64_t)dtype_size(dt), stream);
+  if (he != hipSuccess) return launched(op, he);
+  return launched(op, nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets,
+                                                 perm, t, t * top_k, top_k, nullptr, e, n, k, out,
+                                                 stream));
+}
+
+nvfp4_status nvfp4_gather_qmm_noalloc(const void* x, nvfp4_dtype dt, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, const float* global_scale_w,
+                                      const int32_t* expert_idx, int64_t t, int64_t top_k,
+                                      int64_t e, int64_t n, int64_t k, void* out,
+                                      hipStream_t stream) {
+  const char* op = "gather_qmm_noalloc";
+  if (!dtype_ok(dt))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_noalloc] Unsupported dtype code %d (float32, float16 and bfloat16 only).",
+                (int)dt);
+  if (t <= 0 || top_k <= 0 || e <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[gather_qmm_noalloc] t, top_k, e and n must be positive.");
+  if (nvfp4_status st = check_k(op, k)) return st;
+  if (!x || !w_codes || !w_scales || !expert_idx || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_noalloc] x, w_codes, w_scales, expert_idx and out must not be NULL.");
+  if (!aligned(x, 16) || !aligned(w_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[gather_qmm_noalloc] x and w_codes must be 16-byte aligned.");
+  if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_noalloc] Sizes too large.");
+  if (t * k * (int64_t)dtype_size(dt) >= kOffsetLimit || n * (k / 2) >= kOffsetLimit)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[gather_qmm_noalloc] x and one expert's codes must each stay below 2 GB.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[gather_qmm_noalloc] at most 1024 experts are supported.");
+  const RouteLayout rl = route_layout(t * top_k, e);
+  if (rl.total > kNoAllocScratchBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[gather_qmm_noalloc] the routing tables of %lld pairs and %lld experts need %zu bytes, "
+                "above the library's fixed scratch of %zu bytes (use nvfp4_gather_qmm with a workspace).",
+                (long long)(t * top_k), (long long)e, rl.total, kNoAllocScratchBytes);
+  if (nvfp4_status st = check_device(op, stream)) return st;
+  int dev = 0;
+  hipError_t he = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (he != hipSuccess)
+    return fail(NVFP4_ERR_DEVICE, "[%s] No HIP device behind the stream: %s", op, hipGetErrorString(he));
+  void* scratch = nullptr;
+  if (nvfp4_status st = noalloc_scratch_of(op, dev, &scratch)) return st;
+  char* base = reinterpret_cast<char*>(scratch);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + rl.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + rl.perm);
+  he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
+                               reinterpret_cast<int32_t*>(base + rl.scratch), out,
+                               n * (int64_t)dtype_size(dt), stream);
   if (he != hipSuccess) return launched(op, he);
   return launched(op, nvfp4::launch_gather_gemm(x, dt, w_codes, w_scales, global_scale_w, offsets,
                                                  perm, t, t * top_k, top_k, nullptr, e, n, k, out,

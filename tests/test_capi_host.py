@@ -138,6 +138,25 @@ def test_gather_qmm_errors(L):
     assert ws >= 256 + 256 + rws
 
 
+def test_gather_noalloc_limits(L):
+    """The allocation-free gather takes no workspace; tables beyond its fixed
+    5 MiB scratch are refused on the host with the sizes in the message."""
+    ok = (A, BF16, W, B, G, 0x70000, 1 << 19, 2, 256, 64, 32, C, None)
+    assert L.nvfp4_gather_qmm_noalloc(*ok) == UNSUP and "gfx950" in err(L)  # fits: 2^20 pairs
+    big = list(ok)
+    big[6] = 1 << 20  # 2^21 pairs
+    assert L.nvfp4_gather_qmm_noalloc(*big) == UNSUP and "scratch" in err(L) and "2097152" in err(L)
+    big = list(ok)
+    big[8] = 1024  # 1024 experts with 2^20 pairs
+    assert L.nvfp4_gather_qmm_noalloc(*big) == UNSUP and "scratch" in err(L)
+    bad = list(ok)
+    bad[10] = 24
+    assert L.nvfp4_gather_qmm_noalloc(*bad) == INV and "group size 16" in err(L)
+    bad = list(ok)
+    bad[5] = None
+    assert L.nvfp4_gather_qmm_noalloc(*bad) == INV
+
+
 def test_contraction_offset_limits(L):
     """The matrix-core contractions address x and the weight's codes with
     32-bit offsets: 2 GB or more of either is refused on the host (m > 1)."""
