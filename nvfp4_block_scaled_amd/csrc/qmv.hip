@@ -17,11 +17,14 @@
 //     into a 7.5 us kernel when it was loaded after the weights);
 //   * each wave then issues one row, builds x_hat for its share of x (a
 //     quarter group of 4 elements per lane, the whole vector per workgroup),
-//     issues two more rows, and from then on computes a row and issues the
-//     row kStreamAhead further.  A compute unit accepts only so many weight
-//     loads in flight; a wave issuing beyond that stalls, so the row loads
-//     are spread over the loop instead of all issued up front, and x_hat is
-//     built while only one row per wave is in flight;
+//     and after the workgroup barrier reads its x_hat pieces, issues two
+//     more rows, and from then on computes a row and issues the row
+//     kStreamAhead further.  A compute unit accepts only so many weight loads
+//     in flight; a wave issuing beyond that stalls, so the row loads are
+//     spread over the loop instead of all issued up front, and x_hat is
+//     built while only one row per wave is in flight (measured at n = 14336:
+//     7.5 us per launch, against 8.45 us with rows 1 and 2 issued ahead of
+//     the barrier);
 //   * a row is 3 loads: two 1 KB code runs and its 256 scale bytes (one
 //     dword per lane; each lane's two scale bytes per piece come from the
 //     lane holding them, ds_bpermute);
@@ -353,10 +356,8 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     }
     reinterpret_cast<u32x2*>(xs)[tid] = u32x2{pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
   }
-#pragma unroll
-  for (int i = 1; i < kStreamAhead; ++i) issue(i);
   __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();  // x_hat written; the row loads stay in flight
+  lds_barrier();  // x_hat written; row 0's loads stay in flight
   __builtin_amdgcn_sched_barrier(0);
 
   // 5. this lane's x_hat pieces: elements 32 lane .. + 31 and 2048 + 32 lane ..
@@ -369,6 +370,18 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
       xp[hh][4 * qd] = t.x; xp[hh][4 * qd + 1] = t.y;
       xp[hh][4 * qd + 2] = t.z; xp[hh][4 * qd + 3] = t.w;
     }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // the rest of the window, one row after the other (the wait counter retires
+  // loads in order, so a row's loads must not interleave with the next's).
+  // Issued only now: a wave whose loads exceed what the compute unit accepts
+  // stalls at the issue, and a stall ahead of the barrier above would hold
+  // every wave of the workgroup
+#pragma unroll
+  for (int i = 1; i < kStreamAhead; ++i) {
+    issue(i);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // 6. rows: compute row i, then issue row i + kStreamAhead
