@@ -137,6 +137,54 @@ def timed(fn, iters, warmup, graph=False):
     return start.elapsed_time(end) / iters
 
 
+def _pct(v, q):
+    v = sorted(v)
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def timed_stats(fn, iters, warmup, graph=False, reps=9):
+    """Per-call milliseconds: `mean` over all timed calls, and the median, p10
+    and p90 of the per-call times.  Eager: one HIP event between consecutive
+    calls on the launch stream, so the calls run back to back exactly as in
+    timed().  Graph: `reps` replays of one captured graph of `iters` calls,
+    each replay timed; the spread is then that of the per-call means of the
+    replays."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(iters):
+                    fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for r in range(reps):
+            g.replay()
+            ev[r + 1].record()
+        ev[-1].synchronize()
+        per = [ev[r].elapsed_time(ev[r + 1]) / iters for r in range(reps)]
+        mean = ev[0].elapsed_time(ev[-1]) / (iters * reps)
+    else:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        ev[0].record()
+        for i in range(iters):
+            fn()
+            ev[i + 1].record()
+        ev[-1].synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+        mean = ev[0].elapsed_time(ev[-1]) / iters
+    return dict(mean=mean, median=_pct(per, 0.5), p10=_pct(per, 0.1), p90=_pct(per, 0.9), n=len(per))
+
+
 def bench_qqmm(args, nv, torch, W):
     x, w = W.qqmm_inputs(device="cuda")
     gw = nv.nvfp4_tensor_amax(w)
@@ -163,8 +211,9 @@ def bench_qqmm(args, nv, torch, W):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_step = timed(step, args.steps, 0)
+    st_step = timed_stats(step, args.steps, 0)
     wall = time.perf_counter() - t0
+    ms_step = st_step["mean"]
     flop = 2.0 * M * N * K
     # the same step on the row-major weight
     ms_step_rm = timed(step_row_major, args.steps, 2)
@@ -172,12 +221,13 @@ def bench_qqmm(args, nv, torch, W):
     xhat = nv.nvfp4_quant_dequant(x, gx)
     gemm = lambda: nv.nvfp4_qmm_packed(xhat, wp, gw, out=out)
     settle(gemm, 0.05)
-    ms_gemm = timed(gemm, args.steps, 2)
+    st_gemm = timed_stats(gemm, args.steps, 2)
+    ms_gemm = st_gemm["mean"]
     ms_prepass = timed(lambda: nv.nvfp4_quant_dequant(x, gx, out=xhat), args.steps, 2, graph=True)
     torch.cuda.synchronize()
     return dict(ms_step=ms_step, wall=wall, tflops=flop / ms_step / 1e9, ms_gemm=ms_gemm,
                 gemm_tflops=flop / ms_gemm / 1e9, ms_prepass=ms_prepass, flop=flop,
-                ms_step_rm=ms_step_rm, data=(x, w_host))
+                ms_step_rm=ms_step_rm, data=(x, w_host), st_step=st_step, st_gemm=st_gemm)
 
 
 def bench_qmv(args, nv, torch, W):
@@ -197,14 +247,32 @@ def bench_qmv(args, nv, torch, W):
         state["i"] += 1
         nv.nvfp4_qmv(x, wcs[i], wss[i], gx, gw, out=out)
 
+    # the same weights packed for the matrix cores (the copy the prefill step
+    # reads): one row of x through nvfp4_qqmm_packed, the fp4 matrix-core qmv
+    wps = [nv.nvfp4_mfma_pack(wcs[i], wss[i]) for i in range(copies)]
+    wsp, _ = nv.qqmm_workspace(2, N, K, torch.bfloat16, "cuda")
+
+    def call_packed():
+        i = state["i"] % copies
+        state["i"] += 1
+        nv.nvfp4_qqmm_packed(x, wps[i], gx, gw, out=out, workspace=wsp)
+
     iters = copies * 4
     settle(call, 0.05)
-    ms = timed(call, iters, copies, graph=True)
+    st = timed_stats(call, iters, copies, graph=True)
+    ms = st["mean"]
+    settle(call_packed, 0.05)
+    st_packed = timed_stats(call_packed, iters, copies, graph=True)
+    ms_packed = st_packed["mean"]
     nbytes = per + x.numel() * 2 + N * 2
-    # warm (cache-resident) number for context: always the same copy
+    # warm (cache-resident) numbers for context: always the same copy
     ms_warm = timed(lambda: nv.nvfp4_qmv(x, wc, ws, gx, gw, out=out), 64, 8, graph=True)
+    ms_packed_warm = timed(lambda: nv.nvfp4_qqmm_packed(x, wps[0], gx, gw, out=out, workspace=wsp),
+                           64, 8, graph=True)
     return dict(ms=ms, gbs=nbytes / ms / 1e6, bytes=nbytes, copies=copies, ms_warm=ms_warm,
-                gbs_warm=nbytes / ms_warm / 1e6)
+                gbs_warm=nbytes / ms_warm / 1e6, ms_packed=ms_packed,
+                gbs_packed=nbytes / ms_packed / 1e6, gbs_packed_warm=nbytes / ms_packed_warm / 1e6,
+                st=st, st_packed=st_packed)
 
 
 def bench_small(args, nv, torch, W):
@@ -443,6 +511,84 @@ def bench_gather(args, nv, torch, W):
                 ms_rm=ms_rm, tflops_rm=flop / ms_rm / 1e9)
 
 
+def ceiling_lib():
+    """libnvfp4_ceiling.so: the measurement kernels (HBM read, copy, MFMA loop)."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "nvfp4_block_scaled_amd", "libnvfp4_ceiling.so"))
+    P, U64, I64, I = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_ceiling_read.argtypes = [P, U64, P, P]
+    L.nvfp4_ceiling_copy.argtypes = [P, P, U64, P]
+    L.nvfp4_ceiling_mfma.argtypes = [I64, I, P, P, P]
+    for f in (L.nvfp4_ceiling_read, L.nvfp4_ceiling_copy, L.nvfp4_ceiling_mfma):
+        f.restype = I
+    return L
+
+
+def bench_ceilings(args, torch):
+    """What this GPU allows, measured beside the kernels:
+      read   one pass over 33,067,008 bytes (qmv's weight codes + scales + x +
+             out), rotated over copies totalling > 512 MB as for qmv;
+      copy   32 MiB read + 32 MiB written, rotated the same way;
+      mfma   v_mfma_f32_32x32x16_bf16 back to back (4 waves per CU x 2), and the
+             shader clock it ran at."""
+    L = ceiling_lib()
+    stream = lambda: ctypes_stream(torch)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    rb = 33067008
+    copies = max(2, -(-600_000_000 // rb))
+    bufs = [torch.empty(rb, dtype=torch.uint8, device="cuda").random_(0, 256) for _ in range(copies)]
+    st_i = {"i": 0}
+
+    def rd():
+        i = st_i["i"] % copies
+        st_i["i"] += 1
+        rc = L.nvfp4_ceiling_read(bufs[i].data_ptr(), rb, sink.data_ptr(), stream())
+        assert rc == 0, rc
+
+    settle(rd, 0.05)
+    st_read = timed_stats(rd, copies * 4, copies, graph=True)
+    del bufs
+    cb = 32 << 20
+    ccopies = max(2, -(-600_000_000 // (2 * cb)))
+    srcs = [torch.empty(cb, dtype=torch.uint8, device="cuda").random_(0, 256) for _ in range(ccopies)]
+    dsts = [torch.empty(cb, dtype=torch.uint8, device="cuda") for _ in range(ccopies)]
+
+    def cp():
+        i = st_i["i"] % ccopies
+        st_i["i"] += 1
+        rc = L.nvfp4_ceiling_copy(srcs[i].data_ptr(), dsts[i].data_ptr(), cb, stream())
+        assert rc == 0, rc
+
+    settle(cp, 0.05)
+    st_copy = timed_stats(cp, ccopies * 4, ccopies, graph=True)
+    assert torch.equal(srcs[0], dsts[0]), "ceiling copy is not a copy"
+    del srcs, dsts
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 20000
+
+    def mf():
+        rc = L.nvfp4_ceiling_mfma(iters, blocks, sink.data_ptr(), clocks.data_ptr(), stream())
+        assert rc == 0, rc
+
+    settle(mf, 0.1)
+    st_mfma = timed_stats(mf, 5, 1)
+    cyc, ticks = (int(v) for v in clocks.cpu())
+    sclk = cyc / (ticks / 100e6) / 1e9 if ticks > 0 else None
+    flop = blocks * 4 * iters * 4 * 32768.0
+    return dict(read=st_read, read_bytes=rb, read_copies=copies, copy=st_copy, copy_bytes=cb,
+                mfma=st_mfma, mfma_flop=flop, sclk_ghz=sclk)
+
+
+def ctypes_stream(torch):
+    return torch.cuda.current_stream().cuda_stream
+
+
+def stats_ms(st, scale=1.0, digits=4):
+    """A timed_stats dict as {mean, median, p10, p90} in ms (or us with scale 1e3)."""
+    return {k: round(st[k] * scale, digits) for k in ("mean", "median", "p10", "p90")}
+
+
 def bench_copy(args, torch):
     """A plain device-to-device copy of 512 MiB: the calibration kernel for the
     HBM byte counters (FETCH_SIZE / WRITE_SIZE read against known bytes)."""
@@ -492,7 +638,20 @@ def cpu_baseline(data, seconds_target=20.0):
     flop = 2.0 * rows * cols * K
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=nthreads, kind="oracle",
                 sample=f"oracle qqmm on {rows} of {M} rows x {cols} of {N} weight rows, K={K} "
-                       f"(x round trip, float32 weight decode, double sums): {dt:.2f} s")
+                       f"(x round trip, float32 weight decode, double sums): {dt:.2f} s",
+                threads_used=nthreads, host_cpus=os.cpu_count(), cpu_model=cpu_model())
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or None
 
 
 def main():
@@ -502,7 +661,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="all", choices=["all", "qqmm", "qmv", "small", "backward", "mx", "quantize",
-                                                      "gather", "gather_ex", "copy"])
+                                                      "gather", "gather_ex", "copy", "ceilings"])
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -525,11 +684,19 @@ def main():
             f"{res['qqmm']['flop'] / res['qqmm']['ms_step_rm'] / 1e9:.1f}); "
             f"gemm {res['qqmm']['ms_gemm']:.3f} ms ({res['qqmm']['gemm_tflops']:.1f} TFLOP/s); "
             f"x pre-pass {res['qqmm']['ms_prepass'] * 1e3:.1f} us")
+    if args.only in ("all", "qqmm", "qmv", "ceilings"):
+        log("ceilings (HBM read / copy, bf16 MFMA loop) ...")
+        res["ceil"] = bench_ceilings(args, torch)
+        c = res["ceil"]
+        log(f"  read {c['read']['mean'] * 1e3:.2f} us per 33 MB ({c['read_bytes'] / c['read']['mean'] / 1e6:.0f} GB/s); "
+            f"copy {2 * c['copy_bytes'] / c['copy']['mean'] / 1e6:.0f} GB/s; mfma loop "
+            f"{c['mfma_flop'] / c['mfma']['mean'] / 1e9:.0f} TFLOP/s at sclk {c['sclk_ghz']:.3f} GHz")
     if args.only in ("all", "qmv"):
         log("qmv decode ...")
         res["qmv"] = bench_qmv(args, nv, torch, W)
-        log(f"  {res['qmv']['ms'] * 1e3:.2f} us/launch, {res['qmv']['gbs']:.0f} GB/s "
-            f"(warm {res['qmv']['gbs_warm']:.0f} GB/s)")
+        log(f"  row-major {res['qmv']['ms'] * 1e3:.2f} us/launch, {res['qmv']['gbs']:.0f} GB/s "
+            f"(warm {res['qmv']['gbs_warm']:.0f} GB/s); packed {res['qmv']['ms_packed'] * 1e3:.2f} "
+            f"us/launch, {res['qmv']['gbs_packed']:.0f} GB/s (warm {res['qmv']['gbs_packed_warm']:.0f} GB/s)")
     if args.only in ("all", "small"):
         log("small-batch qqmm (m rows @ the decode weight) ...")
         res["small"] = bench_small(args, nv, torch, W)
@@ -577,9 +744,27 @@ def main():
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded Normal activations/weights of the pages' shapes)"}
+    ceil = res.get("ceil")
+    if ceil is not None:
+        read_gbs = ceil["read_bytes"] / ceil["read"]["mean"] / 1e6
+        mfma_tf = ceil["mfma_flop"] / ceil["mfma"]["mean"] / 1e9
+        line["ceilings"] = {
+            "hbm_read": {"GBps": round(read_gbs, 1), "frac": round(read_gbs / PEAK_HBM_GBS, 4),
+                         "us_per_launch": stats_ms(ceil["read"], 1e3, 3), "bytes": ceil["read_bytes"],
+                         "copies_rotated": ceil["read_copies"],
+                         "kernel": "read_kernel (nvfp4_ceiling_read: 16-byte nontemporal loads, 8 per thread)"},
+            "hbm_copy": {"GBps": round(2 * ceil["copy_bytes"] / ceil["copy"]["mean"] / 1e6, 1),
+                         "frac": round(2 * ceil["copy_bytes"] / ceil["copy"]["mean"] / 1e6 / PEAK_HBM_GBS, 4),
+                         "us_per_launch": stats_ms(ceil["copy"], 1e3, 3),
+                         "bytes_read_and_written": 2 * ceil["copy_bytes"], "kernel": "copy_kernel (nvfp4_ceiling_copy)"},
+            "mfma_bf16_loop": {"TFLOPs": round(mfma_tf, 1), "frac": round(mfma_tf / PEAK_BF16_TFLOPS, 4),
+                               "sclk_GHz": round(ceil["sclk_ghz"], 3) if ceil["sclk_ghz"] else None,
+                               "kernel": "mfma_kernel (nvfp4_ceiling_mfma: v_mfma_f32_32x32x16_bf16, no memory)"},
+            "profiles": "profiles/ceilings_read_copy_mfma.txt"}
     if "qqmm" in res:
         q = res["qqmm"]
         line.update(value=round(q["tflops"], 2), unit="TFLOP/s", ms_per_step=round(q["ms_step"], 4))
+        line["ms_per_step_stats"] = stats_ms(q["st_step"])
         line["config"] = {"workload": "qqmm prefill: x bf16 [2048,4096] (amax + NVFP4 round trip) "
                                       "@ NVFP4 w [14336,4096]^T (packed once for the matrix cores), bf16 out",
                           "m": M, "n": N, "k": K, "group_size": 16}
@@ -589,7 +774,15 @@ def main():
                             "unit": "TFLOP/s", "frac": round(q["gemm_tflops"] / PEAK_BF16_TFLOPS, 4),
                             "traffic": measured_traffic("gemm"), "ms_per_launch": round(q["ms_gemm"], 4),
                             "algorithmic_flop_per_launch": q["flop"],
-                            "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2}
+                            "algorithmic_bytes_per_launch": M * K * 2 + N * K // 2 + N * K // 16 + M * N * 2,
+                            "ms_per_launch_stats": stats_ms(q["st_gemm"])}
+        if ceil is not None and ceil["sclk_ghz"]:
+            sclk = ceil["sclk_ghz"]
+            peak_at = PEAK_BF16_TFLOPS * sclk / 2.4
+            line["roofline"].update(
+                sclk_GHz=round(sclk, 3), peak_at_sclk=round(peak_at, 1),
+                frac_clock_adjusted=round(q["gemm_tflops"] / peak_at, 4),
+                frac_of_mfma_loop_ceiling=round(q["gemm_tflops"] / mfma_tf, 4))
         line["x_prepass_us"] = round(q["ms_prepass"] * 1e3, 2)
         line["row_major_weight_step"] = {"value": round(q["flop"] / q["ms_step_rm"] / 1e9, 2),
                                          "unit": "TFLOP/s", "ms_per_step": round(q["ms_step_rm"], 4)}
@@ -600,7 +793,18 @@ def main():
                        "algorithmic_bytes_per_launch": v["bytes"], "traffic": measured_traffic("qmv"),
                        "weight_copies_rotated": v["copies"],
                        "warm_cache_GBps": round(v["gbs_warm"], 1),
+                       "us_per_launch_stats": stats_ms(v["st"], 1e3, 3),
+                       "kernel": "qmv_stream_kernel<bf16> (nvfp4_qmv, row-major weight)",
+                       "packed_weight": {"GBps": round(v["gbs_packed"], 1),
+                                         "frac": round(v["gbs_packed"] / PEAK_HBM_GBS, 4),
+                                         "us_per_launch": round(v["ms_packed"] * 1e3, 3),
+                                         "us_per_launch_stats": stats_ms(v["st_packed"], 1e3, 3),
+                                         "warm_cache_GBps": round(v["gbs_packed_warm"], 1),
+                                         "kernel": "qmv_packed_kernel<bf16> (nvfp4_qqmm_packed, m = 1)"},
                        "workload": "qmv decode: x bf16 [1,4096] @ NVFP4 w [14336,4096]^T"}
+        if ceil is not None:
+            line["qmv"]["frac_of_read_ceiling"] = round(v["gbs"] / read_gbs, 4)
+            line["qmv"]["packed_weight"]["frac_of_read_ceiling"] = round(v["gbs_packed"] / read_gbs, 4)
     if "small" in res:
         line["small_batch_qqmm"] = {
             f"m={m_}": {k_: {"GBps": round(v["gbs"], 1), "frac": round(v["gbs"] / PEAK_HBM_GBS, 4),

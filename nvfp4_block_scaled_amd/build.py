@@ -13,8 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libnvfp4.so")
+# the benchmark's measurement kernels, a library of their own
+CEILING_LIB = os.path.join(HERE, "libnvfp4_ceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["codec.hip", "qmv.hip", "gemm.hip", "smallm.hip", "mx_codec.hip", "mx_gemm.hip", "mx_qmv.hip", "gather_ex.hip", "capi.hip"]
+SOURCES = ["codec.hip", "qmv.hip", "qmv_packed.hip", "gemm.hip", "smallm.hip", "mx_codec.hip", "mx_gemm.hip", "mx_qmv.hip", "gather_ex.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [
@@ -35,15 +38,21 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+def _link(objs, lib, verbose):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp"] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB, verbose)
     return LIB
 
 

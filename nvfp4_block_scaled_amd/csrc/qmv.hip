@@ -10,6 +10,11 @@
 //
 // Streaming path (16-bit x, k = 4096; qmv_stream_kernel): one 16-wave
 // workgroup per compute unit, each wave up to kStreamRows consecutive rows.
+//   * a compute unit streams at the rate its loads in flight allow (their
+//     number per unit is bounded), so the rows are split evenly over the
+//     workgroups first (56 each at n = 14336) and then over their waves;
+//     giving whole waves 4 rows and the rest 3 left half the units with 64
+//     rows and half with 48 (measured: 7.5 us per launch);
 //   * the global scales and x are the first loads of every wave, and a
 //     barrier puts every such load of the workgroup ahead of its weight
 //     loads: a vector load issued behind a compute unit's weight stream
@@ -271,16 +276,21 @@ template <int DT>
 __global__ void __launch_bounds__(kStreamThreads)
 qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
                   const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                  const float* __restrict__ gw, int n, int q, int rem, void* __restrict__ out) {
+                  const float* __restrict__ gw, int n, int qw, int remw, void* __restrict__ out) {
   constexpr int K = 4096;
   using T = typename Elem<DT>::T;
   __shared__ __attribute__((aligned(16))) uint32_t xs[K / 2];  // x_hat, 16-bit
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gwv = blockIdx.x * kStreamWaves + wave;
-  const int r0 = gwv * q + min(gwv, rem);
-  const int cnt = q + (gwv < rem ? 1 : 0);  // this wave's rows, at most kStreamRows
+  // rows: the workgroups split n as evenly as possible (qw or qw + 1 each),
+  // then each workgroup's waves split its rows (a compute unit's stream is
+  // what one workgroup reads, so the balance that matters is per workgroup)
+  const int g = blockIdx.x;
+  const int rb = g * qw + min(g, remw);
+  const int rw = qw + (g < remw ? 1 : 0);
+  const int r0 = rb + (rw * wave) / kStreamWaves;
+  const int cnt = rb + (rw * (wave + 1)) / kStreamWaves - r0;  // at most kStreamRows
 
   // 1. the global scales (a NULL pointer gets an empty range and reads 0)
   //    and x: quarter group tid, elements 4 tid .. 4 tid + 3
@@ -384,16 +394,24 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // 6. rows: compute row i, then issue row i + kStreamAhead
+  // 6. rows: once row i is in (its scale dword, the row's last load, is
+  //    read), issue row i + kStreamAhead, then compute row i
   const int sshift = 8 * ((2 * lane) & 3);
   float mine = 0.0f;
 #pragma unroll
   for (int i = 0; i < kStreamRows; ++i) {
+    // the two scale bytes of piece hh sit in lane 32 hh + lane / 2
+    uint32_t swv[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      swv[hh] = (uint32_t)__builtin_amdgcn_ds_bpermute((32 * hh + (lane >> 1)) * 4, (int)wr[i].scale);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + kStreamAhead < kStreamRows) issue(i + kStreamAhead);
+    __builtin_amdgcn_sched_barrier(0);
     float acc = 0.0f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      // the two scale bytes of piece hh sit in lane 32 hh + lane / 2
-      const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute((32 * hh + (lane >> 1)) * 4, (int)wr[i].scale);
+      const uint32_t sw = swv[hh];
       float se0, se1;
       {
 #pragma clang fp contract(off)
@@ -409,9 +427,6 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     }
     const float v = wave_sum_uniform(acc);
     mine = (lane == i) ? v : mine;
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + kStreamAhead < kStreamRows) issue(i + kStreamAhead);
-    __builtin_amdgcn_sched_barrier(0);
   }
   if (lane < cnt) reinterpret_cast<T*>(out)[r0 + lane] = from_f32<DT>(mine);
 }
@@ -691,9 +706,8 @@ hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const
       int64_t blocks = (n + kStreamWaves - 1) / kStreamWaves;
       if (blocks > device_cu_count()) blocks = device_cu_count();
       if (blocks < (n + per_wg - 1) / per_wg) blocks = (n + per_wg - 1) / per_wg;
-      const int64_t waves = blocks * kStreamWaves;
       qmv_stream_kernel<DT><<<(int)blocks, kStreamThreads, 0, s>>>(
-          x, gx, wc, ws, gw, (int)n, (int)(n / waves), (int)(n % waves), out);
+          x, gx, wc, ws, gw, (int)n, (int)(n / blocks), (int)(n % blocks), out);
       return hipGetLastError();
     }
   }

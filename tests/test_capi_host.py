@@ -39,8 +39,8 @@ def L():
     lib.nvfp4_debug_set_arch_override(None)
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
 
@@ -51,6 +51,29 @@ def test_library_exports_every_declared_symbol(L):
     for n in names:
         assert hasattr(L, n), n
         assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_ceiling_library_exports_its_header():
+    """libnvfp4_ceiling.so (the benchmark's read / copy / MFMA-loop kernels)
+    loads and exports every function include/nvfp4_ceiling.h declares; its
+    argument checks reject bad sizes before anything is enqueued."""
+    path = os.path.join(ROOT, "nvfp4_block_scaled_amd", "libnvfp4_ceiling.so")
+    if not os.path.exists(path):
+        from nvfp4_block_scaled_amd import build
+        build.build()
+    lib = ctypes.CDLL(path)
+    names = declared_functions(os.path.join(ROOT, "include", "nvfp4_ceiling.h"))
+    assert names == ["nvfp4_ceiling_copy", "nvfp4_ceiling_mfma", "nvfp4_ceiling_read"]
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    lib.nvfp4_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.nvfp4_ceiling_mfma.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    bad = 1  # hipErrorInvalidValue
+    assert lib.nvfp4_ceiling_read(A, 24, B, None) == bad      # not a multiple of 16
+    assert lib.nvfp4_ceiling_read(None, 32, B, None) == bad
+    assert lib.nvfp4_ceiling_mfma(0, 4, B, C, None) == bad
+    assert lib.nvfp4_ceiling_mfma(10, 0, B, C, None) == bad
 
 
 def test_version(L):

@@ -1,0 +1,119 @@
+"""GPU parity of qqmm with one row of 16-bit x against the packed weight: the
+fp4 matrix-core kernel (qmv_packed.hip) that nvfp4_qqmm_packed runs for m = 1
+and 512 <= k <= 8192.
+
+The kernel takes exact products of the stored codes with x_hat split into
+two e2m1 vectors per block, so against the oracle (double sums, one rounding)
+only its float32 summation order differs:
+* exact-grid operands give the float64 product rounded once, bit for bit;
+* general data meets the norm-wise 1e-2 bar, and the fraction of outputs
+  within one unit in the last place of the oracle's is printed and held to
+  a floor (0.99 for bfloat16, 0.97 for the finer float16);
+* every output buffer carries guard bands on both sides.
+Shapes: one tile and less (n = 4, 36), ragged last tiles, many tiles per
+workgroup (k = 512 with n = 64000), k from 512 to 8192 (one and two quarter
+groups of x per thread), and the decode shape n = 14336, k = 4096.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_amd as nv
+import workloads as W
+from _parity import (O, assert_close, assert_values_equal, dev, guarded, host, oracle_dtype, say,
+                     scalar, ulp_fraction)
+
+pytestmark = pytest.mark.gpu
+
+ULP_FLOOR = {torch.bfloat16: 0.99, torch.float16: 0.97}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    nv.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(x, packed, gx, gw, n, dtype):
+    out = guarded((1, n), dtype)
+    nv.nvfp4_qqmm_packed(x, packed, gx, gw, out=out.t)
+    torch.cuda.synchronize()
+    out.check("qmv packed out")
+    return host(out.t)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("k", [512, 2048, 4096, 8192])
+@pytest.mark.parametrize("gx,gw", [(2688.0, 336.0), (None, None)])
+def test_qmv_packed_grid_bit_exact(dtype, k, gx, gw):
+    """Exact-grid x [1, k] and w [300, k] (a partial last tile): every partial
+    sum is exact, so the output is the float64 product rounded once."""
+    say(f"qmv packed grid k={k} {dtype} gx={gx}")
+    x = W.grid_tensor(1, k, seed=500 + k)
+    w = W.grid_tensor(300, k, seed=501 + k)
+    wc, ws = nv.nvfp4_quantize(w.to(dtype).cuda(), scalar(gw))
+    packed = nv.nvfp4_mfma_pack(wc, ws)
+    got = _run(x.to(dtype).cuda(), packed, scalar(gx), scalar(gw), 300, dtype)
+    y = np.asarray(host(x.to(dtype)), np.float64) @ np.asarray(host(w.to(dtype)), np.float64).T
+    ref = np.array([[O.round_to(float(v), oracle_dtype(dtype)) for v in y[0]]], np.float32)
+    assert_values_equal(got, ref, "qmv packed grid")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("n,k", [(4, 512), (36, 512), (64000, 512), (300, 1024), (1028, 2048),
+                                 (8200, 4096), (100, 6144), (2052, 8192)])
+def test_qmv_packed_general(dtype, n, k):
+    """General data against the oracle on every output."""
+    say(f"qmv packed general n={n} k={k} {dtype}")
+    od = oracle_dtype(dtype)
+    x = W.normal((1, k), 1.0, 600 + n + k, od)
+    w = W.normal((n, k), 0.02, 601 + n, od)
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    packed = nv.nvfp4_mfma_pack(dev(oc), dev(os_))
+    got = _run(x.cuda(), packed, scalar(gxh), scalar(gwh), n, dtype)
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od)
+    assert_close(got, ref, what=f"qmv packed n={n} k={k}")
+    frac = ulp_fraction(got, ref, od)
+    say(f"  within 1 ulp: {frac:.4f}")
+    assert frac >= ULP_FLOOR[dtype]
+
+
+def test_qmv_packed_no_global_scales_and_zero_x():
+    """No global scales on either side; an all-zero x gives zeros."""
+    say("qmv packed without global scales, zero x")
+    n, k = 520, 4096
+    x = W.normal((1, k), 1.0, 700, "bf16")
+    w = W.normal((n, k), 0.02, 701, "bf16")
+    oc, os_ = O.quantize(host(w), None)
+    packed = nv.nvfp4_mfma_pack(dev(oc), dev(os_))
+    got = _run(x.cuda(), packed, None, None, n, torch.bfloat16)
+    assert_close(got, O.qqmm(host(x), oc, os_, None, None, dtype="bf16"), what="qmv packed no g")
+    zero = _run(torch.zeros(1, k, dtype=torch.bfloat16, device="cuda"), packed, None, None, n,
+                torch.bfloat16)
+    assert np.all(zero == 0)
+
+
+def test_qmv_packed_decode_14336x4096_every_output():
+    """The decode workload (x bf16 [1, 4096] Normal(0, 1), w [14336, 4096] from
+    Normal(0, 0.02), g = amax of each) through the benchmarked call, every
+    output against the oracle; the row-major qmv on the same weight agrees
+    with it to rounding."""
+    say("qmv packed decode 14336 x 4096")
+    x, w = W.qmv_inputs()
+    xd, wd = x.cuda(), w.cuda()
+    gx, gw = nv.nvfp4_tensor_amax(xd), nv.nvfp4_tensor_amax(wd)
+    wc, ws = nv.nvfp4_quantize(wd, gw)
+    packed = nv.nvfp4_mfma_pack(wc, ws)
+    got = _run(xd, packed, gx, gw, 14336, torch.bfloat16)
+    rm = host(nv.nvfp4_qmv(xd, wc, ws, gx, gw))
+    gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
+    oc, os_ = O.quantize(host(w), gwh)
+    ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype="bf16")
+    assert_close(got, ref, what="qmv packed decode")
+    frac = ulp_fraction(got, ref, "bf16")
+    say(f"  within 1 bf16 ulp: {frac:.4f}")
+    assert frac >= ULP_FLOOR[torch.bfloat16]
+    assert_close(got, rm.reshape(1, -1), tol=2e-3, what="packed vs row-major qmv")
