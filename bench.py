@@ -224,9 +224,10 @@ def bench_qqmm(args, nv, torch, W):
     st_gemm = timed_stats(gemm, args.steps, 2)
     ms_gemm = st_gemm["mean"]
     ms_prepass = timed(lambda: nv.nvfp4_quant_dequant(x, gx, out=xhat), args.steps, 2, graph=True)
+    ms_amax = timed(lambda: nv.nvfp4_tensor_amax(x, out=gx), args.steps, 2, graph=True)
     torch.cuda.synchronize()
     return dict(ms_step=ms_step, wall=wall, tflops=flop / ms_step / 1e9, ms_gemm=ms_gemm,
-                gemm_tflops=flop / ms_gemm / 1e9, ms_prepass=ms_prepass, flop=flop,
+                gemm_tflops=flop / ms_gemm / 1e9, ms_prepass=ms_prepass, ms_amax=ms_amax, flop=flop,
                 ms_step_rm=ms_step_rm, data=(x, w_host), st_step=st_step, st_gemm=st_gemm)
 
 
@@ -683,7 +684,7 @@ def main():
         log(f"  step {res['qqmm']['ms_step']:.3f} ms ({res['qqmm']['tflops']:.1f} TFLOP/s; row-major weight "
             f"{res['qqmm']['flop'] / res['qqmm']['ms_step_rm'] / 1e9:.1f}); "
             f"gemm {res['qqmm']['ms_gemm']:.3f} ms ({res['qqmm']['gemm_tflops']:.1f} TFLOP/s); "
-            f"x pre-pass {res['qqmm']['ms_prepass'] * 1e3:.1f} us")
+            f"x pre-pass {res['qqmm']['ms_prepass'] * 1e3:.1f} us, amax of x {res['qqmm']['ms_amax'] * 1e3:.1f} us")
     if args.only in ("all", "qqmm", "qmv", "ceilings"):
         log("ceilings (HBM read / copy, bf16 MFMA loop) ...")
         res["ceil"] = bench_ceilings(args, torch)
@@ -784,6 +785,7 @@ def main():
                 frac_clock_adjusted=round(q["gemm_tflops"] / peak_at, 4),
                 frac_of_mfma_loop_ceiling=round(q["gemm_tflops"] / mfma_tf, 4))
         line["x_prepass_us"] = round(q["ms_prepass"] * 1e3, 2)
+        line["x_amax_us"] = round(q["ms_amax"] * 1e3, 2)
         line["row_major_weight_step"] = {"value": round(q["flop"] / q["ms_step_rm"] / 1e9, 2),
                                          "unit": "TFLOP/s", "ms_per_step": round(q["ms_step_rm"], 4)}
     if "qmv" in res:

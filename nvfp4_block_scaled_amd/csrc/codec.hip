@@ -23,26 +23,36 @@ constexpr int kThreads = 256;
 
 constexpr int kAmaxBlocks = 256;    // one workgroup per CU
 constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxUnroll = 4;      // 8-element chunks in flight per lane
 
 // The workgroup maxima of one launch meet in a slot of a small ring in device
-// memory: an atomic max on the slot's word (non-negative floats order like
-// their unsigned bits), then, once that atomic has returned, a ticket.  The
-// workgroup that draws the last ticket takes the word and clears it (one
-// atomic exchange), writes out and clears the ticket counter, so nothing has
-// to be cleared before a launch and no cache flush is needed: device-scope
-// atomics meet at one point for every XCD.  Launches take the slots in turn:
-// launches that overlap in time (on different streams) use different slots
-// while fewer than kAmaxSlots of them overlap.  Both arrays start at zero
-// with the module.
+// memory, in two levels.  Workgroup b joins group b % kAmaxGroups: an atomic
+// max on the group's word (non-negative floats order like their unsigned
+// bits), then, once that atomic has returned, a ticket on the group's
+// counter.  The workgroup that draws its group's last ticket takes the group
+// word and clears it (one atomic exchange), clears the group counter, and
+// does the same on the slot's final word and counter; the one that draws the
+// final counter's last ticket writes out.  So nothing has to be cleared
+// before a launch and no cache flush is needed: device-scope atomics meet at
+// one point for every XCD.  One level had all 256 workgroups queue on one
+// word (measured 2.8 us of a 10 us launch); groups of 16 on words 64 bytes
+// apart cut that to about 1.3 us.  Launches take the slots in turn: launches
+// that overlap in time (on different streams) use different slots while
+// fewer than kAmaxSlots of them overlap.  All arrays start at zero with the
+// module.
 constexpr int kAmaxSlots = 64;
+constexpr int kAmaxGroups = 16;
+constexpr int kAmaxLine = 16;  // words per 64-byte line
 __device__ unsigned int amax_tickets[kAmaxSlots];
 __device__ unsigned int amax_words[kAmaxSlots];
+__device__ unsigned int amax_group_tickets[kAmaxSlots * kAmaxGroups * kAmaxLine];
+__device__ unsigned int amax_group_words[kAmaxSlots * kAmaxGroups * kAmaxLine];
 
 // max |x| over n elements: one 1024-thread workgroup per CU, a grid-stride
 // loop over 8-element chunks with four chunks in flight per lane (a whole
-// 16.8 MB activation is one round of loads), a scalar tail, a wave max, a
-// workgroup max through LDS, then the last workgroup's reduction of the
-// workgroup maxima (above).
+// 16.8 MB activation is one round of loads; eight per lane would leave it to
+// the one-chunk loop), a scalar tail, a wave max, a workgroup max through
+// LDS, then the reduction of the workgroup maxima (above).
 template <int DT>
 __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restrict__ x, int64_t n,
                                                             float* __restrict__ out, int slot) {
@@ -51,12 +61,12 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restri
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   float m = 0.0f;
   int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; h + 3 * stride < chunks; h += 4 * stride) {
-    float v[4][8];
+  for (; h + (kAmaxUnroll - 1) * stride < chunks; h += kAmaxUnroll * stride) {
+    float v[kAmaxUnroll][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<DT>(x, h + u * stride, v[u]);
+    for (int u = 0; u < kAmaxUnroll; ++u) load8<DT>(x, h + u * stride, v[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kAmaxUnroll; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[u][i]));
   }
@@ -78,16 +88,27 @@ __global__ void __launch_bounds__(kAmaxThreads) amax_kernel(const void* __restri
     float b = part[0];
 #pragma unroll
     for (int w = 1; w < kAmaxThreads / 64; ++w) b = fmaxf(b, part[w]);
-    __hip_atomic_fetch_max(amax_words + slot, __float_as_uint(b), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int g = blockIdx.x % kAmaxGroups;
+    const unsigned int members = gridDim.x / kAmaxGroups + (g < gridDim.x % kAmaxGroups ? 1u : 0u);
+    const unsigned int groups = gridDim.x < (unsigned)kAmaxGroups ? gridDim.x : kAmaxGroups;
+    unsigned int* gword = amax_group_words + (slot * kAmaxGroups + g) * kAmaxLine;
+    unsigned int* gtick = amax_group_tickets + (slot * kAmaxGroups + g) * kAmaxLine;
+    __hip_atomic_fetch_max(gword, __float_as_uint(b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the max has landed
-    const unsigned int t =
-        __hip_atomic_fetch_add(amax_tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (t == gridDim.x - 1) {  // every other workgroup's max landed before its ticket
-      const unsigned int w =
-          __hip_atomic_exchange(amax_words + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *out = __uint_as_float(w);
-      __hip_atomic_store(amax_tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int t = __hip_atomic_fetch_add(gtick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == members - 1) {  // every other member's max landed before its ticket
+      const unsigned int gm = __hip_atomic_exchange(gword, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gtick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(amax_words + slot, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      const unsigned int t2 =
+          __hip_atomic_fetch_add(amax_tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t2 == groups - 1) {
+        const unsigned int w =
+            __hip_atomic_exchange(amax_words + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *out = __uint_as_float(w);
+        __hip_atomic_store(amax_tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -352,7 +373,7 @@ hipError_t launch_tensor_amax(const void* x, int dt, int64_t n, float* out, hipS
   static std::atomic<unsigned int> next_slot{0};
   const int slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % kAmaxSlots);
   // n == 0 still runs one workgroup, which writes 0
-  const int blocks = grid_for(n / 8 + 1, kAmaxThreads * 4, kAmaxBlocks);
+  const int blocks = grid_for(n / 8 + 1, kAmaxThreads * kAmaxUnroll, kAmaxBlocks);
   switch (dt) {
     case kF32: amax_kernel<kF32><<<blocks, kAmaxThreads, 0, s>>>(x, n, out, slot); break;
     case kF16: amax_kernel<kF16><<<blocks, kAmaxThreads, 0, s>>>(x, n, out, slot); break;

@@ -292,12 +292,11 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   const int r0 = rb + (rw * wave) / kStreamWaves;
   const int cnt = rb + (rw * (wave + 1)) / kStreamWaves - r0;  // at most kStreamRows
 
-  // 1. the global scales (a NULL pointer gets an empty range and reads 0)
-  //    and x: quarter group tid, elements 4 tid .. 4 tid + 3
-  const __amdgpu_buffer_rsrc_t rgx = make_rsrc(gx, gx ? 4 : 0);
-  const __amdgpu_buffer_rsrc_t rgw = make_rsrc(gw, gw ? 4 : 0);
-  const float gx_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgx, 0, 0, 0));
-  const float gw_v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rgw, 0, 0, 0));
+  // 1. the global scales, by scalar loads (they take no slot of the compute
+  //    unit's vector-load queue, which the weight stream needs from the
+  //    start), and x: quarter group tid, elements 4 tid .. 4 tid + 3
+  const float gxs = gx ? *gx : kE4M3Max * kE2M1Max;
+  const float gws = gw ? *gw : kE4M3Max * kE2M1Max;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * sizeof(T));
   const u32x2 xr = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)tid * 8u, 0, 0));
   __builtin_amdgcn_sched_barrier(0);
@@ -321,8 +320,6 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   // 3. the factors 2688/g_x, g_x/2688, g_w/2688: one division, three lanes
   float enc, dec, dec_w;
   {
-    const float gxs = gx ? gx_v : kE4M3Max * kE2M1Max;
-    const float gws = gw ? gw_v : kE4M3Max * kE2M1Max;
     const float num = lane == 0 ? kE4M3Max * kE2M1Max : (lane == 1 ? gxs : gws);
     const float den = lane == 0 ? gxs : kE4M3Max * kE2M1Max;
     float qv;
