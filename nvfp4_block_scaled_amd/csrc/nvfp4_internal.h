@@ -37,10 +37,10 @@ hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, co
                            const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t n,
                            void* out, hipStream_t s);
 
-// qmv_packed.hip: qqmm with one row of 16-bit x against the packed weight,
-// 512 <= k <= 8192 (k % 64 == 0), on the fp4 matrix cores
+// qmv_packed.hip: qqmm with 1 <= m <= 4 rows of 16-bit x against the packed
+// weight, 512 <= k <= 8192 (k % 64 == 0), on the fp4 matrix cores
 bool qmv_packed_ok(int dt, int64_t m, int64_t k);
-hipError_t launch_qmv_packed(const void* x, int dt, const float* gx, const uint8_t* pc,
+hipError_t launch_qmv_packed(const void* x, int dt, int64_t m, const float* gx, const uint8_t* pc,
                              const uint8_t* ps, const float* gw, int64_t n, int64_t k, void* out,
                              hipStream_t s);
 

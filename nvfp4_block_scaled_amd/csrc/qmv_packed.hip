@@ -1,19 +1,20 @@
-// qmv_packed.hip -- qqmm with one row of 16-bit x against the packed weight,
-// on the matrix cores with the weight's fp4 codes as they are stored:
-//   out[n] = T( sum_k x_hat[k] * w[n, k] ),  x_hat the NVFP4 round trip of x
-//   under g_x ("mlx 0.30.7.2 -> 0.30.7.6" diff page 8, qqmm; page 7,
-//   QQMatmul::eval_gpu, the M == 1 case), w decoded with g_w on every block
-//   scale ("[Metal] global scale for qmm" PR 4458, statement).
+// qmv_packed.hip -- qqmm with 1 to 4 rows of 16-bit x against the packed
+// weight, on the matrix cores with the weight's fp4 codes as they are stored:
+//   out[m, n] = T( sum_k x_hat[m, k] * w[n, k] ),  x_hat the NVFP4 round trip
+//   of x under g_x ("mlx 0.30.7.2 -> 0.30.7.6" diff page 8, qqmm; page 7,
+//   QQMatmul::eval_gpu, the M == 1 case and the small batches beside it), w
+//   decoded with g_w on every block scale ("[Metal] global scale for qmm" PR
+//   4458, statement).
 //
 // The register path of qmv.hip spends about one VALU instruction per weight
-// element (a conversion per two codes, a dot product per two elements), and
-// at n = 14336, k = 4096 that work, not the 33 MB stream, sets its time.  Here
-// the matrix cores do the products:
+// element and row of x (a conversion per two codes, a dot product per two
+// elements); here the matrix cores do the products:
 //   * v_mfma_scale_f32_16x16x128_f8f6f4 (both operands e2m1, unit hardware
 //     scales) takes one packed 1 KB code block -- 32 rows x one 64-wide k step
-//     -- per instruction: lane l = i + 16 G loads the block's bytes 16 l ..
-//     + 15, which are row i + 16 (G % 2), codes 32 (G / 2) .. + 31 of the
-//     step, and serve as the first operand's row i, k slice 32 G .. + 31;
+//     -- per instruction and row of x: lane l = i + 16 G loads the block's
+//     bytes 16 l .. + 15, which are row i + 16 (G % 2), codes 32 (G / 2) ..
+//     + 31 of the step, and serve as the first operand's row i, k slice
+//     32 G .. + 31;
 //   * x_hat splits exactly into two e2m1 vectors per block b of 16.  With
 //     sc_b = e4m3(s_b) * g_x/2688 (float32) and d an element's decoded code,
 //     x_hat = T(d * sc_b) = X * T(sc_b) + Y * T(1.5 * sc_b), where X = d for
@@ -29,18 +30,20 @@
 //     and by the weight's block scale e4m3(s), and accumulated in float32;
 //     the row sums are taken across lanes and waves in a fixed order and
 //     multiplied by g_w/2688 at the end.
-// Per 1 KB of codes a lane spends 12 VALU instructions (4 scale decodes, 4
-// products, 4 accumulations) instead of about 40.
+// Per 1 KB of codes and row of x a lane spends 16 VALU instructions (4 to
+// place its 8 bytes of X or Y codes in the operand, 4 products, 4
+// accumulations, and 4 scale decodes shared by the rows of x) instead of
+// about 40.
 //
 // Work split: a workgroup (16 waves, one per CU at k = 4096) takes whole
 // 32-row tiles, at most 128 blocks; its waves take contiguous runs of at most
-// 8 blocks in (tile, step) order.  The workgroup first writes the second
-// operand of every k step into LDS (1 KB per step) and the x coefficients;
+// 8 blocks in (tile, step) order.  The workgroup first writes the X and Y
+// codes of every block of x (8 bytes each) and the coefficients into LDS;
 // each wave stages its blocks' scales (128 bytes per block, one 16-byte load
-// per lane for all 8) in LDS.  As in the streaming qmv, the x and g loads go
-// first, a barrier puts them ahead of the weight loads of every wave, a
-// couple of blocks are in flight while x_hat is built, and the rest of the
-// run is issued a few blocks ahead of the products.
+// per lane for all 8) in LDS.  As in the streaming qmv, the x loads go first,
+// a barrier puts them ahead of the weight loads of every wave, a couple of
+// blocks are in flight while x_hat is built, and the rest of the run is
+// issued as each block arrives.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -52,18 +55,20 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kQpWaves = 16;
 constexpr int kQpThreads = 64 * kQpWaves;
-constexpr int kQpRun = 8;      // blocks per wave at most
-constexpr int kQpAhead0 = 2;   // blocks in flight while x_hat is built
-constexpr int kQpAhead = 4;    // blocks in flight in the loop
+constexpr int kQpRun = 8;        // blocks per wave at most
+constexpr int kQpAhead0 = 2;     // blocks in flight while x_hat is built
+constexpr int kQpAhead = 4;      // blocks in flight in the loop
 constexpr int kQpMinSteps = 8;   // k >= 512: a run of 8 blocks meets at most two tiles
 constexpr int kQpMaxSteps = 128; // k <= 8192
+constexpr int kQpMaxRows = 4;    // rows of x
 
-// LDS: operand table (1 KB per step), coefficients (2 floats per block),
-// scale stage (1 KB per wave), partial row sums (per tile of the workgroup,
-// one 32-row slot per wave: kQpWaves * kQpRun / steps tiles at most).
-constexpr size_t qp_lds(int steps) {
-  return (size_t)steps * (1024 + 32) + kQpWaves * 1024 +
-         (size_t)(kQpWaves * kQpRun / steps) * kQpWaves * 32 * sizeof(float);
+// LDS for M rows of x: X / Y codes (16 bytes per block and row), coefficients
+// (8 bytes per block and row), scale stage (1 KB per wave), partial row sums
+// (per tile of the workgroup, row of x and wave, 32 floats; kQpWaves *
+// kQpRun / steps tiles at most).
+constexpr size_t qp_lds(int steps, int M) {
+  return (size_t)M * steps * 4 * (16 + 8) + kQpWaves * 1024 +
+         (size_t)(kQpWaves * kQpRun / steps) * kQpWaves * M * 32 * sizeof(float);
 }
 
 template <int CTRL>
@@ -71,17 +76,19 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// XR: quarter groups of x per thread (k <= 4096 k: 1, k <= 8192: 2).
-template <int DT, int XR>
+// M rows of x (m <= M are real: the rows past m read as zeros); XR quarter
+// groups of x per thread (M k / 4096 rounded up).
+template <int DT, int M, int XR>
 __global__ void __launch_bounds__(kQpThreads)
-qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+qmv_packed_kernel(const void* __restrict__ x, int m, const float* __restrict__ gx,
                   const uint8_t* __restrict__ pc, const uint8_t* __restrict__ ps,
                   const float* __restrict__ gw, int n, int steps, int tq, int trem,
                   void* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* btab = lds;
-  float* coef = reinterpret_cast<float*>(lds + steps * 1024);
-  uint8_t* stage = lds + steps * (1024 + 32);
+  const int nblk = steps * 4;  // blocks of 16 per row of x
+  u32x2* ctab = reinterpret_cast<u32x2*>(lds);                    // [M][nblk][X, Y]
+  float* coef = reinterpret_cast<float*>(lds + M * nblk * 16);    // [M][nblk][X, Y]
+  uint8_t* stage = lds + M * nblk * 24;
   float* part = reinterpret_cast<float*>(stage + kQpWaves * 1024);
   using T = typename Elem<DT>::T;
   const int tid = threadIdx.x;
@@ -97,35 +104,27 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
 
   // 1. the global scales, by scalar loads (they take no slot of the compute
   //    unit's vector-load queue, which the weight stream needs from the
-  //    start), and x: quarter groups tid + 1024 r, elements 4 (tid + 1024 r) .. + 3
+  //    start), and x: quarter groups tid + 1024 r, elements 4 (tid + 1024 r)
+  //    .. + 3 of x viewed as one vector of m k
   const float gxs = gx ? *gx : kE4M3Max * kE2M1Max;
   const float gws = gw ? *gw : kE4M3Max * kE2M1Max;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)K * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)m * K * sizeof(T));
   u32x2 xr[XR];
 #pragma unroll
   for (int r = 0; r < XR; ++r)
     xr[r] = __builtin_bit_cast(
         u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)(tid + kQpThreads * r) * 8u, 0, 0));
 
-  // 2. the all-zero entries of the operand table (48 of the 64 lanes of every
-  //    step; lane j + 16 G is nonzero only for G = 2 (bb / 2) + h)
-  for (int e = tid; e < 48 * steps; e += kQpThreads) {
-    const int st = e / 48, z = e - 48 * st;
-    const int j = z / 3, u = z - 3 * j;
-    const int gnz = 2 * ((j & 3) >> 1) + (j >> 3);
-    const int G = u + (u >= gnz ? 1 : 0);
-    *reinterpret_cast<u32x4*>(btab + st * 1024 + 16 * (j + 16 * G)) = u32x4{0u, 0u, 0u, 0u};
-  }
-  // this wave's partial-sum slots, one per tile of the workgroup, zero
-  // where its run does not reach (its own later writes follow in order)
-  for (int e = lane; e < nt * 8; e += 64)
-    *reinterpret_cast<f32x4*>(part + ((e >> 3) * kQpWaves + wave) * 32 + 4 * (e & 7)) =
+  // this wave's partial-sum slots, one per tile of the workgroup and row of
+  // x, zero where its run does not reach (its own later writes follow in order)
+  for (int e = lane; e < nt * M * 8; e += 64)
+    *reinterpret_cast<f32x4*>(part + ((e / (M * 8)) * kQpWaves + wave) * M * 32 + 4 * (e % (M * 8))) =
         f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");  // the workgroup's x and scale loads go first
+  asm volatile("s_barrier" ::: "memory");  // the workgroup's x loads go first
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. this wave's run: buffer ranges over exactly its blocks, so that loads
+  // 2. this wave's run: buffer ranges over exactly its blocks, so that loads
   //    past cnt read zeros and every load can be issued unconditionally
   const int64_t gb0 = (int64_t)t0 * steps + b0;
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(pc + gb0 * 1024, (uint64_t)cnt * 1024);
@@ -141,7 +140,7 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // 4. the factors 2688/g_x, g_x/2688, g_w/2688: one division, three lanes
+  // 3. the factors 2688/g_x, g_x/2688, g_w/2688: one division, three lanes
   float enc, dec, dec_w;
   {
     const float num = lane == 0 ? kE4M3Max * kE2M1Max : (lane == 1 ? gxs : gws);
@@ -156,13 +155,13 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     dec_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 2));
   }
 
-  // 5. x's codes, split into X and Y, into the operand table; coefficients.
-  //    The four lanes of a quad hold one block; lane c of the quad writes its
-  //    entry (h = c & 1, xy = c >> 1).
+  // 4. x's codes, split into X and Y, and the coefficients.  The four lanes
+  //    of a quad hold one block (blocks never straddle rows of x); lane 0 of
+  //    the quad writes its X codes and coefficients, lane 1 its Y codes.
 #pragma unroll
   for (int r = 0; r < XR; ++r) {
     const int qg = tid + kQpThreads * r;
-    if (qg < K / 4) {  // K / 4 is a multiple of 16: whole quads
+    if (qg < M * K / 4) {  // K / 4 is a multiple of 16: whole quads
       float v[8];
       unpack8<DT>(u32x4{xr[r].x, xr[r].y, 0u, 0u}, v);
       float am = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
@@ -189,14 +188,12 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
       const uint32_t w0 = dpp_u32<0x00>(xy), w1 = dpp_u32<0x55>(xy);
       const uint32_t w2 = dpp_u32<0xAA>(xy), w3 = dpp_u32<0xFF>(xy);
       const int c = tid & 3;
-      const int isY = c >> 1, h = c & 1;
-      const uint32_t lo = isY ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
-      const uint32_t hi = isY ? ((w2 >> 16) | (w3 & 0xFFFF0000u)) : ((w2 & 0xFFFFu) | (w3 << 16));
-      const int b = qg >> 2;  // block of x
-      const int st = b >> 2, bb = b & 3;
-      const int j = 8 * h + 4 * isY + bb, G = 2 * (bb >> 1) + h;
-      *reinterpret_cast<u32x4*>(btab + st * 1024 + 16 * (j + 16 * G)) =
-          (bb & 1) ? u32x4{0u, 0u, lo, hi} : u32x4{lo, hi, 0u, 0u};
+      const int gb = qg >> 2;  // block of x as one vector: row gb / nblk, block gb % nblk
+      if (c < 2) {
+        const uint32_t lo = c ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+        const uint32_t hi = c ? ((w2 >> 16) | (w3 & 0xFFFF0000u)) : ((w2 & 0xFFFFu) | (w3 << 16));
+        ctab[2 * gb + c] = u32x2{lo, hi};
+      }
       if (c == 0) {
         float sc, sc15;
         {
@@ -204,16 +201,16 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
           sc = e4m3_decode(gs.byte) * dec;
           sc15 = 1.5f * sc;
         }
-        *reinterpret_cast<f32x2*>(coef + 2 * b) =
+        *reinterpret_cast<f32x2*>(coef + 2 * gb) =
             f32x2{to_f32<DT>(from_f32<DT>(sc)), to_f32<DT>(from_f32<DT>(sc15))};
       }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  lds_barrier();  // table and coefficients written; the block loads stay in flight
+  lds_barrier();  // codes and coefficients written; the block loads stay in flight
   __builtin_amdgcn_sched_barrier(0);
 
-  // 6. the rest of the window, then this wave's scales into its stage
+  // 5. the rest of the window, then this wave's scales into its stage
 #pragma unroll
   for (int i = kQpAhead0; i < kQpAhead; ++i) {
     issue(i);
@@ -222,24 +219,34 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   uint8_t* wstage = stage + wave * 1024;
   *reinterpret_cast<u32x4*>(wstage + 16 * lane) = sv;
 
-  // 7. the blocks.  Lane (q = l / 16, j = l % 16) ends with C[4 q + r][j]:
-  //    row 16 h + 4 q + r of the tile, block bb of the step, X or Y.
+  // 6. the blocks.  Lane (q = l / 16, j = l % 16) ends with C[4 q + r][j]:
+  //    row 16 h + 4 q + r of the tile, block bb of the step, X or Y.  As the
+  //    second operand, lane (j, G = l / 16) holds 8 code bytes of block bb
+  //    in half bb % 2 when G = 2 (bb / 2) + h, zeros otherwise.
   const int j = lane & 15, q = lane >> 4;
   const int bb = j & 3, xyi = (j >> 2) & 1, h = j >> 3;
+  const bool nz = q == 2 * (bb >> 1) + h;
+  const uint32_t mlo = (nz && !(bb & 1)) ? 0xFFFFFFFFu : 0u;
+  const uint32_t mhi = (nz && (bb & 1)) ? 0xFFFFFFFFu : 0u;
   const uint32_t sel = (uint32_t)bb | ((uint32_t)(4 + bb) << 8) | 0x0C0C0000u;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int seg = 0;
-  auto flush = [&](int sg) {  // into the slot of tile tf + sg
-    if (tf + sg >= nt) return;  // only blocks past the workgroup's last tile (zeros)
-    f32x4 v = acc;
+  f32x4 acc[M];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[r] += dpp_mov<0xB1>(v[r]);   // quad_perm [1,0,3,2]
-      v[r] += dpp_mov<0x4E>(v[r]);   // quad_perm [2,3,0,1]
-      v[r] += dpp_mov<0x141>(v[r]);  // row_half_mirror: the 8 lanes of one row half
+  for (int r = 0; r < M; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int seg = 0;
+  auto flush = [&](int sg) {  // into the slots of tile tf + sg
+    if (tf + sg >= nt) return;  // only blocks past the workgroup's last tile (zeros)
+#pragma unroll
+    for (int xrow = 0; xrow < M; ++xrow) {
+      f32x4 v = acc[xrow];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] += dpp_mov<0xB1>(v[r]);   // quad_perm [1,0,3,2]
+        v[r] += dpp_mov<0x4E>(v[r]);   // quad_perm [2,3,0,1]
+        v[r] += dpp_mov<0x141>(v[r]);  // row_half_mirror: the 8 lanes of one row half
+      }
+      if ((j & 7) == 0)
+        *reinterpret_cast<f32x4*>(part + (((tf + sg) * kQpWaves + wave) * M + xrow) * 32 + 16 * h + 4 * q) = v;
     }
-    if ((j & 7) == 0)
-      *reinterpret_cast<f32x4*>(part + ((tf + sg) * kQpWaves + wave) * 32 + 16 * h + 4 * q) = v;
   };
 #pragma unroll
   for (int i = 0; i < kQpRun; ++i) {
@@ -247,90 +254,126 @@ qmv_packed_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     st = st >= steps ? st - steps : st;
     if (i > 0 && st == 0) {  // the run enters the next tile
       flush(seg);
-      acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < M; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       ++seg;
     }
-    const u32x4 bv = *reinterpret_cast<const u32x4*>(btab + st * 1024 + 16 * lane);
-    const float cf = coef[2 * (4 * st + bb) + xyi];
     const u32x4 sw = *reinterpret_cast<const u32x4*>(wstage + 128 * i + 16 * (q + 4 * h));
+    u32x2 cv8[M];
+    float cf[M];
+#pragma unroll
+    for (int xrow = 0; xrow < M; ++xrow) {
+      const int gb = xrow * nblk + 4 * st + bb;
+      cv8[xrow] = ctab[2 * gb + xyi];
+      cf[xrow] = coef[2 * gb + xyi];
+    }
     const i32x8 av = {(int)a[i].x, (int)a[i].y, (int)a[i].z, (int)a[i].w, 0, 0, 0, 0};
-    const i32x8 bw = {(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w, 0, 0, 0, 0};
-    const f32x4 cz = {0.0f, 0.0f, 0.0f, 0.0f};
-    const f32x4 cv = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw, cz, 4, 4, 0, 127, 0, 127);
-    // block i is in: issue block i + kQpAhead while the product completes
+    f32x4 cv[M];
+#pragma unroll
+    for (int xrow = 0; xrow < M; ++xrow) {
+      const i32x8 bw = {(int)(cv8[xrow].x & mlo), (int)(cv8[xrow].y & mlo), (int)(cv8[xrow].x & mhi),
+                        (int)(cv8[xrow].y & mhi), 0, 0, 0, 0};
+      const f32x4 cz = {0.0f, 0.0f, 0.0f, 0.0f};
+      cv[xrow] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw, cz, 4, 4, 0, 127, 0, 127);
+    }
+    // block i is in: issue block i + kQpAhead while the products complete
     __builtin_amdgcn_sched_barrier(0);
     if (i + kQpAhead < kQpRun) issue(i + kQpAhead);
     __builtin_amdgcn_sched_barrier(0);
     // byte bb of the scale dwords of rows 4 q + r (+ 16 h)
     const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)__builtin_amdgcn_perm(sw.y, sw.x, sel), false);
     const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)__builtin_amdgcn_perm(sw.w, sw.z, sel), false);
-    acc.x = __builtin_fmaf(cv.x * cf, s01.x, acc.x);
-    acc.y = __builtin_fmaf(cv.y * cf, s01.y, acc.y);
-    acc.z = __builtin_fmaf(cv.z * cf, s23.x, acc.z);
-    acc.w = __builtin_fmaf(cv.w * cf, s23.y, acc.w);
+#pragma unroll
+    for (int xrow = 0; xrow < M; ++xrow) {
+      acc[xrow].x = __builtin_fmaf(cv[xrow].x * cf[xrow], s01.x, acc[xrow].x);
+      acc[xrow].y = __builtin_fmaf(cv[xrow].y * cf[xrow], s01.y, acc[xrow].y);
+      acc[xrow].z = __builtin_fmaf(cv[xrow].z * cf[xrow], s23.x, acc[xrow].z);
+      acc[xrow].w = __builtin_fmaf(cv[xrow].w * cf[xrow], s23.y, acc[xrow].w);
+    }
   }
   flush(seg);
   lds_barrier();
 
-  // 8. row sums: each tile's 16 wave slots in wave order (zeros from the
+  // 7. row sums: each tile's 16 wave slots in wave order (zeros from the
   //    waves whose runs miss the tile)
-  if (tid < nt * 32) {
-    const int tl = tid >> 5, r = tid & 31;
-    const float* ps_ = part + tl * kQpWaves * 32 + r;
+  for (int e = tid; e < nt * M * 32; e += kQpThreads) {
+    const int tl = e / (M * 32), xrow = (e / 32) % M, r = e % 32;
+    const float* ps_ = part + (tl * kQpWaves * M + xrow) * 32 + r;
     float pv[kQpWaves];
 #pragma unroll
-    for (int w = 0; w < kQpWaves; ++w) pv[w] = ps_[32 * w];
+    for (int w = 0; w < kQpWaves; ++w) pv[w] = ps_[32 * M * w];
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < kQpWaves; ++w) s += pv[w];
     const int64_t row = (int64_t)(t0 + tl) * 32 + r;
-    if (row < n) reinterpret_cast<T*>(out)[row] = from_f32<DT>(s * dec_w);
+    if (row < n && xrow < m) reinterpret_cast<T*>(out)[(int64_t)xrow * n + row] = from_f32<DT>(s * dec_w);
   }
 }
 
 template <typename F>
-hipError_t allow_qp_lds(F* kernel) {
+hipError_t allow_qp_lds(F* kernel, size_t bytes) {
   static bool set[64] = {false};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   if (dev < 0 || dev >= 64 || set[dev]) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)qp_lds(kQpMaxSteps));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) set[dev] = true;
   return e;
 }
 
-template <int DT, int XR>
-hipError_t launch_qp_t(const void* x, const float* gx, const uint8_t* pc, const uint8_t* ps,
-                       const float* gw, int64_t n, int64_t k, void* out, hipStream_t s) {
+// the largest LDS any k of the supported range needs with M rows of x
+constexpr size_t qp_lds_max(int M) {
+  size_t mx = 0;
+  for (int s = kQpMinSteps; s <= kQpMaxSteps; ++s)
+    if (qp_lds(s, M) > mx) mx = qp_lds(s, M);
+  return mx;
+}
+
+template <int DT, int M, int XR>
+hipError_t launch_qp_t(const void* x, int64_t m, const float* gx, const uint8_t* pc,
+                       const uint8_t* ps, const float* gw, int64_t n, int64_t k, void* out,
+                       hipStream_t s) {
+  static_assert(qp_lds_max(M) <= 160 * 1024, "LDS");
   const int64_t steps = k / 64;
   const int64_t tiles = (n + 31) / 32;
   const int64_t per = (int64_t)kQpWaves * kQpRun / steps;  // tiles per workgroup at most
   int64_t blocks = tiles < device_cu_count() ? tiles : device_cu_count();
   if (blocks < (tiles + per - 1) / per) blocks = (tiles + per - 1) / per;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (hipError_t e = allow_qp_lds(qmv_packed_kernel<DT, XR>)) return e;
-  qmv_packed_kernel<DT, XR><<<(int)blocks, kQpThreads, qp_lds((int)steps), s>>>(
-      x, gx, pc, ps, gw, (int)n, (int)steps, (int)(tiles / blocks), (int)(tiles % blocks), out);
+  if (hipError_t e = allow_qp_lds(qmv_packed_kernel<DT, M, XR>, qp_lds_max(M))) return e;
+  qmv_packed_kernel<DT, M, XR><<<(int)blocks, kQpThreads, qp_lds((int)steps, M), s>>>(
+      x, (int)m, gx, pc, ps, gw, (int)n, (int)steps, (int)(tiles / blocks), (int)(tiles % blocks), out);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_qp_dt(const void* x, int64_t m, const float* gx, const uint8_t* pc,
+                        const uint8_t* ps, const float* gw, int64_t n, int64_t k, void* out,
+                        hipStream_t s) {
+  const bool wide = k > 4096;
+  if (m == 1)
+    return wide ? launch_qp_t<DT, 1, 2>(x, m, gx, pc, ps, gw, n, k, out, s)
+                : launch_qp_t<DT, 1, 1>(x, m, gx, pc, ps, gw, n, k, out, s);
+  if (m == 2)
+    return wide ? launch_qp_t<DT, 2, 4>(x, m, gx, pc, ps, gw, n, k, out, s)
+                : launch_qp_t<DT, 2, 2>(x, m, gx, pc, ps, gw, n, k, out, s);
+  return wide ? launch_qp_t<DT, 4, 8>(x, m, gx, pc, ps, gw, n, k, out, s)
+              : launch_qp_t<DT, 4, 4>(x, m, gx, pc, ps, gw, n, k, out, s);
 }
 
 }  // namespace
 
 bool qmv_packed_ok(int dt, int64_t m, int64_t k) {
-  return (dt == kF16 || dt == kBF16) && m == 1 && k % 64 == 0 && k >= 64 * kQpMinSteps &&
-         k <= 64 * kQpMaxSteps;
+  return (dt == kF16 || dt == kBF16) && m >= 1 && m <= kQpMaxRows && k % 64 == 0 &&
+         k >= 64 * kQpMinSteps && k <= 64 * kQpMaxSteps;
 }
 
-hipError_t launch_qmv_packed(const void* x, int dt, const float* gx, const uint8_t* pc,
+hipError_t launch_qmv_packed(const void* x, int dt, int64_t m, const float* gx, const uint8_t* pc,
                              const uint8_t* ps, const float* gw, int64_t n, int64_t k, void* out,
                              hipStream_t s) {
-  if (k <= 4096)
-    return dt == kF16 ? launch_qp_t<kF16, 1>(x, gx, pc, ps, gw, n, k, out, s)
-                      : launch_qp_t<kBF16, 1>(x, gx, pc, ps, gw, n, k, out, s);
-  return dt == kF16 ? launch_qp_t<kF16, 2>(x, gx, pc, ps, gw, n, k, out, s)
-                    : launch_qp_t<kBF16, 2>(x, gx, pc, ps, gw, n, k, out, s);
+  return dt == kF16 ? launch_qp_dt<kF16>(x, m, gx, pc, ps, gw, n, k, out, s)
+                    : launch_qp_dt<kBF16>(x, m, gx, pc, ps, gw, n, k, out, s);
 }
 
 }  // namespace nvfp4

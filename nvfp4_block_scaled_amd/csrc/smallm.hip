@@ -699,7 +699,7 @@ hipError_t launch_small_m(const void* x, int dt, bool quantize_x, const float* g
   if (!packed && qmv_rows_ok(dt, m, n, k))  // qmv's register design, one accumulator per row
     return launch_qmv_rows(x, dt, m, quantize_x, gx, wc, ws, gw, n, out, s);
   if (packed && quantize_x && qmv_packed_ok(dt, m, k))  // fp4 codes straight to the matrix cores
-    return launch_qmv_packed(x, dt, gx, wc, ws, gw, n, k, out, s);
+    return launch_qmv_packed(x, dt, m, gx, wc, ws, gw, n, k, out, s);
   return quantize_x ? launch_small_q<true>(dt, x, gx, wc, ws, packed, gw, m, n, k, out, s)
                     : launch_small_q<false>(dt, x, gx, wc, ws, packed, gw, m, n, k, out, s);
 }

@@ -1,6 +1,6 @@
-"""GPU parity of qqmm with one row of 16-bit x against the packed weight: the
-fp4 matrix-core kernel (qmv_packed.hip) that nvfp4_qqmm_packed runs for m = 1
-and 512 <= k <= 8192.
+"""GPU parity of qqmm with 1 to 4 rows of 16-bit x against the packed weight:
+the fp4 matrix-core kernel (qmv_packed.hip) that nvfp4_qqmm_packed runs for
+1 <= m <= 4 and 512 <= k <= 8192.
 
 The kernel takes exact products of the stored codes with x_hat split into
 two e2m1 vectors per block, so against the oracle (double sums, one rounding)
@@ -11,8 +11,9 @@ only its float32 summation order differs:
   a floor (0.99 for bfloat16, 0.97 for the finer float16);
 * every output buffer carries guard bands on both sides.
 Shapes: one tile and less (n = 4, 36), ragged last tiles, many tiles per
-workgroup (k = 512 with n = 64000), k from 512 to 8192 (one and two quarter
-groups of x per thread), and the decode shape n = 14336, k = 4096.
+workgroup (k = 512 with n = 64000), k from 512 to 8192 (one to eight quarter
+groups of x per thread), m = 1, 2, 3 (padded to four rows inside) and 4, and
+the decode shape n = 14336, k = 4096.
 """
 import numpy as np
 import pytest
@@ -37,7 +38,7 @@ def _cuda():
 
 
 def _run(x, packed, gx, gw, n, dtype):
-    out = guarded((1, n), dtype)
+    out = guarded((x.shape[0], n), dtype)
     nv.nvfp4_qqmm_packed(x, packed, gx, gw, out=out.t)
     torch.cuda.synchronize()
     out.check("qmv packed out")
@@ -45,37 +46,40 @@ def _run(x, packed, gx, gw, n, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("k", [512, 2048, 4096, 8192])
+@pytest.mark.parametrize("m,k", [(1, 512), (1, 2048), (1, 4096), (1, 8192), (2, 4096), (3, 512),
+                                 (4, 4096), (4, 8192)])
 @pytest.mark.parametrize("gx,gw", [(2688.0, 336.0), (None, None)])
-def test_qmv_packed_grid_bit_exact(dtype, k, gx, gw):
-    """Exact-grid x [1, k] and w [300, k] (a partial last tile): every partial
+def test_qmv_packed_grid_bit_exact(dtype, m, k, gx, gw):
+    """Exact-grid x [m, k] and w [300, k] (a partial last tile): every partial
     sum is exact, so the output is the float64 product rounded once."""
-    say(f"qmv packed grid k={k} {dtype} gx={gx}")
-    x = W.grid_tensor(1, k, seed=500 + k)
+    say(f"qmv packed grid m={m} k={k} {dtype} gx={gx}")
+    x = W.grid_tensor(m, k, seed=500 + k + m)
     w = W.grid_tensor(300, k, seed=501 + k)
     wc, ws = nv.nvfp4_quantize(w.to(dtype).cuda(), scalar(gw))
     packed = nv.nvfp4_mfma_pack(wc, ws)
     got = _run(x.to(dtype).cuda(), packed, scalar(gx), scalar(gw), 300, dtype)
     y = np.asarray(host(x.to(dtype)), np.float64) @ np.asarray(host(w.to(dtype)), np.float64).T
-    ref = np.array([[O.round_to(float(v), oracle_dtype(dtype)) for v in y[0]]], np.float32)
+    ref = np.array([[O.round_to(float(v), oracle_dtype(dtype)) for v in row] for row in y], np.float32)
     assert_values_equal(got, ref, "qmv packed grid")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("n,k", [(4, 512), (36, 512), (64000, 512), (300, 1024), (1028, 2048),
-                                 (8200, 4096), (100, 6144), (2052, 8192)])
-def test_qmv_packed_general(dtype, n, k):
+@pytest.mark.parametrize("m,n,k", [(1, 4, 512), (1, 36, 512), (1, 64000, 512), (1, 300, 1024),
+                                   (1, 1028, 2048), (1, 8200, 4096), (1, 100, 6144), (1, 2052, 8192),
+                                   (2, 36, 512), (2, 3000, 4096), (2, 520, 8192), (3, 1028, 2048),
+                                   (3, 20000, 512), (4, 4, 4096), (4, 14336, 4096), (4, 300, 8192)])
+def test_qmv_packed_general(dtype, m, n, k):
     """General data against the oracle on every output."""
-    say(f"qmv packed general n={n} k={k} {dtype}")
+    say(f"qmv packed general m={m} n={n} k={k} {dtype}")
     od = oracle_dtype(dtype)
-    x = W.normal((1, k), 1.0, 600 + n + k, od)
+    x = W.normal((m, k), 1.0, 600 + n + k + m, od)
     w = W.normal((n, k), 0.02, 601 + n, od)
     gxh, gwh = O.tensor_amax(host(x)), O.tensor_amax(host(w))
     oc, os_ = O.quantize(host(w), gwh)
     packed = nv.nvfp4_mfma_pack(dev(oc), dev(os_))
     got = _run(x.cuda(), packed, scalar(gxh), scalar(gwh), n, dtype)
     ref = O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od)
-    assert_close(got, ref, what=f"qmv packed n={n} k={k}")
+    assert_close(got, ref, what=f"qmv packed m={m} n={n} k={k}")
     frac = ulp_fraction(got, ref, od)
     say(f"  within 1 ulp: {frac:.4f}")
     assert frac >= ULP_FLOOR[dtype]
@@ -117,3 +121,38 @@ def test_qmv_packed_decode_14336x4096_every_output():
     say(f"  within 1 bf16 ulp: {frac:.4f}")
     assert frac >= ULP_FLOOR[torch.bfloat16]
     assert_close(got, rm.reshape(1, -1), tol=2e-3, what="packed vs row-major qmv")
+
+
+@pytest.mark.parametrize("k", [2048, 4096])
+@pytest.mark.parametrize("seed", [3630, 3677])
+def test_in_kernel_round_trip_float16_is_the_pages_order(k, seed):
+    """The x round trip done inside the contraction kernels rounds like the
+    pages' (float32 products, then float16) for float16 x.  With these seeds
+    some block's float32 x_hat lands on a float16 midpoint, where a single
+    rounding straight to float16 (a fused multiply-convert) picks the other
+    neighbour for every element with that block scale and code.  A one-hot
+    weight (6 at [i, i], g_w = 2688) makes output i equal 6 * x_hat_i exactly,
+    so each kernel's x_hat is read back and compared with the oracle's bit for
+    bit: qmv (row-major), the packed fp4 kernel (m = 1, 2), the small-batch
+    kernels (row-major m = 2, packed m = 5)."""
+    say(f"in-kernel round trip float16 k={k} seed={seed}")
+    x1 = W.normal((1, k), 1.0, seed, "f16")
+    w = torch.zeros(k, k, dtype=torch.float16)
+    w[torch.arange(k), torch.arange(k)] = 6.0
+    gw = scalar(2688.0)
+    wc, ws = nv.nvfp4_quantize(w.cuda(), gw)
+    packed = nv.nvfp4_mfma_pack(wc, ws)
+    gxh = O.tensor_amax(host(x1))
+    gx = scalar(gxh)
+    xhat = O.quant_dequant(host(x1), gxh, dtype="f16").astype(np.float64)
+    want1 = (6.0 * xhat).astype(np.float16).astype(np.float32)
+    x2 = torch.cat([x1, x1]).contiguous()
+    x5 = torch.cat([x1] * 5).contiguous()
+    got = {"qmv": (nv.nvfp4_qmv(x1.cuda(), wc, ws, gx, gw), 1),
+           "qqmm_packed m=1": (nv.nvfp4_qqmm_packed(x1.cuda(), packed, gx, gw), 1),
+           "qqmm_packed m=2": (nv.nvfp4_qqmm_packed(x2.cuda(), packed, gx, gw), 2),
+           "qqmm m=2": (nv.nvfp4_qqmm(x2.cuda(), wc, ws, gx, gw), 2),
+           "qqmm_packed m=5": (nv.nvfp4_qqmm_packed(x5.cuda(), packed, gx, gw), 5)}
+    torch.cuda.synchronize()
+    for what, (y, m) in got.items():
+        assert_values_equal(host(y).reshape(m, k), np.repeat(want1, m, 0), f"{what} x_hat")
