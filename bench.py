@@ -61,8 +61,9 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "650c1c25433e7e46", 367338375),
-    "qmv": ("qmv.hip", "c90cac9378cc713f", 33185306),
+    "gemm": ("gemm.hip", "bc9e610dac8a61d3", 367323260),
+    "qmv": ("qmv.hip", "e2db1d090ce51c11", 33205684),
+    "qmv_packed": ("qmv_packed.hip", "e091a454e1cf89e3", 33216896),
 }
 
 
@@ -802,6 +803,7 @@ def main():
                                          "us_per_launch": round(v["ms_packed"] * 1e3, 3),
                                          "us_per_launch_stats": stats_ms(v["st_packed"], 1e3, 3),
                                          "warm_cache_GBps": round(v["gbs_packed_warm"], 1),
+                                         "traffic": measured_traffic("qmv_packed"),
                                          "kernel": "qmv_packed_kernel<bf16> (nvfp4_qqmm_packed, m = 1)"},
                        "workload": "qmv decode: x bf16 [1,4096] @ NVFP4 w [14336,4096]^T"}
         if ceil is not None:
