@@ -373,7 +373,13 @@ nvfp4_status nvfp4_mfma_pack(const uint8_t* codes, const uint8_t* scales, int64_
  * of nvfp4_qqmm) the results equal the row-major calls' bit for bit; with
  * 1 <= m <= 16 the packed small-batch kernel sums in another order than the
  * row-major one (32-row instead of 16-row tiles), so the two agree to
- * rounding, not bitwise.
+ * rounding, not bitwise.  nvfp4_qqmm_packed with 1 <= m <= 4 rows of
+ * bfloat16 x and 512 <= k <= 8192 runs the fp4 matrix-core kernel, which
+ * feeds the stored weight codes to the matrix cores and x_hat as two e2m1
+ * vectors per block times per-block coefficients; that split is x_hat itself
+ * while x_hat stays out of bfloat16's subnormal range, i.e. for g_x >= 2688 *
+ * 2^-116 (about 3.2e-32) or without global scales.  Below that bound x_hat
+ * elements that are bfloat16 subnormals may differ by one subnormal step.
  */
 nvfp4_status nvfp4_qqmm_packed(const void* x, nvfp4_dtype dt, const float* global_scale_x,
                                const uint8_t* packed_codes, const uint8_t* packed_scales,

@@ -37,7 +37,7 @@ hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, co
                            const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t n,
                            void* out, hipStream_t s);
 
-// qmv_packed.hip: qqmm with 1 <= m <= 4 rows of 16-bit x against the packed
+// qmv_packed.hip: qqmm with 1 <= m <= 4 rows of bfloat16 x against the packed
 // weight, 512 <= k <= 8192 (k % 64 == 0), on the fp4 matrix cores
 bool qmv_packed_ok(int dt, int64_t m, int64_t k);
 hipError_t launch_qmv_packed(const void* x, int dt, int64_t m, const float* gx, const uint8_t* pc,

@@ -1,4 +1,4 @@
-// qmv_packed.hip -- qqmm with 1 to 4 rows of 16-bit x against the packed
+// qmv_packed.hip -- qqmm with 1 to 4 rows of bfloat16 x against the packed
 // weight, on the matrix cores with the weight's fp4 codes as they are stored:
 //   out[m, n] = T( sum_k x_hat[m, k] * w[n, k] ),  x_hat the NVFP4 round trip
 //   of x under g_x ("mlx 0.30.7.2 -> 0.30.7.6" diff page 8, qqmm; page 7,
@@ -19,8 +19,13 @@
 //     sc_b = e4m3(s_b) * g_x/2688 (float32) and d an element's decoded code,
 //     x_hat = T(d * sc_b) = X * T(sc_b) + Y * T(1.5 * sc_b), where X = d for
 //     |d| in {0, 0.5, 1, 2, 4} (else 0) and Y = d / 1.5 for |d| in {1.5, 3, 6}
-//     (else 0): a power of two passes through the rounding to T unchanged
-//     (outside T's subnormal range, which float16 x can reach);
+//     (else 0): a power of two passes through the rounding to T unchanged as
+//     long as the results stay out of T's subnormal range.  For bfloat16
+//     that holds whenever g_x >= 2688 * 2^-116 (about 3.2e-32: the smallest
+//     nonzero sc_b is 2^-9 g_x/2688, and half of it must be a normal bfloat16)
+//     or without a global scale (sc_b >= 2^-9); float16 x reaches its
+//     subnormals with ordinary data (a block of amax below about 4e-4), so
+//     float16 x takes the kernels that round every element itself;
 //   * the second operand's 16 columns are j = 8 h + 4 xy + bb (row half h,
 //     X or Y, block bb of the step).  Column j holds the X (xy = 0) or Y codes
 //     of block bb, and zeros at the other blocks and in the k slices where
@@ -364,16 +369,18 @@ hipError_t launch_qp_dt(const void* x, int64_t m, const float* gx, const uint8_t
 
 }  // namespace
 
+// bfloat16 x only: the split of x_hat above is exact for it (see the top of
+// the file); float16 x would reach T's subnormals with ordinary data.
 bool qmv_packed_ok(int dt, int64_t m, int64_t k) {
-  return (dt == kF16 || dt == kBF16) && m >= 1 && m <= kQpMaxRows && k % 64 == 0 &&
-         k >= 64 * kQpMinSteps && k <= 64 * kQpMaxSteps;
+  return dt == kBF16 && m >= 1 && m <= kQpMaxRows && k % 64 == 0 && k >= 64 * kQpMinSteps &&
+         k <= 64 * kQpMaxSteps;
 }
 
 hipError_t launch_qmv_packed(const void* x, int dt, int64_t m, const float* gx, const uint8_t* pc,
                              const uint8_t* ps, const float* gw, int64_t n, int64_t k, void* out,
                              hipStream_t s) {
-  return dt == kF16 ? launch_qp_dt<kF16>(x, m, gx, pc, ps, gw, n, k, out, s)
-                    : launch_qp_dt<kBF16>(x, m, gx, pc, ps, gw, n, k, out, s);
+  if (dt != kBF16) return hipErrorInvalidValue;
+  return launch_qp_dt<kBF16>(x, m, gx, pc, ps, gw, n, k, out, s);
 }
 
 }  // namespace nvfp4

@@ -23,10 +23,10 @@ pytestmark = pytest.mark.gpu
 MFMA_FRO_GUARD = 5e-3
 
 
-def _fp4_m1(m, k):
-    """nvfp4_qqmm_packed with 1 to 4 rows of x and 512 <= k <= 8192 runs the
-    fp4 matrix-core kernel, which sums in its own order."""
-    return 1 <= m <= 4 and k % 64 == 0 and 512 <= k <= 8192
+def _fp4_m1(m, k, dtype):
+    """nvfp4_qqmm_packed with 1 to 4 rows of bfloat16 x and 512 <= k <= 8192
+    runs the fp4 matrix-core kernel, which sums in its own order."""
+    return dtype == torch.bfloat16 and 1 <= m <= 4 and k % 64 == 0 and 512 <= k <= 8192
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -112,7 +112,7 @@ def test_small_qqmm_and_qmm(dtype, m, n, k):
         fro, _ = assert_close(host(yp), O.qqmm(host(x), oc, os_, gxh, gwh, dtype=od),
                               what="small qqmm packed")
         assert fro <= MFMA_FRO_GUARD
-        if not _fp4_m1(m, k):  # m <= 4 runs the fp4 kernel (own summation order)
+        if not _fp4_m1(m, k, dtype):  # m <= 4 runs the fp4 kernel (own summation order)
             assert torch.equal(yp.view(torch.int16), ypm_xhat.view(torch.int16)), \
                 "packed: in-kernel round trip differs from quant_dequant"
         fro, _ = assert_close(host(ypm), _qmm_ref(host(x), oc, os_, gwh, od), what="small qmm packed")
@@ -229,5 +229,5 @@ def test_k4096_general(dtype, m, n):
         assert fro <= MFMA_FRO_GUARD
         fro, _ = assert_close(host(yp_qmm), qmm_ref, what="k=4096 qmm packed")
         assert fro <= MFMA_FRO_GUARD
-        if not _fp4_m1(m, 4096):  # m <= 4: the fp4 kernel, another summation order
+        if not _fp4_m1(m, 4096, dtype):  # m <= 4: the fp4 kernel, another summation order
             assert torch.equal(yp_qqmm.view(torch.int16), yp_xhat.view(torch.int16))
