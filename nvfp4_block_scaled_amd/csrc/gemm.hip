@@ -329,21 +329,26 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     group 2 h + u / 2 -- so a lane's codes for the whole k-step are 16
 //     consecutive bytes (groups 2h and 2h + 1), dword u feeding sub-step u; A
 //     is read from LDS in the same k order;
-//   * A goes through three LDS stages (three separate LDS arrays, so that the
-//     compiler can tell a stage being filled from the ones being read): in the
-//     middle of step i, right after the step's one barrier, every wave loads
-//     its quarter of A(i + 2) from global memory straight into LDS
-//     (buffer_load ... lds: no registers, no LDS store instructions); the
-//     barrier of step i + 1 first waits for that load.  The barrier carries no
-//     memory fence, so the weight loads stay in flight across it.  A
+//   * A goes through four LDS stages (four separate LDS arrays, so that the
+//     compiler can tell a stage being filled from the ones being read): from
+//     the middle of step i, right after the step's one barrier, every wave
+//     loads its quarter of A(i + 3) from global memory straight into LDS
+//     (buffer_load ... lds: no registers, no LDS store instructions), one
+//     1 KB load every few MFMA pairs over the second half of the step; the
+//     barrier of step i + 2 first waits for those loads.  Issued all at
+//     once, the loads of every CU reach the L2 in one burst per step; spread
+//     out, the same GEMM measured 4 % faster (2048 x 14336 x 4096: 196.9 ->
+//     188.8 us on one machine; a fourth stage alone changed nothing).  The
+//     barrier carries no memory fence, so the weight loads stay in flight
+//     across it.  A
 //     fragments are read three MFMA pairs ahead, running into the first
 //     fragments of step i + 1, so a step starts without waiting for LDS;
 //   * fragment pair q of a step (sub-step q / 8, row tile q % 8) carries one
 //     dword of the decode of step i + 1's weights (two codes by
 //     v_cvt_scalef32_pk_f32_fp4, two multiplies by e4m3(s) * g/2688, one
 //     conversion to two 16-bit values; every eighth pair also decodes a scale);
-//   * the k loop is unrolled by six steps (three A stages x two weight register
-//     sets), so every stage and register set is fixed in the code;
+//   * the k loop is unrolled by four steps (four A stages, two weight
+//     register sets), so every stage and register set is fixed in the code;
 //   * workgroups are mapped so that each of the 8 XCDs (round-robin dispatch)
 //     works on its own contiguous set of weight column panels;
 //   * with 128-row tiles (used up to 128 rows) every number above halves
@@ -353,6 +358,7 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     allocator keeps every accumulator in place (left to itself it splits
 //     them between the two files and moves them around every k-step).
 constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
+constexpr int kAStages = 4;                // LDS stages of A
 constexpr int kBLoadsPerStep = 4;          // weight loads issued per k-step and wave
 constexpr int kPackCodeBlock = 1024;       // packed codes per 32-column tile and k-step
 constexpr int kPackScaleBlock = 128;       // packed scales per 32-column tile and k-step
@@ -375,13 +381,18 @@ __device__ __forceinline__ void mfma32_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The main loop's barrier: this wave's global-to-LDS load of the A stage
-// needed next has landed -- it was issued a step ago and only the
-// kBLoadsPerStep weight loads of this step are younger -- then meet the other
-// waves.
+// The main loop's barrier in the middle of step i: this wave's global-to-LDS
+// loads of A(i + 1) have landed -- issued in step i - 2, they are older than
+// the weight loads of steps i + 1 and i + 2 (kBLoadsPerStep each) and the RT
+// loads of A(i + 2), which may stay in flight -- then meet the other waves.
+template <int RT>
 __device__ __forceinline__ void a_stage_barrier() {
-  static_assert(kBLoadsPerStep == 4, "the wait count below is the number of weight loads per step");
-  asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+  static_assert(kBLoadsPerStep == 4, "the wait counts below count 4 weight loads per step");
+  static_assert(RT == 8 || RT == 4, "the wait counts below count RT loads of A per step");
+  if constexpr (RT == 8)
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
 }
 
 // Raw weights of one k-step for one lane: for each of its 2 column tiles, the
@@ -413,8 +424,9 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[kStage];
   __shared__ __attribute__((aligned(1024))) uint8_t sa2[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa3[kStage];
   __shared__ int out_rows[TM];
-  uint8_t* const stage[3] = {sa0, sa1, sa2};
+  uint8_t* const stage[kAStages] = {sa0, sa1, sa2, sa3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -528,13 +540,16 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   const int c_step = PACKED ? kPackCodeBlock : BK / 2;    // code bytes per k-step
   const int s_step = PACKED ? kPackScaleBlock : BK / 16;  // scale bytes per k-step
 
-  // this wave's quarter of A(kt) into stage si, straight from global memory
-  auto load_a = [&](int kt, int si) {
+  // load j (1 KB) of this wave's quarter of A(kt) into stage si, straight
+  // from global memory
+  auto load_a_one = [&](int kt, int si, int j) {
     const int so = kt * BK * (int)sizeof(T);
     uint8_t* dst = stage[si] + wave * (kStage / 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(dst + j * 1024), 16, a_off[j], so, 0, 0);
+  };
+  auto load_a = [&](int kt, int si) {
 #pragma unroll
-    for (int j = 0; j < RT; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(dst + j * 1024), 16, a_off[j], so, 0, 0);
+    for (int j = 0; j < RT; ++j) load_a_one(kt, si, j);
   };
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
@@ -575,16 +590,19 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   BRaw raw[2];        // raw weights of even / odd k-steps
   V8 ar[4];           // A fragment ring: fragment q of a step in ar[q % 4]
 
-  // Step kt, at position P of the six-step cycle (kt = P mod 6): MFMAs on
-  // A(kt) (stage P % 3) and the fragments bf[P % 2]; loads the raw weights of
+  // Step kt, at position P of the four-step cycle (kt = P mod 4): MFMAs on
+  // A(kt) (stage P) and the fragments bf[P % 2]; loads the raw weights of
   // kt + 2 into raw[P % 2] (which held those of kt) and decodes raw[1 - P % 2]
-  // (kt + 1) into bf[1 - P % 2]; in its middle, after the barrier, loads
-  // A(kt + 2) into stage (P + 2) % 3.  The body is straight-line: past the end
-  // of k the loads re-read the last k-step and the extra work is discarded, so
-  // every wait the compiler places counts exactly the loads that are in flight.
+  // (kt + 1) into bf[1 - P % 2]; in its middle, after the barrier (every wave
+  // is past step kt - 1), starts loading A(kt + 3) into stage (P + 3) % 4,
+  // which held A(kt - 1): one load every NQ / (2 RT) fragment pairs.  The body
+  // is straight-line: past the end of k the loads re-read the last k-step and
+  // the extra work is discarded, so every wait the compiler places counts
+  // exactly the loads that are in flight.
   auto step = [&](auto pos, int kt) {
     constexpr int P = decltype(pos)::value;
-    constexpr int cur = P % 3, nxt = (P + 1) % 3, nw = (P + 2) % 3, rs = P % 2;
+    constexpr int cur = P, nxt = (P + 1) % kAStages, nw = (P + 3) % kAStages, rs = P % 2;
+    constexpr int kASpread = NQ / 2 / RT;  // fragment pairs between two A loads
     load_b(min(kt + 2, KT - 1), raw[rs]);
     const uint8_t* la = stage[cur];
     const uint8_t* ln = stage[nxt];
@@ -621,19 +639,19 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
         const int d = q * DPQ + j;
         bf[1 - rs][d >> 4][(d >> 2) & 3][d & 3] = part[j];
       }
-      if (q == NQ / 2 - 1) {
-        a_stage_barrier();
-        load_a(min(kt + 2, KT - 1), nw);
-      }
+      if (q == NQ / 2 - 1) a_stage_barrier<RT>();
+      if (q >= NQ / 2 - 1 && (q - (NQ / 2 - 1)) % kASpread == 0 && (q - (NQ / 2 - 1)) / kASpread < RT)
+        load_a_one(min(kt + 3, KT - 1), nw, (q - (NQ / 2 - 1)) / kASpread);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---------------------------------------------------------------- prologue
-  // A(0), A(1) into stages 0 and 1, raw weights of steps 0 and 1, step 0's
-  // fragments decoded, the first three A fragments read.
+  // A(0), A(1), A(2) into stages 0 to 2, raw weights of steps 0 and 1, step
+  // 0's fragments decoded, the first three A fragments read.
   load_a(0, 0);
   load_a(min(1, KT - 1), 1);
+  load_a(min(2, KT - 1), 2);
   load_b(0, raw[0]);
   load_b(min(1, KT - 1), raw[1]);
 #pragma unroll
@@ -662,22 +680,16 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   using P1 = std::integral_constant<int, 1>;
   using P2 = std::integral_constant<int, 2>;
   using P3 = std::integral_constant<int, 3>;
-  using P4 = std::integral_constant<int, 4>;
-  using P5 = std::integral_constant<int, 5>;
   int kt = 0;
-  for (; kt + 6 <= KT; kt += 6) {
+  for (; kt + 4 <= KT; kt += 4) {
     step(P0{}, kt);
     step(P1{}, kt + 1);
     step(P2{}, kt + 2);
     step(P3{}, kt + 3);
-    step(P4{}, kt + 4);
-    step(P5{}, kt + 5);
   }
   if (kt < KT) step(P0{}, kt);
   if (kt + 1 < KT) step(P1{}, kt + 1);
   if (kt + 2 < KT) step(P2{}, kt + 2);
-  if (kt + 3 < KT) step(P3{}, kt + 3);
-  if (kt + 4 < KT) step(P4{}, kt + 4);
   mfma32_fence();
 
   // ---------------------------------------------------------------- epilogue
