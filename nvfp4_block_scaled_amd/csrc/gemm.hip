@@ -551,11 +551,17 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
 #pragma unroll
     for (int j = 0; j < RT; ++j) load_a_one(kt, si, j);
   };
+  auto load_b_code = [&](int kt, BRaw& b, int t) {
+    b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * c_step, 0));
+  };
+  auto load_b_scale = [&](int kt, BRaw& b, int t) {
+    b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * s_step, 0);
+  };
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * c_step, 0));
-      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * s_step, 0);
+      load_b_code(kt, b, t);
+      load_b_scale(kt, b, t);
     }
   };
   // effective scale of group 2 fh + gi (gi = 0, 1) of column tile t
@@ -591,11 +597,14 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   V8 ar[4];           // A fragment ring: fragment q of a step in ar[q % 4]
 
   // Step kt, at position P of the four-step cycle (kt = P mod 4): MFMAs on
-  // A(kt) (stage P) and the fragments bf[P % 2]; loads the raw weights of
-  // kt + 2 into raw[P % 2] (which held those of kt) and decodes raw[1 - P % 2]
-  // (kt + 1) into bf[1 - P % 2]; in its middle, after the barrier (every wave
-  // is past step kt - 1), starts loading A(kt + 3) into stage (P + 3) % 4,
-  // which held A(kt - 1): one load every NQ / (2 RT) fragment pairs.  The body
+  // A(kt) (stage P) and the fragments bf[P % 2]; over its first half loads
+  // the raw weights of kt + 2 into raw[P % 2] (which held those of kt), one
+  // load every NQ / 8 fragment pairs, and decodes raw[1 - P % 2] (kt + 1)
+  // into bf[1 - P % 2]; in its middle, after the barrier (every wave is past
+  // step kt - 1), starts loading A(kt + 3) into stage (P + 3) % 4, which held
+  // A(kt - 1): one load every NQ / (2 RT) fragment pairs.  (The four weight
+  // loads spread over the first half instead of issued together measured 3 %
+  // faster on the 2048 x 14336 x 4096 product.)  The body
   // is straight-line: past the end of k the loads re-read the last k-step and
   // the extra work is discarded, so every wait the compiler places counts
   // exactly the loads that are in flight.
@@ -603,7 +612,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
     constexpr int P = decltype(pos)::value;
     constexpr int cur = P, nxt = (P + 1) % kAStages, nw = (P + 3) % kAStages, rs = P % 2;
     constexpr int kASpread = NQ / 2 / RT;  // fragment pairs between two A loads
-    load_b(min(kt + 2, KT - 1), raw[rs]);
+    const int kb = min(kt + 2, KT - 1);
     const uint8_t* la = stage[cur];
     const uint8_t* ln = stage[nxt];
     const BRaw& rnext = raw[1 - rs];
@@ -639,6 +648,10 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
         const int d = q * DPQ + j;
         bf[1 - rs][d >> 4][(d >> 2) & 3][d & 3] = part[j];
       }
+      if (q == 0) load_b_code(kb, raw[rs], 0);
+      if (q == NQ / 8) load_b_scale(kb, raw[rs], 0);
+      if (q == NQ / 4) load_b_code(kb, raw[rs], 1);
+      if (q == 3 * NQ / 8) load_b_scale(kb, raw[rs], 1);
       if (q == NQ / 2 - 1) a_stage_barrier<RT>();
       if (q >= NQ / 2 - 1 && (q - (NQ / 2 - 1)) % kASpread == 0 && (q - (NQ / 2 - 1)) / kASpread < RT)
         load_a_one(min(kt + 3, KT - 1), nw, (q - (NQ / 2 - 1)) / kASpread);
