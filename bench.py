@@ -61,9 +61,9 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "bc9e610dac8a61d3", 367323260),
-    "qmv": ("qmv.hip", "e2db1d090ce51c11", 33205684),
-    "qmv_packed": ("qmv_packed.hip", "e091a454e1cf89e3", 33216896),
+    "gemm": ("gemm.hip", "4f43cb0dc4b00d31", 366611133),
+    "qmv": ("qmv.hip", "a8a360731669253c", 33205669),
+    "qmv_packed": ("qmv_packed.hip", "3cf35278ebaa424f", 33231216),
 }
 
 
