@@ -52,15 +52,16 @@
 // Generic path (any k % 16 == 0 up to 32768): one group per lane per sweep,
 // x_hat in LDS as float32 padded to 17 words per group (conflict-free reads).
 //
-// A few rows (qmv_rows_kernel, 1 <= m <= 2 rows of 16-bit x, k = 4096): the
-// register path with one accumulator per x row.  The weight stream is the
-// same; each decoded code pair feeds m v_dot2 products, so the VALU work per
-// weight element grows as 0.5 + 0.5 m instructions while the bytes stay put
-// (past two rows it outgrows the stream, and the matrix-core kernels of
-// smallm.hip do better).
-// x_hat is x's round trip under g_x (qqmm) or x as given (quantized_matmul).
-// With m = 1 and the round trip of x done beforehand the sums are qmv's,
-// operation for operation.
+// A few rows (1 <= m <= 2 rows of 16-bit x, k = 4096; qmv_stream_kernel with
+// MR = 2): the streaming path with one accumulator per x row.  The weight
+// stream is the same; each decoded code pair feeds one v_dot2 per row, so the
+// VALU work per weight element grows as 0.5 + 0.5 m instructions while the
+// bytes stay put (past two rows it outgrows the stream, and the matrix-core
+// kernels of smallm.hip do better).  Measured at n = 14336 (cold weights):
+// qqmm with two rows 9.5 us, against 12.1 us for the register design that
+// issued all of a wave's rows up front.  x_hat is x's round trip under g_x
+// (qqmm) or x as given (quantized_matmul); row j's sums are those of qmv on
+// x_hat row j, operation for operation.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -76,7 +77,6 @@ constexpr int kThreadsQ = kWaves * 64;
 // at n = 14336 (cold weights): 1 row 9.0 us, 2 rows 8.3 us, 4 rows 8.45 us,
 // 7 rows (one workgroup per CU) 8.9-9.0 us.
 constexpr int kMaxRows = 2;
-constexpr int kRowsMaxR = 8;  // rows per wave of qmv_rows_kernel
 
 // Partial dot product of one group of 16 (codes in dwords c0, c1) with
 // x_hat (16-bit pairs xp[0..7], or floats xf[0..15]).
@@ -272,14 +272,57 @@ struct StreamRow {
   uint32_t scale;
 };
 
-template <int DT>
+// exact e2m1 pair decode and 16-bit dot product of one x type
+template <int DT> struct Dot2;
+template <> struct Dot2<kBF16> {
+  using V = bf16x2;
+  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_bf16<B>(w); }
+  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
+  }
+};
+template <> struct Dot2<kF16> {
+  using V = f16x2;
+  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_f16<B>(w); }
+  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2, b), c, false);
+  }
+};
+
+// Two e2m1 codes times the 16-bit pairs at xp of MR rows of x_hat (each
+// decoded pair feeds one v_dot2 per row; row j's sum is group_dot16's).
+template <int DT, int MR>
+__device__ __forceinline__ void group_dot16_rows(uint32_t c0, uint32_t c1, const uint32_t (*xp)[2][16],
+                                                 int hh, int off, float (&p)[MR]) {
+  using D = Dot2<DT>;
+#pragma unroll
+  for (int j = 0; j < MR; ++j) p[j] = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint32_t w = b < 4 ? c0 : c1;
+    typename D::V d;
+    switch (b & 3) {
+      case 0: d = D::template dec<0>(w); break;
+      case 1: d = D::template dec<1>(w); break;
+      case 2: d = D::template dec<2>(w); break;
+      default: d = D::template dec<3>(w); break;
+    }
+#pragma unroll
+    for (int j = 0; j < MR; ++j) p[j] = D::dot(d, xp[j][hh][off + b], p[j]);
+  }
+}
+
+// MR rows of x (MR = 1: qmv; MR = 2: two-row qqmm / quantized_matmul, rows
+// past m read zeros and are not stored); QX: x goes through the round trip
+// (else it is taken as given)
+template <int DT, int MR, bool QX>
 __global__ void __launch_bounds__(kStreamThreads)
-qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
+qmv_stream_kernel(const void* __restrict__ x, int m, const float* __restrict__ gx,
                   const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                   const float* __restrict__ gw, int n, int qw, int remw, void* __restrict__ out) {
   constexpr int K = 4096;
   using T = typename Elem<DT>::T;
-  __shared__ __attribute__((aligned(16))) uint32_t xs[K / 2];  // x_hat, 16-bit
+  __shared__ __attribute__((aligned(16))) uint32_t xs[MR * K / 2];  // x_hat, 16-bit
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -297,8 +340,12 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   //    start), and x: quarter group tid, elements 4 tid .. 4 tid + 3
   const float gxs = gx ? *gx : kE4M3Max * kE2M1Max;
   const float gws = gw ? *gw : kE4M3Max * kE2M1Max;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, K * sizeof(T));
-  const u32x2 xr = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)tid * 8u, 0, 0));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)m * K * sizeof(T));
+  u32x2 xr[MR];
+#pragma unroll
+  for (int j = 0; j < MR; ++j)
+    xr[j] = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)(j * K / 4 + tid) * 8u, 0, 0));
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");  // the workgroup's x and scale loads go first
   __builtin_amdgcn_sched_barrier(0);
@@ -332,10 +379,16 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     dec_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 2));
   }
 
-  // 4. x_hat of this quarter group (lanes 4j .. 4j + 3 hold one group of 16)
-  {
+  // 4. x_hat of this quarter group of each row (lanes 4j .. 4j + 3 hold one
+  //    group of 16), or x as given
+#pragma unroll
+  for (int j = 0; j < MR; ++j) {
+    if constexpr (!QX) {
+      reinterpret_cast<u32x2*>(xs)[j * K / 4 + tid] = xr[j];
+      continue;
+    }
     float v[8];
-    unpack8<DT>(u32x4{xr.x, xr.y, 0u, 0u}, v);
+    unpack8<DT>(u32x4{xr[j].x, xr[j].y, 0u, 0u}, v);
     float a = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
                     fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
     a = fmaxf(a, dpp_mov<0xB1>(a));  // quad_perm [1,0,3,2]
@@ -361,23 +414,25 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
 #pragma clang fp contract(off)
       o[0] = d0.x * sc; o[1] = d0.y * sc; o[2] = d1.x * sc; o[3] = d1.y * sc;
     }
-    reinterpret_cast<u32x2*>(xs)[tid] = u32x2{pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
+    reinterpret_cast<u32x2*>(xs)[j * K / 4 + tid] = u32x2{pack2<DT>(o[0], o[1]), pack2<DT>(o[2], o[3])};
   }
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();  // x_hat written; row 0's loads stay in flight
   __builtin_amdgcn_sched_barrier(0);
 
   // 5. this lane's x_hat pieces: elements 32 lane .. + 31 and 2048 + 32 lane ..
-  uint32_t xp[2][16];
+  uint32_t xp[MR][2][16];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
+  for (int j = 0; j < MR; ++j)
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const u32x4 t = reinterpret_cast<const u32x4*>(xs)[(hh * 2048 + 32 * lane) / 8 + qd];
-      xp[hh][4 * qd] = t.x; xp[hh][4 * qd + 1] = t.y;
-      xp[hh][4 * qd + 2] = t.z; xp[hh][4 * qd + 3] = t.w;
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const u32x4 t = reinterpret_cast<const u32x4*>(xs)[(j * K + hh * 2048 + 32 * lane) / 8 + qd];
+        xp[j][hh][4 * qd] = t.x; xp[j][hh][4 * qd + 1] = t.y;
+        xp[j][hh][4 * qd + 2] = t.z; xp[j][hh][4 * qd + 3] = t.w;
+      }
     }
-  }
 
   __builtin_amdgcn_sched_barrier(0);
   // the rest of the window, one row after the other (the wait counter retires
@@ -394,7 +449,9 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   // 6. rows: once row i is in (its scale dword, the row's last load, is
   //    read), issue row i + kStreamAhead, then compute row i
   const int sshift = 8 * ((2 * lane) & 3);
-  float mine = 0.0f;
+  float mine[MR];
+#pragma unroll
+  for (int j = 0; j < MR; ++j) mine[j] = 0.0f;
 #pragma unroll
   for (int i = 0; i < kStreamRows; ++i) {
     // the two scale bytes of piece hh sit in lane 32 hh + lane / 2
@@ -405,7 +462,9 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
     __builtin_amdgcn_sched_barrier(0);
     if (i + kStreamAhead < kStreamRows) issue(i + kStreamAhead);
     __builtin_amdgcn_sched_barrier(0);
-    float acc = 0.0f;
+    float acc[MR];
+#pragma unroll
+    for (int j = 0; j < MR; ++j) acc[j] = 0.0f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const uint32_t sw = swv[hh];
@@ -417,15 +476,26 @@ qmv_stream_kernel(const void* __restrict__ x, const float* __restrict__ gx,
         se1 = e4m3_decode_byte<1>(sb) * dec_w;
       }
       const u32x4 c = wr[i].code[hh];
-      const float p0 = group_dot16<DT>(c.x, c.y, &xp[hh][0], nullptr);
-      const float p1 = group_dot16<DT>(c.z, c.w, &xp[hh][8], nullptr);
-      acc = __builtin_fmaf(p0, se0, acc);
-      acc = __builtin_fmaf(p1, se1, acc);
+      float p0[MR], p1[MR];
+      group_dot16_rows<DT, MR>(c.x, c.y, xp, hh, 0, p0);
+      group_dot16_rows<DT, MR>(c.z, c.w, xp, hh, 8, p1);
+#pragma unroll
+      for (int j = 0; j < MR; ++j) {
+        acc[j] = __builtin_fmaf(p0[j], se0, acc[j]);
+        acc[j] = __builtin_fmaf(p1[j], se1, acc[j]);
+      }
     }
-    const float v = wave_sum_uniform(acc);
-    mine = (lane == i) ? v : mine;
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+      const float v = wave_sum_uniform(acc[j]);
+      mine[j] = (lane == i) ? v : mine[j];
+    }
   }
-  if (lane < cnt) reinterpret_cast<T*>(out)[r0 + lane] = from_f32<DT>(mine);
+  if (lane < cnt) {
+#pragma unroll
+    for (int j = 0; j < MR; ++j)
+      if (j < m) reinterpret_cast<T*>(out)[(int64_t)j * n + r0 + lane] = from_f32<DT>(mine[j]);
+  }
 }
 
 // ------------------------------------------------------------------ generic path
@@ -483,197 +553,6 @@ qmv_generic_kernel(const void* __restrict__ x, const float* __restrict__ gx,
   }
 }
 
-// ------------------------------------------------------------------ a few x rows
-
-constexpr int kRowsMaxM = 2;
-
-template <int DT> struct Dot2;
-template <> struct Dot2<kBF16> {
-  using V = bf16x2;
-  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_bf16<B>(w); }
-  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2, b), c, false);
-  }
-};
-template <> struct Dot2<kF16> {
-  using V = f16x2;
-  template <int B> static __device__ __forceinline__ V dec(uint32_t w) { return e2m1_decode2_f16<B>(w); }
-  static __device__ __forceinline__ float dot(V a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2, b), c, false);
-  }
-};
-
-// Rows of x past m are never computed; their loads read zeros (buffer range).
-template <int DT, int R>
-__global__ void __launch_bounds__(kThreadsQ)
-qmv_rows_kernel(const void* __restrict__ x, int m, bool qx, const float* __restrict__ gx,
-                const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
-                const float* __restrict__ gw, int n, void* __restrict__ out) {
-  constexpr int K = 4096;
-  constexpr int HPR = K / 8;  // half groups per x row: one per thread
-  using T = typename Elem<DT>::T;
-  using D = Dot2<DT>;
-  __shared__ __attribute__((aligned(16))) u32x4 xs[kRowsMaxM * HPR];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // 1. half group tid of every x row, first in the load queue
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)m * K * 2);
-  u32x4 xr[kRowsMaxM];
-#pragma unroll
-  for (int j = 0; j < kRowsMaxM; ++j)
-    xr[j] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(j * HPR + tid) * 16u, 0, 0));
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. every weight load of this wave's R rows (rows past n re-read row n - 1)
-  const int r0 = (blockIdx.x * kWaves + wave) * R;
-  RowPiece wp[R][2];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int r = min(r0 + i, n - 1);
-    const uint8_t* crow = wc + (int64_t)r * (K / 2);
-    const uint8_t* srow = ws + (int64_t)r * (K / 16);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int e0 = hh * 2048 + 32 * lane;
-      wp[i][hh].code = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + e0 / 2));
-      wp[i][hh].scale =
-          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(srow + ((e0 / 16) & ~3)));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // 3. the x_hat rows into LDS
-  {
-    const float enc = global_encode(gx);
-    const float dec = global_decode(gx);
-#pragma unroll
-    for (int j = 0; j < kRowsMaxM; ++j) {
-      if (j < m) {
-        u32x4 v = xr[j];
-        if (qx) {
-          float f[8], o[8];
-          unpack8<DT>(v, f);
-          xhat_half_group<DT>(f, enc, dec, o);  // lane pairs hold the two halves of a group
-          typedef T T8 __attribute__((ext_vector_type(8)));
-          T8 t;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) t[i] = from_f32<DT>(o[i]);
-          v = __builtin_bit_cast(u32x4, t);
-        }
-        xs[j * HPR + tid] = v;
-      }
-    }
-  }
-  lds_barrier();  // the weight loads stay in flight
-
-  // 4. this lane's x_hat pieces (elements 2048 hh + 32 lane .. + 31 of each row)
-  uint32_t xp[kRowsMaxM][2][16];
-#pragma unroll
-  for (int j = 0; j < kRowsMaxM; ++j) {
-    if (j < m) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 t = xs[j * HPR + (hh * 2048 + 32 * lane) / 8 + q];
-          xp[j][hh][4 * q] = t.x; xp[j][hh][4 * q + 1] = t.y;
-          xp[j][hh][4 * q + 2] = t.z; xp[j][hh][4 * q + 3] = t.w;
-        }
-      }
-    }
-  }
-
-  // 5. rows: per group, the 8 decoded pairs dotted with each x row, the
-  //    partial sums times e4m3(s) * g_w/2688; lane i keeps row r0 + i
-  const float dec_w = global_decode(gw);
-  const int sshift = 8 * ((2 * lane) & 3);
-  float mine[kRowsMaxM];
-#pragma unroll
-  for (int j = 0; j < kRowsMaxM; ++j) mine[j] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float acc[kRowsMaxM];
-#pragma unroll
-    for (int j = 0; j < kRowsMaxM; ++j) acc[j] = 0.0f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const RowPiece& pc = wp[i][hh];
-      float se0, se1;
-      {
-#pragma clang fp contract(off)
-        const uint32_t sc = pc.scale >> sshift;
-        se0 = e4m3_decode_byte<0>(sc) * dec_w;
-        se1 = e4m3_decode_byte<1>(sc) * dec_w;
-      }
-      const uint32_t cw[4] = {pc.code.x, pc.code.y, pc.code.z, pc.code.w};
-      typename D::V d[16];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        d[4 * u] = D::template dec<0>(cw[u]);
-        d[4 * u + 1] = D::template dec<1>(cw[u]);
-        d[4 * u + 2] = D::template dec<2>(cw[u]);
-        d[4 * u + 3] = D::template dec<3>(cw[u]);
-      }
-#pragma unroll
-      for (int j = 0; j < kRowsMaxM; ++j) {
-        if (j < m) {
-          float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) p0 = D::dot(d[t], xp[j][hh][t], p0);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) p1 = D::dot(d[8 + t], xp[j][hh][8 + t], p1);
-          acc[j] = __builtin_fmaf(p0, se0, acc[j]);
-          acc[j] = __builtin_fmaf(p1, se1, acc[j]);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kRowsMaxM; ++j) {
-      if (j < m) {
-        const float v = wave_sum_uniform(acc[j]);
-        mine[j] = (lane == i) ? v : mine[j];
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // consume rows in load order
-  }
-  // 6. lane i stores row r0 + i of every output row
-  if (lane < R && r0 + lane < n) {
-#pragma unroll
-    for (int j = 0; j < kRowsMaxM; ++j)
-      if (j < m) reinterpret_cast<T*>(out)[(int64_t)j * n + r0 + lane] = from_f32<DT>(mine[j]);
-  }
-}
-
-template <int DT, int R>
-void launch_rows(const void* x, int m, bool qx, const float* gx, const uint8_t* wc,
-                 const uint8_t* ws, const float* gw, int64_t n, void* out, int64_t blocks,
-                 hipStream_t s) {
-  qmv_rows_kernel<DT, R><<<(int)blocks, kThreadsQ, 0, s>>>(x, m, qx, gx, wc, ws, gw, (int)n, out);
-}
-
-template <int DT>
-hipError_t launch_rows_t(const void* x, int m, bool qx, const float* gx, const uint8_t* wc,
-                         const uint8_t* ws, const float* gw, int64_t n, void* out, hipStream_t s) {
-  int64_t blocks = (n + kWaves * kRowsMaxR - 1) / (kWaves * kRowsMaxR);
-  if (blocks < 256) blocks = 256;
-  const int rpw = (int)((n + blocks * kWaves - 1) / (blocks * kWaves));
-  blocks = (n + (int64_t)kWaves * rpw - 1) / ((int64_t)kWaves * rpw);
-  switch (rpw) {
-    case 1: launch_rows<DT, 1>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 2: launch_rows<DT, 2>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 3: launch_rows<DT, 3>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 4: launch_rows<DT, 4>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 5: launch_rows<DT, 5>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 6: launch_rows<DT, 6>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    case 7: launch_rows<DT, 7>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-    default: launch_rows<DT, 8>(x, m, qx, gx, wc, ws, gw, n, out, blocks, s); break;
-  }
-  return hipGetLastError();
-}
-
 template <int DT, int CH, int R>
 void launch_reg(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                 const float* gw, int64_t n, void* out, int64_t blocks, hipStream_t s) {
@@ -691,22 +570,31 @@ void launch_reg_r(int r, const void* x, const float* gx, const uint8_t* wc, cons
     launch_reg<DT, CH, 2>(x, gx, wc, ws, gw, n, out, blocks, s);
 }
 
+// the streaming kernel (16-bit x, k = 4096, n < 2^31) with MR rows of x:
+// one 16-wave workgroup per compute unit, more when a wave would get more
+// than kStreamRows rows
+template <int DT, int MR>
+hipError_t launch_stream(const void* x, int m, bool qx, const float* gx, const uint8_t* wc,
+                         const uint8_t* ws, const float* gw, int64_t n, void* out, hipStream_t s) {
+  const int64_t per_wg = (int64_t)kStreamWaves * kStreamRows;
+  int64_t blocks = (n + kStreamWaves - 1) / kStreamWaves;
+  if (blocks > device_cu_count()) blocks = device_cu_count();
+  if (blocks < (n + per_wg - 1) / per_wg) blocks = (n + per_wg - 1) / per_wg;
+  if (qx)
+    qmv_stream_kernel<DT, MR, true><<<(int)blocks, kStreamThreads, 0, s>>>(
+        x, m, gx, wc, ws, gw, (int)n, (int)(n / blocks), (int)(n % blocks), out);
+  else
+    qmv_stream_kernel<DT, MR, false><<<(int)blocks, kStreamThreads, 0, s>>>(
+        x, m, gx, wc, ws, gw, (int)n, (int)(n / blocks), (int)(n % blocks), out);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const uint8_t* ws,
                         const float* gw, int64_t n, int64_t k, void* out, hipStream_t s) {
   const int chunks = (k % 4096 == 0) ? (int)(k / 4096) : 0;
   if constexpr (DT != kF32) {
-    if (chunks == 1 && n < 0x7FFFFFFF) {
-      // one 16-wave workgroup per compute unit, more when a wave would get
-      // more than kStreamRows rows
-      const int64_t per_wg = (int64_t)kStreamWaves * kStreamRows;
-      int64_t blocks = (n + kStreamWaves - 1) / kStreamWaves;
-      if (blocks > device_cu_count()) blocks = device_cu_count();
-      if (blocks < (n + per_wg - 1) / per_wg) blocks = (n + per_wg - 1) / per_wg;
-      qmv_stream_kernel<DT><<<(int)blocks, kStreamThreads, 0, s>>>(
-          x, gx, wc, ws, gw, (int)n, (int)(n / blocks), (int)(n % blocks), out);
-      return hipGetLastError();
-    }
+    if (chunks == 1 && n < 0x7FFFFFFF) return launch_stream<DT, 1>(x, 1, true, gx, wc, ws, gw, n, out, s);
   }
   const bool reg_path = chunks == 1 || (chunks == 2 && DT != kF32);
   if (reg_path) {
@@ -741,15 +629,17 @@ hipError_t launch_qmv_t(const void* x, const float* gx, const uint8_t* wc, const
 }  // namespace
 
 bool qmv_rows_ok(int dt, int64_t m, int64_t n, int64_t k) {
-  return (dt == kBF16 || dt == kF16) && m >= 1 && m <= kRowsMaxM && k == 4096 && n >= 1 &&
-         n < 0x7FFFFFFF;
+  return (dt == kBF16 || dt == kF16) && m >= 1 && m <= 2 && k == 4096 && n >= 1 && n < 0x7FFFFFFF;
 }
 
 hipError_t launch_qmv_rows(const void* x, int dt, int64_t m, bool quantize_x, const float* gx,
                            const uint8_t* wc, const uint8_t* ws, const float* gw, int64_t n,
                            void* out, hipStream_t s) {
-  return dt == kF16 ? launch_rows_t<kF16>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s)
-                    : launch_rows_t<kBF16>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s);
+  if (m == 1)
+    return dt == kF16 ? launch_stream<kF16, 1>(x, 1, quantize_x, gx, wc, ws, gw, n, out, s)
+                      : launch_stream<kBF16, 1>(x, 1, quantize_x, gx, wc, ws, gw, n, out, s);
+  return dt == kF16 ? launch_stream<kF16, 2>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s)
+                    : launch_stream<kBF16, 2>(x, (int)m, quantize_x, gx, wc, ws, gw, n, out, s);
 }
 
 hipError_t launch_qmv(const void* x, int dt, const float* gx, const uint8_t* wc,

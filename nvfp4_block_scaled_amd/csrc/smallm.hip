@@ -696,7 +696,7 @@ bool small_m_ok(int dt, bool packed, int64_t m, int64_t n, int64_t k) {
 hipError_t launch_small_m(const void* x, int dt, bool quantize_x, const float* gx,
                           const uint8_t* wc, const uint8_t* ws, bool packed, const float* gw,
                           int64_t m, int64_t n, int64_t k, void* out, hipStream_t s) {
-  if (!packed && qmv_rows_ok(dt, m, n, k))  // qmv's register design, one accumulator per row
+  if (!packed && qmv_rows_ok(dt, m, n, k))  // qmv's streaming design, one accumulator per row
     return launch_qmv_rows(x, dt, m, quantize_x, gx, wc, ws, gw, n, out, s);
   if (packed && quantize_x && qmv_packed_ok(dt, m, k))  // fp4 codes straight to the matrix cores
     return launch_qmv_packed(x, dt, m, gx, wc, ws, gw, n, k, out, s);

@@ -193,7 +193,7 @@ def test_k4096_general(dtype, m, n):
     """General data at k = 4096 over ragged n: qqmm and qmm against the
     oracle, row-major and packed; qqmm equals qmm on the separately computed
     x_hat bit for bit; up to two rows the row-major path gives, row by row,
-    the bits of qmv (the same register design and summation order)."""
+    the bits of qmv (the same streaming design and summation order)."""
     say(f"k=4096 general m={m} n={n} {dtype}")
     od = oracle_dtype(dtype)
     x = W.normal((m, 4096), 1.0, 180 + m, od)
