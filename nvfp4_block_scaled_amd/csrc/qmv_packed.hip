@@ -46,7 +46,7 @@
 // codes of every block of x (8 bytes each) and the coefficients into LDS;
 // each wave stages its blocks' scales (128 bytes per block, one 16-byte load
 // per lane for all 8) in LDS.  As in the streaming qmv, the x loads go first,
-// a barrier puts them ahead of the weight loads of every wave, a couple of
+// a barrier puts them ahead of the weight loads of every wave, two or four
 // blocks are in flight while x_hat is built, and the rest of the run is
 // issued as each block arrives.
 #include "nvfp4_device.h"
@@ -61,7 +61,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kQpWaves = 16;
 constexpr int kQpThreads = 64 * kQpWaves;
 constexpr int kQpRun = 8;        // blocks per wave at most
-constexpr int kQpAhead0 = 2;     // blocks in flight while x_hat is built
+// blocks in flight while x_hat is built: measured at n = 14336, k = 4096
+// (cold weights), four ahead took m = 1 from 7.63 to 7.47 us and m = 4 from
+// 11.1 to 10.7, while m = 2 went from 8.2 to 8.7 (two ahead kept there)
+template <int M> constexpr int qp_ahead0() { return M == 2 ? 2 : 4; }
 constexpr int kQpAhead = 4;      // blocks in flight in the loop
 constexpr int kQpMinSteps = 8;   // k >= 512: a run of 8 blocks meets at most two tiles
 constexpr int kQpMaxSteps = 128; // k <= 8192
@@ -81,8 +84,8 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// M rows of x (m <= M are real: the rows past m read as zeros); XR quarter
-// groups of x per thread (M k / 4096 rounded up).
+// M rows of x (m <= M are real: the rows past m read as zeros); XR half
+// groups of x per thread (M k / 8192 rounded up).
 template <int DT, int M, int XR>
 __global__ void __launch_bounds__(kQpThreads)
 qmv_packed_kernel(const void* __restrict__ x, int m, const float* __restrict__ gx,
@@ -109,16 +112,16 @@ qmv_packed_kernel(const void* __restrict__ x, int m, const float* __restrict__ g
 
   // 1. the global scales, by scalar loads (they take no slot of the compute
   //    unit's vector-load queue, which the weight stream needs from the
-  //    start), and x: quarter groups tid + 1024 r, elements 4 (tid + 1024 r)
-  //    .. + 3 of x viewed as one vector of m k
+  //    start), and x: half groups tid + 1024 r, elements 8 (tid + 1024 r)
+  //    .. + 7 of x viewed as one vector of m k
   const float gxs = gx ? *gx : kE4M3Max * kE2M1Max;
   const float gws = gw ? *gw : kE4M3Max * kE2M1Max;
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint64_t)m * K * sizeof(T));
-  u32x2 xr[XR];
+  u32x4 xr[XR];
 #pragma unroll
   for (int r = 0; r < XR; ++r)
     xr[r] = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)(tid + kQpThreads * r) * 8u, 0, 0));
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(tid + kQpThreads * r) * 16u, 0, 0));
 
   // this wave's partial-sum slots, one per tile of the workgroup and row of
   // x, zero where its run does not reach (its own later writes follow in order)
@@ -139,6 +142,7 @@ qmv_packed_kernel(const void* __restrict__ x, int m, const float* __restrict__ g
   auto issue = [&](int i) {
     a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)(i * 1024) + 16u * lane, 0, 2));
   };
+  constexpr int kQpAhead0 = qp_ahead0<M>();
 #pragma unroll
   for (int i = 0; i < kQpAhead0; ++i) {
     issue(i);
@@ -160,46 +164,43 @@ qmv_packed_kernel(const void* __restrict__ x, int m, const float* __restrict__ g
     dec_w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qv), 2));
   }
 
-  // 4. x's codes, split into X and Y, and the coefficients.  The four lanes
-  //    of a quad hold one block (blocks never straddle rows of x); lane 0 of
-  //    the quad writes its X codes and coefficients, lane 1 its Y codes.
+  // 4. x's codes, split into X and Y, and the coefficients.  The two lanes
+  //    of a pair hold one block (blocks never straddle rows of x), 8 codes
+  //    each: each writes its half of the block's X and Y code words, and the
+  //    even lane the coefficients.
 #pragma unroll
   for (int r = 0; r < XR; ++r) {
-    const int qg = tid + kQpThreads * r;
-    if (qg < M * K / 4) {  // K / 4 is a multiple of 16: whole quads
+    const int hg = tid + kQpThreads * r;
+    if (hg < M * K / 8) {  // K / 8 is even: whole pairs
       float v[8];
-      unpack8<DT>(u32x4{xr[r].x, xr[r].y, 0u, 0u}, v);
-      float am = fmaxf(fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                       fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
-      am = fmaxf(am, dpp_mov<0xB1>(am));  // quad_perm [1,0,3,2]
-      am = fmaxf(am, dpp_mov<0x4E>(am));  // quad_perm [2,3,0,1]
-      const GroupScale gs = group_scale_from_amax(am, enc);
-      float y[4];
+      unpack8<DT>(xr[r], v);
+      float am = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(v[i]));
+      am = fmaxf(am, dpp_mov<0xB1>(am));  // quad_perm [1,0,3,2]: the pair partner
+      const GroupScale gs = group_scale_from_amax(am, enc);
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
 #pragma clang fp contract(off)
         y[i] = v[i] * gs.enc_b;
       }
       uint32_t cw = 0;
       cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[0], y[1], 1.0f, 0);
       cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[2], y[3], 1.0f, 1);
-      // per nibble s.mmm: magnitudes 3, 5, 7 (1.5, 3, 6) are Y codes, Y = code - 1
-      const uint32_t m0 = cw & 0x1111u, m1 = (cw >> 1) & 0x1111u, m2 = (cw >> 2) & 0x1111u;
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[4], y[5], 1.0f, 2);
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[6], y[7], 1.0f, 3);
+      // per nibble s.mmm: magnitudes 3, 5, 7 (1.5, 3, 6) are Y codes, Y =
+      // code - 1 (bit 0 of such a nibble is set: no borrow between nibbles)
+      const uint32_t m0 = cw & 0x11111111u, m1 = (cw >> 1) & 0x11111111u, m2 = (cw >> 2) & 0x11111111u;
       const uint32_t isy = m0 & (m1 | m2);
       const uint32_t ymask = isy * 0xFu;
-      const uint32_t xc = cw & ~ymask & 0xFFFFu;
-      const uint32_t yc = (cw - isy) & ymask;
-      const uint32_t xy = xc | (yc << 16);
-      const uint32_t w0 = dpp_u32<0x00>(xy), w1 = dpp_u32<0x55>(xy);
-      const uint32_t w2 = dpp_u32<0xAA>(xy), w3 = dpp_u32<0xFF>(xy);
-      const int c = tid & 3;
-      const int gb = qg >> 2;  // block of x as one vector: row gb / nblk, block gb % nblk
-      if (c < 2) {
-        const uint32_t lo = c ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
-        const uint32_t hi = c ? ((w2 >> 16) | (w3 & 0xFFFF0000u)) : ((w2 & 0xFFFFu) | (w3 << 16));
-        ctab[2 * gb + c] = u32x2{lo, hi};
-      }
-      if (c == 0) {
+      const int gb = hg >> 1;  // block of x as one vector: row gb / nblk, block gb % nblk
+      const int half = hg & 1;
+      uint32_t* ct = reinterpret_cast<uint32_t*>(ctab);
+      ct[4 * gb + half] = cw & ~ymask;             // X codes, elements 8 half .. + 7
+      ct[4 * gb + 2 + half] = (cw - isy) & ymask;  // Y codes
+      if (half == 0) {
         float sc, sc15;
         {
 #pragma clang fp contract(off)
@@ -358,13 +359,12 @@ hipError_t launch_qp_dt(const void* x, int64_t m, const float* gx, const uint8_t
                         hipStream_t s) {
   const bool wide = k > 4096;
   if (m == 1)
-    return wide ? launch_qp_t<DT, 1, 2>(x, m, gx, pc, ps, gw, n, k, out, s)
-                : launch_qp_t<DT, 1, 1>(x, m, gx, pc, ps, gw, n, k, out, s);
+    return launch_qp_t<DT, 1, 1>(x, m, gx, pc, ps, gw, n, k, out, s);
   if (m == 2)
-    return wide ? launch_qp_t<DT, 2, 4>(x, m, gx, pc, ps, gw, n, k, out, s)
-                : launch_qp_t<DT, 2, 2>(x, m, gx, pc, ps, gw, n, k, out, s);
-  return wide ? launch_qp_t<DT, 4, 8>(x, m, gx, pc, ps, gw, n, k, out, s)
-              : launch_qp_t<DT, 4, 4>(x, m, gx, pc, ps, gw, n, k, out, s);
+    return wide ? launch_qp_t<DT, 2, 2>(x, m, gx, pc, ps, gw, n, k, out, s)
+                : launch_qp_t<DT, 2, 1>(x, m, gx, pc, ps, gw, n, k, out, s);
+  return wide ? launch_qp_t<DT, 4, 4>(x, m, gx, pc, ps, gw, n, k, out, s)
+              : launch_qp_t<DT, 4, 2>(x, m, gx, pc, ps, gw, n, k, out, s);
 }
 
 }  // namespace
