@@ -61,6 +61,11 @@
  *       of the decoded values are summed without rounding either operand to
  *       T first (the pages hand both operands' codes and scales to a
  *       block-scaled product); only the sum is rounded to T.
+ *   R24 gather_qmm in an mx mode: the routed product of R10 with the
+ *       expert's weight decoded as R22 (float32, exact), x used as given and
+ *       no global scale (validate_global_scale admits none outside nvfp4);
+ *       the pages' gather_qmm takes the same mode argument as the other
+ *       quantized products.
  */
 #include <math.h>
 #include <stdint.h>
@@ -624,4 +629,41 @@ void orc_mx_qqmm_subset(const float* x, int dtype, int64_t m, int64_t k, int bit
   free(wr);
   free(xc);
   free(xs);
+}
+
+/* gather_qmm in an mx mode on a subset of (token, slot) pairs and output
+ * columns (reading R24): out[t, j, n] = T( sum_k x[t, k] * w_e[n, k] ),
+ * e = idx[t, j], w_e the float32 decode of expert e's mx codes [e, n, row
+ * bytes] and E8M0 scales [e, n, k/32] (R22); products summed in double, one
+ * rounding to T.  A pair whose expert lies outside [0, e_count) multiplies
+ * nothing: its row is zero (the library's documented contract for such
+ * pairs; the pages define no product for them).  out is [np, nn]. */
+void orc_mx_gather_qmm_subset(const float* x, int dtype, int64_t k, int bits,
+                              const uint8_t* wcodes, const uint8_t* wscales, int64_t e_count,
+                              int64_t n, const int32_t* idx, int64_t top_k,
+                              const int64_t* pairs_t, const int64_t* pairs_j, int64_t np,
+                              const int64_t* ni, int64_t nn, float* out, int nthreads) {
+  const int64_t rb = mx_row_bytes(k, bits);
+#pragma omp parallel num_threads(nthreads)
+  {
+    float* wr = (float*)malloc(sizeof(float) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t a = 0; a < np; ++a) {
+      const int64_t t = pairs_t[a], j = pairs_j[a];
+      const int64_t e = idx[t * top_k + j];
+      for (int64_t b = 0; b < nn; ++b) {
+        if (e < 0 || e >= e_count) {
+          out[a * nn + b] = 0.0f;
+          continue;
+        }
+        const int64_t row = e * n + ni[b];
+        for (int64_t i = 0; i < k; ++i)
+          wr[i] = mx_value(wcodes + row * rb, wscales + row * (k / 32), i, bits);
+        double acc = 0.0;
+        for (int64_t i = 0; i < k; ++i) acc += (double)x[t * k + i] * (double)wr[i];
+        out[a * nn + b] = orc_round_to((float)acc, dtype);
+      }
+    }
+    free(wr);
+  }
 }

@@ -81,6 +81,9 @@ def lib():
         L.orc_mx_qqmm_subset.restype = None
         L.orc_mx_qqmm_subset.argtypes = [_P, _INT, _I64, _I64, _INT, _P, _P, _I64, _P, _I64,
                                          _P, _I64, _P, _INT]
+        L.orc_mx_gather_qmm_subset.restype = None
+        L.orc_mx_gather_qmm_subset.argtypes = [_P, _INT, _I64, _INT, _P, _P, _I64, _I64, _P, _I64,
+                                               _P, _P, _I64, _P, _I64, _P, _INT]
         L.orc_set_mutant.restype = None
         L.orc_set_mutant.argtypes = [_INT]
         L.orc_get_mutant.restype = _INT
@@ -403,9 +406,40 @@ def mx_qqmm(x, w_codes, w_scales, mode, dtype="bf16", rows=None, cols=None, nthr
     return out
 
 
+def mx_gather_qmm(x, w_codes, w_scales, idx, mode, dtype="bf16", pairs=None, cols=None,
+                  nthreads=None):
+    """gather_qmm in an mx mode: rows of out[t, j, cols] = T(x[t] @ w_hat[e]^T),
+    e = idx[t, j], for the (t, j) pairs given (all by default); x as given,
+    w_codes [e, n, row bytes] and E8M0 w_scales [e, n, k/32].  Returns
+    [len(pairs), len(cols)], or [t, top_k, len(cols)] with pairs=None."""
+    bits = _bits(mode)
+    x = _f32(x)
+    t_count, k = x.shape
+    w_codes = np.ascontiguousarray(w_codes, dtype=np.uint8)
+    w_scales = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    e_count, n = w_codes.shape[0], w_codes.shape[1]
+    assert w_codes.shape[2] == mx_code_bytes(k, mode) and w_scales.shape[2] * 32 == k
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    top_k = idx.shape[1]
+    if pairs is None:
+        tt, jj = np.meshgrid(np.arange(t_count), np.arange(top_k), indexing="ij")
+        pt, pj = tt.reshape(-1).astype(np.int64), jj.reshape(-1).astype(np.int64)
+    else:
+        pt = np.ascontiguousarray([p[0] for p in pairs], np.int64)
+        pj = np.ascontiguousarray([p[1] for p in pairs], np.int64)
+    ni = np.arange(n, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+    out = np.empty((pt.size, ni.size), np.float32)
+    lib().orc_mx_gather_qmm_subset(_ptr(x), _dt(dtype), k, bits, _ptr(w_codes), _ptr(w_scales),
+                                   e_count, n, _ptr(idx), top_k, _ptr(pt), _ptr(pj), pt.size,
+                                   _ptr(ni), ni.size, _ptr(out), int(nthreads or default_threads()))
+    if pairs is None:
+        out = out.reshape(t_count, top_k, ni.size)
+    return out
+
+
 __all__ = [
     "MUT_E8M0_NEAREST", "MX_BITS", "e8m0_value", "e8m0_encode_up", "mx_code_bytes",
-    "mx_quantize", "mx_dequantize", "mx_quant_dequant", "mx_qqmm",
+    "mx_quantize", "mx_dequantize", "mx_quant_dequant", "mx_qqmm", "mx_gather_qmm",
     "F32", "F16", "BF16", "MUT_NONE", "MUT_DROP_GW", "MUT_DROP_GX", "MUT_GW_ON_SUM",
     "MUT_AMAX6_BF16", "MUT_ENC_ORDER", "mutant", "quantize_columnwise", "quant_dequant_columnwise",
     "qqmm_vjp", "gather_qmm_indexed", "e2m1_value", "e2m1_encode", "e4m3_value",

@@ -278,3 +278,72 @@ def test_round_trip_error_within_half_a_grid_step(mode):
                         2.0 ** -9)
     assert (np.abs(x - xh) <= step / 2 * sc).all()
     assert (y <= MAXVAL[mode]).all()
+
+
+# ------------------------------------------------------------------ gather_qmm
+
+def _decode_independently(codes, scales, mode):
+    """w_hat from the format definitions, not through the oracle: e2m1 by its
+    value table (sign in bit 3, element 2j in the low nibble of byte j), e4m3
+    through torch's float8_e4m3fn, times 2^(s - 127) by ldexp."""
+    codes = np.asarray(codes, np.uint8)
+    if mode == "mxfp4":
+        nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], -1)
+        mag = np.array(E2M1, np.float64)[nib & 7]
+        vals = np.where(nib & 8, -mag, mag)
+    else:
+        vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    s = np.repeat(np.asarray(scales, np.int64), 32, axis=-1)
+    return np.ldexp(vals, s - 127)
+
+
+def _gather_exact(x, ws, idx, dtype):
+    y = np.stack([[x[t].astype(np.float64) @ ws[e].astype(np.float64).T for e in row]
+                  for t, row in enumerate(idx)])
+    return np.array([[[O.round_to(float(v), dtype) for v in r] for r in p] for p in y], np.float32)
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_gather_qmm_exact_on_grid_experts(mode, dtype):
+    """Three experts of grid blocks (each group of 32 exactly representable,
+    a different power of two per expert and group), x on the e2m1 grid: every
+    product is exact in float64, so each (t, j) row is the product with the
+    raw weights of expert idx[t, j] rounded once.  A wrong expert, layout or
+    block scale changes the bits."""
+    e_count, n, k = 3, 40, 96
+    ws = [_grid_blocks(n, k, mode, 30 + e, [3 * e - 4, e, -e]) for e in range(e_count)]
+    codes, scales = zip(*(O.mx_quantize(w, mode) for w in ws))
+    codes, scales = np.stack(codes), np.stack(scales)
+    x = W.grid_tensor(7, k, seed=33).numpy()
+    idx = np.random.default_rng(34).integers(0, e_count, (7, 2)).astype(np.int32)
+    got = O.mx_gather_qmm(x, codes, scales, idx, mode, dtype=dtype)
+    np.testing.assert_array_equal(got, _gather_exact(x, ws, idx, dtype))
+    swapped = O.mx_gather_qmm(x, codes[::-1].copy(), scales[::-1].copy(), idx, mode, dtype=dtype)
+    assert not np.array_equal(swapped, got)
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp8"])
+def test_gather_qmm_general_against_an_independent_decode(mode):
+    """General data: the float64 product with weights decoded from the format
+    definitions (sum order only), subsets consistent with the whole, and a
+    pair whose expert is out of range gives a zero row."""
+    e_count, n, k = 4, 24, 128
+    w = W.normal((e_count * n, k), 0.02, 40, "bf16").float().numpy()
+    codes, scales = O.mx_quantize(w, mode)
+    codes = codes.reshape(e_count, n, -1)
+    scales = scales.reshape(e_count, n, -1)
+    x = W.normal((5, k), 1.0, 41, "bf16").float().numpy()
+    idx = np.array([[0, 3], [2, 2], [1, 0], [3, 1], [2, 0]], np.int32)
+    got = O.mx_gather_qmm(x, codes, scales, idx, mode, dtype="f32")
+    wh = _decode_independently(codes, scales, mode)
+    want = np.stack([[x[t].astype(np.float64) @ wh[e].T for e in row] for t, row in enumerate(idx)])
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-9)
+    sub = O.mx_gather_qmm(x, codes, scales, idx, mode, dtype="f32", pairs=[(4, 1), (1, 0)],
+                          cols=[23, 0, 5])
+    np.testing.assert_array_equal(sub, got[[4, 1], [1, 0]][:, [23, 0, 5]])
+    bad = idx.copy()
+    bad[2, 1] = e_count
+    y = O.mx_gather_qmm(x, codes, scales, bad, mode, dtype="f32")
+    assert (y[2, 1] == 0).all()
+    np.testing.assert_array_equal(np.delete(y.reshape(10, n), 5, 0), np.delete(got.reshape(10, n), 5, 0))
