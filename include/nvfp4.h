@@ -248,8 +248,9 @@ nvfp4_status nvfp4_qqmm_vjp(const void* x, const void* w, const void* dy, nvfp4_
 
 /*
  * nvfp4_gather_qmm_workspace_size -- bytes of device workspace
- * nvfp4_gather_qmm (and nvfp4_gather_qmm_packed) needs: the routing tables
- * (expert offsets, the pair order) and the routing's per-chunk counts.
+ * nvfp4_gather_qmm (and nvfp4_gather_qmm_packed, nvfp4_mx_gather_qmm) needs:
+ * the routing tables (expert offsets, the pair order) and the routing's
+ * per-chunk counts.
  * 0 for non-positive sizes or t * top_k >= 2^31.
  */
 size_t nvfp4_gather_qmm_workspace_size(int64_t t, int64_t top_k, int64_t e, int64_t n,
@@ -573,6 +574,37 @@ nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode m
                                   const uint8_t* packed_codes, const uint8_t* packed_scales,
                                   int64_t m, int64_t n, int64_t k, void* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * nvfp4_mx_gather_qmm -- nvfp4_gather_qmm with per-expert weights in an mx
+ * mode (the gather_qmm op takes the same mode argument as the other
+ * quantized products, "mlx 0.30.7.2 -> 0.30.7.6" diff page 8; the mx decode
+ * of fp_dequantize there, no global scale):
+ *     out[t, j, :] = T( x[t, :] @ w_hat[idx[t, j]]^T ),
+ * w_hat = code value * 2^(s - 127), exact in float32; x used as given.  The
+ * pairs are grouped by expert as in nvfp4_gather_qmm; for float16 and
+ * bfloat16 x the decoded weights are rounded to T for the matrix cores
+ * (exact unless a block scale puts them outside T's normal range), float32
+ * x runs a float32 kernel; float32 accumulation.
+ *   x           device [t, k] of type dt, 16-byte aligned
+ *   w_codes     device uint8 [e, n, k/2] (mxfp4, element 2j in the low
+ *               nibble of byte j) or [e, n, k] (mxfp8), 16-byte aligned
+ *   w_scales    device uint8 [e, n, k/32], E8M0
+ *   expert_idx  device int32 [t, top_k]; a pair whose index lies outside
+ *               [0, e) multiplies no expert and its output row is zeros
+ *   out         device [t, top_k, n] of type dt, written
+ *   workspace   device, nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k)
+ *               bytes, 256-byte aligned (the routing tables)
+ * Errors: bad dtype or mode, NULL or misaligned pointer, t, top_k, e, n <= 0,
+ * k not a positive multiple of 32, workspace too small; UNSUPPORTED for more
+ * than 1024 experts, t * top_k >= 2^31, or x or one expert's codes of 2 GB
+ * or more.
+ */
+nvfp4_status nvfp4_mx_gather_qmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                 const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                                 int64_t n, int64_t k, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Test hook: treat every device as having this gcnArchName (NULL restores the

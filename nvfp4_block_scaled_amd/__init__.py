@@ -93,6 +93,7 @@ def load_library():
         "nvfp4_mx_qqmm_workspace_size": (SZ, [I, I64, I64, I64, I]),
         "nvfp4_mx_qqmm": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
         "nvfp4_mx_qqmm_packed": (I, [P, I, I, P, P, I64, I64, I64, P, P, SZ, P]),
+        "nvfp4_mx_gather_qmm": (I, [P, I, I, P, P, P, I64, I64, I64, I64, I64, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -761,6 +762,40 @@ def dequantize(w, scales, group_size=None, bits=None, mode="nvfp4", global_scale
     return nvfp4_dequantize(w, scales, global_scale, dtype)
 
 
+def nvfp4_mx_gather_qmm(x, w_codes, w_scales, expert_idx, mode, out=None, workspace=None):
+    """out[t, j, :] = x[t] @ w_hat[expert_idx[t, j]]^T with mx weights
+    (codes [e, n, k/2] for mxfp4 or [e, n, k] for mxfp8, scales [e, n, k/32])."""
+    L = load_library()
+    bits = _mx_mode(mode)
+    _dev(x, "x")
+    _dev(expert_idx, "expert_idx")
+    _dev(w_codes, "w_codes")
+    _dev(w_scales, "w_scales")
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2:
+        raise ValueError("expert_idx must be int32 [t, top_k]")
+    if x.dim() != 2:
+        raise ValueError("x must be [t, k]")
+    t, k = x.shape
+    top_k = expert_idx.shape[1]
+    if expert_idx.shape[0] != t:
+        raise ValueError("expert_idx rows must match x rows")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.uint8 or w_codes.dim() != 3:
+        raise ValueError("w_codes and w_scales must be uint8 [e, n, .]")
+    e, n = w_codes.shape[0], w_codes.shape[1]
+    if w_codes.shape[2] != _mx_code_cols(k, mode) or tuple(w_scales.shape) != (e, n, k // 32):
+        raise ValueError("w_codes / w_scales do not match x's inner size")
+    if out is None:
+        out = torch.empty((t, top_k, n), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace, nbytes = gather_workspace(t, top_k, e, n, k, x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(L.nvfp4_mx_gather_qmm(_ptr(x), _dtype_code(x, "x"), bits, _ptr(w_codes), _ptr(w_scales),
+                                 _ptr(expert_idx), t, top_k, e, n, k, _ptr(out), _ptr(workspace),
+                                 nbytes, _stream()))
+    return out
+
+
 def qqmm(x, w, scales, group_size=None, bits=None, mode="nvfp4", global_scale_x=None,
          global_scale_w=None):
     _mode_check(group_size, bits, mode, (global_scale_x, global_scale_w))
@@ -770,9 +805,16 @@ def qqmm(x, w, scales, group_size=None, bits=None, mode="nvfp4", global_scale_x=
 
 
 def gather_qmm(x, w, scales, rhs_indices, global_scale=None, lhs_indices=None, transpose=True,
-               sorted_indices=False):
+               sorted_indices=False, group_size=None, bits=None, mode="nvfp4"):
     """The MoE form (x [t, k], rhs_indices [t, top_k]) by default; with
-    lhs_indices, transpose=False or sorted_indices the indexed form."""
+    lhs_indices, transpose=False or sorted_indices the indexed form.  The mx
+    modes take the MoE form."""
+    _mode_check(group_size, bits, mode, (global_scale,))
+    if mode != "nvfp4":
+        if lhs_indices is not None or not transpose or x.dim() != 2 or rhs_indices.dim() != 2:
+            raise ValueError(f"[gather_qmm] mode {mode!r}: only x [t, k] with rhs_indices "
+                             "[t, top_k] and transpose=True")
+        return nvfp4_mx_gather_qmm(x, w, scales, rhs_indices, mode)
     if lhs_indices is None and transpose and not sorted_indices and x.dim() == 2 \
             and rhs_indices.dim() == 2 and rhs_indices.shape[0] == x.shape[0]:
         return nvfp4_gather_qmm(x, w, scales, rhs_indices, global_scale)
@@ -787,4 +829,5 @@ __all__ = [
     "MX_MODES", "MxPacked", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_quant_dequant",
     "nvfp4_mx_pack", "mx_qqmm_workspace", "nvfp4_mx_qqmm", "nvfp4_mx_qqmm_packed",
     "nvfp4_mx_quantize_packed", "nvfp4_mx_mm_packed", "nvfp4_gather_qmm_indexed",
+    "nvfp4_mx_gather_qmm",
 ]

@@ -1144,4 +1144,45 @@ nvfp4_status nvfp4_mx_qqmm_packed(const void* x, nvfp4_dtype dt, nvfp4_mx_mode m
   return launched(op, e);
 }
 
+nvfp4_status nvfp4_mx_gather_qmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
+                                 const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const int32_t* expert_idx, int64_t t, int64_t top_k, int64_t e,
+                                 int64_t n, int64_t k, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const char* op = "mx_gather_qmm";
+  if (t <= 0 || top_k <= 0 || e <= 0 || n <= 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_gather_qmm] t, top_k, e and n must be positive.");
+  if (nvfp4_status st = check_mx(op, x, dt, mode, t, k)) return st;
+  if (!w_codes || !w_scales || !expert_idx || !out)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mx_gather_qmm] w_codes, w_scales, expert_idx and out must not be NULL.");
+  if (!aligned(w_codes, 16))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_gather_qmm] w_codes must be 16-byte aligned.");
+  if (t * top_k >= ((int64_t)1 << 31) || n > INT32_MAX || k > INT32_MAX)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mx_gather_qmm] Sizes too large.");
+  const int64_t row_bytes = mode == NVFP4_MXFP8 ? k : k / 2;
+  if (t * k * (int64_t)dtype_size(dt) >= kOffsetLimit || n * row_bytes >= kOffsetLimit)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "[mx_gather_qmm] x and one expert's codes must each stay below 2 GB.");
+  if (e > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED, "[mx_gather_qmm] at most 1024 experts are supported.");
+  const size_t need = nvfp4_gather_qmm_workspace_size(t, top_k, e, n, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "[mx_gather_qmm] workspace of %zu bytes is smaller than %zu.", workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "[mx_gather_qmm] workspace must be 256-byte aligned.");
+  if (nvfp4_status st = check_device(op, stream)) return st;
+  const RouteLayout rl = route_layout(t * top_k, e);
+  char* wsb = reinterpret_cast<char*>(workspace);
+  int32_t* offsets = reinterpret_cast<int32_t*>(wsb + rl.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(wsb + rl.perm);
+  hipError_t he = nvfp4::launch_moe_route(expert_idx, t * top_k, 1, e, offsets, perm,
+                                          reinterpret_cast<int32_t*>(wsb + rl.scratch), out,
+                                          n * (int64_t)dtype_size(dt), stream);
+  if (he != hipSuccess) return launched(op, he);
+  return launched(op, nvfp4::launch_mx_gather_gemm(x, dt, mode, w_codes, w_scales, offsets, perm, t,
+                                                    t * top_k, top_k, e, n, k, out, stream));
+}
+
 }  // extern "C"

@@ -4,7 +4,11 @@
 // with w decoded with its global scale on every block scale ("mlx 0.30.7.2 ->
 // 0.30.7.6" diff page 8, qqmm and page 7, QQMatmul::eval_gpu; "[Metal]
 // global scale for qmm" PR 4458, statement: the global factor sits inside
-// the dequantization, per expert for gather_qmm).
+// the dequantization, per expert for gather_qmm).  gather_qmm also takes
+// weights in the mx modes (diff page 8, fp_dequantize: groups of 32, e2m1 or
+// e4m3 codes, E8M0 scales 2^(s - 127), no global scale); the kernels'
+// weight-format parameter WF selects NVFP4 (kWfNv), mxfp4 (kWfMx4) or mxfp8
+// (kWfMx8).
 //
 // Three kernels, by operand type and shape:
 //   * mfma_gemm_fast_kernel / mfma_gemm_fast2_kernel (16-bit x, k % 64 == 0,
@@ -12,6 +16,8 @@
 //     weights decoded in registers, A staged through LDS; it reads the weight
 //     either row-major or in the packed layout of mfma_pack_kernel (details
 //     at the kernel body);
+//     (mfma_gemm_mx4_kernel / mfma_gemm_mx4_2_kernel run the same body on
+//     row-major mxfp4 weights);
 //   * mfma_gemm_kernel (16-bit x, any k % 16 == 0): the general matrix-core
 //     path on v_mfma_f32_16x16x32, 256 x 256 x 64 tiles with both A and the
 //     decoded weight tile (written by the VALU) in double-buffered LDS;
@@ -30,6 +36,12 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kGemmThreads = 256;
 constexpr int kTileElems = BM * BK;  // 16-bit elements per LDS tile
+
+// weight formats: NVFP4 (e2m1, e4m3 scale per 16, global scale), mxfp4
+// (e2m1, E8M0 scale per 32), mxfp8 (e4m3, E8M0 scale per 32)
+constexpr int kWfNv = 0, kWfMx4 = 4, kWfMx8 = 8;
+template <int WF> constexpr int64_t wf_code_bytes(int64_t k) { return WF == kWfMx8 ? k : k / 2; }
+template <int WF> constexpr int64_t wf_scale_bytes(int64_t k) { return WF == kWfNv ? k / 16 : k / 32; }
 
 template <int DT> struct Mfma;
 template <> struct Mfma<kBF16> {
@@ -79,6 +91,22 @@ __device__ __forceinline__ typename Mfma<DT>::V8 decode8(uint32_t word, float se
   return o;
 }
 
+// Decode 8 e4m3 codes (lo: elements 0..3, hi: 4..7, byte i = element i) with
+// the block scale into T.
+template <int DT>
+__device__ __forceinline__ typename Mfma<DT>::V8 decode8_fp8(uint32_t lo, uint32_t hi, float se) {
+  const float v[8] = {e4m3_decode_byte<0>(lo), e4m3_decode_byte<1>(lo), e4m3_decode_byte<2>(lo),
+                      e4m3_decode_byte<3>(lo), e4m3_decode_byte<0>(hi), e4m3_decode_byte<1>(hi),
+                      e4m3_decode_byte<2>(hi), e4m3_decode_byte<3>(hi)};
+  typename Mfma<DT>::V8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma clang fp contract(off)
+    o[i] = from_f32<DT>(v[i] * se);
+  }
+  return o;
+}
+
 // ------------------------------------------------------------------ general path (k % 16 == 0)
 //
 // Workgroup tile 256 x 256 x 64, four waves in a 2 x 2 grid, each a 128 x 128
@@ -88,8 +116,11 @@ __device__ __forceinline__ typename Mfma<DT>::V8 decode8(uint32_t word, float se
 // element is decoded once per workgroup.  Both LDS tiles are double-buffered;
 // LDS rows of 64 elements have their 16-byte chunks XOR-swizzled by row; the
 // MFMA takes the weight fragment first, so each lane ends with 4 consecutive
-// output columns of one row.  Partial k-steps load group by group.
-template <int DT, bool GATHER>
+// output columns of one row.  Partial k-steps load group by group.  The mx
+// formats (WF) load a whole group of 32 per thread half and decode it with
+// its E8M0 scale; their k is a multiple of 32, so a group is either whole or
+// past the end.
+template <int DT, bool GATHER, int WF = kWfNv>
 __global__ void __launch_bounds__(kGemmThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc,
@@ -167,11 +198,12 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
   }
 
   const T* A = reinterpret_cast<const T*>(a_base);
-  const int64_t kc = K >> 1;   // code bytes per row
-  const int64_t ksc = K >> 4;  // scale bytes per row
+  const int64_t kc = wf_code_bytes<WF>(K);    // code bytes per row
+  const int64_t ksc = wf_scale_bytes<WF>(K);  // scale bytes per row
 
   u32x4 a_reg[8];
   u32x4 b_code[2];
+  u32x4 b_hi[2];  // mxfp8: the second 16 code bytes of the half's group
   uint32_t b_scale[2];
 
   // whole 64-wide k tiles with 16-byte aligned code rows and 2-byte aligned
@@ -187,6 +219,25 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
         a_reg[i] = *reinterpret_cast<const u32x4*>(A + a_row[i] * K + kk);
       else
         a_reg[i] = u32x4{0, 0, 0, 0};
+    }
+    if constexpr (WF != kWfNv) {
+      (void)bfull;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int g = (k0 >> 5) + b_half;  // this half's group of 32
+        u32x4 c = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
+        uint32_t sc = 0;
+        if (b_row[i] >= 0 && 32 * g < K) {
+          const uint8_t* cp = wc + b_row[i] * kc + (int64_t)g * (WF == kWfMx8 ? 32 : 16);
+          c = *reinterpret_cast<const u32x4*>(cp);
+          if constexpr (WF == kWfMx8) c2 = *reinterpret_cast<const u32x4*>(cp + 16);
+          sc = ws[b_row[i] * ksc + g];
+        }
+        b_code[i] = c;
+        b_hi[i] = c2;
+        b_scale[i] = sc;
+      }
+      return;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -226,6 +277,21 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       int r = (tid >> 1) + 128 * i;
+      if constexpr (WF != kWfNv) {
+        const float se = e8m0_value(b_scale[i]);
+        const uint32_t cw[8] = {b_code[i].x, b_code[i].y, b_code[i].z, b_code[i].w,
+                                b_hi[i].x,   b_hi[i].y,   b_hi[i].z,   b_hi[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          V8 v;
+          if constexpr (WF == kWfMx4)
+            v = decode8<DT>(cw[j], se);
+          else
+            v = decode8_fp8<DT>(cw[2 * j], cw[2 * j + 1], se);
+          *reinterpret_cast<V8*>(lb + lds_off(r, 4 * b_half + j)) = v;
+        }
+        continue;
+      }
       float se0, se1;
       {
 #pragma clang fp contract(off)
@@ -408,13 +474,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // RT = 32-row tiles per workgroup: 8 (256 rows, 256 accumulators per wave, one
 // workgroup per CU) or 4 (128 rows, 128 accumulators per wave, two workgroups
 // per CU, so that each SIMD interleaves two waves' instruction streams).
-template <int DT, bool GATHER, bool PACKED, int RT>
+template <int DT, bool GATHER, bool PACKED, int RT, int WF = kWfNv>
 __device__ __forceinline__ void
 mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
                     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ ws,
                     const float* __restrict__ gw, int M, int N, int K, void* __restrict__ out,
                     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
                     int top_k, int E, int tiles_m, const int32_t* __restrict__ amap, int seg) {
+  static_assert(WF == kWfNv || (WF == kWfMx4 && !PACKED), "mxfp4 weights row-major only");
   using T = typename Elem<DT>::T;
   using V8 = typename Mfma<DT>::V8;
   constexpr int TM = 32 * RT;              // tile rows
@@ -486,7 +553,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   const int KT = K / BK;
   const int64_t col_tiles = (N + 31) / 32;
   const uint64_t wc_bytes = PACKED ? (uint64_t)col_tiles * KT * kPackCodeBlock : (uint64_t)N * (K / 2);
-  const uint64_t ws_bytes = PACKED ? (uint64_t)col_tiles * KT * kPackScaleBlock : (uint64_t)N * (K / 16);
+  const uint64_t ws_bytes = PACKED ? (uint64_t)col_tiles * KT * kPackScaleBlock : (uint64_t)N * wf_scale_bytes<WF>(K);
   const __amdgpu_buffer_rsrc_t rs_c = make_rsrc(wc + (int64_t)expert * wc_bytes, wc_bytes);
   const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(ws + (int64_t)expert * ws_bytes, ws_bytes);
 
@@ -524,6 +591,8 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   // Packed: the 1 KB code block of (tile, kt) holds lane l's 16 bytes at
   // 16 l, the 128-byte scale block column c's dword at 4 c (one contiguous
   // run per load).  Tiles past n read as zeros (buffer range checks).
+  // mxfp4 (row-major): the same code bytes; the step's two E8M0 scales, one
+  // per lane half, are a 16-bit load at col * K/32 + 2 kt.
   uint32_t c_off[2], s_off[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -534,11 +603,11 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
     } else {
       const int col = min(bn + wave * 64 + t * 32 + fr, N - 1);
       c_off[t] = (uint32_t)col * (uint32_t)(K / 2) + fh * 16;
-      s_off[t] = (uint32_t)col * (uint32_t)(K / 16);
+      s_off[t] = (uint32_t)col * (uint32_t)wf_scale_bytes<WF>(K);
     }
   }
   const int c_step = PACKED ? kPackCodeBlock : BK / 2;    // code bytes per k-step
-  const int s_step = PACKED ? kPackScaleBlock : BK / 16;  // scale bytes per k-step
+  const int s_step = PACKED ? kPackScaleBlock : (int)wf_scale_bytes<WF>(BK);  // scale bytes per k-step
 
   // load j (1 KB) of this wave's quarter of A(kt) into stage si, straight
   // from global memory
@@ -555,7 +624,10 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
     b.code[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, c_off[t], kt * c_step, 0));
   };
   auto load_b_scale = [&](int kt, BRaw& b, int t) {
-    b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * s_step, 0);
+    if constexpr (WF == kWfMx4)
+      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b16(rs_s, s_off[t], kt * s_step, 0);
+    else
+      b.scale[t] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, s_off[t], kt * s_step, 0);
   };
   auto load_b = [&](int kt, BRaw& b) {
 #pragma unroll
@@ -564,8 +636,10 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
       load_b_scale(kt, b, t);
     }
   };
-  // effective scale of group 2 fh + gi (gi = 0, 1) of column tile t
+  // effective scale of group 2 fh + gi (gi = 0, 1) of column tile t (mxfp4:
+  // of group fh, whatever gi)
   auto scale_of = [&](const BRaw& b, int t, int gi) -> float {
+    if constexpr (WF == kWfMx4) return e8m0_value((b.scale[t] >> (8 * fh)) & 0xFFu);
     float se;
     {
 #pragma clang fp contract(off)
@@ -779,6 +853,18 @@ mfma_gemm_fast2_kernel(NVFP4_FAST_ARGS) {
   mfma_gemm_fast_body<DT, GATHER, PACKED, 4>(NVFP4_FAST_PASS);
 }
 
+// the same two tilings for gather_qmm on row-major mxfp4 weights
+template <int DT>
+__global__ void __launch_bounds__(kGemmThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_gemm_mx4_kernel(NVFP4_FAST_ARGS) {
+  mfma_gemm_fast_body<DT, true, false, 8, kWfMx4>(NVFP4_FAST_PASS);
+}
+template <int DT>
+__global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_gemm_mx4_2_kernel(NVFP4_FAST_ARGS) {
+  mfma_gemm_fast_body<DT, true, false, 4, kWfMx4>(NVFP4_FAST_PASS);
+}
+
 // ------------------------------------------------------------------ packed weight layout
 //
 // The fast path reads, per k-step, 16 code bytes and one scale dword for each
@@ -822,8 +908,9 @@ constexpr int FT = 64, FK = 16;
 // out tile 64 x 64, 256 threads with 4 x 4 outputs each; the weight tile is
 // decoded to float32 e2m1(q) * (e4m3(s) * g/2688) while staged in LDS.
 // TRANS: each expert's weight is [K, N] quantized along N (gather_qmm with
-// transpose = False, out = x @ w): element (n, k) is row k, column n.
-template <bool GATHER, bool TRANS = false>
+// transpose = False, out = x @ w): element (n, k) is row k, column n.  WF: the
+// weight format (mx weights: code value times 2^(s - 127), [N, K] only).
+template <bool GATHER, bool TRANS = false, int WF = kWfNv>
 __global__ void __launch_bounds__(256)
 f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
                 const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
@@ -890,7 +977,20 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
       la[kk][r] = av;
       float wv = 0.f;
       int n = bn + r;
-      if (n < N && k < K) {
+      if constexpr (WF != kWfNv) {
+        static_assert(!TRANS, "mx weights are [N, K]");
+        if (n < N && k < K) {
+          const int64_t row = wbase + n;
+          float cv;
+          if constexpr (WF == kWfMx4) {
+            const uint32_t byte = wc[row * (K >> 1) + (k >> 1)];
+            cv = e2m1_decode((k & 1) ? (byte >> 4) : (byte & 15u));
+          } else {
+            cv = e4m3_decode(wc[row * K + k]);
+          }
+          wv = cv * e8m0_value(ws[row * (K >> 5) + (k >> 5)]);
+        }
+      } else if (n < N && k < K) {
         uint32_t code, sbyte;
         if constexpr (TRANS) {
           const int64_t row = (int64_t)expert * K + k;
@@ -1096,7 +1196,7 @@ int64_t route_chunk_rows(int64_t rows) {
 
 // ------------------------------------------------------------------ launchers
 
-template <bool GATHER, bool PACKED, int RT>
+template <bool GATHER, bool PACKED, int RT, int WF = kWfNv>
 hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
                           const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
                           const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
@@ -1112,7 +1212,24 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
   KER<D, GATHER, PACKED><<<(int)blocks, kGemmThreads, 0, s_stream>>>(                              \
       a, a_rows, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e,    \
       (int)tiles_m, amap, seg)
-  if constexpr (RT == 8) {
+#define NVFP4_LAUNCH_MX(KER, D)                                                                  \
+  KER<D><<<(int)blocks, kGemmThreads, 0, s_stream>>>(                                              \
+      a, a_rows, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e,    \
+      (int)tiles_m, amap, seg)
+  if constexpr (WF == kWfMx4) {
+    static_assert(GATHER && !PACKED, "mxfp4 weights: gather_qmm, row-major");
+    if constexpr (RT == 8) {
+      if (dt == kF16)
+        NVFP4_LAUNCH_MX(mfma_gemm_mx4_kernel, kF16);
+      else
+        NVFP4_LAUNCH_MX(mfma_gemm_mx4_kernel, kBF16);
+    } else {
+      if (dt == kF16)
+        NVFP4_LAUNCH_MX(mfma_gemm_mx4_2_kernel, kF16);
+      else
+        NVFP4_LAUNCH_MX(mfma_gemm_mx4_2_kernel, kBF16);
+    }
+  } else if constexpr (RT == 8) {
     if (dt == kF16)
       NVFP4_LAUNCH(mfma_gemm_fast_kernel, kF16);
     else
@@ -1124,10 +1241,11 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
       NVFP4_LAUNCH(mfma_gemm_fast2_kernel, kBF16);
   }
 #undef NVFP4_LAUNCH
+#undef NVFP4_LAUNCH_MX
   return hipGetLastError();
 }
 
-template <bool GATHER, bool PACKED>
+template <bool GATHER, bool PACKED, int WF = kWfNv>
 hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc, const uint8_t* ws,
                        const float* gw, int64_t rows, int64_t n, int64_t k, void* out,
                        const int32_t* offsets, const int32_t* perm, int64_t top_k, int64_t e,
@@ -1140,8 +1258,8 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
   // tile count.  Both compute every output element in the same order.
   const int64_t tiles8 = ((rows + 255) / 256) * ((n + BN - 1) / BN);
   if (rows <= 128 || (!GATHER && tiles8 < device_cu_count()))
-    return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                             top_k, e, amap, 0, s);
+    return launch_fast_rt<GATHER, PACKED, 4, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets,
+                                                 perm, top_k, e, amap, 0, s);
   if constexpr (GATHER) {
     // each expert's whole 256-row tiles and any remainder of more than 128
     // rows on 256-row tiles, then the remainders of at most 128 rows on
@@ -1149,13 +1267,13 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
     // whole tile, while a remainder above 128 rows costs the same MFMA work
     // either way and, in the first launch, fills the last round of tiles
     // (same summation order for every output either way)
-    if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out,
-                                                           offsets, perm, top_k, e, amap, 1, s))
+    if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k,
+                                                               out, offsets, perm, top_k, e, amap, 1, s))
       return err;
-    return launch_fast_rt<GATHER, PACKED, 4>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
-                                             top_k, e, amap, 2, s);
+    return launch_fast_rt<GATHER, PACKED, 4, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets,
+                                                 perm, top_k, e, amap, 2, s);
   }
-  return launch_fast_rt<GATHER, PACKED, 8>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
+  return launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
                                            top_k, e, amap, 0, s);
 }
 
@@ -1261,6 +1379,46 @@ hipError_t launch_gather_gemm(const void* x, int dt, const uint8_t* wc, const ui
     mfma_gemm_kernel<kBF16, true><<<(int)blocks, kGemmThreads, 0, s>>>(
         x, wc, ws, gw, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, amap);
   return hipGetLastError();
+}
+
+namespace {
+
+template <int WF>
+hipError_t launch_mx_gather_wf(const void* x, int dt, const uint8_t* wc, const uint8_t* ws,
+                               const int32_t* offsets, const int32_t* perm, int64_t x_rows,
+                               int64_t rows, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                               void* out, hipStream_t s) {
+  if (dt == kF32) {
+    const int64_t blocks = ((rows + FT - 1) / FT + e) * ((n + FT - 1) / FT);
+    f32_gemm_kernel<true, false, WF><<<(int)blocks, 256, 0, s>>>(
+        reinterpret_cast<const float*>(x), wc, ws, nullptr, (int)rows, (int)n, (int)k,
+        reinterpret_cast<float*>(out), offsets, perm, (int)top_k, (int)e, nullptr);
+    return hipGetLastError();
+  }
+  if constexpr (WF == kWfMx4) {
+    if (k % BK == 0 && n % 4 == 0)
+      return launch_fast<true, false, kWfMx4>(dt, x, x_rows, wc, ws, nullptr, rows, n, k, out, offsets,
+                                              perm, top_k, e, nullptr, s);
+  }
+  const int64_t blocks = ((rows + BM - 1) / BM + e) * ((n + BN - 1) / BN);
+  if (dt == kF16)
+    mfma_gemm_kernel<kF16, true, WF><<<(int)blocks, kGemmThreads, 0, s>>>(
+        x, wc, ws, nullptr, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, nullptr);
+  else
+    mfma_gemm_kernel<kBF16, true, WF><<<(int)blocks, kGemmThreads, 0, s>>>(
+        x, wc, ws, nullptr, (int)rows, (int)n, (int)k, out, offsets, perm, (int)top_k, (int)e, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mx_gather_gemm(const void* x, int dt, int mode, const uint8_t* wc, const uint8_t* ws,
+                                 const int32_t* offsets, const int32_t* perm, int64_t x_rows,
+                                 int64_t rows, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                                 void* out, hipStream_t s) {
+  if (mode == 8)
+    return launch_mx_gather_wf<kWfMx8>(x, dt, wc, ws, offsets, perm, x_rows, rows, top_k, e, n, k, out, s);
+  return launch_mx_gather_wf<kWfMx4>(x, dt, wc, ws, offsets, perm, x_rows, rows, top_k, e, n, k, out, s);
 }
 
 }  // namespace nvfp4

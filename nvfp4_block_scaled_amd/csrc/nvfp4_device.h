@@ -385,10 +385,13 @@ __device__ __forceinline__ uint32_t e8m0_encode_up(float v) {
 }
 
 // 2^(b - 127) for b in 0..254 (2^-127 is the float32 subnormal 0x00400000),
-// NaN for 255.
+// NaN for 255: the bits b << 23, plus bit 22 for bytes 0 and 255 (those
+// with (b + 1) & 0xFF below 2).  Plain integer arithmetic, no compare: a
+// select on a just-loaded byte may be compiled into a branch, which the
+// hand-scheduled matrix-core loops must not contain.
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return b == 0u ? __uint_as_float(0x00400000u)
-                 : (b == 255u ? __uint_as_float(0x7FC00000u) : __uint_as_float(b << 23));
+  const uint32_t special = (((b + 1u) & 0xFFu) - 2u) >> 31;  // 1 for b = 0 and b = 255
+  return __uint_as_float((b << 23) | (special << 22));
 }
 
 // 1 / 2^(b - 127) = 2^(127 - b), exact, for b in 0..254.

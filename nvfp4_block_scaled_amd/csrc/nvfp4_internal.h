@@ -67,6 +67,13 @@ hipError_t launch_gather_gemm_t_f32(const float* x, const uint8_t* wc, const uin
                                    const float* gw, const int32_t* offsets, const int32_t* perm,
                                    int64_t rows, int64_t top_k, const int32_t* amap, int64_t e,
                                    int64_t n, int64_t k, float* out, hipStream_t s);
+// the same contraction (no x-row map) on row-major mx weights: mode 4 (mxfp4
+// codes [e, n, k/2]) or 8 (mxfp8 codes [e, n, k]), E8M0 scales [e, n, k/32],
+// k % 32 == 0
+hipError_t launch_mx_gather_gemm(const void* x, int dt, int mode, const uint8_t* wc, const uint8_t* ws,
+                                 const int32_t* offsets, const int32_t* perm, int64_t x_rows,
+                                 int64_t rows, int64_t top_k, int64_t e, int64_t n, int64_t k,
+                                 void* out, hipStream_t s);
 // the packed weight layout of the matrix-core path (gemm.hip, mfma_pack_kernel)
 constexpr int64_t kPackK = 64;             // k must be a multiple of this
 constexpr int64_t kPackCodeBytes = 1024;   // per 32-row tile and 64-wide k-step

@@ -547,9 +547,11 @@ static unsigned mx_code_at(const uint8_t* codes_row, int64_t i, int bits) {
  * ([DIFF-8] fp_quantize; [DIFF-7] fp_quantize_rowwise with use_mx_scale). */
 void orc_mx_quantize(const float* x, int64_t rows, int64_t k, int bits, uint8_t* codes,
                      uint8_t* scales) {
-  unsigned q[32];
   int64_t rb = mx_row_bytes(k, bits);
+  /* rows are independent: one thread per row at a time */
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
+    unsigned q[32];
     for (int64_t b = 0; b < k / 32; ++b) {
       scales[r * (k / 32) + b] = (uint8_t)mx_encode_group(x + r * k + b * 32, bits, q);
       uint8_t* out = codes + r * rb + (bits == 8 ? b * 32 : b * 16);

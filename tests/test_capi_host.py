@@ -380,3 +380,28 @@ def test_gather_indexed_errors(L):
     assert call(args(nb=need - 1)) == INV and "workspace" in err(L)
     assert call(args(e=2000)) == UNSUP
     assert call(args(dt=7)) == INV
+
+
+def test_mx_gather_qmm_errors(L):
+    ws = L.nvfp4_gather_qmm_workspace_size(10, 2, 4, 16, 64)
+    ok = (A, BF16, 4, W, B, 0x70000, 10, 2, 4, 16, 64, C, 0x60000, ws, None)
+    assert L.nvfp4_mx_gather_qmm(*ok) == UNSUP and "gfx950" in err(L)  # validation passed
+    for i, v, what in ((2, 6, "mx mode"), (1, 7, "dtype"), (10, 48, "group size 32"),
+                       (10, 0, "group size 32"), (13, ws - 4, "workspace"), (12, 0x60010, "aligned"),
+                       (5, None, "NULL"), (3, W + 8, "aligned"), (0, A + 8, "aligned"),
+                       (6, 0, "positive"), (9, 0, "positive")):
+        bad = list(ok)
+        bad[i] = v
+        assert L.nvfp4_mx_gather_qmm(*bad) == INV, (i, v)
+        assert "[mx_gather_qmm]" in err(L) and what in err(L), err(L)
+    bad = list(ok)
+    bad[8] = 2000
+    assert L.nvfp4_mx_gather_qmm(*bad) == UNSUP and "1024 experts" in err(L)
+    # one expert's mxfp8 codes of 2 GB or more (n * k bytes) are refused; the
+    # same sizes in mxfp4 (half the bytes) pass validation
+    gws = L.nvfp4_gather_qmm_workspace_size(64, 2, 8, 1 << 17, 1 << 14)
+    big = (A, BF16, 8, W, B, 0x70000, 64, 2, 8, 1 << 17, 1 << 14, C, 0x60000, gws, None)
+    assert L.nvfp4_mx_gather_qmm(*big) == UNSUP and "2 GB" in err(L)
+    big = list(big)
+    big[2] = 4
+    assert L.nvfp4_mx_gather_qmm(*big) == UNSUP and "gfx950" in err(L)

@@ -88,6 +88,34 @@ def doubly_grid(rows, cols, seed, scale=1.0, col_exponent_period=0):
     return (x * scale).contiguous()
 
 
+def mx_grid_tensor(rows, k, mode, seed, exps):
+    """float32 [rows, k] for the mx modes whose every group of 32 is stored
+    exactly: values on the element grid with +maxval and -maxval (6 for
+    mxfp4, 448 for mxfp8) at two distinct uniform positions of each group,
+    the group times 2^e, e cycled from `exps` over the groups in row order.
+    mxfp4 draws the other magnitudes from the e2m1 grid; mxfp8 from the e4m3
+    values in [64, 448] (the top three binades), which keeps every product
+    sum over a few hundred elements exact in float32."""
+    assert k % 32 == 0 and mode in ("mxfp4", "mxfp8")
+    g = _gen(seed)
+    if mode == "mxfp4":
+        levels, top = torch.tensor(E2M1_GRID[1:], dtype=torch.float32), 6.0
+    else:
+        levels = torch.tensor([(1 + m / 8) * 2.0 ** e for e in (6, 7, 8) for m in range(8)
+                               if (1 + m / 8) * 2.0 ** e <= 448.0], dtype=torch.float32)
+        top = 448.0
+    mags = levels[torch.randint(0, len(levels), (rows, k), generator=g)]
+    sign = torch.where(torch.rand(rows, k, generator=g) < 0.5, -1.0, 1.0)
+    x = (mags * sign).view(rows, k // 32, 32)
+    for r in range(rows):
+        for b in range(k // 32):
+            p = torch.randperm(32, generator=g)[:2]
+            x[r, b, p[0]] = top
+            x[r, b, p[1]] = -top
+            x[r, b] *= 2.0 ** exps[(r * (k // 32) + b) % len(exps)]
+    return x.view(rows, k).contiguous()
+
+
 def grid_case(name, seed=11):
     """The four exact-grid cases of osaurus-ai/mlx pull request 31 ("The test").
 
