@@ -496,6 +496,14 @@ def bench_gather(args, nv, torch, W):
     for e in range(E):
         nv.nvfp4_tensor_amax(w[e], out=g[e:e + 1])
         nv.nvfp4_quantize(w[e], g[e:e + 1], codes=wc[e], scales=wsc[e])
+    # the same experts in the mx modes (row-major, as nvfp4_mx_gather_qmm takes them)
+    mxw = {}
+    for mode, cb in (("mxfp4", Kk // 2), ("mxfp8", Kk)):
+        c = torch.empty(E, Nn, cb, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(E, Nn, Kk // 32, dtype=torch.uint8, device="cuda")
+        for e in range(E):
+            nv.nvfp4_mx_quantize(w[e], mode, codes=c[e], scales=sc[e])
+        mxw[mode] = (c, sc)
     del w
     # the experts' packed copy for the matrix-core kernel, made once (untimed)
     wp = nv.nvfp4_mfma_pack(wc, wsc)
@@ -509,8 +517,15 @@ def bench_gather(args, nv, torch, W):
     settle(gq_rm, 0.05)
     ms_rm = timed(gq_rm, max(3, args.steps // 4), 2)
     flop = 2.0 * T * top_k * Nn * Kk
+    mx = {}
+    for mode, (c, sc) in mxw.items():
+        call = lambda c=c, sc=sc, mode=mode: nv.nvfp4_mx_gather_qmm(x, c, sc, idx, mode, out=out,
+                                                                    workspace=wsp)
+        settle(call, 0.05)
+        ms_mx = timed(call, max(3, args.steps // 4), 2)
+        mx[mode] = dict(ms=ms_mx, tflops=flop / ms_mx / 1e9, frac=flop / ms_mx / 1e9 / PEAK_BF16_TFLOPS)
     return dict(ms=ms, tflops=flop / ms / 1e9, flop=flop, frac=flop / ms / 1e9 / PEAK_BF16_TFLOPS,
-                ms_rm=ms_rm, tflops_rm=flop / ms_rm / 1e9)
+                ms_rm=ms_rm, tflops_rm=flop / ms_rm / 1e9, mx=mx)
 
 
 def ceiling_lib():
@@ -730,6 +745,8 @@ def main():
         res["gather"] = bench_gather(args, nv, torch, W)
         log(f"  {res['gather']['ms']:.3f} ms, {res['gather']['tflops']:.1f} TFLOP/s (row-major weight "
             f"{res['gather']['ms_rm']:.3f} ms, {res['gather']['tflops_rm']:.1f} TFLOP/s)")
+        for mode, d in res["gather"]["mx"].items():
+            log(f"  {mode} weights: {d['ms']:.3f} ms, {d['tflops']:.1f} TFLOP/s")
 
     if args.only in ("all", "gather_ex"):
         log("gather_qmm indexed forms (transpose = False; sorted_indices) ...")
@@ -852,8 +869,12 @@ def main():
                               "frac": round(gq["frac"], 4), "ms": round(gq["ms"], 4),
                               "row_major_weight": {"value": round(gq["tflops_rm"], 2),
                                                    "ms": round(gq["ms_rm"], 4)},
+                              "mx_weights": {mode: {"value": round(d["tflops"], 2), "frac": round(d["frac"], 4),
+                                                    "ms": round(d["ms"], 4)}
+                                             for mode, d in gq["mx"].items()},
                               "workload": "4096 tokens x top-2 of 8 experts, NVFP4 w [8,14336,4096] "
-                                          "(packed once for the matrix cores)"}
+                                          "(packed once for the matrix cores); mx_weights: the same "
+                                          "experts in mxfp4 / mxfp8, row-major (nvfp4_mx_gather_qmm)"}
     if "gather_ex" in res:
         line["gather_qmm_indexed"] = {k_: {"value": round(v["tflops"], 2), "unit": "TFLOP/s",
                                            "frac": round(v["tflops"] / PEAK_BF16_TFLOPS, 4),

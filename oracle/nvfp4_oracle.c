@@ -61,7 +61,7 @@
  *       of the decoded values are summed without rounding either operand to
  *       T first (the pages hand both operands' codes and scales to a
  *       block-scaled product); only the sum is rounded to T.
- *   R24 gather_qmm in an mx mode: the routed product of R10 with the
+ *   R27 gather_qmm in an mx mode: the routed product of R10 with the
  *       expert's weight decoded as R22 (float32, exact), x used as given and
  *       no global scale (validate_global_scale admits none outside nvfp4);
  *       the pages' gather_qmm takes the same mode argument as the other
@@ -634,7 +634,7 @@ void orc_mx_qqmm_subset(const float* x, int dtype, int64_t m, int64_t k, int bit
 }
 
 /* gather_qmm in an mx mode on a subset of (token, slot) pairs and output
- * columns (reading R24): out[t, j, n] = T( sum_k x[t, k] * w_e[n, k] ),
+ * columns (reading R27): out[t, j, n] = T( sum_k x[t, k] * w_e[n, k] ),
  * e = idx[t, j], w_e the float32 decode of expert e's mx codes [e, n, row
  * bytes] and E8M0 scales [e, n, k/32] (R22); products summed in double, one
  * rounding to T.  A pair whose expert lies outside [0, e_count) multiplies
