@@ -1071,7 +1071,7 @@ MxLayout mx_layout(int mode, int64_t m, int64_t n, int64_t k, bool packed_w) {
 size_t nvfp4_mx_qqmm_workspace_size(nvfp4_mx_mode mode, int64_t m, int64_t n, int64_t k,
                                     int packed_w) {
   if (!mx_mode_ok(mode) || m <= 0 || n <= 0 || k <= 0 || k % 32 != 0) return 0;
-  if (!packed_w && nvfp4::mx_qmv_ok(m, n, k)) return 0;  // the matrix-vector kernel needs none
+  if (!packed_w && nvfp4::mx_qmv_ok(mode, m, n, k)) return 0;  // the matrix-vector kernel needs none
   return mx_layout(mode, m, n, k, packed_w != 0).total;
 }
 
@@ -1110,11 +1110,11 @@ nvfp4_status nvfp4_mx_qqmm(const void* x, nvfp4_dtype dt, nvfp4_mx_mode mode,
   if (nvfp4_status st =
           mx_qqmm_common(op, x, dt, mode, w_codes, w_scales, m, n, k, out, workspace, workspace_bytes))
     return st;
-  const bool qmv = nvfp4::mx_qmv_ok(m, n, k);  // one row of x: the streaming matrix-vector kernel
+  const bool qmv = nvfp4::mx_qmv_ok(mode, m, n, k);  // one row of x: the streaming matrix-vector kernel
   const MxLayout l = mx_layout(mode, m, n, k, false);
   if (nvfp4_status st = mx_workspace_ok(op, workspace, workspace_bytes, qmv ? 0 : l.total)) return st;
   if (nvfp4_status st = check_device(op, stream)) return st;
-  if (qmv) return launched(op, nvfp4::launch_mx_qmv(x, dt, mode, w_codes, w_scales, n, out, stream));
+  if (qmv) return launched(op, nvfp4::launch_mx_qmv(x, dt, mode, w_codes, w_scales, n, k, out, stream));
   uint8_t* base = reinterpret_cast<uint8_t*>(workspace);
   hipError_t e = nvfp4::launch_mx_pack(w_codes, w_scales, mode, n, k, base + l.wc, base + l.ws, stream);
   if (e == hipSuccess)

@@ -131,11 +131,12 @@ hipError_t launch_mx_quantize_packed(const void* x, int dt, int bits, int64_t ro
 hipError_t launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int bits, int64_t rows,
                           int64_t k, uint8_t* pc, uint8_t* ps, hipStream_t s);
 // y [m, n] of type dt from the packed x (m rows) and w (n rows); the packed
-// mx_qmv.hip: qqmm in an mx mode (4 or 8) with one row of x, k = 4096,
-// row-major weight codes [n, k * mode / 8] and scales [n, k / 32]
-bool mx_qmv_ok(int64_t m, int64_t n, int64_t k);
+// mx_qmv.hip: qqmm in an mx mode (4 or 8) with one row of x, k % 32 == 0 and
+// at most 8 KB of codes per row, row-major weight codes [n, k * mode / 8] and
+// scales [n, k / 32]
+bool mx_qmv_ok(int mode, int64_t m, int64_t n, int64_t k);
 hipError_t launch_mx_qmv(const void* x, int dt, int mode, const uint8_t* wc, const uint8_t* ws,
-                         int64_t n, void* out, hipStream_t s);
+                         int64_t n, int64_t k, void* out, hipStream_t s);
 // operands must be below kMxMaxPackedBytes
 constexpr size_t kMxMaxPackedBytes = 0x7F000000u;
 hipError_t launch_mx_gemm(const uint8_t* xpc, const uint8_t* xps, const uint8_t* wpc,

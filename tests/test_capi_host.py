@@ -264,11 +264,18 @@ def test_mx_argument_errors(L):
     assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 0, 520, 192, G, W, need, None) == INV
     assert L.nvfp4_mx_qqmm(A, BF16, 4, None, C, 300, 520, 192, G, W, need, None) == INV
     assert L.nvfp4_mx_qqmm(A, BF16, 4, B, C, 300, 520, 192, G, W, need, None) == UNSUP
-    # one row of x at k = 4096: the matrix-vector kernel, no workspace (NULL accepted)
+    # one row of x with up to 8 KB of codes per row: the matrix-vector kernel,
+    # no workspace (NULL accepted); longer rows take the matrix-core kernel
     assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 14336, 4096, 0) == 0
     assert L.nvfp4_mx_qqmm_workspace_size(8, 1, 14336, 4096, 0) == 0
     assert L.nvfp4_mx_qqmm_workspace_size(8, 1, 14336, 4096, 1) > 0
-    assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 300, 2048, 0) > 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 300, 2048, 0) == 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 300, 32, 0) == 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 300, 16384, 0) == 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 1, 300, 16416, 0) > 0
+    assert L.nvfp4_mx_qqmm_workspace_size(8, 1, 300, 8192, 0) == 0
+    assert L.nvfp4_mx_qqmm_workspace_size(8, 1, 300, 8224, 0) > 0
+    assert L.nvfp4_mx_qqmm_workspace_size(4, 2, 300, 2048, 0) > 0
     assert L.nvfp4_mx_qqmm(A, BF16, 8, B, C, 1, 14336, 4096, G, None, 0, None) == UNSUP
     need_p8 = L.nvfp4_mx_qqmm_workspace_size(8, 300, 520, 192, 1)
     assert need_p8 > need_p  # mxfp8 codes take twice the bytes

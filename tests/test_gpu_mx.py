@@ -9,12 +9,13 @@ import torch
 
 import nvfp4_block_scaled_amd as nv
 import workloads as W
-from _parity import (O, assert_bytes_equal, assert_close, assert_values_equal, dev, host,
+from _parity import (O, assert_bytes_equal, assert_close, assert_values_equal, dev, guarded, host,
                      oracle_dtype, say)
 
 pytestmark = pytest.mark.gpu
 
 MODES = ["mxfp4", "mxfp8"]
+MX_BITS = {"mxfp4": 4, "mxfp8": 8}
 MAXVAL = {"mxfp4": 6.0, "mxfp8": 448.0}
 E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
 # the product accumulates exact float32 products in float32: apart from the
@@ -202,6 +203,10 @@ def test_mx_qqmm_general(mode, dtype, m, n, k):
     ref = O.mx_qqmm(host(x), oc, os_, mode, dtype=od)
     fro, _ = assert_close(host(y), ref, what=f"mx qqmm {mode}")
     assert fro <= MX_FRO_GUARD
+    if m == 1:  # the row-major call takes the matrix-vector kernel (another summation order)
+        fro, _ = assert_close(host(yp), ref, what=f"mx qqmm packed {mode}")
+        assert fro <= MX_FRO_GUARD
+        return
     assert torch.equal(y.view(torch.uint8) if dtype == torch.float32 else y.view(torch.int16),
                        yp.view(torch.uint8) if dtype == torch.float32 else yp.view(torch.int16))
 
@@ -214,13 +219,32 @@ def test_mx_qmv_exact_on_grid_operands(mode, dtype, n):
     round-trip exactly and every partial sum is exact in float32 (mxfp8: x
     nonzero in 8 groups only, so that the sum stays within 24 bits), so the
     product equals the float64 product rounded once."""
-    say(f"mx qmv grid {mode} {dtype} n={n}")
-    x = _grid(1, 4096, mode, 41, [0, -1])
-    if mode == "mxfp8":
-        keep = np.zeros(128, bool)
-        keep[np.random.default_rng(42).choice(128, 8, replace=False)] = True
-        x = (x.reshape(1, 128, 32) * keep[None, :, None]).reshape(1, 4096).astype(np.float32)
-    w = _grid(n, 4096, mode, 43, [-2, -1])
+    _qmv_grid(mode, dtype, n, 4096)
+
+
+# (mode, k) for the matrix-vector kernel's row lengths: one piece of 16 bytes
+# per lane or fewer (k = 32), a partial second, third or fifth 1 KB load per
+# row, and the longest rows it takes (8 KB of codes)
+QMV_K = [("mxfp4", 32), ("mxfp4", 2080), ("mxfp4", 6144), ("mxfp4", 16384),
+         ("mxfp8", 32), ("mxfp8", 1056), ("mxfp8", 5120), ("mxfp8", 8192)]
+
+
+@pytest.mark.parametrize("mode,k", QMV_K)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_mx_qmv_exact_on_grid_operands_any_k(mode, k, dtype):
+    """The matrix-vector kernel at other row lengths, as above."""
+    _qmv_grid(mode, dtype, 300, k)
+
+
+def _qmv_grid(mode, dtype, n, k):
+    say(f"mx qmv grid {mode} {dtype} n={n} k={k}")
+    g = k // 32
+    x = _grid(1, k, mode, 41, [0, -1])
+    if mode == "mxfp8" or k > 4096:
+        keep = np.zeros(g, bool)
+        keep[np.random.default_rng(42).choice(g, min(g, 8), replace=False)] = True
+        x = (x.reshape(1, g, 32) * keep[None, :, None]).reshape(1, k).astype(np.float32)
+    w = _grid(n, k, mode, 43, [-2, -1])
     oc, os_ = O.mx_quantize(w, mode)
     y = nv.nvfp4_mx_qqmm(torch.from_numpy(x).to(dtype).cuda(), dev(oc), dev(os_), mode)
     torch.cuda.synchronize()
@@ -228,6 +252,27 @@ def test_mx_qmv_exact_on_grid_operands(mode, dtype, n):
     exact = x.astype(np.float64) @ w.astype(np.float64).T
     ref = np.array([[O.round_to(float(v), od) for v in row] for row in exact], np.float32)
     assert_values_equal(host(y), ref, f"mx qmv grid {dtype}")
+
+
+@pytest.mark.parametrize("mode,k", QMV_K)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_mx_qmv_general_any_k(mode, k, dtype):
+    """General data at the kernel's other row lengths, n = 1000, with guard
+    bands around the output."""
+    say(f"mx qmv {mode} {dtype} k={k}")
+    od = oracle_dtype(dtype)
+    n = 1000
+    x = W.normal((1, k), 1.0, 560 + k, od)
+    w = W.normal((n, k), 0.02, 561 + k, od)
+    oc, os_ = O.mx_quantize(host(w), mode)
+    out = guarded((1, n), dtype)
+    assert nv.load_library().nvfp4_mx_qqmm_workspace_size(MX_BITS[mode], 1, n, k, 0) == 0
+    nv.nvfp4_mx_qqmm(x.cuda(), dev(oc), dev(os_), mode, out=out.t)
+    torch.cuda.synchronize()
+    out.check("mx qmv out")
+    ref = O.mx_qqmm(host(x), oc, os_, mode, dtype=od)
+    fro, _ = assert_close(host(out.t), ref, what=f"mx qmv {mode} k={k}")
+    assert fro <= MX_FRO_GUARD
 
 
 @pytest.mark.parametrize("mode", MODES)
