@@ -334,3 +334,23 @@ def test_mlx_style_names_dispatch_the_mx_modes(mode):
     assert torch.equal(y, y2)
     with pytest.raises(ValueError):
         nv.quantize(w, mode=mode, global_scale=torch.ones(1, device="cuda"))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mx_dequantize_every_scale_byte(mode):
+    """Every E8M0 byte 0..255 as a block scale (byte 0: 2^-127, a float32
+    subnormal; 255: NaN) over every code value, decoded to float32 on the
+    device and by the oracle: the same values, NaN where the oracle's are."""
+    say(f"mx dequantize, every scale byte, {mode}")
+    rng = np.random.default_rng(77)
+    scales = np.arange(256, dtype=np.uint8).reshape(8, 32)  # 8 rows of 32 groups
+    k = 32 * 32
+    cb = k // 2 if mode == "mxfp4" else k
+    codes = rng.integers(0, 256, (8, cb), dtype=np.uint8)
+    if mode == "mxfp8":  # the codes 0..255 in turn: each of them under 32 scale bytes
+        codes[:, :] = np.resize(np.arange(256, dtype=np.uint8), cb)
+    got = nv.nvfp4_mx_dequantize(dev(codes), dev(scales), mode, dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.mx_dequantize(codes, scales, mode, "f32")
+    assert_values_equal(host(got), ref, f"mx dequantize every scale byte {mode}")
+    assert np.isnan(ref[7, 31 * 32:]).all()  # byte 255
