@@ -144,12 +144,14 @@ def _pct(v, q):
 
 
 def timed_stats(fn, iters, warmup, graph=False, reps=9):
-    """Per-call milliseconds: `mean` over all timed calls, and the median, p10
-    and p90 of the per-call times.  Eager: one HIP event between consecutive
-    calls on the launch stream, so the calls run back to back exactly as in
-    timed().  Graph: `reps` replays of one captured graph of `iters` calls,
-    each replay timed; the spread is then that of the per-call means of the
-    replays."""
+    """Per-call milliseconds: `mean`, and the median, p10 and p90 of per-call
+    means.  Eager: `mean` is that of `iters` calls run back to back between
+    two HIP events on the launch stream, as in timed(); the spread comes from
+    `reps` further passes of `iters` calls, each pass between two events (an
+    event recorded between single calls leaves the GPU idle for about 6 us on
+    this runtime, so per-call events would inflate every call).  Graph:
+    `reps` replays of one captured graph of `iters` calls, each replay timed;
+    `mean` over all replays, the spread over the replays' per-call means."""
     import torch
     for _ in range(warmup):
         fn()
@@ -175,14 +177,21 @@ def timed_stats(fn, iters, warmup, graph=False, reps=9):
         per = [ev[r].elapsed_time(ev[r + 1]) / iters for r in range(reps)]
         mean = ev[0].elapsed_time(ev[-1]) / (iters * reps)
     else:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
-        ev[0].record()
-        for i in range(iters):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(iters):
             fn()
-            ev[i + 1].record()
+        end.record()
+        end.synchronize()
+        mean = start.elapsed_time(end) / iters
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for r in range(reps):
+            for _ in range(iters):
+                fn()
+            ev[r + 1].record()
         ev[-1].synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
-        mean = ev[0].elapsed_time(ev[-1]) / iters
+        per = [ev[r].elapsed_time(ev[r + 1]) / iters for r in range(reps)]
     return dict(mean=mean, median=_pct(per, 0.5), p10=_pct(per, 0.1), p90=_pct(per, 0.9), n=len(per))
 
 
