@@ -160,7 +160,7 @@ def test_small_no_global_scales_and_zero_rows():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 9, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 9, 16])
 @pytest.mark.parametrize("k", [2048, 4096])
 def test_k4096_grid_bit_exact_row_major_and_packed(dtype, m, k):
     """k = 2048 / 4096, the decode's width: exact-grid x [m, k] and w [300, k]
@@ -187,8 +187,8 @@ def test_k4096_grid_bit_exact_row_major_and_packed(dtype, m, k):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("m,n", [(1, 1000), (2, 33), (2, 2049), (3, 300), (5, 14336), (8, 4100), (12, 300),
-                                 (16, 14336)])
+@pytest.mark.parametrize("m,n", [(1, 1000), (2, 33), (2, 2049), (3, 300), (4, 33), (4, 14336), (5, 14336),
+                                 (8, 4100), (12, 300), (16, 14336)])
 def test_k4096_general(dtype, m, n):
     """General data at k = 4096 over ragged n: qqmm and qmm against the
     oracle, row-major and packed; qqmm equals qmm on the separately computed
