@@ -454,11 +454,13 @@ __device__ __forceinline__ void mfma32_fence() {
 template <int RT>
 __device__ __forceinline__ void a_stage_barrier() {
   static_assert(kBLoadsPerStep == 4, "the wait counts below count 4 weight loads per step");
-  static_assert(RT == 8 || RT == 4, "the wait counts below count RT loads of A per step");
+  static_assert(RT == 8 || RT == 4 || RT == 2, "the wait counts below count RT loads of A per step");
   if constexpr (RT == 8)
     asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else
+  else if constexpr (RT == 4)
     asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
 }
 
 // Raw weights of one k-step for one lane: for each of its 2 column tiles, the
@@ -472,8 +474,9 @@ struct BRaw {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // RT = 32-row tiles per workgroup: 8 (256 rows, 256 accumulators per wave, one
-// workgroup per CU) or 4 (128 rows, 128 accumulators per wave, two workgroups
-// per CU, so that each SIMD interleaves two waves' instruction streams).
+// workgroup per CU), 4 (128 rows, 128 accumulators per wave, two workgroups
+// per CU, so that each SIMD interleaves two waves' instruction streams) or 2
+// (64 rows, 64 accumulators per wave: the gather's per-expert remainders).
 template <int DT, bool GATHER, bool PACKED, int RT, int WF = kWfNv>
 __device__ __forceinline__ void
 mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
@@ -508,7 +511,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   if constexpr (GATHER) {
     // seg 0: all of each expert's rows; 1: its whole 256-row tiles, plus a
     // remainder of more than 128 rows on one more (partial) 256-row tile; 2:
-    // a remainder of at most 128 rows, on one 128-row tile
+    // a remainder of at most 128 rows, on one 128-row or up to two 64-row tiles
     int acc_tiles = 0;
     expert = -1;
     for (int e = 0; e < E; ++e) {
@@ -700,7 +703,7 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
         if (q3 < NQ)
           ar[q3 & 3] = *reinterpret_cast<const V8*>(la + a_rd[q3 / RT] + (q3 % RT) * 4096);
         else
-          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd[0] + (q3 - NQ) * 4096);
+          ar[q3 & 3] = *reinterpret_cast<const V8*>(ln + a_rd[(q3 - NQ) / RT] + ((q3 - NQ) % RT) * 4096);
       }
       // decode: dword d of step kt + 1's 32 is column tile d / 16, sub-step
       // (d / 4) % 4, dword d % 4; DPQ of them ride on each fragment pair
@@ -778,6 +781,16 @@ mfma_gemm_fast_body(const void* __restrict__ a_base, int64_t a_rows,
   if (kt + 1 < KT) step(P1{}, kt + 1);
   if (kt + 2 < KT) step(P2{}, kt + 2);
   mfma32_fence();
+  // the fence carries no data dependence on the accumulators, so the
+  // compiler may place their reads (copies to VGPRs) ahead of it; tying
+  // each one to an asm after the fence keeps every read behind the wait
+  // states (64-row tiles: with few registers in use the copies went to the
+  // top of the epilogue, straight after the last MFMAs of a k-step count
+  // of 3 mod 4, and read two accumulators before those MFMAs wrote them)
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < RT; ++i) asm volatile("" : "+a"(acc[t][i]));
 
   // ---------------------------------------------------------------- epilogue
   // acc[t][i][v]: tile row 32 i + fr, tile column 64 w + 32 t + 8 (v / 4) +
@@ -851,6 +864,15 @@ template <int DT, bool GATHER, bool PACKED>
 __global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mfma_gemm_fast2_kernel(NVFP4_FAST_ARGS) {
   mfma_gemm_fast_body<DT, GATHER, PACKED, 4>(NVFP4_FAST_PASS);
+}
+
+// 64-row tiles: the remainders of at most 128 routed rows per expert that
+// gather_qmm leaves after its 256-row tiles (a 128-row tile for a remainder
+// of a few dozen rows would multiply mostly padding)
+template <int DT, bool GATHER, bool PACKED>
+__global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mfma_gemm_fast4_kernel(NVFP4_FAST_ARGS) {
+  mfma_gemm_fast_body<DT, GATHER, PACKED, 2>(NVFP4_FAST_PASS);
 }
 
 // the same two tilings for gather_qmm on row-major mxfp4 weights
@@ -1205,7 +1227,7 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
   // tile rows: an upper bound for the gather (per-expert counts live on the
   // device; surplus workgroups return at once)
   const int64_t tiles_m = seg == 1 ? rows / 256 + std::min<int64_t>(e, rows / 129)
-                        : seg == 2 ? e
+                        : seg == 2 ? e * ((128 + TM - 1) / TM)
                                    : (rows + TM - 1) / TM + (GATHER ? e : 0);
   const int64_t blocks = tiles_m * ((n + BN - 1) / BN);
 #define NVFP4_LAUNCH(KER, D)                                                                     \
@@ -1234,6 +1256,11 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
       NVFP4_LAUNCH(mfma_gemm_fast_kernel, kF16);
     else
       NVFP4_LAUNCH(mfma_gemm_fast_kernel, kBF16);
+  } else if constexpr (RT == 2) {
+    if (dt == kF16)
+      NVFP4_LAUNCH(mfma_gemm_fast4_kernel, kF16);
+    else
+      NVFP4_LAUNCH(mfma_gemm_fast4_kernel, kBF16);
   } else {
     if (dt == kF16)
       NVFP4_LAUNCH(mfma_gemm_fast2_kernel, kF16);
@@ -1267,11 +1294,15 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
     // whole tile, while a remainder above 128 rows costs the same MFMA work
     // either way and, in the first launch, fills the last round of tiles
     // (same summation order for every output either way)
+    // (NVFP4 weights: the remainders on 64-row tiles, one or two per expert;
+    // at the MoE shape they are a few dozen rows for some experts and the
+    // 128-row tiles left this launch mostly multiplying padding)
     if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k,
                                                                out, offsets, perm, top_k, e, amap, 1, s))
       return err;
-    return launch_fast_rt<GATHER, PACKED, 4, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets,
-                                                 perm, top_k, e, amap, 2, s);
+    constexpr int kTailRT = WF == kWfNv ? 2 : 4;
+    return launch_fast_rt<GATHER, PACKED, kTailRT, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out,
+                                                       offsets, perm, top_k, e, amap, 2, s);
   }
   return launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
                                            top_k, e, amap, 0, s);

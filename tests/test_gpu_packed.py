@@ -137,3 +137,33 @@ def test_qqmm_packed_prefill_2048x14336x4096_equals_row_major():
     got = host(y)[rows][:, cols]
     fro, _ = assert_close(got, ref, what="qqmm packed prefill")
     assert fro <= MFMA_FRO_GUARD
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_gather_tail_remainders(dtype):
+    """Per-expert row counts whose remainders past the 256-row tiles are 1,
+    63, 64, 65, 127, 128, 100 and 200 rows, plus an expert with none: the
+    remainders of at most 128 rows run on one or two 64-row tiles, 200 on a
+    partial 256-row tile.  Every output against the oracle, and the packed
+    weight bit for bit against the row-major one."""
+    counts = [257, 319, 64, 65, 127, 128, 0, 612, 456]
+    E, N, K = len(counts), 320, 256
+    T = sum(counts)
+    say(f"gather_qmm tail remainders {dtype} E={E} T={T} N={N} K={K}")
+    od = oracle_dtype(dtype)
+    labels = np.repeat(np.arange(E, dtype=np.int32), counts)
+    np.random.default_rng(240).shuffle(labels)
+    idx = torch.from_numpy(labels.reshape(T, 1).copy())
+    x = W.normal((T, K), 1.0, 241, od)
+    w = W.normal((E, N, K), 0.02, 242, od)
+    gs = np.array([O.tensor_amax(host(w[e])) for e in range(E)], np.float32)
+    codes = np.stack([O.quantize(host(w[e]), float(gs[e]))[0] for e in range(E)])
+    scales = np.stack([O.quantize(host(w[e]), float(gs[e]))[1] for e in range(E)])
+    packed = nv.nvfp4_mfma_pack(dev(codes), dev(scales))
+    y = nv.nvfp4_gather_qmm_packed(x.cuda(), packed, idx.cuda(), dev(gs))
+    y_rm = nv.nvfp4_gather_qmm(x.cuda(), dev(codes), dev(scales), idx.cuda(), dev(gs))
+    torch.cuda.synchronize()
+    ref = O.gather_qmm(host(x), codes, scales, idx.numpy(), gs, dtype=od)
+    fro, _ = assert_close(host(y_rm), ref, what="gather tails row-major")
+    assert fro <= MFMA_FRO_GUARD
+    assert torch.equal(y.view(torch.int16), y_rm.view(torch.int16))

@@ -130,17 +130,19 @@ def mx_asm(tmp_path_factory):
 
 
 def test_fast_gemm_stage_waits_cover_the_next_stage(gemm_asm):
-    """Every 256-row (vmcnt 16) and 128-row (vmcnt 12) fast-kernel instance:
-    NVFP4 row-major and packed, gather and not, bf16 and f16, and mxfp4."""
-    ks = _kernels(gemm_asm, r"mfma_gemm_(fast|fast2|mx4|mx4_2)_kernel")
-    assert len(ks) >= 12, sorted(ks)
+    """Every 256-row (vmcnt 16), 128-row (vmcnt 12) and 64-row (vmcnt 10)
+    fast-kernel instance: NVFP4 row-major and packed, gather and not, bf16
+    and f16, and mxfp4."""
+    ks = _kernels(gemm_asm, r"mfma_gemm_(fast|fast2|fast4|mx4|mx4_2)_kernel")
+    assert len(ks) >= 16, sorted(ks)
+    assert any("fast4" in name for name in ks), sorted(ks)
     for name, body in ks.items():
-        two = "fast2" in name or "mx4_2" in name
+        wait = 10 if "fast4" in name else 12 if ("fast2" in name or "mx4_2" in name) else 16
         seq = _linearize(body)
-        checked = _replay(seq, 12 if two else 16, lag=1)
+        checked = _replay(seq, wait, lag=1)
         assert checked >= 8, (name, checked)
         with pytest.raises(AssertionError):  # A of the step after next is in flight
-            _replay(seq, 12 if two else 16, lag=0)
+            _replay(seq, wait, lag=0)
 
 
 def test_mx_gemm_stage_waits_cover_the_next_stage(mx_asm):
@@ -156,3 +158,27 @@ def test_mx_gemm_stage_waits_cover_the_next_stage(mx_asm):
         assert checked >= 8, (name, checked)
         with pytest.raises(AssertionError):
             _replay(seq, wait, lag=ns - 3)
+
+
+def test_fast_gemm_accumulators_read_after_the_final_fence(gemm_asm):
+    """The pinned-accumulator MFMAs are inline asm, so the compiler does not
+    know that their results land only after several dozen cycles; the fixed
+    s_nop fence after the k loop supplies the wait.  The fence carries no
+    data dependence on the accumulators, so without the empty asm that ties
+    each one to a point after it, the compiler may copy them out of the AGPRs
+    ahead of the fence: the 64-row tiles did, straight after the last MFMAs
+    of the post-loop step taken when the k-step count is 3 mod 4, and read
+    two accumulators before their last products landed.  Check every
+    instance: no accumulator read in the code laid out just ahead of the
+    final fence (the epilogue's reads follow it)."""
+    ks = _kernels(gemm_asm, r"mfma_gemm_(fast|fast2|fast4|mx4|mx4_2)_kernel")
+    assert any("fast4" in name for name in ks), sorted(ks)
+    for name, body in ks.items():
+        nops = [i for i, ln in enumerate(body) if re.match(r"^\s*s_nop 7\b", ln)]
+        assert len(nops) >= 16, (name, len(nops))  # the fences before and after the loop
+        fence = nops[-1]
+        window = body[max(0, fence - 400):fence]
+        early = [ln.strip() for ln in window if re.match(r"^\s*v_accvgpr_read", ln)]
+        assert not early, (name, early[:4])
+        after = [ln for ln in body[fence:] if re.match(r"^\s*v_accvgpr_read", ln)]
+        assert len(after) >= 64, (name, len(after))
