@@ -173,12 +173,23 @@ def test_fast_gemm_accumulators_read_after_the_final_fence(gemm_asm):
     final fence (the epilogue's reads follow it)."""
     ks = _kernels(gemm_asm, r"mfma_gemm_(fast|fast2|fast4|mx4|mx4_2)_kernel")
     assert any("fast4" in name for name in ks), sorted(ks)
+    mfma_dst = re.compile(r"^\s*v_mfma\w*\s+a\[(\d+):(\d+)\]")
+    acc_read = re.compile(r"^\s*v_accvgpr_read_b32\s+v\d+,\s*a(\d+)\b")
     for name, body in ks.items():
+        # the accumulators: the AGPRs the MFMAs write (others may hold spilled values)
+        accs = set()
+        for ln in body:
+            m = mfma_dst.match(ln)
+            if m:
+                accs.update(range(int(m.group(1)), int(m.group(2)) + 1))
+        assert len(accs) >= 64, (name, len(accs))
         nops = [i for i, ln in enumerate(body) if re.match(r"^\s*s_nop 7\b", ln)]
         assert len(nops) >= 16, (name, len(nops))  # the fences before and after the loop
         fence = nops[-1]
-        window = body[max(0, fence - 400):fence]
-        early = [ln.strip() for ln in window if re.match(r"^\s*v_accvgpr_read", ln)]
+
+        def reads(lines):
+            return [ln.strip() for ln in lines
+                    if acc_read.match(ln) and int(acc_read.match(ln).group(1)) in accs]
+        early = reads(body[max(0, fence - 400):fence])
         assert not early, (name, early[:4])
-        after = [ln for ln in body[fence:] if re.match(r"^\s*v_accvgpr_read", ln)]
-        assert len(after) >= 64, (name, len(after))
+        assert len(reads(body[fence:])) >= len(accs), name
