@@ -164,13 +164,18 @@ def test_qqmm_every_k_step_count(dtype, ksteps):
     assert fro <= MFMA_FRO_GUARD
 
 
-@pytest.mark.parametrize("ksteps", [3, 5, 7])
+@pytest.mark.parametrize("ksteps", [1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_gather_qmm_k_step_counts(ksteps):
+    """One to nine 64-wide k-steps (the main loop takes four at a time, then a
+    tail of up to three).  Expert 0 gets 114 rows, all of them a remainder on
+    two 64-row tiles, the others a partial 256-row tile each; at 3 and 7
+    k-steps the 64-row tiles once read two of their accumulators before the
+    last products landed."""
     E, T, N, K, top_k = 3, 200, 260, 64 * ksteps, 2
     say(f"gather_qmm k-steps {T}x{top_k} E={E} N={N} K={K}")
     x = W.normal((T, K), 1.0, 80 + ksteps, "bf16")
     w = W.normal((E, N, K), 0.02, 90 + ksteps, "bf16")
-    idx = W.expert_indices(T, E, top_k, seed=100 + ksteps)
+    idx = W.expert_indices(T, E, top_k, seed=103)  # loads 114 / 150 / 136
     gs = np.array([O.tensor_amax(host(w[e])) for e in range(E)], np.float32)
     codes = np.stack([O.quantize(host(w[e]), float(gs[e]))[0] for e in range(E)])
     scales = np.stack([O.quantize(host(w[e]), float(gs[e]))[1] for e in range(E)])
