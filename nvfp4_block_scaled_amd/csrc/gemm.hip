@@ -16,8 +16,8 @@
 //     weights decoded in registers, A staged through LDS; it reads the weight
 //     either row-major or in the packed layout of mfma_pack_kernel (details
 //     at the kernel body);
-//     (mfma_gemm_mx4_kernel / mfma_gemm_mx4_2_kernel / mfma_gemm_mx4_4_kernel
-//     run the same body on row-major mxfp4 weights);
+//     (mfma_gemm_mx4_kernel / mfma_gemm_mx4_2_kernel run the same body on
+//     row-major mxfp4 weights);
 //   * mfma_gemm_kernel (16-bit x, any k % 16 == 0): the general matrix-core
 //     path on v_mfma_f32_16x16x32, 256 x 256 x 64 tiles with both A and the
 //     decoded weight tile (written by the VALU) in double-buffered LDS;
@@ -886,11 +886,6 @@ __global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_p
 mfma_gemm_mx4_2_kernel(NVFP4_FAST_ARGS) {
   mfma_gemm_fast_body<DT, true, false, 4, kWfMx4>(NVFP4_FAST_PASS);
 }
-template <int DT>
-__global__ void __launch_bounds__(kGemmThreads, 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
-mfma_gemm_mx4_4_kernel(NVFP4_FAST_ARGS) {
-  mfma_gemm_fast_body<DT, true, false, 2, kWfMx4>(NVFP4_FAST_PASS);
-}
 
 // ------------------------------------------------------------------ packed weight layout
 //
@@ -1250,11 +1245,6 @@ hipError_t launch_fast_rt(int dt, const void* a, int64_t a_rows, const uint8_t* 
         NVFP4_LAUNCH_MX(mfma_gemm_mx4_kernel, kF16);
       else
         NVFP4_LAUNCH_MX(mfma_gemm_mx4_kernel, kBF16);
-    } else if constexpr (RT == 2) {
-      if (dt == kF16)
-        NVFP4_LAUNCH_MX(mfma_gemm_mx4_4_kernel, kF16);
-      else
-        NVFP4_LAUNCH_MX(mfma_gemm_mx4_4_kernel, kBF16);
     } else {
       if (dt == kF16)
         NVFP4_LAUNCH_MX(mfma_gemm_mx4_2_kernel, kF16);
@@ -1304,14 +1294,15 @@ hipError_t launch_fast(int dt, const void* a, int64_t a_rows, const uint8_t* wc,
     // whole tile, while a remainder above 128 rows costs the same MFMA work
     // either way and, in the first launch, fills the last round of tiles
     // (same summation order for every output either way)
-    // (the remainders on 64-row tiles, one or two per expert; at the MoE
-    // shape they are a few dozen rows for some experts and the 128-row tiles
-    // left this launch mostly multiplying padding)
+    // (NVFP4 weights: the remainders on 64-row tiles, one or two per expert;
+    // at the MoE shape they are a few dozen rows for some experts and the
+    // 128-row tiles left this launch mostly multiplying padding)
     if (hipError_t err = launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k,
                                                                out, offsets, perm, top_k, e, amap, 1, s))
       return err;
-    return launch_fast_rt<GATHER, PACKED, 2, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets,
-                                                 perm, top_k, e, amap, 2, s);
+    constexpr int kTailRT = WF == kWfNv ? 2 : 4;
+    return launch_fast_rt<GATHER, PACKED, kTailRT, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out,
+                                                       offsets, perm, top_k, e, amap, 2, s);
   }
   return launch_fast_rt<GATHER, PACKED, 8, WF>(dt, a, a_rows, wc, ws, gw, rows, n, k, out, offsets, perm,
                                            top_k, e, amap, 0, s);
