@@ -1065,11 +1065,12 @@ f32_gemm_kernel(const float* __restrict__ A, const uint8_t* __restrict__ wc,
 //
 // Routing sorts the routed rows by expert, stably (ascending row id within an
 // expert): row q of the entries * mr rows goes to expert idx[q / mr].  It is a
-// counting sort in three launches over chunks of rows (a multiple of 1024
-// rows, at most kRouteMaxChunks chunks):
+// counting sort over chunks of rows (a multiple of 1024 rows, at most
+// kRouteMaxChunks chunks), in three launches or, for small count tables, two:
 //   count    one workgroup per chunk: the chunk's per-expert counts;
 //   scan     one workgroup: offsets[x], the exclusive prefix of the experts'
-//            totals, and each chunk's first slot per expert;
+//            totals, and each chunk's first slot per expert (for small count
+//            tables every scatter workgroup does this itself);
 //   scatter  one workgroup per chunk, in steps of 1024 rows: a row's slot is
 //            its expert's running slot, plus the same-expert rows of earlier
 //            waves of the step, plus its rank among the same-expert lanes of
@@ -1126,6 +1127,29 @@ route_count_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int
   for (int x = tid; x <= E; x += kRouteThreads) counts[blockIdx.x * (E + 1) + x] = hist[x];
 }
 
+// Exclusive prefix over buckets 0 .. E, in place: tot[x] (the buckets'
+// totals, zero past E) becomes the first slot of bucket x.  Thread t holds
+// buckets 2t and 2t + 1; part is scratch.  Every thread of the workgroup calls
+// it.
+__device__ __forceinline__ void route_bucket_prefix(int* tot, int* part) {
+  const int tid = threadIdx.x;
+  const int mine = tot[2 * tid] + tot[2 * tid + 1];
+  part[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int excl = part[tid] - mine;
+  const int o0 = excl, o1 = excl + tot[2 * tid];
+  __syncthreads();
+  tot[2 * tid] = o0;
+  tot[2 * tid + 1] = o1;
+  __syncthreads();
+}
+
 // counts [chunks][E + 1] in, each chunk's first slot per bucket out
 __global__ void __launch_bounds__(kRouteThreads)
 route_scan_kernel(int32_t* __restrict__ counts, int chunks, int E, int32_t* __restrict__ offsets) {
@@ -1144,36 +1168,21 @@ route_scan_kernel(int32_t* __restrict__ counts, int chunks, int E, int32_t* __re
     tot[x] = run;
   }
   __syncthreads();
-  // exclusive prefix over buckets 0 .. E (thread t holds buckets 2t, 2t + 1)
-  const int mine = tot[2 * tid] + tot[2 * tid + 1];
-  part[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const int excl = part[tid] - mine;
-  const int o0 = excl, o1 = excl + tot[2 * tid];
-  __syncthreads();
-  tot[2 * tid] = o0;
-  tot[2 * tid + 1] = o1;
-  __syncthreads();
+  route_bucket_prefix(tot, part);
   for (int x = tid; x <= E; x += kRouteThreads) offsets[x] = tot[x];
   for (int i = tid; i < chunks * (E + 1); i += kRouteThreads) counts[i] += tot[i % (E + 1)];
 }
 
-__global__ void __launch_bounds__(kRouteThreads)
-route_scatter_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int chunk,
-                     const int32_t* __restrict__ starts, int32_t* __restrict__ perm,
-                     uint8_t* __restrict__ zero_out, int64_t row_bytes) {
-  __shared__ int base[kRouteMaxE + 1];
-  __shared__ int wcnt[kRouteWaves * (kRouteMaxE + 1)];
+// The chunk's rows in steps of 1024: a row's slot is its bucket's running
+// slot base[b], plus the same-bucket rows of earlier waves of the step, plus
+// its rank among the same-bucket lanes of its wave.
+__device__ __forceinline__ void route_scatter_chunk(const int32_t* __restrict__ idx, int rows, int mr,
+                                                    int E, int chunk, int* base, int* wcnt,
+                                                    int32_t* __restrict__ perm,
+                                                    uint8_t* __restrict__ zero_out, int64_t row_bytes) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  for (int x = tid; x <= E; x += kRouteThreads) base[x] = starts[blockIdx.x * (E + 1) + x];
   const int q0 = blockIdx.x * chunk;
   const int q1 = min(rows, q0 + chunk);
   for (int qb = q0; qb < q1; qb += kRouteThreads) {
@@ -1206,6 +1215,53 @@ route_scatter_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, i
     }
     __syncthreads();
   }
+}
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_scatter_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int chunk,
+                     const int32_t* __restrict__ starts, int32_t* __restrict__ perm,
+                     uint8_t* __restrict__ zero_out, int64_t row_bytes) {
+  __shared__ int base[kRouteMaxE + 1];
+  __shared__ int wcnt[kRouteWaves * (kRouteMaxE + 1)];
+  for (int x = threadIdx.x; x <= E; x += kRouteThreads) base[x] = starts[blockIdx.x * (E + 1) + x];
+  route_scatter_chunk(idx, rows, mr, E, chunk, base, wcnt, perm, zero_out, row_bytes);
+}
+
+// The scan folded into the scatter, for small count tables (chunks x (E + 1)
+// at most kRouteFusedCounts): every workgroup reads the whole table, takes
+// the buckets' totals and its chunk's share of the rows before it, and runs
+// the bucket prefix itself; workgroup 0 writes offsets.  Same slots as the
+// scan kernel, one launch fewer.
+constexpr int kRouteFusedCounts = 4096;
+
+__global__ void __launch_bounds__(kRouteThreads)
+route_scan_scatter_kernel(const int32_t* __restrict__ idx, int rows, int mr, int E, int chunk,
+                          const int32_t* __restrict__ counts, int chunks,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                          uint8_t* __restrict__ zero_out, int64_t row_bytes) {
+  __shared__ int tot[2 * kRouteThreads];
+  __shared__ int part[kRouteThreads];
+  __shared__ int base[kRouteMaxE + 1];
+  __shared__ int wcnt[kRouteWaves * (kRouteMaxE + 1)];
+  const int tid = threadIdx.x;
+  for (int x = tid; x < 2 * kRouteThreads; x += kRouteThreads) {
+    int run = 0, before = 0;
+    if (x <= E) {
+      for (int c = 0; c < chunks; ++c) {
+        if (c == (int)blockIdx.x) before = run;
+        run += counts[c * (E + 1) + x];
+      }
+      base[x] = before;
+    }
+    tot[x] = run;
+  }
+  __syncthreads();
+  route_bucket_prefix(tot, part);
+  for (int x = tid; x <= E; x += kRouteThreads) {
+    base[x] += tot[x];
+    if (blockIdx.x == 0) offsets[x] = tot[x];
+  }
+  route_scatter_chunk(idx, rows, mr, E, chunk, base, wcnt, perm, zero_out, row_bytes);
 }
 
 int64_t route_chunk_rows(int64_t rows) {
@@ -1368,6 +1424,12 @@ hipError_t launch_moe_route(const int32_t* idx, int64_t entries, int64_t rows_pe
   const int chunks = (int)((rows + chunk - 1) / chunk);
   route_count_kernel<<<chunks, kRouteThreads, 0, s>>>(idx, (int)rows, (int)rows_per_entry, (int)e,
                                                       (int)chunk, scratch);
+  if ((int64_t)chunks * (e + 1) <= kRouteFusedCounts) {
+    route_scan_scatter_kernel<<<chunks, kRouteThreads, 0, s>>>(
+        idx, (int)rows, (int)rows_per_entry, (int)e, (int)chunk, scratch, chunks, offsets, perm,
+        reinterpret_cast<uint8_t*>(zero_out), row_bytes);
+    return hipGetLastError();
+  }
   route_scan_kernel<<<1, kRouteThreads, 0, s>>>(scratch, chunks, (int)e, offsets);
   route_scatter_kernel<<<chunks, kRouteThreads, 0, s>>>(idx, (int)rows, (int)rows_per_entry, (int)e,
                                                         (int)chunk, scratch, perm,
