@@ -49,32 +49,13 @@ template <> struct Mfma<kBF16> {
   static __device__ __forceinline__ f32x4 run(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // Accumulator pinned to AGPRs (see mfma_gemm_fast_kernel).  The operands
-  // are VGPRs written by LDS loads (ordered by s_waitcnt) or by VALU code at
-  // least a k-step earlier.
-  static __device__ __forceinline__ void run_agpr(V8 a, V8 b, f32x4& c) {
-    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  }
 };
 template <> struct Mfma<kF16> {
   using V8 = f16x8;
   static __device__ __forceinline__ f32x4 run(V8 a, V8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ void run_agpr(V8 a, V8 b, f32x4& c) {
-    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  }
 };
-
-// Wait states around the pinned-accumulator MFMAs, which the compiler cannot
-// see: before the first MFMA (the accumulators were just zeroed by VALU
-// writes) and before the accumulators are read back (an MFMA result needs
-// more than a dozen wait states before another instruction may read it).
-// The scheduling barrier keeps every instruction on its side.
-__device__ __forceinline__ void mfma_fence() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // element offset of chunk c (8 elements) of row r inside a 64-wide LDS tile
 __device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
@@ -423,12 +404,18 @@ mfma_gemm_kernel(const void* __restrict__ a_base, const uint8_t* __restrict__ wc
 //     MFMAs are written with AGPR-constrained operands so the register
 //     allocator keeps every accumulator in place (left to itself it splits
 //     them between the two files and moves them around every k-step).
-constexpr int kAStageBytes = BM * BK * 2;  // 32 KB of 16-bit A per stage
 constexpr int kAStages = 4;                // LDS stages of A
 constexpr int kBLoadsPerStep = 4;          // weight loads issued per k-step and wave
 constexpr int kPackCodeBlock = 1024;       // packed codes per 32-column tile and k-step
 constexpr int kPackScaleBlock = 128;       // packed scales per 32-column tile and k-step
 
+// The 32x32x16 MFMA with its accumulator pinned to AGPRs, as inline asm (the
+// register allocator then keeps the 256 accumulators of a 256-row tile in
+// place).  The compiler sees neither the instruction's latency nor its
+// hazards: the operands are VGPRs written by LDS loads (ordered by waits) or
+// by VALU code a k-step earlier, and mfma32_fence() plus the empty asm that
+// ties each accumulator after it keep every read of the results behind their
+// wait states.
 template <int DT> struct Mfma32;
 template <> struct Mfma32<kBF16> {
   static __device__ __forceinline__ void run_agpr(bf16x8 a, bf16x8 b, f32x16& c) {
