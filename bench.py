@@ -61,7 +61,7 @@ M, N, K = 2048, 14336, 4096
 # includes, source_hash), else it is reported
 # as null.  Summary and commands: profiles/hbm_traffic_qqmm_gemm_and_qmv.txt.
 MEASURED_TRAFFIC = {
-    "gemm": ("gemm.hip", "4de1bef093eca3fc", 360639434),
+    "gemm": ("gemm.hip", "5234486403a77559", 360639669),
     "qmv": ("qmv.hip", "d60a195df5353e3e", 33206718),
     "qmv_packed": ("qmv_packed.hip", "3e6aa809d46492b5", 33226101),
 }
