@@ -224,8 +224,10 @@ def test_qqmm_prefill_2048x14336x4096_sampled():
 
 # ------------------------------------------------------------------ routing / gather
 
+# (3000, 300, 4): 12 chunks x 301 counts, the scan folded into the scatter near
+# its table limit; (4096, 1024, 2): 8 x 1025 counts, count / scan / scatter
 @pytest.mark.parametrize("t,e,top_k", [(1, 1, 1), (257, 8, 2), (4096, 8, 2), (3000, 64, 4),
-                                        (100, 5, 3)])
+                                        (100, 5, 3), (3000, 300, 4), (4096, 1024, 2)])
 def test_moe_route_bit_exact(t, e, top_k):
     say(f"moe_route t={t} e={e} top_k={top_k}")
     idx = W.expert_indices(t, e, top_k, seed=t + e)
