@@ -26,7 +26,11 @@ def _cuda():
 @pytest.mark.parametrize("shape,dtype", [((0,), torch.bfloat16), ((1,), torch.bfloat16),
                                          ((7,), torch.float16), ((33, 77), torch.float16),
                                          ((1000003,), torch.float32),
-                                         ((4096, 4096), torch.bfloat16)])
+                                         ((4096, 4096), torch.bfloat16),
+                                         # several rounds of the grid-stride loop, with
+                                         # single chunks and a scalar tail after them
+                                         ((14336, 4096), torch.bfloat16),
+                                         ((16777216 + 5 * 262144 * 8 + 13,), torch.float16)])
 def test_tensor_amax(shape, dtype):
     say(f"tensor_amax {shape} {dtype}")
     x = W.normal(shape, 3.0, 7, oracle_dtype(dtype), outlier_frac=0.001, outlier_mult=50.0)
