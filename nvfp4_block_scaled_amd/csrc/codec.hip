@@ -339,7 +339,11 @@ __device__ __forceinline__ void dequantize_one(uint32_t word, uint32_t s, float 
   store8<DT>(out, h, o);
 }
 
-// One lane per half group (one code dword), two in flight per iteration.
+// One lane per half group (one code dword), four in flight per lane, strided
+// by the grid so that every store instruction of a wave writes 1 KB
+// contiguously (four consecutive half groups per lane made each store stride
+// 64 bytes: 15.6 us against 10.8 for a 4096 x 4096 weight; two in flight
+// 10.7-10.8, four 10.45-10.5).
 template <int DT>
 __global__ void __launch_bounds__(kThreads)
 dequantize_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -347,15 +351,17 @@ dequantize_kernel(const uint32_t* __restrict__ codes, const uint8_t* __restrict_
   const float dec = global_decode(gscale);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; h + stride < halves; h += 2 * stride) {
-    uint32_t w0 = __builtin_nontemporal_load(codes + h);
-    uint32_t w1 = __builtin_nontemporal_load(codes + h + stride);
-    uint32_t s0 = scales[h >> 1];
-    uint32_t s1 = scales[(h + stride) >> 1];
-    dequantize_one<DT>(w0, s0, dec, h, out);
-    dequantize_one<DT>(w1, s1, dec, h + stride, out);
+  for (; h + 3 * stride < halves; h += 4 * stride) {
+    uint32_t w[4], sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(codes + h + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = scales[(h + u * stride) >> 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dequantize_one<DT>(w[u], sc[u], dec, h + u * stride, out);
   }
-  if (h < halves) dequantize_one<DT>(__builtin_nontemporal_load(codes + h), scales[h >> 1], dec, h, out);
+  for (; h < halves; h += stride)
+    dequantize_one<DT>(__builtin_nontemporal_load(codes + h), scales[h >> 1], dec, h, out);
 }
 
 int grid_for(int64_t work, int per_block, int max_blocks) {
@@ -450,7 +456,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, int64_
                              const float* g, void* out, int dt, hipStream_t s) {
   const int64_t halves = rows * k / 8;
   if (halves == 0) return hipSuccess;
-  int blocks = grid_for(halves, kThreads * 2, 1 << 20);
+  int blocks = grid_for(halves, kThreads * 4, 1 << 20);
   const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
   switch (dt) {
     case kF32: dequantize_kernel<kF32><<<blocks, kThreads, 0, s>>>(c32, scales, halves, g, out); break;
